@@ -1,0 +1,239 @@
+"""CPU oracle for one tensor-parallel rank's Megatron-style layer forward.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg are the only callers.  Nothing here is shared
+with, or imported by, the GPU library.
+
+Everything is computed in fp64 from bf16 inputs widened exactly: the GEMM and
+activations live in ``oracle.c`` (triple loop, k ascending, no FMA); this
+module strings them together the way the pages define the layer:
+
+* "Megatron-LM 深度学习与源码分析文档", part 2 (核心并行技术) section 2 (Tensor
+  Parallel): column split W = [W_1..W_p], Y_i = X W_i, all-gather
+  Y = [Y_1..Y_p]; row split W = [W_1; ..; W_p], X = [X_1..X_p], Y_i = X_i W_i,
+  Y = sum_i Y_i; [Q,K,V] = X W_qkv with num_heads/TP heads per rank;
+  MLP Z = phi(X W_1), Y = Z W_2 with fc1 column-parallel and fc2 row-parallel.
+* "ai阅读megatron": Column/RowParallelLinear forward call F.linear(x, weight)
+  (weights stored [out x in]); the MoE layer forward (router logits, top-k,
+  dispatch, expert MLPs, weighted combine); TransformerConfig
+  (activation_func = F.gelu, gated_linear_unit, num_query_groups).
+* "快速入门" section 5.1: linear_fc1 = [gate_proj ; up_proj],
+  linear_qkv = [q ; k ; v]; down_proj (fc2) split along its input dimension.
+
+Readings where the pages leave a step open (each listed in the design notes):
+exact-erf GeLU; SwiGLU = silu(first half) * second half with each rank holding
+[gate_r ; up_r]; row-parallel partials carry no bias and b_2 is added once after
+the sum; the stored fc1->fc2 activation Z is bf16 (chained mode rounds it);
+MoE routing = softmax over all experts then top-k by probability (ties to the
+lower expert index), weights not renormalised, tokens ascending within an expert.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+ACT_NONE, ACT_GELU, ACT_SWIGLU = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = os.path.join(_HERE, "liboracle.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run oracle/build.py (or __graft_entry__.build())")
+        lib = ctypes.CDLL(path)
+        i64, vp = ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_linear.argtypes = [vp, i64, vp, i64, vp, ctypes.c_int, i64, i64, i64, vp, i64]
+        lib.oracle_round_bf16.argtypes = [vp, i64, vp]
+        lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_f64.restype = ctypes.c_double
+        lib.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+        lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
+        lib.oracle_gelu.argtypes = [ctypes.c_double]
+        lib.oracle_gelu.restype = ctypes.c_double
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        lib.oracle_silu.restype = ctypes.c_double
+        _lib = lib
+    return _lib
+
+
+# ----------------------------------------------------------------------------- scalars
+def gelu(x: float) -> float:
+    return _load().oracle_gelu(float(x))
+
+
+def silu(x: float) -> float:
+    return _load().oracle_silu(float(x))
+
+
+def f64_to_bf16(x: float) -> int:
+    return int(_load().oracle_f64_to_bf16(float(x)))
+
+
+def bf16_to_f64(h: int) -> float:
+    return _load().oracle_bf16_to_f64(int(h))
+
+
+def widen(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> exact float64 values."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """fp64 -> bf16 bit patterns, round to nearest, ties to even."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().oracle_round_bf16(a.ctypes.data, a.size, out.ctypes.data)
+    return out
+
+
+# ----------------------------------------------------------------------------- one linear
+def _rowpitch(a: np.ndarray) -> int:
+    assert a.dtype == np.uint16 and a.ndim == 2 and a.strides[1] == 2, "2-D bf16 array with unit column stride"
+    return a.strides[0] // 2
+
+
+def linear(X: np.ndarray, Wt: np.ndarray, bias: np.ndarray | None = None, act: int = ACT_NONE) -> np.ndarray:
+    """act(X . Wt^T + bias) in fp64.  X [M x K], Wt [N x K] ([out x in]); SWIGLU halves N (rows [gate; up])."""
+    M, K = X.shape
+    N, K2 = Wt.shape
+    assert K == K2, "inner dimensions differ"
+    if act == ACT_SWIGLU:
+        assert N % 2 == 0
+    nout = N // 2 if act == ACT_SWIGLU else N
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.uint16)
+        assert bias.shape == (N,)
+    Y = np.empty((M, nout), dtype=np.float64)
+    if M and nout:
+        _load().oracle_linear(X.ctypes.data, _rowpitch(X), Wt.ctypes.data, _rowpitch(Wt),
+                              None if bias is None else bias.ctypes.data, act, M, N, K, Y.ctypes.data, nout)
+    return Y
+
+
+# ----------------------------------------------------------------------------- tensor-parallel pieces
+def column_shard(Wt: np.ndarray, p: int, r: int) -> np.ndarray:
+    """Rank r's rows of a column-parallel weight stored [out x in] (output dimension split)."""
+    n = Wt.shape[0] // p
+    return Wt[r * n:(r + 1) * n]
+
+
+def row_shard(Wt: np.ndarray, p: int, r: int) -> np.ndarray:
+    """Rank r's columns of a row-parallel weight stored [out x in] (input dimension split)."""
+    k = Wt.shape[1] // p
+    return Wt[:, r * k:(r + 1) * k]
+
+
+def column_parallel(X, Wt, bias, p: int, act: int = ACT_NONE):
+    """Y_r = act(X W_r + b_r) for every rank r (Wt rank-major [p*N_l x K]); returns the list of Y_r."""
+    out = []
+    for r in range(p):
+        b = None if bias is None else column_shard(bias.reshape(-1, 1), p, r).reshape(-1)
+        out.append(linear(X, column_shard(Wt, p, r), b, act))
+    return out
+
+
+def row_parallel_partials(Z_list, Wt, p: int):
+    """P_r = Z_r . W_r (no bias) for every rank r, W_r the r-th input-dimension block of Wt [N x p*K_l]."""
+    return [linear(Z_list[r], row_shard(Wt, p, r)) for r in range(p)]
+
+
+def row_parallel_sum(partials, bias=None) -> np.ndarray:
+    """Y = sum_r P_r (+ b once), summed in fp64 in rank order."""
+    Y = np.zeros_like(partials[0])
+    for P in partials:
+        Y = Y + P
+    if bias is not None:
+        Y = Y + widen(bias)[None, :]
+    return Y
+
+
+def mlp(X, W1t, b1, W2t, b2, act: int, p: int, r0: int = 0, r1: int | None = None):
+    """The p-way tensor-parallel MLP, shards r0..r1-1, chained through bf16 Z.
+
+    W1t is rank-major [p*N1 x H] (N1 = F/p, or 2F/p holding [gate_r ; up_r] for SWIGLU);
+    W2t is [H x F] with rank r owning input columns r*F/p .. (r+1)*F/p.
+    Returns dict(Z=[bf16 Z_r], P=[fp64 P_r], Y=fp64 sum + b2 when all shards were computed else None).
+    """
+    r1 = p if r1 is None else r1
+    N1 = W1t.shape[0] // p
+    Z, P = [], []
+    for r in range(r0, r1):
+        b = None if b1 is None else b1[r * N1:(r + 1) * N1]
+        Zr = round_bf16(linear(X, W1t[r * N1:(r + 1) * N1], b, act))
+        Z.append(Zr)
+        P.append(linear(Zr, row_shard(W2t, p, r)))
+    Y = row_parallel_sum(P, b2) if (r0, r1) == (0, p) else None
+    return dict(Z=Z, P=P, Y=Y)
+
+
+def qkv(X, Wqkv_t, bias, nq_local: int, ng_local: int, head_dim: int):
+    """[Q_r | K_r | V_r] = X W_qkv,r + b for one rank: nq_local query heads and ng_local key/value groups."""
+    if ng_local <= 0 or nq_local % ng_local:
+        raise ValueError("query heads per rank must be a multiple of key/value groups per rank")
+    n = (nq_local + 2 * ng_local) * head_dim
+    assert Wqkv_t.shape[0] == n
+    Y = linear(X, Wqkv_t, bias)
+    q, k = nq_local * head_dim, ng_local * head_dim
+    return Y, (Y[:, :q], Y[:, q:q + k], Y[:, q + k:])
+
+
+# ----------------------------------------------------------------------------- MoE
+def moe_route(logits: np.ndarray, k: int):
+    """Softmax over all experts (fp64, max subtracted), top-k by probability, ties to the lower index.
+
+    Returns (expert_offsets [E+1] int32, token_idx [T*k] int32, token_w [T*k] fp64): rows grouped by
+    expert in ascending expert order, tokens ascending within an expert.
+    """
+    T, E = logits.shape
+    lg = np.asarray(logits, dtype=np.float32)
+    choice = []  # per token: list of (expert, weight)
+    for t in range(T):
+        row = [float(v) for v in lg[t]]
+        m = max(row)
+        ex = [math.exp(v - m) for v in row]
+        s = sum(ex)
+        prob = [v / s for v in ex]
+        order = sorted(range(E), key=lambda e: (-row[e], e))
+        choice.append([(e, prob[e]) for e in order[:k]])
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    idx, wts = [], []
+    for e in range(E):
+        for t in range(T):
+            for ee, w in choice[t]:
+                if ee == e:
+                    idx.append(t)
+                    wts.append(w)
+        offsets[e + 1] = len(idx)
+    return offsets, np.array(idx, dtype=np.int32), np.array(wts, dtype=np.float64)
+
+
+def moe_mlp(X, logits, W1t_list, W2t_list, k: int, tokens=None):
+    """out[t] = sum over the token's k experts of w * W2_e(SwiGLU(W1_e x_t)), Z chained through bf16.
+
+    ``tokens`` restricts the computation to a subset of token rows (all rows by default).
+    Returns (out fp64 [len(tokens) x H], routing tables).
+    """
+    T = X.shape[0]
+    offsets, idx, w = moe_route(logits, k)
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    pos = {int(t): i for i, t in enumerate(tokens)}
+    H_out = W2t_list[0].shape[0]
+    out = np.zeros((len(tokens), H_out), dtype=np.float64)
+    for e in range(len(W1t_list)):
+        rows = [(j, int(idx[j])) for j in range(offsets[e], offsets[e + 1]) if int(idx[j]) in pos]
+        if not rows:
+            continue
+        Xe = np.ascontiguousarray(X[[t for _, t in rows]])
+        Ze = round_bf16(linear(Xe, W1t_list[e], None, ACT_SWIGLU))
+        Ye = linear(Ze, W2t_list[e])
+        for n, (j, t) in enumerate(rows):
+            out[pos[t]] += w[j] * Ye[n]
+    return out, (offsets, idx, w)

@@ -1,0 +1,340 @@
+"""Pins of the CPU oracle to facts fixed outside it.
+
+Each test checks the oracle against something other than itself: exact
+rational arithmetic, closed forms of linear algebra, textbook function values
+(tests/golden/), the format definition of bfloat16, and the shard identities
+that the pages state for tensor parallelism ("Megatron-LM 深度学习与源码分析文档",
+part 2 section 2: Y = [Y_1..Y_p] for the column split, Y = sum_i Y_i for the
+row split).  Shapes are rectangular (M, N, K all different) so that a
+transposed operand, a swapped index or a dropped term fails.
+"""
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _bits(values):
+    """Exact bf16 bit patterns of values that are bf16-representable."""
+    a = np.asarray(values, dtype=np.float32)
+    u = a.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "value is not exactly representable in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def _frac(bits):
+    return [[Fraction(float(v)) for v in row] for row in synth.bf16_bits_to_f32(bits)]
+
+
+def _exact_linear(X, W, b=None):
+    Xf, Wf = _frac(X), _frac(W)
+    bf = [Fraction(float(v)) for v in synth.bf16_bits_to_f32(b)] if b is not None else None
+    M, K = len(Xf), len(Xf[0])
+    N = len(Wf)
+    out = [[sum((Xf[i][k] * Wf[j][k] for k in range(K)), Fraction(0)) for j in range(N)] for i in range(M)]
+    if bf is not None:
+        out = [[out[i][j] + bf[j] for j in range(N)] for i in range(M)]
+    return out
+
+
+# ----------------------------------------------------------------------------- GEMM
+@pytest.mark.parametrize("M,N,K", [(5, 7, 9), (3, 11, 16), (8, 2, 33), (1, 1, 1)])
+def test_gemm_matches_exact_rational(M, N, K):
+    X = synth.normal_bf16(11, M, K, 1.0)
+    W = synth.normal_bf16(12, N, K, 0.5)
+    b = synth.normal_bf16(13, 1, N, 0.25)[0]
+    Y = oracle.linear(X, W, b)
+    exact = _exact_linear(X, W, b)
+    Xa, Wa = np.abs(oracle.widen(X)), np.abs(oracle.widen(W))
+    for i in range(M):
+        for j in range(N):
+            bound = (K + 1) * 2.0 ** -53 * (float(np.dot(Xa[i], Wa[j])) + abs(float(oracle.widen(b)[j])))
+            assert abs(Fraction(Y[i, j]) - exact[i][j]) <= Fraction(bound) + Fraction(1, 2 ** 1000)
+
+
+def test_gemm_small_integers_exact():
+    M, N, K = 6, 10, 32
+    X = synth.ternary_bf16(21, M, K)
+    W = synth.ternary_bf16(22, N, K)
+    Y = oracle.linear(X, W)
+    exact = _exact_linear(X, W)
+    assert all(Fraction(Y[i, j]) == exact[i][j] for i in range(M) for j in range(N))
+
+
+def test_identity_weight_returns_input():
+    X = synth.normal_bf16(31, 7, 12, 1.0)
+    Y = oracle.linear(X, _bits(np.eye(12)))
+    assert np.array_equal(Y, oracle.widen(X))
+
+
+def test_permutation_weight_permutes_columns():
+    K = 9
+    perm = np.array([4, 0, 8, 2, 7, 1, 3, 6, 5, 0, 8])  # N = 11 rows, each picks one input column
+    W = np.zeros((len(perm), K), dtype=np.float32)
+    W[np.arange(len(perm)), perm] = 1.0
+    X = synth.normal_bf16(32, 5, K, 1.0)
+    Y = oracle.linear(X, _bits(W))
+    assert np.array_equal(Y, oracle.widen(X)[:, perm])
+
+
+def test_rank_one_closed_form():
+    u = np.array([1, -2, 0.5, 3])        # M = 4
+    v = np.array([2, 1, -1, 0.25, 4])    # K = 5
+    a = np.array([1, 0.5, -3])           # N = 3
+    bvec = np.array([-1, 2, 0.5, 1, 0.125])
+    X, W = _bits(np.outer(u, v)), _bits(np.outer(a, bvec))
+    Y = oracle.linear(X, W)
+    assert np.array_equal(Y, float(np.dot(v, bvec)) * np.outer(u, a))
+
+
+def test_linearity_in_x():
+    X1 = synth.ternary_bf16(41, 4, 24)
+    X2 = synth.ternary_bf16(42, 4, 24)
+    W = synth.normal_bf16(43, 6, 24, 0.5)
+    s = oracle.widen(X1) + oracle.widen(X2)  # entries in {-2..2}: exact in bf16
+    Xs = _bits(s)
+    assert np.allclose(oracle.linear(Xs, W), oracle.linear(X1, W) + oracle.linear(X2, W), rtol=0, atol=1e-12)
+
+
+def test_bias_is_added_exactly_once():
+    X = np.zeros((3, 8), dtype=np.uint16)
+    W = synth.normal_bf16(51, 5, 8, 1.0)
+    b = synth.normal_bf16(52, 1, 5, 1.0)[0]
+    assert np.array_equal(oracle.linear(X, W, b), np.tile(oracle.widen(b), (3, 1)))
+
+
+def test_strided_views_are_read_with_their_pitch():
+    big = synth.normal_bf16(53, 9, 40, 1.0)
+    W = synth.normal_bf16(54, 6, 16, 1.0)
+    view = big[2:7, 8:24]
+    assert np.array_equal(oracle.linear(view, W), oracle.linear(np.ascontiguousarray(view), W))
+
+
+# ----------------------------------------------------------------------------- activations
+def _one_by_one(x, act, w=(1.0,)):
+    X = _bits([[x]])
+    W = _bits([[v] for v in w])
+    return oracle.linear(X, W, None, act)[0, 0]
+
+
+def test_gelu_matches_normal_cdf_table():
+    for x, phi in _golden("normal_cdf.txt"):
+        x, phi = float(x), float(phi)
+        assert abs(_one_by_one(x, oracle.ACT_GELU) - x * phi) <= 4e-16 * x
+        assert abs(_one_by_one(-x, oracle.ACT_GELU) - (-x * (1 - phi))) <= 4e-16 * x
+
+
+def test_gelu_is_the_erf_form_not_tanh():
+    tanh_gelu = 0.5 * (1 + math.tanh(math.sqrt(2 / math.pi) * (1 + 0.044715)))
+    assert abs(oracle.gelu(1.0) - tanh_gelu) > 1e-4
+    assert oracle.gelu(0.0) == 0.0
+    for x in (0.3, 1.7, 4.0):
+        assert abs((oracle.gelu(x) - oracle.gelu(-x)) - x) < 1e-15 * max(1, x)
+    assert oracle.gelu(40.0) == 40.0 and oracle.gelu(-40.0) == 0.0
+
+
+def test_silu_matches_logistic_closed_form():
+    for x, sig in _golden("logistic.txt"):
+        x, sig = float(x), float(sig)
+        assert abs(oracle.silu(x) - x * sig) <= 2e-16 * abs(x)
+    assert oracle.silu(0.0) == 0.0
+    for x in (0.4, 2.5):
+        assert abs((oracle.silu(x) - oracle.silu(-x)) - x) < 1e-15
+
+
+def test_swiglu_gates_the_first_half_and_multiplies_the_second():
+    # Wt = [gate ; up] rows: gate pre-activation x, up pre-activation c*x.
+    sig1 = float(_golden("logistic.txt")[0][1])
+    sig2 = float(_golden("logistic.txt")[1][1])
+    assert abs(_one_by_one(1.0, oracle.ACT_SWIGLU, (1.0, 2.0)) - 2.0 * sig1) < 1e-15
+    assert abs(_one_by_one(1.0, oracle.ACT_SWIGLU, (2.0, 1.0)) - 2.0 * sig2) < 1e-15
+
+
+def test_swiglu_zero_gate_and_equal_gate_up():
+    X = synth.normal_bf16(61, 4, 16, 1.0)
+    G = synth.normal_bf16(62, 6, 16, 0.3)
+    zero = np.zeros_like(G)
+    assert np.all(oracle.linear(X, np.vstack([zero, G]), None, oracle.ACT_SWIGLU) == 0.0)
+    g = oracle.linear(X, G)
+    z = oracle.linear(X, np.vstack([G, G]), None, oracle.ACT_SWIGLU)
+    assert np.allclose(z, g * g / (1 + np.exp(-g)), rtol=1e-14, atol=0)
+
+
+# ----------------------------------------------------------------------------- bf16 rounding
+def test_bf16_round_to_nearest_even_table():
+    for row in _golden("bf16_rne.txt"):
+        value = float(eval(row[0], {"__builtins__": {}}))  # exact binary fractions written as expressions
+        if row[0].startswith("-0.0"):
+            value = -0.0
+        assert oracle.f64_to_bf16(value) == int(row[1], 16), row
+        assert oracle.f64_to_bf16(-value) == int(row[1], 16) ^ 0x8000, row
+    assert oracle.f64_to_bf16(float("nan")) & 0x7FFF > 0x7F80
+
+
+def test_bf16_round_trip_is_identity_on_bf16_values():
+    bits = np.arange(0, 0x7F80, 7, dtype=np.uint16)
+    back = oracle.round_bf16(oracle.widen(bits))
+    assert np.array_equal(back, bits)
+
+
+def test_bf16_rounding_is_nearest():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(4000) * 10.0 ** rng.integers(-30, 30, 4000)
+    r = oracle.widen(oracle.round_bf16(x))
+    # the nearest bf16 value: no bf16 neighbour is closer
+    bits = oracle.round_bf16(x)
+    up, dn = oracle.widen(bits + 1), oracle.widen(bits - 1)
+    assert np.all(np.abs(r - x) <= np.abs(up - x)) and np.all(np.abs(r - x) <= np.abs(dn - x))
+
+
+# ----------------------------------------------------------------------------- shard identities
+@pytest.mark.parametrize("p", [2, 4])
+def test_column_split_concat_equals_unsharded(p):
+    X = synth.normal_bf16(71, 9, 24, 1.0)
+    W = synth.normal_bf16(72, 4 * p, 24, 0.2)
+    b = synth.normal_bf16(73, 1, 4 * p, 0.1)[0]
+    for act in (oracle.ACT_NONE, oracle.ACT_GELU):
+        Ys = oracle.column_parallel(X, W, b, p, act)
+        assert np.array_equal(np.hstack(Ys), oracle.linear(X, W, b, act))
+
+
+def test_swiglu_column_split_with_rank_local_gate_up_equals_unsharded():
+    p, F, H = 4, 12, 20
+    X = synth.normal_bf16(74, 7, H, 1.0)
+    G = synth.normal_bf16(75, F, H, 0.2)
+    U = synth.normal_bf16(76, F, H, 0.2)
+    full = oracle.linear(X, np.vstack([G, U]), None, oracle.ACT_SWIGLU)
+    fl = F // p
+    rank_major = np.vstack([np.vstack([G[r * fl:(r + 1) * fl], U[r * fl:(r + 1) * fl]]) for r in range(p)])
+    Ys = oracle.column_parallel(X, rank_major, None, p, oracle.ACT_SWIGLU)
+    assert np.array_equal(np.hstack(Ys), full)
+
+
+@pytest.mark.parametrize("p", [2, 3])
+def test_row_split_sum_equals_unsharded(p):
+    M, N, K = 5, 7, 12 * p
+    Z = synth.normal_bf16(81, M, K, 1.0)
+    W = synth.normal_bf16(82, N, K, 0.2)
+    b = synth.normal_bf16(83, 1, N, 0.1)[0]
+    Zs = [np.ascontiguousarray(Z[:, r * (K // p):(r + 1) * (K // p)]) for r in range(p)]
+    Y = oracle.row_parallel_sum(oracle.row_parallel_partials(Zs, W, p), b)
+    ref = oracle.linear(Z, W, b)
+    bound = (K + p + 1) * 2.0 ** -53 * (np.abs(oracle.widen(Z)) @ np.abs(oracle.widen(W)).T + np.abs(oracle.widen(b)))
+    assert np.all(np.abs(Y - ref) <= bound)
+
+
+def test_mlp_tp2_equals_tp1():
+    M, H, F = 6, 16, 24
+    X = synth.normal_bf16(91, M, H, 1.0)
+    W1 = synth.normal_bf16(92, F, H, 0.2)
+    b1 = synth.normal_bf16(93, 1, F, 0.1)[0]
+    W2 = synth.normal_bf16(94, H, F, 0.2)
+    b2 = synth.normal_bf16(95, 1, H, 0.1)[0]
+    y1 = oracle.mlp(X, W1, b1, W2, b2, oracle.ACT_GELU, p=1)["Y"]
+    y2 = oracle.mlp(X, W1, b1, W2, b2, oracle.ACT_GELU, p=2)["Y"]
+    assert np.allclose(y1, y2, rtol=0, atol=1e-13)
+    half = oracle.mlp(X, W1, b1, W2, b2, oracle.ACT_GELU, p=2, r0=1, r1=2)
+    assert half["Y"] is None and len(half["P"]) == 1
+
+
+def test_mlp_zero_gate_gives_bias():
+    M, H, F = 4, 8, 6
+    X = synth.normal_bf16(96, M, H, 1.0)
+    W1 = np.vstack([np.zeros((F, H), np.uint16), synth.normal_bf16(97, F, H, 0.2)])
+    W2 = synth.normal_bf16(98, H, F, 0.2)
+    b2 = synth.normal_bf16(99, 1, H, 0.1)[0]
+    y = oracle.mlp(X, W1, None, W2, b2, oracle.ACT_SWIGLU, p=1)["Y"]
+    assert np.array_equal(y, np.tile(oracle.widen(b2), (M, 1)))
+
+
+def test_qkv_split_and_gqa_rule():
+    d, nq, ng, H = 4, 4, 2, 16
+    X = synth.normal_bf16(101, 3, H, 1.0)
+    W = synth.normal_bf16(102, (nq + 2 * ng) * d, H, 0.2)
+    Y, (q, k, v) = oracle.qkv(X, W, None, nq, ng, d)
+    assert q.shape == (3, nq * d) and k.shape == (3, ng * d) and v.shape == (3, ng * d)
+    assert np.array_equal(np.hstack([q, k, v]), oracle.linear(X, W))
+    with pytest.raises(ValueError):
+        oracle.qkv(X, W[: (3 + 2 * 2) * d], None, 3, 2, d)
+
+
+# ----------------------------------------------------------------------------- MoE
+def _softmax_decimal(row):
+    getcontext().prec = 50
+    ex = [Decimal(float(v)).exp() for v in row]
+    s = sum(ex)
+    return [float(e / s) for e in ex]
+
+
+def test_moe_routing_counts_distinct_and_brute_force_topk():
+    T, E, k = 37, 8, 2
+    logits = synth.normal_f32(111, T, E)
+    offsets, idx, w = oracle.moe_route(logits, k)
+    assert offsets[0] == 0 and offsets[-1] == T * k and np.all(np.diff(offsets) >= 0)
+    per_token = {t: [] for t in range(T)}
+    for e in range(E):
+        seg = idx[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(seg) > 0), "tokens ascending within an expert"
+        for j in range(offsets[e], offsets[e + 1]):
+            per_token[int(idx[j])].append((e, float(w[j])))
+    for t in range(T):
+        probs = _softmax_decimal(logits[t])
+        brute = sorted(range(E), key=lambda e: (-probs[e], e))[:k]
+        got = per_token[t]
+        assert sorted(e for e, _ in got) == sorted(brute)
+        for e, wt in got:
+            assert abs(wt - probs[e]) < 1e-15
+
+
+def test_moe_identical_experts_scale_the_dense_mlp():
+    T, H, F, E, k = 9, 8, 6, 4, 2
+    X = synth.normal_bf16(121, T, H, 1.0)
+    logits = synth.normal_f32(122, T, E)
+    W1 = synth.normal_bf16(123, 2 * F, H, 0.3)
+    W2 = synth.normal_bf16(124, H, F, 0.3)
+    out, (offsets, idx, w) = oracle.moe_mlp(X, logits, [W1] * E, [W2] * E, k)
+    dense = oracle.mlp(X, W1, None, W2, None, oracle.ACT_SWIGLU, p=1)["Y"]
+    wsum = np.zeros(T)
+    for j in range(len(idx)):
+        wsum[idx[j]] += w[j]
+    assert np.allclose(out, wsum[:, None] * dense, rtol=1e-14, atol=1e-15)
+
+
+def test_moe_single_expert_top1_is_dense_swiglu_mlp():
+    T, H, F = 5, 8, 6
+    X = synth.normal_bf16(131, T, H, 1.0)
+    logits = synth.normal_f32(132, T, 1)
+    W1 = synth.normal_bf16(133, 2 * F, H, 0.3)
+    W2 = synth.normal_bf16(134, H, F, 0.3)
+    out, _ = oracle.moe_mlp(X, logits, [W1], [W2], 1)
+    dense = oracle.mlp(X, W1, None, W2, None, oracle.ACT_SWIGLU, p=1)["Y"]
+    assert np.array_equal(out, dense)
+
+
+def test_moe_token_subset_matches_full():
+    T, H, F, E = 12, 8, 4, 3
+    X = synth.normal_bf16(141, T, H, 1.0)
+    logits = synth.normal_f32(142, T, E)
+    W1 = [synth.normal_bf16(150 + e, 2 * F, H, 0.3) for e in range(E)]
+    W2 = [synth.normal_bf16(160 + e, H, F, 0.3) for e in range(E)]
+    full, _ = oracle.moe_mlp(X, logits, W1, W2, 2)
+    sub, _ = oracle.moe_mlp(X, logits, W1, W2, 2, tokens=[3, 7, 11])
+    assert np.array_equal(sub, full[[3, 7, 11]])
