@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Throughput of one tensor-parallel rank's layer forward (bf16) on one MI355X.
+
+A step is one pass of the per-rank hot path over one batch of synthetic input
+already resident in HBM: QKV column-parallel GEMM + bias, attention
+out-projection row-parallel GEMM, fc1 column-parallel GEMM with fused bias +
+GeLU (or SwiGLU), fc2 row-parallel GEMM (and for the MoE workload the router
+and the grouped expert GEMMs).  The default workload is the GPT-345M-shaped
+layer at TP=1 with 4096 tokens; --workload picks another.
+
+Prints one JSON line: TFLOP/s (algorithmic 2*M*N*K over the step's GEMMs),
+the dominant kernel's roofline position (HIP events around each GEMM inside
+the timed region, on the stream the kernels are launched on), and the CPU
+oracle timed on a bounded sample of the same workload on this host's cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 FLOP/clk
+HBM_PEAK_GBS = 8000.0
+METRIC = "TFLOP/s per TP-rank QKV+MLP forward (bf16) and % of MI355X MFMA peak"
+WORKLOADS = {"gpt345m": 1, "gpt3_175b_rank0": 2, "llama70b_rank0": 3, "moe": 4, "tiny": 0}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "gemm.h"):
+        with open(os.path.join(ROOT, "megatron_tensor_transformer_03_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel_label):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    e = rec.get(workload, {}).get(kernel_label)
+    if not e or e.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return e["hbm_bytes_per_launch"]
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle on a bounded row sample of the same workload; TFLOP/s of algorithmic work done."""
+    import numpy as np
+    import oracle
+    import synth
+    d = w.dims
+    t0 = time.perf_counter()
+    if "E" in d:
+        # route everything, then expert MLPs for token chunks until the budget is spent
+        logits = synth.host_rows(w.tensors["logits"])
+        E, F, H, k = d["E"], d["F"], d["H"], d["k"]
+        W1 = [synth.host_rows(w.tensors["W1t"], range(e * 2 * F, (e + 1) * 2 * F)) for e in range(E)]
+        W2 = [synth.host_rows(w.tensors["W2t"], range(e * H, (e + 1) * H)) for e in range(E)]
+        X = synth.host_rows(w.tensors["X"])
+        t0 = time.perf_counter()
+        done, tok = 0, 0
+        per_token = k * 2 * (2 * F * H + H * F)
+        while tok < d["T"] and time.perf_counter() - t0 < budget_s:
+            toks = list(range(tok, min(tok + 4, d["T"])))
+            oracle.moe_mlp(X, logits, W1, W2, k, tokens=toks)
+            tok += len(toks)
+            done += len(toks) * per_token
+        el = time.perf_counter() - t0
+        return dict(value=done / el / 1e12, unit="TFLOP/s", cores=oracle.num_threads(), kind="oracle",
+                    sample=f"{tok} of {d['T']} tokens (routing + both expert MLPs per token), fp64, {el:.1f} s")
+    p = d["p"]
+    h = {k: synth.host_rows(v) for k, v in w.tensors.items() if k not in ("X", "ctx")}
+    t0 = time.perf_counter()
+    rows_done, flop = 0, 0
+    per_row = w.flop // d["M"]  # every GEMM of the step has M = tokens rows
+    chunk = 16
+    while rows_done < d["M"] and time.perf_counter() - t0 < budget_s:
+        rows = list(range(rows_done, min(rows_done + chunk, d["M"])))
+        X = synth.host_rows(w.tensors["X"], rows)
+        if "nq" in d:
+            oracle.qkv(X, h["Wqkv_t"], h.get("bqkv"), d["nq"] // p, d["ng"] // p, d["d"])
+        if "ctx" in w.tensors:
+            oracle.linear(synth.host_rows(w.tensors["ctx"], rows), h["Wo_t"], h.get("bo") if p == 1 else None)
+        if d["ranks"] == "all":
+            oracle.mlp(X, h["W1t"], h.get("b1"), h["W2t"], h.get("b2"), d["act"], p)
+        else:
+            Z = oracle.round_bf16(oracle.linear(X, h["W1t"], h.get("b1"), d["act"]))
+            oracle.linear(Z, h["W2t"])
+        rows_done += len(rows)
+        flop += len(rows) * per_row
+    el = time.perf_counter() - t0
+    return dict(value=flop / el / 1e12, unit="TFLOP/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{rows_done} of {d['M']} token rows through every GEMM of the step, fp64, {el:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gpt345m", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Each rank's share is the single-GPU kernel; see the sharding notes in the design document.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import megatron_tensor_transformer_03_amd as mtp
+    from megatron_tensor_transformer_03_amd.layer import RankForward
+    import synth
+    from synth import configs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mtp.lib()  # fail loudly if the HIP library is missing
+
+    if args.copy_calibration:
+        n = 1 << 28  # 1 GiB of fp32
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": 5}), flush=True)
+        return
+
+    w = configs.by_index(WORKLOADS[args.workload])
+    inputs = synth.device_inputs(w)
+    run = RankForward(w.dims, inputs)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        run.step()
+    torch.cuda.synchronize()
+
+    # per-kernel events inside the timed region, on the stream the library launches on
+    ev = []
+
+    def mark(label):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ev[-1].append((label, e))
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        ev.append([])
+        run.step(mark)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+
+    per_kernel = {}
+    for marks in ev:
+        for (label, e0), (_, e1) in zip(marks[:-1], marks[1:]):
+            per_kernel.setdefault(label, []).append(e0.elapsed_time(e1))
+    flop_by_label = {}
+    for label, m, n, k in w.gemms:
+        flop_by_label[label] = flop_by_label.get(label, 0) + 2 * m * n * k
+    if "E" in w.dims:
+        flop_by_label = {"moe_mlp": w.flop}
+    if w.dims.get("ranks") == "all" and w.dims.get("p", 1) > 1:
+        flop_by_label = {"mlp": w.flop}
+    avg = {lb: sum(v) / len(v) for lb, v in per_kernel.items()}
+    dom = max((lb for lb in avg if lb in flop_by_label), key=lambda lb: avg[lb])
+    achieved = flop_by_label[dom] / (avg[dom] * 1e-3) / 1e12
+    flop = w.flop
+    value = flop / (ms * 1e-3) / 1e12
+    traffic = measured_traffic(w.name, dom)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "desc": w.desc, "flop_per_step": flop,
+                   "pct_of_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+                   "gemms": [[lb, m, n, k] for lb, m, n, k in w.gemms],
+                   "per_gemm_us": {lb: round(1000 * v, 2) for lb, v in avg.items()},
+                   "per_gemm_tflops": {lb: round(flop_by_label[lb] / (avg[lb] * 1e-3) / 1e12, 1)
+                                       for lb in avg if lb in flop_by_label}},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * mtp.h - one tensor-parallel rank's share of a Megatron-style Transformer
+ * layer forward, on an AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the pages' statement of tensor parallelism:
+ *  - "Megatron-LM 深度学习与源码分析文档", part 2 (核心并行技术), section 2
+ *    (Tensor Parallel): ColumnParallelLinear W = [W_1..W_p], Y_i = X W_i with
+ *    an optional all-gather Y = [Y_1..Y_p]; RowParallelLinear
+ *    W = [W_1; ..; W_p], X = [X_1..X_p], Y_i = X_i W_i, Y = sum_i Y_i (an
+ *    all-reduce); QKV projection [Q,K,V] = X W_qkv with num_heads/TP heads
+ *    per rank; MLP Z = phi(X W_1), Y = Z W_2 with fc1 column-parallel (4H/TP,
+ *    wider for SwiGLU) and fc2 row-parallel.
+ *  - "ai阅读megatron": ColumnParallelLinear / RowParallelLinear forward
+ *    (F.linear(x, weight): weights stored [out x in]); TransformerConfig
+ *    (activation_func = F.gelu, gated_linear_unit, num_query_groups,
+ *    num_moe_experts, moe_router_topk); MoELayer forward (router logits,
+ *    top-k, dispatch, expert MLPs, weighted combine).
+ *  - "快速入门" section 5.1 (weight mapping): linear_qkv = [q; k; v],
+ *    linear_fc1 = [gate_proj; up_proj], down_proj split along its input.
+ *
+ * On one GPU the cross-rank collectives become identities: the all-gather is
+ * each shard writing its own column block of one output (through ldy), and
+ * the all-reduce is an fp32 sum of the shards' partial products in rank order.
+ *
+ * Conventions for every call:
+ *  - bf16 tensors are raw bit patterns (uint16_t), row-major with the given
+ *    row pitch (in elements).  Weights are [out x in].  Accumulation is fp32;
+ *    every conversion to bf16 rounds to nearest, ties to even.
+ *  - Pointers are device pointers owned by the caller.  The library never
+ *    allocates, frees, synchronises, or keeps a pointer after returning.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL is the default stream)
+ *    and the call returns at once.  Faults surface at the caller's next sync.
+ *  - Every argument is validated before anything is enqueued; on an error
+ *    nothing is launched and no output is touched.  Requirements: required
+ *    pointers non-NULL; sizes >= 1; K (the inner dimension) and every row
+ *    pitch multiples of 8; pitches at least the row width; bf16/fp32 pointers
+ *    16-byte aligned; the current device a gfx950.
+ *  - Outputs must not alias inputs.  Calls are reentrant; the only shared
+ *    state is an immutable per-device property cache filled on first use.
+ */
+#ifndef MTP_H_
+#define MTP_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MTP_ABI_VERSION 1
+
+typedef uint16_t mtp_bf16;
+
+typedef enum {
+  MTP_OK = 0,
+  MTP_ERR_NULL = 1,        /* a required pointer is NULL */
+  MTP_ERR_SHAPE = 2,       /* a size, pitch, rank range or head/group rule is violated */
+  MTP_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+  MTP_ERR_UNSUPPORTED = 4, /* no device, or the current device is not a gfx950 */
+  MTP_ERR_LAUNCH = 5       /* the runtime refused a kernel launch */
+} mtp_status;
+
+typedef enum { MTP_ACT_NONE = 0, MTP_ACT_GELU = 1, MTP_ACT_SWIGLU = 2 } mtp_act;
+
+/*
+ * ColumnParallelLinear forward of one shard (part 2 section 2, Y_i = X W_i),
+ * with its bias and activation fused:
+ *   Y[M x Nout] = act(X[M x K] . Wt[N x K]^T + bias[N])
+ *   NONE, GELU (exact erf form):  Nout = N.
+ *   SWIGLU: the N rows of Wt are [gate (N/2 rows) ; up (N/2 rows)] and
+ *           Y[i][j] = silu(pre[i][j]) * pre[i][N/2 + j], Nout = N/2; N even.
+ * bias may be NULL.  The all-gather of the shards is the identity when each
+ * shard r writes to Y + r * Nout with ldy = p * Nout.
+ */
+mtp_status mtp_column_linear(const mtp_bf16* X, int64_t ldx, const mtp_bf16* Wt, int64_t ldw,
+                             const mtp_bf16* bias, mtp_bf16* Y, int64_t ldy, int64_t M, int64_t N,
+                             int64_t K, mtp_act act, void* stream);
+
+/*
+ * RowParallelLinear partial product of one shard (Y_i = X_i W_i) and the
+ * local form of the all-reduce Y = sum_i Y_i:
+ *   P = Z[M x Kp] . Wt[N x Kp]^T in fp32, no bias.  Wt is this rank's input
+ *   block of the full [N x K] weight: pass Wt + r*Kp with ldw = K.
+ *   accumulate = 0: Yacc = P;  accumulate = 1: Yacc += P  (fp32).
+ *   If Y != NULL (the last shard): Y = bf16(Yacc_after + bias), bias added
+ *   once here (bias may be NULL).  Yacc may be NULL only when
+ *   accumulate == 0 and Y != NULL (a single shard: Y = bf16(P + bias)).
+ * Summing the shards by calling r = 0..p-1 in order on one stream is
+ * deterministic.
+ */
+mtp_status mtp_row_linear_partial(const mtp_bf16* Z, int64_t ldz, const mtp_bf16* Wt, int64_t ldw,
+                                  float* Yacc, int64_t ldacc, int accumulate, const mtp_bf16* bias,
+                                  mtp_bf16* Y, int64_t ldy, int64_t M, int64_t N, int64_t Kp,
+                                  void* stream);
+
+/*
+ * Tensor-parallel MLP, Z = phi(X W_1), Y = Z W_2, for shards r0..r1-1 of a
+ * p-way split, computed in turn:
+ *   Z_r   = act(X . W1t_r^T + b1_r)       -> Z_ws (bf16, [M x F/p])
+ *   Yacc (+)= Z_r . W2t_r^T               (fp32, rank order)
+ * X is [M x H] (pitch H).  W1t is rank-major [p * N1 x H] with N1 = F/p
+ * (GELU/NONE) or 2F/p holding [gate_r ; up_r] (SWIGLU); b1 is [p * N1] or
+ * NULL.  W2t is [H x F] (pitch F); rank r owns its columns r*F/p..(r+1)*F/p.
+ * When [r0, r1) = [0, p) the last shard writes Y = bf16(Yacc + b2) (b2 may be
+ * NULL); with p = 1 Yacc may be NULL and Y is written directly.  Otherwise Y
+ * must be NULL and Yacc holds the partial sum over [r0, r1).  Requires
+ * F % p == 0, 0 <= r0 < r1 <= p, H % 8 == 0, (F/p) % 8 == 0.
+ */
+mtp_status mtp_mlp_forward(const mtp_bf16* X, int64_t M, int64_t H, int64_t F, int p, int r0, int r1,
+                           const mtp_bf16* W1t, const mtp_bf16* b1, const mtp_bf16* W2t,
+                           const mtp_bf16* b2, mtp_act act, mtp_bf16* Z_ws, float* Yacc, mtp_bf16* Y,
+                           void* stream);
+
+/*
+ * QKV projection of one rank (part 2 section 2, [Q,K,V] = X W_qkv, heads/TP
+ * per rank; grouped-query attention keeps num_query_groups/TP key/value
+ * groups per rank):
+ *   QKV[M x Nq] = X[M x H] . Wqkv_t^T + bias, Nq = (nq_local + 2*ng_local) * head_dim,
+ * columns [Q_r (nq_local*head_dim) | K_r (ng_local*head_dim) | V_r (same)].
+ * Wqkv_t is [Nq x H] with pitch ldw; bias is [Nq] or NULL; output pitch ldo.
+ * Requires nq_local % ng_local == 0 and head_dim % 8 == 0.
+ */
+mtp_status mtp_qkv_forward(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t H, const mtp_bf16* Wqkv_t,
+                           int64_t ldw, const mtp_bf16* bias, int nq_local, int ng_local, int head_dim,
+                           mtp_bf16* QKV, int64_t ldo, void* stream);
+
+/*
+ * MoE router ("ai阅读megatron", MoELayer forward: router logits, top-k):
+ * softmax over the E experts of each token (fp32), then the k most probable
+ * experts (ties to the lower index).  Outputs, rows grouped by expert in
+ * ascending expert order and ascending token order within an expert:
+ *   expert_offsets [E+1] (int32, offsets[0] = 0, offsets[E] = T*k),
+ *   token_idx [T*k] (int32 token of each dispatched row),
+ *   token_w  [T*k] (fp32 softmax probability, not renormalised).
+ * logits is [T x E] fp32 (pitch E).  Requires 1 <= k <= min(E, 8), E <= 64.
+ */
+mtp_status mtp_moe_route(const float* logits, int64_t T, int E, int k, int32_t* expert_offsets,
+                         int32_t* token_idx, float* token_w, void* stream);
+
+/*
+ * Expert MLPs of an MoE layer as grouped GEMMs over the routed rows, and the
+ * weighted combine:
+ *   for each dispatched row j of expert e (token t = token_idx[j]):
+ *     z_j = SwiGLU(X[t] . W1t_e^T)                 -> Z_ws[j] (bf16, [T*k x F])
+ *     Yacc[t] += token_w[j] * (z_j . W2t_e^T)      (fp32; Yacc is zeroed first)
+ *   Y = bf16(Yacc)  ([T x H]).
+ * W1t is [E][2F x H] ([gate; up] per expert), W2t is [E][H x F].  The routing
+ * tables are device arrays as written by mtp_moe_route (no host copy is
+ * made).  With k = 2 every output element is the sum of two products added
+ * to zero, so the fp32 result does not depend on their order.
+ */
+mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, int64_t F, int k,
+                               const int32_t* expert_offsets, const int32_t* token_idx,
+                               const float* token_w, const mtp_bf16* W1t, const mtp_bf16* W2t,
+                               mtp_bf16* Z_ws, float* Yacc, mtp_bf16* Y, void* stream);
+
+/* Static text for a status code. */
+const char* mtp_status_string(mtp_status s);
+/* Detail of the last failing call on this thread ("" if none). */
+const char* mtp_last_error(void);
+/* MTP_ABI_VERSION of the built library. */
+int mtp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTP_H_ */

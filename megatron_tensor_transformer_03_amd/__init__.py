@@ -1,0 +1,140 @@
+"""One tensor-parallel rank's share of a Megatron-style Transformer layer forward on MI355X (gfx950).
+
+Thin Python binding over ``libmtp.so`` (C ABI in ``include/mtp.h``).  The
+functions carry the C names and only marshal arguments: sizes and row pitches
+are read from the torch tensors, pointers are passed through, and the work is
+enqueued on the tensors' current HIP stream.  Every step runs in the library's
+kernels; if the library is missing or refuses a call, an exception is raised.
+PyTorch provides device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+ACT_NONE, ACT_GELU, ACT_SWIGLU = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmtp.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "mtp.h")
+
+_lib = None
+
+
+class MTPError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        super().__init__(f"{fn} failed: status {status} ({detail})")
+        self.status = status
+
+
+def lib():
+    """The loaded libmtp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python megatron_tensor_transformer_03_amd/build.py` "
+                               "or __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        sig = {
+            "mtp_column_linear": [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, ci, vp],
+            "mtp_row_linear_partial": [vp, i64, vp, i64, vp, i64, ci, vp, vp, i64, i64, i64, i64, vp],
+            "mtp_mlp_forward": [vp, i64, i64, i64, ci, ci, ci, vp, vp, vp, vp, ci, vp, vp, vp, vp],
+            "mtp_qkv_forward": [vp, i64, i64, i64, vp, i64, vp, ci, ci, ci, vp, i64, vp],
+            "mtp_moe_route": [vp, i64, ci, ci, vp, vp, vp, vp],
+            "mtp_moe_mlp_forward": [vp, i64, i64, ci, i64, ci, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ci
+        L.mtp_status_string.argtypes = [ci]
+        L.mtp_status_string.restype = ctypes.c_char_p
+        L.mtp_last_error.argtypes = []
+        L.mtp_last_error.restype = ctypes.c_char_p
+        L.mtp_abi_version.restype = ci
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> list[str]:
+    """Function names declared in include/mtp.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|mtp_status|int)\s+(mtp_\w+)\s*\(", text, re.M)))
+
+
+def _check(fn, status):
+    if status != 0:
+        L = lib()
+        raise MTPError(fn, status, L.mtp_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _ld(t):
+    assert t.dim() == 2 and t.stride(1) == 1, "2-D tensor with unit column stride"
+    return t.stride(0)
+
+
+def _stream(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def mtp_column_linear(X, Wt, bias, Y, act=ACT_NONE):
+    """Y = act(X . Wt^T + bias); Wt [N x K] ([gate; up] rows for SWIGLU, then Y is [M x N/2])."""
+    M, K = X.shape
+    N = Wt.shape[0]
+    _check("mtp_column_linear", lib().mtp_column_linear(
+        _ptr(X), _ld(X), _ptr(Wt), _ld(Wt), _ptr(bias), _ptr(Y), _ld(Y), M, N, K, act, _stream(X)))
+    return Y
+
+
+def mtp_row_linear_partial(Z, Wt, Yacc=None, accumulate=False, bias=None, Y=None):
+    """Yacc (=|+=) Z . Wt^T in fp32; if Y is given, Y = bf16(Yacc + bias).  Wt is this rank's [N x Kp] view."""
+    M, Kp = Z.shape
+    N = Wt.shape[0]
+    _check("mtp_row_linear_partial", lib().mtp_row_linear_partial(
+        _ptr(Z), _ld(Z), _ptr(Wt), _ld(Wt), _ptr(Yacc), _ld(Yacc) if Yacc is not None else 0, int(bool(accumulate)),
+        _ptr(bias), _ptr(Y), _ld(Y) if Y is not None else 0, M, N, Kp, _stream(Z)))
+    return Y if Y is not None else Yacc
+
+
+def mtp_mlp_forward(X, W1t, b1, W2t, b2, act, p, r0, r1, Z_ws, Yacc=None, Y=None):
+    """Shards r0..r1-1 of the p-way MLP: Z_r = act(X W1_r + b1_r); Yacc (+)= Z_r W2_r; Y on the last shard."""
+    M, H = X.shape
+    F = W2t.shape[1]
+    _check("mtp_mlp_forward", lib().mtp_mlp_forward(
+        _ptr(X), M, H, F, p, r0, r1, _ptr(W1t), _ptr(b1), _ptr(W2t), _ptr(b2), act, _ptr(Z_ws), _ptr(Yacc), _ptr(Y),
+        _stream(X)))
+    return Y if Y is not None else Yacc
+
+
+def mtp_qkv_forward(X, Wqkv_t, bias, nq_local, ng_local, head_dim, QKV):
+    """[Q_r | K_r | V_r] = X . Wqkv_t^T + bias for one rank."""
+    M, H = X.shape
+    _check("mtp_qkv_forward", lib().mtp_qkv_forward(
+        _ptr(X), _ld(X), M, H, _ptr(Wqkv_t), _ld(Wqkv_t), _ptr(bias), nq_local, ng_local, head_dim, _ptr(QKV),
+        _ld(QKV), _stream(X)))
+    return QKV
+
+
+def mtp_moe_route(logits, k, expert_offsets, token_idx, token_w):
+    """Softmax + top-k routing tables of [T x E] fp32 logits (see include/mtp.h)."""
+    T, E = logits.shape
+    assert logits.stride(1) == 1 and logits.stride(0) == E
+    _check("mtp_moe_route", lib().mtp_moe_route(
+        _ptr(logits), T, E, k, _ptr(expert_offsets), _ptr(token_idx), _ptr(token_w), _stream(logits)))
+
+
+def mtp_moe_mlp_forward(X, E, F, k, expert_offsets, token_idx, token_w, W1t, W2t, Z_ws, Yacc, Y):
+    """Expert SwiGLU MLPs over the routed rows and the weighted combine into Y [T x H]."""
+    T, H = X.shape
+    _check("mtp_moe_mlp_forward", lib().mtp_moe_mlp_forward(
+        _ptr(X), T, H, E, F, k, _ptr(expert_offsets), _ptr(token_idx), _ptr(token_w), _ptr(W1t), _ptr(W2t),
+        _ptr(Z_ws), _ptr(Yacc), _ptr(Y), _stream(X)))
+    return Y

@@ -1,0 +1,252 @@
+// The C ABI (include/mtp.h): argument validation, then launches on the caller's stream.
+//
+// Every check runs before the first launch, so a rejected call enqueues
+// nothing and touches no output.  The only state is a per-device cache of
+// "is this a gfx950" filled on first use.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/mtp.h"
+#include "gemm.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mtp_status fail(mtp_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+constexpr int64_t kIntMax = 0x7FFFFFFF;
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_dev_ok[64];
+
+mtp_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(MTP_ERR_UNSUPPORTED, "no HIP device is available");
+  if (dev < 64) {
+    int c = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (c == 1) return MTP_OK;
+    if (c == 2) return fail(MTP_ERR_UNSUPPORTED, "device %d is not a gfx950", dev);
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return fail(MTP_ERR_UNSUPPORTED, "cannot read the properties of device %d", dev);
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  if (!ok) return fail(MTP_ERR_UNSUPPORTED, "device %d is %s, not a gfx950", dev, prop.gcnArchName);
+  return MTP_OK;
+}
+
+mtp_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  g_err[0] = 0;
+  return MTP_OK;
+}
+
+// A bf16 operand of `rows` x `cols` with pitch ld: non-NULL, aligned, pitch a multiple of 8 covering the row.
+mtp_status check_mat(const void* p, const char* name, int64_t cols, int64_t ld) {
+  if (!p) return fail(MTP_ERR_NULL, "%s is NULL", name);
+  if (misaligned(p)) return fail(MTP_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  if (ld < cols || ld % 8 != 0) return fail(MTP_ERR_SHAPE, "%s: pitch %lld must be >= %lld and a multiple of 8", name,
+                                            (long long)ld, (long long)cols);
+  return MTP_OK;
+}
+
+mtp_status check_vec(const void* p, const char* name) {
+  if (p && misaligned(p)) return fail(MTP_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return MTP_OK;
+}
+
+mtp_status check_dims(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1) return fail(MTP_ERR_SHAPE, "sizes must be >= 1 (M=%lld N=%lld K=%lld)", (long long)M,
+                                           (long long)N, (long long)K);
+  if (M > kIntMax || N > kIntMax || K > kIntMax) return fail(MTP_ERR_SHAPE, "a size exceeds 2^31-1");
+  if (K % 8 != 0) return fail(MTP_ERR_SHAPE, "the inner dimension %lld is not a multiple of 8", (long long)K);
+  return MTP_OK;
+}
+
+#define TRY(x)                     \
+  do {                             \
+    mtp_status s_ = (x);           \
+    if (s_ != MTP_OK) return s_;   \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int mtp_abi_version(void) { return MTP_ABI_VERSION; }
+
+const char* mtp_last_error(void) { return g_err; }
+
+const char* mtp_status_string(mtp_status s) {
+  switch (s) {
+    case MTP_OK: return "ok";
+    case MTP_ERR_NULL: return "a required pointer is NULL";
+    case MTP_ERR_SHAPE: return "invalid size, pitch or rank range";
+    case MTP_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MTP_ERR_UNSUPPORTED: return "no gfx950 device";
+    case MTP_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+mtp_status mtp_column_linear(const mtp_bf16* X, int64_t ldx, const mtp_bf16* Wt, int64_t ldw, const mtp_bf16* bias,
+                             mtp_bf16* Y, int64_t ldy, int64_t M, int64_t N, int64_t K, mtp_act act, void* stream) {
+  TRY(check_dims(M, N, K));
+  if (act != MTP_ACT_NONE && act != MTP_ACT_GELU && act != MTP_ACT_SWIGLU)
+    return fail(MTP_ERR_SHAPE, "unknown activation %d", (int)act);
+  if (act == MTP_ACT_SWIGLU && N % 2 != 0) return fail(MTP_ERR_SHAPE, "SwiGLU needs an even N (got %lld)", (long long)N);
+  const int64_t nout = act == MTP_ACT_SWIGLU ? N / 2 : N;
+  TRY(check_mat(X, "X", K, ldx));
+  TRY(check_mat(Wt, "Wt", K, ldw));
+  TRY(check_mat(Y, "Y", nout, ldy));
+  TRY(check_vec(bias, "bias"));
+  TRY(check_device());
+  mtp::GemmParams p;
+  p.A = X; p.lda = ldx; p.B = Wt; p.ldb = ldw; p.bias = bias; p.Y = Y; p.ldy = ldy;
+  p.M = (int)M; p.Nout = (int)nout; p.K = (int)K; p.up_offset = nout;
+  p.act = act == MTP_ACT_GELU ? 1 : 0;
+  return launched(mtp::gemm(p, act == MTP_ACT_SWIGLU ? mtp::MODE_SWIGLU : mtp::MODE_COL, (hipStream_t)stream),
+                  "column linear");
+}
+
+mtp_status mtp_row_linear_partial(const mtp_bf16* Z, int64_t ldz, const mtp_bf16* Wt, int64_t ldw, float* Yacc,
+                                  int64_t ldacc, int accumulate, const mtp_bf16* bias, mtp_bf16* Y, int64_t ldy,
+                                  int64_t M, int64_t N, int64_t Kp, void* stream) {
+  TRY(check_dims(M, N, Kp));
+  TRY(check_mat(Z, "Z", Kp, ldz));
+  TRY(check_mat(Wt, "Wt", Kp, ldw));
+  if (!Yacc && !Y) return fail(MTP_ERR_NULL, "Yacc and Y are both NULL");
+  if (!Yacc && accumulate) return fail(MTP_ERR_NULL, "accumulate needs Yacc");
+  if (Yacc) TRY(check_mat(Yacc, "Yacc", N, ldacc));
+  if (Y) TRY(check_mat(Y, "Y", N, ldy));
+  TRY(check_vec(bias, "bias"));
+  TRY(check_device());
+  mtp::GemmParams p;
+  p.A = Z; p.lda = ldz; p.B = Wt; p.ldb = ldw; p.Yacc = Yacc; p.ldacc = ldacc; p.accumulate = accumulate ? 1 : 0;
+  p.bias = bias; p.Y = Y; p.ldy = ldy; p.M = (int)M; p.Nout = (int)N; p.K = (int)Kp;
+  return launched(mtp::gemm(p, mtp::MODE_ROW, (hipStream_t)stream), "row-parallel partial");
+}
+
+mtp_status mtp_mlp_forward(const mtp_bf16* X, int64_t M, int64_t H, int64_t F, int p, int r0, int r1,
+                           const mtp_bf16* W1t, const mtp_bf16* b1, const mtp_bf16* W2t, const mtp_bf16* b2,
+                           mtp_act act, mtp_bf16* Z_ws, float* Yacc, mtp_bf16* Y, void* stream) {
+  if (p < 1 || F < 1 || F % p != 0) return fail(MTP_ERR_SHAPE, "F=%lld must be a positive multiple of p=%d", (long long)F, p);
+  if (r0 < 0 || r1 > p || r0 >= r1) return fail(MTP_ERR_SHAPE, "rank range [%d, %d) is not inside [0, %d)", r0, r1, p);
+  if (act != MTP_ACT_NONE && act != MTP_ACT_GELU && act != MTP_ACT_SWIGLU)
+    return fail(MTP_ERR_SHAPE, "unknown activation %d", (int)act);
+  const int64_t Fl = F / p;
+  const int64_t N1 = act == MTP_ACT_SWIGLU ? 2 * Fl : Fl;
+  TRY(check_dims(M, N1, H));
+  TRY(check_dims(M, H, Fl));
+  if ((int64_t)p * N1 > kIntMax) return fail(MTP_ERR_SHAPE, "fc1 weight has too many rows");
+  TRY(check_mat(X, "X", H, H));
+  TRY(check_mat(W1t, "W1t", H, H));
+  TRY(check_mat(W2t, "W2t", F, F));
+  TRY(check_mat(Z_ws, "Z_ws", Fl, Fl));
+  TRY(check_vec(b1, "b1"));
+  TRY(check_vec(b2, "b2"));
+  const bool full = r0 == 0 && r1 == p;
+  if (!full && Y) return fail(MTP_ERR_SHAPE, "Y is written only when all p shards are computed");
+  if (!Yacc && !(full && p == 1 && Y)) return fail(MTP_ERR_NULL, "Yacc is NULL");
+  if (Yacc) TRY(check_mat(Yacc, "Yacc", H, H));
+  if (Y) TRY(check_mat(Y, "Y", H, H));
+  TRY(check_device());
+  hipStream_t st = (hipStream_t)stream;
+  for (int r = r0; r < r1; ++r) {
+    mtp::GemmParams f1;
+    f1.A = X; f1.lda = H; f1.B = W1t + (int64_t)r * N1 * H; f1.ldb = H;
+    f1.bias = b1 ? b1 + (int64_t)r * N1 : nullptr;
+    f1.Y = Z_ws; f1.ldy = Fl; f1.M = (int)M; f1.Nout = (int)Fl; f1.K = (int)H; f1.up_offset = Fl;
+    f1.act = act == MTP_ACT_GELU ? 1 : 0;
+    mtp_status s = launched(mtp::gemm(f1, act == MTP_ACT_SWIGLU ? mtp::MODE_SWIGLU : mtp::MODE_COL, st), "fc1");
+    if (s != MTP_OK) return s;
+    mtp::GemmParams f2;
+    f2.A = Z_ws; f2.lda = Fl; f2.B = W2t + (int64_t)r * Fl; f2.ldb = F;
+    f2.Yacc = Yacc; f2.ldacc = H; f2.accumulate = r > r0 ? 1 : 0;
+    const bool last = full && r == p - 1;
+    f2.Y = last ? Y : nullptr; f2.ldy = H; f2.bias = last ? b2 : nullptr;
+    f2.M = (int)M; f2.Nout = (int)H; f2.K = (int)Fl;
+    s = launched(mtp::gemm(f2, mtp::MODE_ROW, st), "fc2");
+    if (s != MTP_OK) return s;
+  }
+  return MTP_OK;
+}
+
+mtp_status mtp_qkv_forward(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t H, const mtp_bf16* Wqkv_t, int64_t ldw,
+                           const mtp_bf16* bias, int nq_local, int ng_local, int head_dim, mtp_bf16* QKV, int64_t ldo,
+                           void* stream) {
+  if (nq_local < 1 || ng_local < 1 || head_dim < 1)
+    return fail(MTP_ERR_SHAPE, "heads, groups and head_dim must be >= 1");
+  if (nq_local % ng_local != 0)
+    return fail(MTP_ERR_SHAPE, "query heads per rank (%d) must be a multiple of key/value groups per rank (%d)",
+                nq_local, ng_local);
+  const int64_t N = ((int64_t)nq_local + 2 * (int64_t)ng_local) * head_dim;
+  return mtp_column_linear(X, ldx, Wqkv_t, ldw, bias, QKV, ldo, M, N, H, MTP_ACT_NONE, stream);
+}
+
+mtp_status mtp_moe_route(const float* logits, int64_t T, int E, int k, int32_t* expert_offsets, int32_t* token_idx,
+                         float* token_w, void* stream) {
+  if (!logits || !expert_offsets || !token_idx || !token_w) return fail(MTP_ERR_NULL, "a routing pointer is NULL");
+  if (misaligned(logits) || misaligned(expert_offsets) || misaligned(token_idx) || misaligned(token_w))
+    return fail(MTP_ERR_ALIGN, "routing arrays must be 16-byte aligned");
+  if (E < 1 || E > mtp::kMaxExperts) return fail(MTP_ERR_SHAPE, "E=%d must be in [1, %d]", E, mtp::kMaxExperts);
+  if (k < 1 || k > E || k > 8) return fail(MTP_ERR_SHAPE, "k=%d must be in [1, min(E, 8)]", k);
+  if (T < 1 || T * k > kIntMax) return fail(MTP_ERR_SHAPE, "T=%lld out of range", (long long)T);
+  TRY(check_device());
+  return launched(mtp::moe_route(logits, (int)T, E, k, expert_offsets, token_idx, token_w, (hipStream_t)stream),
+                  "router");
+}
+
+mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, int64_t F, int k,
+                               const int32_t* expert_offsets, const int32_t* token_idx, const float* token_w,
+                               const mtp_bf16* W1t, const mtp_bf16* W2t, mtp_bf16* Z_ws, float* Yacc, mtp_bf16* Y,
+                               void* stream) {
+  if (!expert_offsets || !token_idx || !token_w) return fail(MTP_ERR_NULL, "a routing table is NULL");
+  if (misaligned(expert_offsets) || misaligned(token_idx) || misaligned(token_w))
+    return fail(MTP_ERR_ALIGN, "routing tables must be 16-byte aligned");
+  if (E < 1 || E > mtp::kMaxExperts) return fail(MTP_ERR_SHAPE, "E=%d must be in [1, %d]", E, mtp::kMaxExperts);
+  if (k < 1 || k > E || k > 8) return fail(MTP_ERR_SHAPE, "k=%d must be in [1, min(E, 8)]", k);
+  TRY(check_dims(T, 2 * F, H));
+  TRY(check_dims(T, H, F));
+  if (T * k > kIntMax) return fail(MTP_ERR_SHAPE, "T*k exceeds 2^31-1");
+  TRY(check_mat(X, "X", H, H));
+  TRY(check_mat(W1t, "W1t", H, H));
+  TRY(check_mat(W2t, "W2t", F, F));
+  TRY(check_mat(Z_ws, "Z_ws", F, F));
+  TRY(check_mat(Yacc, "Yacc", H, H));
+  TRY(check_mat(Y, "Y", H, H));
+  TRY(check_device());
+  hipStream_t st = (hipStream_t)stream;
+  mtp_status s = launched(mtp::fill_zero_f32(Yacc, T, H, H, st), "zero Yacc");
+  if (s != MTP_OK) return s;
+  mtp::GemmParams f1;
+  f1.A = X; f1.lda = H; f1.a_rows = token_idx; f1.B = W1t; f1.ldb = H; f1.up_offset = F;
+  f1.Y = Z_ws; f1.ldy = F; f1.Nout = (int)F; f1.K = (int)H;
+  f1.group_offsets = expert_offsets; f1.groups = E; f1.group_stride_B = 2 * F * H;
+  s = launched(mtp::gemm_grouped(f1, mtp::MODE_SWIGLU, (int)(T * k), st), "grouped fc1");
+  if (s != MTP_OK) return s;
+  mtp::GemmParams f2;
+  f2.A = Z_ws; f2.lda = F; f2.B = W2t; f2.ldb = F; f2.Yacc = Yacc; f2.ldacc = H;
+  f2.row_w = token_w; f2.out_rows = token_idx; f2.Nout = (int)H; f2.K = (int)F;
+  f2.group_offsets = expert_offsets; f2.groups = E; f2.group_stride_B = H * F;
+  s = launched(mtp::gemm_grouped(f2, mtp::MODE_COMBINE, (int)(T * k), st), "grouped fc2");
+  if (s != MTP_OK) return s;
+  return launched(mtp::f32_to_bf16_rows(Yacc, H, Y, H, T, H, st), "combine to bf16");
+}
+
+}  // extern "C"

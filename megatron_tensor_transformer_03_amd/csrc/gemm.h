@@ -1,0 +1,48 @@
+// Internal interface of the GEMM kernel family (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtp {
+
+constexpr int kMaxExperts = 64;
+
+enum GemmMode { MODE_COL = 0, MODE_SWIGLU = 1, MODE_ROW = 2, MODE_COMBINE = 3 };
+
+// C = A . B^T over K, A [rows x K] (pitch lda, optional row gather), B [N x K] (pitch ldb).
+struct GemmParams {
+  const uint16_t* A = nullptr;
+  int64_t lda = 0;
+  const int32_t* a_rows = nullptr;  // A row of output row j is a_rows[j] (grouped fc1 gather)
+  const uint16_t* B = nullptr;
+  int64_t ldb = 0;
+  int64_t up_offset = 0;            // SWIGLU: row offset of the up half within B (= Nout)
+  const uint16_t* bias = nullptr;   // [N] (COL/ROW) or [2 * Nout] (SWIGLU)
+  uint16_t* Y = nullptr;            // bf16 output
+  int64_t ldy = 0;
+  float* Yacc = nullptr;            // fp32 partial / combine target
+  int64_t ldacc = 0;
+  const float* row_w = nullptr;     // COMBINE: weight of each row
+  const int32_t* out_rows = nullptr;// COMBINE: output row of each row
+  int M = 0;                        // rows (ungrouped)
+  int Nout = 0;                     // output columns (SWIGLU: half the B rows used)
+  int K = 0;
+  int act = 0;                      // COL: 0 none, 1 erf-GeLU
+  int accumulate = 0;               // ROW: Yacc += P
+  const int32_t* group_offsets = nullptr;  // grouped: [groups + 1] row offsets in device memory
+  int groups = 0;
+  int64_t group_stride_B = 0;       // grouped: elements between consecutive groups' B
+};
+
+hipError_t gemm(const GemmParams& p, int mode, hipStream_t st);
+// rows_upper: total rows over all groups (an upper bound is enough; spare tiles exit).
+hipError_t gemm_grouped(const GemmParams& p, int mode, int rows_upper, hipStream_t st);
+
+// MoE helpers (moe.hip).
+hipError_t moe_route(const float* logits, int T, int E, int k, int32_t* offsets, int32_t* token_idx,
+                     float* token_w, hipStream_t st);
+hipError_t fill_zero_f32(float* dst, int64_t rows, int64_t cols, int64_t ld, hipStream_t st);
+hipError_t f32_to_bf16_rows(const float* src, int64_t lds, uint16_t* dst, int64_t ldd, int64_t rows,
+                            int64_t cols, hipStream_t st);
+
+}  // namespace mtp

@@ -1,0 +1,169 @@
+// MoE routing and small elementwise kernels.
+//
+// Router ("ai阅读megatron", MoELayer forward: router logits -> top-k ->
+// dispatch): per token, softmax over the E experts in fp32 and the k largest
+// logits (softmax is monotone, so this is the k most probable experts; ties go
+// to the lower expert index).  The dispatch tables group rows by expert in
+// ascending expert order and keep tokens ascending within an expert, which
+// needs a stable scatter: one workgroup walks the tokens in 1024-token
+// chunks, ranks each token within its expert by wave ballots plus an
+// across-wave prefix, and carries the running per-expert base between chunks.
+// The work is O(T * E) and runs in a few microseconds; it is not a GEMM.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm.h"
+
+namespace mtp {
+
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kMaxTopK = 8;
+
+struct Choice {
+  uint64_t mask;        // bit e set if expert e was chosen
+  int e[kMaxTopK];      // chosen experts, most probable first
+  float w[kMaxTopK];    // their softmax probabilities
+};
+
+__device__ __forceinline__ void choose(const float* __restrict__ lg, int E, int k, Choice& c) {
+  float mx = lg[0];
+  for (int e = 1; e < E; ++e) mx = fmaxf(mx, lg[e]);
+  float sum = 0.f;
+  for (int e = 0; e < E; ++e) sum += expf(lg[e] - mx);
+  c.mask = 0;
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s) {
+    c.e[s] = -1;
+    c.w[s] = 0.f;
+    if (s < k) {
+      int best = -1;
+      float bv = 0.f;
+      for (int e = 0; e < E; ++e) {
+        if ((c.mask >> e) & 1ull) continue;
+        const float v = lg[e];
+        if (best < 0 || v > bv) { best = e; bv = v; }
+      }
+      c.mask |= 1ull << best;
+      c.e[s] = best;
+      c.w[s] = expf(bv - mx) / sum;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ token_idx,
+                                                              float* __restrict__ token_w) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int base[kMaxExperts];
+  __shared__ int wcnt[kMaxExperts][kRouteWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < kMaxExperts) cnt[tid] = 0;
+  __syncthreads();
+  // pass 1: tokens per expert (integer sums: order-free)
+  for (int t = tid; t < T; t += kRouteThreads) {
+    Choice c;
+    choose(logits + (int64_t)t * E, E, k, c);
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s)
+      if (s < k) atomicAdd(&cnt[c.e[s]], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      offsets[e] = run;
+      base[e] = run;
+      run += cnt[e];
+    }
+    offsets[E] = run;
+  }
+  __syncthreads();
+  // pass 2: stable scatter, 1024 tokens at a time; all lanes stay converged for the ballots
+  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < T; c0 += kRouteThreads) {
+    const int t = c0 + tid;
+    Choice c;
+    c.mask = 0;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) { c.e[s] = -1; c.w[s] = 0.f; }
+    if (t < T) choose(logits + (int64_t)t * E, E, k, c);
+    int rank[kMaxTopK];
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) rank[s] = 0;
+    for (int e = 0; e < E; ++e) {
+      const bool mine = (c.mask >> e) & 1ull;
+      const uint64_t b = __ballot(mine);
+      if (lane == 0) wcnt[e][wave] = __popcll(b);
+      const int r = __popcll(b & lt_mask);
+#pragma unroll
+      for (int s = 0; s < kMaxTopK; ++s)
+        if (c.e[s] == e) rank[s] = r;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+      if (s < k && t < T) {
+        const int e = c.e[s];
+        int pos = base[e] + rank[s];
+        for (int w = 0; w < wave; ++w) pos += wcnt[e][w];
+        token_idx[pos] = t;
+        token_w[pos] = c.w[s];
+      }
+    }
+    __syncthreads();
+    if (tid < E) {
+      int add = 0;
+      for (int w = 0; w < kRouteWaves; ++w) add += wcnt[tid][w];
+      base[tid] += add;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void fill_zero_kernel(float* __restrict__ dst, int64_t rows, int64_t cols, int64_t ld) {
+  const int64_t total = rows * cols;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / cols;
+    dst[r * ld + (i - r * cols)] = 0.f;
+  }
+}
+
+__global__ void f32_to_bf16_kernel(const float* __restrict__ src, int64_t lds, uint16_t* __restrict__ dst, int64_t ldd,
+                                   int64_t rows, int64_t cols4) {
+  const int64_t total = rows * cols4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / cols4, c = (i - r * cols4) * 4;
+    const float4 v = *reinterpret_cast<const float4*>(src + r * lds + c);
+    const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)v.x) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.y) << 16);
+    const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)v.z) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.w) << 16);
+    *reinterpret_cast<uint2*>(dst + r * ldd + c) = make_uint2(lo, hi);
+  }
+}
+
+static unsigned grid_for(int64_t n) {
+  int64_t b = (n + 255) / 256;
+  return (unsigned)(b < 1 ? 1 : (b > 8192 ? 8192 : b));
+}
+
+hipError_t moe_route(const float* logits, int T, int E, int k, int32_t* offsets, int32_t* token_idx, float* token_w,
+                     hipStream_t st) {
+  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, st, logits, T, E, k, offsets, token_idx, token_w);
+  return hipGetLastError();
+}
+
+hipError_t fill_zero_f32(float* dst, int64_t rows, int64_t cols, int64_t ld, hipStream_t st) {
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(rows * cols)), dim3(256), 0, st, dst, rows, cols, ld);
+  return hipGetLastError();
+}
+
+// cols must be a multiple of 4 and both pitches multiples of 4 (callers validate pitches as multiples of 8).
+hipError_t f32_to_bf16_rows(const float* src, int64_t lds, uint16_t* dst, int64_t ldd, int64_t rows, int64_t cols,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(grid_for(rows * cols / 4)), dim3(256), 0, st, src, lds, dst, ldd, rows,
+                     cols / 4);
+  return hipGetLastError();
+}
+
+}  // namespace mtp

@@ -1,0 +1,94 @@
+"""One rank's layer forward as a sequence of C-ABI calls (argument marshalling only).
+
+The per-rank hot path of a Megatron-style layer ("Megatron-LM 深度学习与源码分析文档",
+part 2 section 2): the QKV ColumnParallelLinear, the attention out-projection
+RowParallelLinear (its input, the attention context, is an input here: core
+attention is not part of this path), and the MLP with fc1 column-parallel
+(bias + GeLU or SwiGLU fused) and fc2 row-parallel.  For an MoE layer the
+router and the expert MLPs ("ai阅读megatron", MoELayer forward).
+
+``dims`` uses the keys of ``synth.configs``; ``inputs`` holds device tensors
+named as there.  Outputs are allocated once by ``RankForward`` and reused by
+every ``step()``.
+"""
+from __future__ import annotations
+
+import megatron_tensor_transformer_03_amd as mtp
+
+
+class RankForward:
+    """Buffers and launch sequence for one workload's per-rank forward on the current device."""
+
+    def __init__(self, dims: dict, inputs: dict):
+        import torch
+        self.d, self.t = dims, inputs
+        dev = next(iter(inputs.values())).device
+        bf, f32 = torch.bfloat16, torch.float32
+        self.out = {}
+        if "E" in dims:  # MoE expert MLP
+            T, H, E, F, k = dims["T"], dims["H"], dims["E"], dims["F"], dims["k"]
+            self.out.update(offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                            token_idx=torch.empty(T * k, dtype=torch.int32, device=dev),
+                            token_w=torch.empty(T * k, dtype=f32, device=dev),
+                            Z=torch.empty(T * k, F, dtype=bf, device=dev),
+                            Yacc=torch.empty(T, H, dtype=f32, device=dev),
+                            Y=torch.empty(T, H, dtype=bf, device=dev))
+            return
+        M, H, p = dims["M"], dims["H"], dims["p"]
+        if "nq" in dims:
+            nq_l, ng_l, d = dims["nq"] // p, dims["ng"] // p, dims["d"]
+            self.out["qkv"] = torch.empty(M, (nq_l + 2 * ng_l) * d, dtype=bf, device=dev)
+        if "ctx" in inputs:
+            if p == 1:
+                self.out["attn_out"] = torch.empty(M, H, dtype=bf, device=dev)
+            else:
+                self.out["attn_partial"] = torch.empty(M, H, dtype=f32, device=dev)
+        F_l = dims["F"] // p
+        self.out["Z"] = torch.empty(M, F_l, dtype=bf, device=dev)
+        if dims["ranks"] == "all":
+            self.out["Y"] = torch.empty(M, H, dtype=bf, device=dev)
+            if p > 1:  # fp32 sum over the shards
+                self.out["Yacc"] = torch.empty(M, H, dtype=f32, device=dev)
+        else:
+            self.out["mlp_partial"] = torch.empty(M, H, dtype=f32, device=dev)
+
+    def step(self, mark=None):
+        """Enqueue one forward.  ``mark(label)``, if given, is called before each launch and once at the end
+        (label None): a caller can record stream events there to time each GEMM."""
+        d, t, o = self.d, self.t, self.out
+        mark = mark or (lambda label: None)
+        if "E" in d:
+            mark("route")
+            mtp.mtp_moe_route(t["logits"], d["k"], o["offsets"], o["token_idx"], o["token_w"])
+            mark("moe_mlp")
+            mtp.mtp_moe_mlp_forward(t["X"], d["E"], d["F"], d["k"], o["offsets"], o["token_idx"], o["token_w"],
+                                    t["W1t"], t["W2t"], o["Z"], o["Yacc"], o["Y"])
+            mark(None)
+            return o
+        p = d["p"]
+        if "nq" in d:
+            mark("qkv")
+            mtp.mtp_qkv_forward(t["X"], t["Wqkv_t"], t.get("bqkv"), d["nq"] // p, d["ng"] // p, d["d"], o["qkv"])
+        if "ctx" in t:
+            mark("out_proj")
+            if p == 1:  # the whole layer: the all-reduce is the identity, bias added here
+                mtp.mtp_row_linear_partial(t["ctx"], t["Wo_t"], None, False, t.get("bo"), o["attn_out"])
+            else:       # this rank's fp32 partial of the all-reduce
+                mtp.mtp_row_linear_partial(t["ctx"], t["Wo_t"], o["attn_partial"])
+        if d["ranks"] == "all" and p > 1:
+            # every shard in turn; the all-reduce is the fp32 sum in rank order
+            mark("mlp")
+            mtp.mtp_mlp_forward(t["X"], t["W1t"], t.get("b1"), t["W2t"], t.get("b2"), d["act"], p, 0, p, o["Z"],
+                                o["Yacc"], o["Y"])
+        else:
+            # one shard (p = 1: the whole MLP): fc1 column linear with bias + activation fused, then fc2 as a
+            # row-parallel partial; with p = 1 the sum over shards is the identity and b2 is added in its epilogue
+            mark("fc1")
+            mtp.mtp_column_linear(t["X"], t["W1t"], t.get("b1"), o["Z"], d["act"])
+            mark("fc2")
+            if p == 1:
+                mtp.mtp_row_linear_partial(o["Z"], t["W2t"], None, False, t.get("b2"), o["Y"])
+            else:
+                mtp.mtp_row_linear_partial(o["Z"], t["W2t"], o["mlp_partial"])
+        mark(None)
+        return o

@@ -59,6 +59,7 @@ def _load():
         lib.oracle_gelu.restype = ctypes.c_double
         lib.oracle_silu.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
+        lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -78,6 +79,11 @@ def f64_to_bf16(x: float) -> int:
 
 def bf16_to_f64(h: int) -> float:
     return _load().oracle_bf16_to_f64(int(h))
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's loops use."""
+    return int(_load().oracle_num_threads())
 
 
 def widen(bits: np.ndarray) -> np.ndarray:

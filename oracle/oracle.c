@@ -24,6 +24,7 @@
  * rational arithmetic, closed forms and textbook values.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -80,7 +81,7 @@ void oracle_linear(const uint16_t *X, int64_t ldx, const uint16_t *Wt, int64_t l
                    const uint16_t *bias, int act, int64_t M, int64_t N, int64_t K, double *Y,
                    int64_t ldy) {
   const int64_t nout = act == ACT_SWIGLU ? N / 2 : N;
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for collapse(2) schedule(dynamic, 64)
   for (int64_t i = 0; i < M; ++i) {
     for (int64_t j = 0; j < nout; ++j) {
       double pre = 0.0;
@@ -109,3 +110,6 @@ void oracle_round_bf16(const double *src, int64_t n, uint16_t *dst) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) dst[i] = oracle_f64_to_bf16(src[i]);
 }
+
+/* Threads an OpenMP loop of this library uses (for reporting the CPU baseline's core count). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }

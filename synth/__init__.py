@@ -125,3 +125,34 @@ def gpu_normal_f32_(t, seed: int, r0: int = 0):
     if rc:
         raise RuntimeError(f"synth_gpu_normal_f32 failed ({rc})")
     return t
+
+
+def device_inputs(workload, device="cuda"):
+    """Allocate and fill every input tensor of a workload (synth.configs) on the GPU, bit-identical to the host
+    generator.  1-D tensors (biases) are generated as one row."""
+    import torch
+    out = {}
+    for name, spec in workload.tensors.items():
+        if spec.kind == "f32":
+            t = torch.empty(spec.shape, dtype=torch.float32, device=device)
+            gpu_normal_f32_(t, spec.seed)
+        else:
+            t = torch.empty(spec.shape, dtype=torch.bfloat16, device=device)
+            gpu_normal_bf16_(t, spec.seed, spec.sigma)
+        out[name] = t
+    return out
+
+
+def host_rows(spec, rows=None):
+    """Rows of one workload tensor on the host (all rows by default): uint16 bf16 bits, or float32 for 'f32'."""
+    shape = spec.shape if len(spec.shape) == 2 else (1, spec.shape[0])
+    if rows is None:
+        rows = range(shape[0])
+    rows = list(rows)
+    gen = (lambda r0, n: normal_f32(spec.seed, n, shape[1], r0)) if spec.kind == "f32" else \
+        (lambda r0, n: normal_bf16(spec.seed, n, shape[1], spec.sigma, r0))
+    if rows == list(range(rows[0], rows[0] + len(rows))):
+        out = gen(rows[0], len(rows))
+    else:
+        out = np.concatenate([gen(r, 1) for r in rows], axis=0)
+    return out if len(spec.shape) == 2 else out.reshape(-1)

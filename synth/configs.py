@@ -49,7 +49,7 @@ def tiny_gelu_mlp_tp2() -> Workload:
     M, H, F, p = 128, 256, 1024, 2
     w = Workload("tiny_gelu_mlp_tp2",
                  "GeLU MLP, TP=2, both shards on one device: X[128x256], fc1 2x512, fc2 2x512")
-    w.dims = dict(M=M, H=H, F=F, p=p, act=ACT_GELU)
+    w.dims = dict(M=M, H=H, F=F, p=p, act=ACT_GELU, ranks="all")
     w.tensors = dict(X=T((M, H), 1001), W1t=T((F, H), 1002, W_SIGMA), b1=T((F,), 1003, B_SIGMA),
                      W2t=T((H, F), 1004, W_SIGMA), b2=T((H,), 1005, B_SIGMA))
     w.gemms = [("fc1", M, F // p, H)] * p + [("fc2", M, H, F // p)] * p
@@ -60,7 +60,7 @@ def gpt345m_tp1() -> Workload:
     M, H, nh, d, F = 4096, 1024, 16, 64, 4096
     w = Workload("gpt345m_layer_tp1_4096tok",
                  "GPT-345M-shaped layer, TP=1: H=1024, 16 heads x 64, ffn 4096 GeLU, 4096 tokens")
-    w.dims = dict(M=M, H=H, nq=nh, ng=nh, d=d, F=F, p=1, act=ACT_GELU)
+    w.dims = dict(M=M, H=H, nq=nh, ng=nh, d=d, F=F, p=1, act=ACT_GELU, ranks="all")
     nqkv = (nh + 2 * nh) * d
     w.tensors = dict(X=T((M, H), 2001), Wqkv_t=T((nqkv, H), 2002, W_SIGMA), bqkv=T((nqkv,), 2003, B_SIGMA),
                      ctx=T((M, nh * d), 2004), Wo_t=T((H, nh * d), 2005, W_SIGMA), bo=T((H,), 2006, B_SIGMA),
@@ -76,7 +76,7 @@ def gpt3_175b_tp8_rank0() -> Workload:
     nq_l = nh // p
     w = Workload("gpt3_175b_tp8_rank0_2048tok",
                  "GPT-3 175B-shaped layer, rank 0 of TP=8: 12 heads x 128 per rank, fc1 shard 6144 GeLU, 2048 tokens")
-    w.dims = dict(M=M, H=H, nq=nh, ng=nh, d=d, F=F, p=p, act=ACT_GELU)
+    w.dims = dict(M=M, H=H, nq=nh, ng=nh, d=d, F=F, p=p, act=ACT_GELU, ranks="rank0")
     nqkv = 3 * nq_l * d
     F_l = F // p
     w.tensors = dict(X=T((M, H), 3001), Wqkv_t=T((nqkv, H), 3002, W_SIGMA), bqkv=T((nqkv,), 3003, B_SIGMA),
@@ -91,7 +91,7 @@ def llama70b_tp8_rank0() -> Workload:
     M, H, nq, ng, d, p, F = 4096, 8192, 64, 8, 128, 8, 28672
     w = Workload("llama70b_gqa_swiglu_tp8_rank0_4096tok",
                  "70B-class GQA/SwiGLU layer, rank 0 of TP=8: 8 q-heads + 1 kv-group per rank, ffn 28672")
-    w.dims = dict(M=M, H=H, nq=nq, ng=ng, d=d, F=F, p=p, act=ACT_SWIGLU)
+    w.dims = dict(M=M, H=H, nq=nq, ng=ng, d=d, F=F, p=p, act=ACT_SWIGLU, ranks="rank0")
     nqkv = (nq // p + 2 * (ng // p)) * d
     F_l = F // p
     w.tensors = dict(X=T((M, H), 4001), Wqkv_t=T((nqkv, H), 4002, W_SIGMA),
@@ -105,10 +105,9 @@ def moe_8x_top2() -> Workload:
     w = Workload("moe_8expert_top2_4096tok",
                  "MoE expert MLP, 8 experts SwiGLU ffn 14336, top-2 of 4096 tokens, H=4096")
     w.dims = dict(T=Tn, H=H, E=E, F=F, k=k)
-    w.tensors = dict(X=T((Tn, H), 5001), logits=T((Tn, E), 5002, kind="f32"))
-    for e in range(E):
-        w.tensors[f"W1t_{e}"] = T((2 * F, H), 5100 + e, W_SIGMA)
-        w.tensors[f"W2t_{e}"] = T((H, F), 5200 + e, W_SIGMA)
+    # expert e's weights are rows e*2F..(e+1)*2F of W1t ([gate; up]) and rows e*H..(e+1)*H of W2t
+    w.tensors = dict(X=T((Tn, H), 5001), logits=T((Tn, E), 5002, kind="f32"),
+                     W1t=T((E * 2 * F, H), 5003, W_SIGMA), W2t=T((E * H, F), 5004, W_SIGMA))
     w.gemms = [("moe_fc1", Tn * k, 2 * F, H), ("moe_fc2", Tn * k, H, F)]
     return w
 

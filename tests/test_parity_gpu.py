@@ -1,0 +1,311 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded inputs.
+
+Bar: integer-valued cases bit-exact; floating point within relative Frobenius
+error 4e-3 and elementwise |diff| <= 1e-2 * max|ref|.  Full-size workloads are
+run in the launch configuration the benchmark times and checked on sampled
+rows that the oracle computes one by one (every output row depends only on its
+input row).
+"""
+import numpy as np
+import pytest
+
+import megatron_tensor_transformer_03_amd as mtp
+from megatron_tensor_transformer_03_amd.layer import RankForward
+import oracle
+import synth
+from synth import configs
+from _parity import assert_close, bits, compare, sample_rows, to_dev, widen_bits
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mtp.lib()  # the HIP library must be built; no fallback exists
+    yield
+    torch.cuda.synchronize()
+
+
+# Share of bf16 outputs equal to the round-to-nearest-even of the exact value.  Rounding to nearest even
+# (the reading taken for every fp32 -> bf16 conversion) keeps this near 1; truncation would give about one
+# half.  fp32 accumulation over K up to 12288 terms moves a few per cent of values across a rounding
+# boundary, so the floor is 0.95.
+EXACT_FRAC_MIN = 0.95
+
+
+def _exact_bits_frac(G_bits, R):
+    return float(np.mean(G_bits == oracle.round_bf16(R)))
+
+
+def _close(G, R, what=""):
+    rel, mx = assert_close(G, R, what)
+    say(f"{what}: rel_fro={rel:.3e} max_rel={mx:.3e}")
+
+
+# ----------------------------------------------------------------------------- generator
+def test_device_generator_matches_host():
+    for seed, rows, cols, sigma, r0 in [(1, 3, 40, 1.0, 0), (77, 129, 264, 0.02, 5), (9, 1, 8, 0.01, 1000)]:
+        say("generator", seed, rows, cols)
+        t = torch.empty(rows, cols, dtype=torch.bfloat16, device="cuda")
+        synth.gpu_normal_bf16_(t, seed, sigma, r0)
+        assert np.array_equal(bits(t), synth.normal_bf16(seed, rows, cols, sigma, r0))
+    t = torch.empty(50, 72, dtype=torch.bfloat16, device="cuda")
+    synth.gpu_ternary_bf16_(t, 5)
+    assert np.array_equal(bits(t), synth.ternary_bf16(5, 50, 72))
+    f = torch.empty(33, 8, dtype=torch.float32, device="cuda")
+    synth.gpu_normal_f32_(f, 6)
+    assert np.array_equal(f.cpu().numpy(), synth.normal_f32(6, 33, 8))
+
+
+# ----------------------------------------------------------------------------- integer-exact (bitwise)
+@pytest.mark.parametrize("M,N,K,with_bias", [
+    (1, 8, 8, False), (7, 5, 16, True), (130, 200, 96, True), (300, 520, 248, False), (257, 129, 72, True),
+    (4100, 3000, 64, True),  # large enough for the 256 x 256 tile
+])
+def test_integer_exact_column_linear(M, N, K, with_bias):
+    say("int column", M, N, K, with_bias)
+    Xb, Wb = synth.ternary_bf16(201, M, K), synth.ternary_bf16(202, N, K)
+    bb = synth.ternary_bf16(203, 1, N)[0] if with_bias else None
+    # write into a column block of a wider output (the in-place all-gather): columns 8 .. 8+N of a padded row
+    ldy = ((N + 7) // 8) * 8 + 16
+    Yfull = torch.full((M, ldy), 7.0, dtype=torch.bfloat16, device="cuda")
+    Y = Yfull[:, 8:8 + N]
+    mtp.mtp_column_linear(to_dev(Xb), to_dev(Wb), None if bb is None else to_dev(bb), Y)
+    torch.cuda.synchronize()
+    R = oracle.linear(Xb, Wb, bb)
+    assert np.array_equal(bits(Y), oracle.round_bf16(R))
+    rest = bits(Yfull)
+    mask = np.ones(rest.shape, bool)
+    mask[:, 8:8 + N] = False
+    assert np.all(rest[mask] == 0x40E0), "columns outside the shard were touched"
+
+
+@pytest.mark.parametrize("M,N,Kp,p", [(77, 130, 64, 3), (256, 256, 64, 2), (1, 8, 8, 4)])
+def test_integer_exact_row_partials_and_sum(M, N, Kp, p):
+    say("int row", M, N, Kp, p)
+    Zb, Wb = synth.ternary_bf16(211, M, p * Kp), synth.ternary_bf16(212, N, p * Kp)
+    bb = synth.ternary_bf16(213, 1, N)[0]
+    Z, W, b = to_dev(Zb), to_dev(Wb), to_dev(bb)
+    ldacc = ((N + 7) // 8) * 8
+    Yacc = torch.empty(M, ldacc, dtype=torch.float32, device="cuda")[:, :N]
+    Y = torch.empty(M, ldacc, dtype=torch.bfloat16, device="cuda")[:, :N]
+    for r in range(p):
+        last = r == p - 1
+        mtp.mtp_row_linear_partial(Z[:, r * Kp:(r + 1) * Kp], W[:, r * Kp:(r + 1) * Kp], Yacc, r > 0,
+                                   b if last else None, Y if last else None)
+    torch.cuda.synchronize()
+    P = oracle.row_parallel_partials([np.ascontiguousarray(Zb[:, r * Kp:(r + 1) * Kp]) for r in range(p)], Wb, p)
+    S = oracle.row_parallel_sum(P)
+    assert np.array_equal(Yacc.cpu().numpy().astype(np.float64), S)
+    assert np.array_equal(bits(Y), oracle.round_bf16(S + widen_bits(bb)[None, :]))
+    # a single shard straight to bf16 (p = 1 all-reduce is the identity)
+    Y1 = torch.empty(M, ldacc, dtype=torch.bfloat16, device="cuda")[:, :N]
+    mtp.mtp_row_linear_partial(Z[:, :Kp], W[:, :Kp], None, False, b, Y1)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(Y1), oracle.round_bf16(P[0] + widen_bits(bb)[None, :]))
+
+
+# ----------------------------------------------------------------------------- activations, small full checks
+@pytest.mark.parametrize("M,N,K", [(200, 300, 136), (64, 64, 64), (513, 1030, 256)])
+def test_gelu_column_linear(M, N, K):
+    say("gelu", M, N, K)
+    Xb, Wb = synth.normal_bf16(221, M, K, 1.0), synth.normal_bf16(222, N, K, 0.05)
+    bb = synth.normal_bf16(223, 1, N, 0.1)[0]
+    Y = torch.empty(M, ((N + 7) // 8) * 8, dtype=torch.bfloat16, device="cuda")[:, :N]
+    mtp.mtp_column_linear(to_dev(Xb), to_dev(Wb), to_dev(bb), Y, mtp.ACT_GELU)
+    torch.cuda.synchronize()
+    R = oracle.linear(Xb, Wb, bb, oracle.ACT_GELU)
+    G = bits(Y)
+    _close(widen_bits(G), R, "gelu")
+    assert _exact_bits_frac(G, R) >= EXACT_FRAC_MIN
+
+
+@pytest.mark.parametrize("M,F,K", [(200, 136, 200), (33, 8, 64), (700, 520, 128)])
+def test_swiglu_column_linear(M, F, K):
+    say("swiglu", M, F, K)
+    Xb = synth.normal_bf16(231, M, K, 1.0)
+    Wb = synth.normal_bf16(232, 2 * F, K, 0.1)
+    bb = synth.normal_bf16(233, 1, 2 * F, 0.1)[0]
+    Y = torch.empty(M, F, dtype=torch.bfloat16, device="cuda")
+    mtp.mtp_column_linear(to_dev(Xb), to_dev(Wb), to_dev(bb), Y, mtp.ACT_SWIGLU)
+    torch.cuda.synchronize()
+    R = oracle.linear(Xb, Wb, bb, oracle.ACT_SWIGLU)
+    G = bits(Y)
+    _close(widen_bits(G), R, "swiglu")
+    assert _exact_bits_frac(G, R) >= EXACT_FRAC_MIN
+
+
+def test_degenerate_shapes():
+    say("degenerate")
+    # M = 1, N = 1, K = 8: one element
+    Xb, Wb = synth.normal_bf16(241, 1, 8, 1.0), synth.normal_bf16(242, 1, 8, 1.0)
+    Y = torch.zeros(1, 8, dtype=torch.bfloat16, device="cuda")[:, :1]
+    mtp.mtp_column_linear(to_dev(Xb), to_dev(Wb), None, Y, mtp.ACT_GELU)
+    torch.cuda.synchronize()
+    _close(widen_bits(bits(Y)), oracle.linear(Xb, Wb, None, oracle.ACT_GELU))
+    # zero weights: output is exactly the (activated) bias
+    Xb = synth.normal_bf16(243, 100, 64, 1.0)
+    Wz = np.zeros((40, 64), np.uint16)
+    bb = synth.normal_bf16(244, 1, 40, 1.0)[0]
+    Y = torch.empty(100, 40, dtype=torch.bfloat16, device="cuda")
+    mtp.mtp_column_linear(to_dev(Xb), to_dev(Wz), to_dev(bb), Y)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(Y), np.tile(bb, (100, 1)))
+
+
+# ----------------------------------------------------------------------------- workload 1: tiny GeLU MLP, TP=2
+def test_tiny_mlp_tp2_shards_identities():
+    w = configs.tiny_gelu_mlp_tp2()
+    say(w.name)
+    d, S = w.dims, w.tensors
+    h = {k: synth.host_rows(v) for k, v in S.items()}
+    t = synth.device_inputs(w)
+    for k in h:
+        assert np.array_equal(bits(t[k]).reshape(h[k].shape), h[k])
+    M, H, F, p = d["M"], d["H"], d["F"], d["p"]
+    run = RankForward(d, t)
+    o = run.step()
+    torch.cuda.synchronize()
+    ref = oracle.mlp(h["X"], h["W1t"], h["b1"], h["W2t"], h["b2"], oracle.ACT_GELU, p)
+    _close(widen_bits(bits(o["Y"])), ref["Y"], "Y")
+    _close(o["Yacc"].cpu().numpy(), ref["P"][0] + ref["P"][1], "sum of partials")
+    _close(widen_bits(bits(o["Z"])), widen_bits(ref["Z"][1]), "Z of the last shard")
+    # the sharded result against the unsharded layer (p = 1): the row all-reduce identity
+    ref1 = oracle.mlp(h["X"], h["W1t"], h["b1"], h["W2t"], h["b2"], oracle.ACT_GELU, 1)
+    _close(widen_bits(bits(o["Y"])), ref1["Y"], "Y vs unsharded")
+    # partial rank ranges leave the partial sum in Yacc
+    for r0, r1 in [(0, 1), (1, 2)]:
+        Yacc = torch.empty(M, H, dtype=torch.float32, device="cuda")
+        mtp.mtp_mlp_forward(t["X"], t["W1t"], t["b1"], t["W2t"], t["b2"], mtp.ACT_GELU, p, r0, r1, run.out["Z"], Yacc)
+        torch.cuda.synchronize()
+        _close(Yacc.cpu().numpy(), sum(ref["P"][r0:r1]), f"Yacc[{r0},{r1})")
+    # column all-gather identity: both shards written in place equal the unsharded fc1, bit for bit
+    Zfull = torch.empty(M, F, dtype=torch.bfloat16, device="cuda")
+    for r in range(p):
+        mtp.mtp_column_linear(t["X"], t["W1t"][r * (F // p):(r + 1) * (F // p)], t["b1"][r * (F // p):(r + 1) * (F // p)],
+                              Zfull[:, r * (F // p):(r + 1) * (F // p)], mtp.ACT_GELU)
+    Zun = torch.empty(M, F, dtype=torch.bfloat16, device="cuda")
+    mtp.mtp_column_linear(t["X"], t["W1t"], t["b1"], Zun, mtp.ACT_GELU)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(Zfull), bits(Zun))
+    _close(widen_bits(bits(Zun)), oracle.linear(h["X"], h["W1t"], h["b1"], oracle.ACT_GELU), "fc1 unsharded")
+
+
+# ----------------------------------------------------------------------------- full-size workloads, sampled rows
+def _host_weights(w, names):
+    return {k: synth.host_rows(w.tensors[k]) for k in names if k in w.tensors}
+
+
+def _check_dense_workload(w, nrows, seed):
+    d = w.dims
+    p = d["p"]
+    say(w.name, "inputs")
+    t = synth.device_inputs(w)
+    run = RankForward(d, t)
+    say(w.name, "step")
+    o = run.step()
+    torch.cuda.synchronize()
+    rows = sample_rows(d["M"], nrows, seed)
+    say(w.name, "oracle on", len(rows), "rows")
+    h = _host_weights(w, ["Wqkv_t", "bqkv", "Wo_t", "bo", "W1t", "b1", "W2t", "b2"])
+    X = synth.host_rows(w.tensors["X"], rows)
+    act = d["act"]
+    nq_l, ng_l = d["nq"] // p, d["ng"] // p
+    Rq, _ = oracle.qkv(X, h["Wqkv_t"], h.get("bqkv"), nq_l, ng_l, d["d"])
+    _close(widen_bits(bits(o["qkv"][rows])), Rq, "qkv")
+    if "ctx" in w.tensors:
+        C = synth.host_rows(w.tensors["ctx"], rows)
+        if p == 1:
+            Ro = oracle.row_parallel_sum([oracle.linear(C, h["Wo_t"])], h.get("bo"))
+            _close(widen_bits(bits(o["attn_out"][rows])), Ro, "out-proj")
+        else:
+            Ro = oracle.linear(C, h["Wo_t"])
+            _close(o["attn_partial"][rows].cpu().numpy(), Ro, "out-proj partial")
+    if d["ranks"] == "all":
+        ref = oracle.mlp(X, h["W1t"], h.get("b1"), h["W2t"], h.get("b2"), act, p)
+        _close(widen_bits(bits(o["Y"][rows])), ref["Y"], "mlp Y")
+        Zr = ref["Z"][-1]
+    else:
+        Zr = oracle.round_bf16(oracle.linear(X, h["W1t"], h.get("b1"), act))
+        _close(o["mlp_partial"][rows].cpu().numpy(), oracle.linear(Zr, h["W2t"]), "mlp partial")
+    Zg = bits(o["Z"][rows])
+    _close(widen_bits(Zg), widen_bits(Zr), "Z")
+    frac = float(np.mean(Zg == Zr))
+    say(f"Z bit-exact fraction {frac:.4f}")
+    assert frac >= EXACT_FRAC_MIN
+    return run
+
+
+def test_gpt345m_layer_full_size():
+    run = _check_dense_workload(configs.gpt345m_tp1(), 64, 1)
+    # determinism: a second step gives the same bits
+    first = {k: v.clone() for k, v in run.out.items()}
+    run.step()
+    torch.cuda.synchronize()
+    for k, v in run.out.items():
+        assert torch.equal(v, first[k]), k
+
+
+def test_gpt3_175b_rank0_full_size():
+    _check_dense_workload(configs.gpt3_175b_tp8_rank0(), 24, 2)
+    torch.cuda.empty_cache()
+
+
+def test_llama70b_rank0_full_size():
+    _check_dense_workload(configs.llama70b_tp8_rank0(), 24, 3)
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------- MoE
+def _moe_check(T, H, E, F, k, seed, tokens=None):
+    Xs = configs.T((T, H), seed)
+    Ls = configs.T((T, E), seed + 1, kind="f32")
+    W1s = configs.T((E * 2 * F, H), seed + 2, 0.05)
+    W2s = configs.T((E * H, F), seed + 3, 0.05)
+    w = configs.Workload("moe", "", dict(X=Xs, logits=Ls, W1t=W1s, W2t=W2s), dict(T=T, H=H, E=E, F=F, k=k))
+    return w
+
+
+def _run_moe(w, tokens):
+    d = w.dims
+    say("moe", d)
+    t = synth.device_inputs(w)
+    run = RankForward(d, t)
+    o = run.step()
+    torch.cuda.synchronize()
+    logits = synth.host_rows(w.tensors["logits"])
+    offs, idx, wts = oracle.moe_route(logits, d["k"])
+    assert np.array_equal(o["offsets"].cpu().numpy(), offs)
+    assert np.array_equal(o["token_idx"].cpu().numpy(), idx)
+    assert np.allclose(o["token_w"].cpu().numpy(), wts, rtol=2e-6, atol=0)
+    experts = sorted({e for e in range(d["E"]) for j in range(offs[e], offs[e + 1]) if int(idx[j]) in set(tokens)})
+    E, F, H = d["E"], d["F"], d["H"]
+    W1 = [synth.host_rows(w.tensors["W1t"], range(e * 2 * F, (e + 1) * 2 * F)) if e in experts else None
+          for e in range(E)]
+    W2 = [synth.host_rows(w.tensors["W2t"], range(e * H, (e + 1) * H)) if e in experts else None for e in range(E)]
+    X = synth.host_rows(w.tensors["X"])
+    say("moe oracle on", len(tokens), "tokens,", len(experts), "experts")
+    R, _ = oracle.moe_mlp(X, logits, W1, W2, d["k"], tokens=tokens)
+    _close(widen_bits(bits(o["Y"][tokens])), R, "moe Y")
+    return o
+
+
+@pytest.mark.parametrize("T,H,E,F,k", [(300, 64, 4, 96, 2), (100, 128, 1, 64, 1), (513, 256, 8, 136, 2)])
+def test_moe_small_full(T, H, E, F, k):
+    w = _moe_check(T, H, E, F, k, 300 + T)
+    _run_moe(w, list(range(T)))
+
+
+def test_moe_8x_top2_full_size():
+    w = configs.moe_8x_top2()
+    tokens = sample_rows(w.dims["T"], 8, 5)
+    _run_moe(w, tokens)
+    torch.cuda.empty_cache()
