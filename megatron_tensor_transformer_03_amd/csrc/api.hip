@@ -78,6 +78,17 @@ mtp_status check_dims(int64_t M, int64_t N, int64_t K) {
   return MTP_OK;
 }
 
+// The GEMM kernels address each operand through a buffer resource based at the tile's first row, with
+// 32-bit byte offsets: a tile's rows (up to 256, plus the up-projection offset for SwiGLU) must span
+// less than 2 GiB.
+constexpr int64_t kWindow = (int64_t)1 << 31;
+mtp_status check_window(const char* name, int64_t rows, int64_t ld) {
+  if (2 * rows * ld >= kWindow - 64)
+    return fail(MTP_ERR_SHAPE, "%s: %lld rows of pitch %lld exceed the 2 GiB addressing window", name,
+                (long long)rows, (long long)ld);
+  return MTP_OK;
+}
+
 #define TRY(x)                     \
   do {                             \
     mtp_status s_ = (x);           \
@@ -115,10 +126,12 @@ mtp_status mtp_column_linear(const mtp_bf16* X, int64_t ldx, const mtp_bf16* Wt,
   TRY(check_mat(Wt, "Wt", K, ldw));
   TRY(check_mat(Y, "Y", nout, ldy));
   TRY(check_vec(bias, "bias"));
+  TRY(check_window("X", 256, ldx));
+  TRY(check_window("Wt", (act == MTP_ACT_SWIGLU ? nout : 0) + 256, ldw));
   TRY(check_device());
   mtp::GemmParams p;
   p.A = X; p.lda = ldx; p.B = Wt; p.ldb = ldw; p.bias = bias; p.Y = Y; p.ldy = ldy;
-  p.M = (int)M; p.Nout = (int)nout; p.K = (int)K; p.up_offset = nout;
+  p.M = (int)M; p.Nout = (int)nout; p.K = (int)K; p.up_offset = nout; p.a_src_rows = M;
   p.act = act == MTP_ACT_GELU ? 1 : 0;
   return launched(mtp::gemm(p, act == MTP_ACT_SWIGLU ? mtp::MODE_SWIGLU : mtp::MODE_COL, (hipStream_t)stream),
                   "column linear");
@@ -135,10 +148,12 @@ mtp_status mtp_row_linear_partial(const mtp_bf16* Z, int64_t ldz, const mtp_bf16
   if (Yacc) TRY(check_mat(Yacc, "Yacc", N, ldacc));
   if (Y) TRY(check_mat(Y, "Y", N, ldy));
   TRY(check_vec(bias, "bias"));
+  TRY(check_window("Z", 256, ldz));
+  TRY(check_window("Wt", 256, ldw));
   TRY(check_device());
   mtp::GemmParams p;
   p.A = Z; p.lda = ldz; p.B = Wt; p.ldb = ldw; p.Yacc = Yacc; p.ldacc = ldacc; p.accumulate = accumulate ? 1 : 0;
-  p.bias = bias; p.Y = Y; p.ldy = ldy; p.M = (int)M; p.Nout = (int)N; p.K = (int)Kp;
+  p.bias = bias; p.Y = Y; p.ldy = ldy; p.M = (int)M; p.Nout = (int)N; p.K = (int)Kp; p.a_src_rows = M;
   return launched(mtp::gemm(p, mtp::MODE_ROW, (hipStream_t)stream), "row-parallel partial");
 }
 
@@ -165,13 +180,16 @@ mtp_status mtp_mlp_forward(const mtp_bf16* X, int64_t M, int64_t H, int64_t F, i
   if (!Yacc && !(full && p == 1 && Y)) return fail(MTP_ERR_NULL, "Yacc is NULL");
   if (Yacc) TRY(check_mat(Yacc, "Yacc", H, H));
   if (Y) TRY(check_mat(Y, "Y", H, H));
+  TRY(check_window("X", 256, H));
+  TRY(check_window("W1t", (act == MTP_ACT_SWIGLU ? Fl : 0) + 256, H));
+  TRY(check_window("W2t", 256, F));
   TRY(check_device());
   hipStream_t st = (hipStream_t)stream;
   for (int r = r0; r < r1; ++r) {
     mtp::GemmParams f1;
     f1.A = X; f1.lda = H; f1.B = W1t + (int64_t)r * N1 * H; f1.ldb = H;
     f1.bias = b1 ? b1 + (int64_t)r * N1 : nullptr;
-    f1.Y = Z_ws; f1.ldy = Fl; f1.M = (int)M; f1.Nout = (int)Fl; f1.K = (int)H; f1.up_offset = Fl;
+    f1.Y = Z_ws; f1.ldy = Fl; f1.M = (int)M; f1.Nout = (int)Fl; f1.K = (int)H; f1.up_offset = Fl; f1.a_src_rows = M;
     f1.act = act == MTP_ACT_GELU ? 1 : 0;
     mtp_status s = launched(mtp::gemm(f1, act == MTP_ACT_SWIGLU ? mtp::MODE_SWIGLU : mtp::MODE_COL, st), "fc1");
     if (s != MTP_OK) return s;
@@ -180,7 +198,7 @@ mtp_status mtp_mlp_forward(const mtp_bf16* X, int64_t M, int64_t H, int64_t F, i
     f2.Yacc = Yacc; f2.ldacc = H; f2.accumulate = r > r0 ? 1 : 0;
     const bool last = full && r == p - 1;
     f2.Y = last ? Y : nullptr; f2.ldy = H; f2.bias = last ? b2 : nullptr;
-    f2.M = (int)M; f2.Nout = (int)H; f2.K = (int)Fl;
+    f2.M = (int)M; f2.Nout = (int)H; f2.K = (int)Fl; f2.a_src_rows = M;
     s = launched(mtp::gemm(f2, mtp::MODE_ROW, st), "fc2");
     if (s != MTP_OK) return s;
   }
@@ -230,19 +248,23 @@ mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, i
   TRY(check_mat(Z_ws, "Z_ws", F, F));
   TRY(check_mat(Yacc, "Yacc", H, H));
   TRY(check_mat(Y, "Y", H, H));
+  TRY(check_window("X", T, H));
+  TRY(check_window("W1t", F + 256, H));
+  TRY(check_window("W2t", 256, F));
+  TRY(check_window("Z_ws", 256, F));
   TRY(check_device());
   hipStream_t st = (hipStream_t)stream;
   mtp_status s = launched(mtp::fill_zero_f32(Yacc, T, H, H, st), "zero Yacc");
   if (s != MTP_OK) return s;
   mtp::GemmParams f1;
   f1.A = X; f1.lda = H; f1.a_rows = token_idx; f1.B = W1t; f1.ldb = H; f1.up_offset = F;
-  f1.Y = Z_ws; f1.ldy = F; f1.Nout = (int)F; f1.K = (int)H;
+  f1.Y = Z_ws; f1.ldy = F; f1.Nout = (int)F; f1.K = (int)H; f1.a_src_rows = T;
   f1.group_offsets = expert_offsets; f1.groups = E; f1.group_stride_B = 2 * F * H;
   s = launched(mtp::gemm_grouped(f1, mtp::MODE_SWIGLU, (int)(T * k), st), "grouped fc1");
   if (s != MTP_OK) return s;
   mtp::GemmParams f2;
   f2.A = Z_ws; f2.lda = F; f2.B = W2t; f2.ldb = F; f2.Yacc = Yacc; f2.ldacc = H;
-  f2.row_w = token_w; f2.out_rows = token_idx; f2.Nout = (int)H; f2.K = (int)F;
+  f2.row_w = token_w; f2.out_rows = token_idx; f2.Nout = (int)H; f2.K = (int)F; f2.a_src_rows = T * k;
   f2.group_offsets = expert_offsets; f2.groups = E; f2.group_stride_B = H * F;
   s = launched(mtp::gemm_grouped(f2, mtp::MODE_COMBINE, (int)(T * k), st), "grouped fc2");
   if (s != MTP_OK) return s;

@@ -14,6 +14,7 @@ struct GemmParams {
   const uint16_t* A = nullptr;
   int64_t lda = 0;
   const int32_t* a_rows = nullptr;  // A row of output row j is a_rows[j] (grouped fc1 gather)
+  int64_t a_src_rows = 0;           // rows of A addressable from p.A (bounds its buffer resource)
   const uint16_t* B = nullptr;
   int64_t ldb = 0;
   int64_t up_offset = 0;            // SWIGLU: row offset of the up half within B (= Nout)
