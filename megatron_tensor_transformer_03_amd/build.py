@@ -10,7 +10,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmtp.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["gemm.hip", "moe.hip", "api.hip"]
-FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-munsafe-fp-atomics",
+FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++20", "-munsafe-fp-atomics",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
 
 

@@ -13,23 +13,26 @@
 // ragged per-expert row ranges read from device memory.
 //
 // Design (gfx950, CDNA4):
-//  * Block tile BM x BN, K step 64, waves in a WAVES_M x WAVES_N grid; each wave
-//    owns a (BM/WAVES_M) x (BN/WAVES_N) tile of v_mfma_f32_32x32x16_bf16
-//    fragments accumulated in fp32 (the 32x32x16 form sustains ~97% of the
-//    dense bf16 rate on gfx950; the 16x16x32 form measured ~85%).  The large
-//    tile is 256 x 256 with 8 waves (two per SIMD, 128 accumulators each) so
-//    one wave's MFMAs cover the other's LDS traffic and barrier waits.
+//  * A tile configuration (Cfg) fixes the block tile BM x BN, the wave grid, the
+//    K step BK and the number NS of LDS stages.  Each wave owns a
+//    (BM/WAVES_M) x (BN/WAVES_N) tile of v_mfma_f32_32x32x16_bf16 fragments
+//    accumulated in fp32 (the 32x32x16 form sustains ~97% of the dense bf16
+//    rate on gfx950; the 16x16x32 form measured ~85%).  The large tile is
+//    256 x 256 with 8 waves (two per SIMD, 128 accumulators each).
 //  * Operands are swapped in the MFMA (weights as the first operand) so a
-//    lane's accumulators hold runs of 4 consecutive output columns of one row:
-//    the epilogue stores 8 B (bf16) or 16 B (fp32) per lane.
-//  * Global -> LDS: buffer_load_dwordx4 ... lds (direct to LDS, no VGPR
-//    round trip, no ds_write), 8 lanes per 128-byte row segment, one K step
-//    ahead, LDS double-buffered, one barrier per K step.  Buffer resources
-//    make out-of-range rows read as zero without faulting.
-//  * LDS rows are 128 B; 16-byte chunks are XOR-swizzled by (row >> 1) & 7 so
-//    the fragment reads (16 consecutive rows at one chunk per 16 lanes) and the
-//    staging writes (two rows per 16 lanes) both hit distinct banks of the
-//    64-bank LDS (bank conflicts measured with SQ_LDS_BANK_CONFLICT).
+//    lane's accumulators hold runs of 4 consecutive output columns of one row.
+//  * Global -> LDS: buffer_load_dwordx4 ... lds (direct to LDS, no VGPR round
+//    trip, no ds_write) into an NS-deep ring of LDS stages, NS - 1 K steps
+//    ahead of the MFMAs, one barrier per K step.  Each stage is its own LDS
+//    variable so the compiler sees that a DMA into one stage does not alias
+//    the fragment reads of another.  Buffer resources make out-of-range rows
+//    read as zero without faulting, and the K position is a scalar offset, so
+//    the loop has no vector address arithmetic.  (With one step of lead the
+//    DMA latency, ~2-3K cycles under load, was exposed on every step.)
+//  * LDS rows are BK * 2 bytes; 16-byte chunks are XOR-swizzled per row so the
+//    fragment reads (16 lanes read one chunk of 16 consecutive rows) hit
+//    distinct banks of the 64-bank (256 B per cycle) LDS.
+//  * bf16 epilogues stage each wave's tile through LDS and store whole rows.
 //  * Tile order is XCD-aware: consecutive workgroup ids land on different XCDs
 //    (8 L2 slices), so ids are remapped to give each XCD a contiguous band of
 //    tiles, grouped GROUP_M rows at a time for A/B panel reuse in its L2.
@@ -37,6 +40,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "gemm.h"
 
@@ -45,13 +49,32 @@ namespace mtp {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BK = 64;          // K elements per stage: 128 bytes per row
-constexpr int kChunks = BK / 8; // 16-byte chunks per LDS row
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int NS_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BK = BK_, NS = NS_;
+  static constexpr int NWAVES = WAVES_M * WAVES_N, NT = 64 * NWAVES;
+  static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;  // wave tile
+  static constexpr int FM = TM / 32, FN = TN / 32;             // 32 x 32 MFMA tiles per wave
+  static constexpr int CPR = BK / 8;                           // 16-byte chunks per LDS row
+  static constexpr int RPL = 256 / (2 * BK);                   // LDS rows per 256-byte bank line
+  static constexpr int ROWS_PER_DMA = 64 / CPR;                // rows one 64-lane DMA instruction fills
+  static constexpr int A_G = BM / ROWS_PER_DMA / NWAVES;       // DMA instructions per wave per stage (A)
+  static constexpr int B_G = BN / ROWS_PER_DMA / NWAVES;       // (B)
+  static constexpr int STAGE = (BM + BN) * BK;                 // elements per LDS stage
+  static_assert(BK == 32 || BK == 64, "K step");
+  static_assert(NS >= 2 && NS <= 4, "LDS stages");
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "32 x 32 fragments");
+  static_assert(BM % (ROWS_PER_DMA * NWAVES) == 0 && BN % (ROWS_PER_DMA * NWAVES) == 0, "DMA split");
+  static_assert(NS * STAGE * 2 <= 160 * 1024, "LDS capacity");
+};
 
-// LDS layout of a 128-byte row: its eight 16-byte chunks are permuted by XOR with (row >> 1) & 7.  The
-// LDS serves 256 bytes (64 banks) per cycle, i.e. two rows; a fragment read has 16 lanes read one chunk
-// of 16 consecutive rows, which this permutation spreads over all 16 bank groups.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3); }
+// Element offset of (row, 16-byte chunk) in an LDS stage: rows of BK elements, chunks permuted by XOR with
+// (row / RPL) & (CPR - 1).  A fragment read has 16 lanes read one chunk of 16 consecutive rows; the RPL rows
+// that share a 256-byte bank line differ in their permutation, so those 16 reads hit 16 distinct bank groups.
+template <class C>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * C::BK + ((chunk ^ ((row / C::RPL) & (C::CPR - 1))) << 3);
+}
 
 __device__ __forceinline__ uint16_t to_bf16(float x) {
   __bf16 h = (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
@@ -64,7 +87,18 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 __device__ __forceinline__ float from_bf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f)); }
+// Exact-erf GeLU, gelu(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)).  erf is evaluated with Abramowitz &
+// Stegun 7.1.26 (|error| <= 1.5e-7 absolute, far below bf16 resolution): for z >= 0,
+// 1 - erf(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z).  Written as
+// 1 + erf(z) = 2 - q (z >= 0) or q (z < 0, by symmetry) so there is no cancellation for negative x.
+__device__ __forceinline__ float gelu_erf(float x) {
+  const float z = fabsf(x) * 0.70710678118654752440f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f), -0.284496736f),
+                              0.254829592f);
+  const float q = poly * __expf(-z * z);
+  return 0.5f * x * (x >= 0.f ? 2.0f - q : q);
+}
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
@@ -104,22 +138,26 @@ __device__ __forceinline__ void store4_bf16(uint16_t* dst, const float v[4], int
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool GROUPED, bool KFULL>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams p) {
-  constexpr int NT = 64 * WAVES_M * WAVES_N;
-  constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
-  constexpr int FM = TM / 32, FN = TN / 32;   // 32 x 32 MFMA tiles per wave
-  constexpr int ROWS_PER_PASS = NT / kChunks; // tile rows one load instruction covers
-  constexpr int A_IT = BM / ROWS_PER_PASS, B_IT = BN / ROWS_PER_PASS;
-  static_assert(TM % 32 == 0 && TN % 32 == 0, "32 x 32 fragments");
+template <class C, int MODE, bool GROUPED, bool KFULL>
+__global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NS = C::NS, WAVES_N = C::WAVES_N, NWAVES = C::NWAVES;
+  constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, CPR = C::CPR, RPL = C::RPL;
+  constexpr int A_G = C::A_G, B_G = C::B_G, ROWS_PER_DMA = C::ROWS_PER_DMA;
   static_assert(MODE != MODE_SWIGLU || TN % 64 == 0, "gate/up fragment pairs");
-  static_assert(BM % ROWS_PER_PASS == 0 && BN % ROWS_PER_PASS == 0, "load split");
   constexpr int NB_OUT = MODE == MODE_SWIGLU ? BN / 2 : BN;  // output columns per tile
 
-  // two separate LDS arrays (not one indexed by parity) so the compiler can tell that the DMA into one
-  // does not alias the fragment reads from the other, and waits for it only where it is consumed
-  __shared__ __attribute__((aligned(16))) uint16_t smem0[(BM + BN) * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t smem1[(BM + BN) * BK];
+  // one LDS variable per stage (see the design notes); unused ones are a token 16 bytes
+  __shared__ __attribute__((aligned(16))) uint16_t lds0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds1[C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds2[NS > 2 ? C::STAGE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t lds3[NS > 3 ? C::STAGE : 8];
+  auto stage_buf = [&](auto I) -> uint16_t* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return lds0;
+    else if constexpr (i == 1) return lds1;
+    else if constexpr (i == 2) return lds2;
+    else return lds3;
+  };
 
   // ---- tile placement
   int tm, tn;
@@ -170,20 +208,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   // converted value lands in a vector register, which turns every buffer load into a waterfall loop)
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(a_base, 2 * a_extent < (int64_t)kOOB ? 2 * a_extent : (int64_t)kOOB);
   const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(b_base, 2 * b_extent < (int64_t)kOOB ? 2 * b_extent : (int64_t)kOOB);
-  // Direct-to-LDS loads: one buffer_load_dwordx4 ... lds moves 64 lanes x 16 B = eight 128-byte LDS rows,
-  // lane l filling row (l >> 3), chunk (l & 7) of its group.  The LDS layout is swizzled (see swz), so each
-  // lane loads the global chunk that lands at its slot: c = (l & 7) ^ ((row >> 1) & 7).
-  constexpr int NWAVES = WAVES_M * WAVES_N;
-  constexpr int A_G = BM / 8 / NWAVES, B_G = BN / 8 / NWAVES;  // 8-row groups per wave
-  static_assert(BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0, "DMA split");
+  // Direct-to-LDS loads: one buffer_load_dwordx4 ... lds moves 64 lanes x 16 B = ROWS_PER_DMA LDS rows,
+  // lane l filling row (l / CPR), chunk (l % CPR) of its group.  The LDS layout is swizzled (see swz), so
+  // each lane loads the global chunk that lands at its slot.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int lrow = lane >> 3;
+  const int lrow = lane / CPR;
   uint32_t a_off[A_G], b_off[B_G];
   int a_kc[A_G], b_kc[B_G];  // K element offset of each lane's chunk
 #pragma unroll
   for (int i = 0; i < A_G; ++i) {
-    const int r = 8 * (wave_u * A_G + i) + lrow;
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int r = ROWS_PER_DMA * (wave_u * A_G + i) + lrow;
+    const int c = (lane % CPR) ^ ((r / RPL) & (CPR - 1));
     a_kc[i] = 8 * c;
     if (p.a_rows) {
       const int m = m0 + r;
@@ -194,8 +229,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   }
 #pragma unroll
   for (int i = 0; i < B_G; ++i) {
-    const int r = 8 * (wave_u * B_G + i) + lrow;
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int r = ROWS_PER_DMA * (wave_u * B_G + i) + lrow;
+    const int c = (lane % CPR) ^ ((r / RPL) & (CPR - 1));
     b_kc[i] = 8 * c;
     int n = r;
     if constexpr (MODE == MODE_SWIGLU) {
@@ -206,7 +241,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   }
   typedef __attribute__((address_space(3))) void* lds_ptr;
   // The scalar offset is not part of the hardware range check (only the per-lane offset is), so it stays
-  // inside the rows: a prefetch past the last K step re-reads step 0 into a buffer that is never consumed
+  // inside the rows: a prefetch past the last K step re-reads step 0 into a stage that is never consumed
   // (KFULL) or is redirected out of range per lane (!KFULL, reading zeros).
   auto dma_stage = [&](int k0, uint16_t* sbuf) {
     const int soff = k0 < p.K ? 2 * k0 : 0;
@@ -214,14 +249,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
     for (int i = 0; i < A_G; ++i) {
       uint32_t vo = a_off[i];
       if constexpr (!KFULL) vo = k0 + a_kc[i] < p.K ? vo : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr)(sbuf + (wave_u * A_G + i) * 8 * BK), 16, vo, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr)(sbuf + (wave_u * A_G + i) * ROWS_PER_DMA * BK), 16,
+                                               vo, soff, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < B_G; ++i) {
       uint32_t vo = b_off[i];
       if constexpr (!KFULL) vo = k0 + b_kc[i] < p.K ? vo : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr)(sbuf + BM * BK + (wave_u * B_G + i) * 8 * BK), 16, vo,
-                                               soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          b_rsrc, (lds_ptr)(sbuf + BM * BK + (wave_u * B_G + i) * ROWS_PER_DMA * BK), 16, vo, soff, 0, 0);
     }
   };
 
@@ -238,116 +274,188 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   auto mma_step = [&](const uint16_t* sA, const uint16_t* sB, int ks) {
     bf16x8 af[FM], bfr[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(sA + swz(wm0 + 32 * i + fr, 2 * ks + fk));
+    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(sA + swz<C>(wm0 + 32 * i + fr, 2 * ks + fk));
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(sB + swz(wn0 + 32 * j + fr, 2 * ks + fk));
+    for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(sB + swz<C>(wn0 + 32 * j + fr, 2 * ks + fk));
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
   };
-  // K steps, rounded up to an even count: the loop body covers two steps (one per LDS buffer) and has no
-  // branches, so the compiler's wait counts stay exact.  With KFULL the step count is even and every chunk
-  // is in range; otherwise chunks at or past K read as zero, so an odd step count runs one all-zero step.
-  const int KT2 = ((p.K + BK - 1) / BK + 1) & ~1;
-  // One K step on LDS buffer P: start the DMA of step kt + 1 into the other buffer, run this step's MFMAs,
-  // then wait for this wave's DMA and meet the other waves at the barrier.
-  auto body = [&](auto parity, int kt) {
-    constexpr int P = decltype(parity)::value;
-    uint16_t* cur = P == 0 ? smem0 : smem1;
-    uint16_t* nxt = P == 0 ? smem1 : smem0;
-    dma_stage((kt + 1) * BK, nxt);
+  // K steps, rounded up to a multiple of NS: the loop body covers NS steps (one per LDS stage, each stage a
+  // compile-time choice) and has no branches, so the compiler's wait counts stay exact.  With KFULL the
+  // step count is a multiple of NS and every chunk is in range; otherwise chunks at or past K read as zero,
+  // so padding steps multiply zeros.
+  const int KT = (p.K + BK - 1) / BK;
+  const int KTS = (KT + NS - 1) / NS * NS;
+  // vmcnt(n): wait until at most n of this wave's DMA instructions are outstanding (expcnt, lgkmcnt free).
+  constexpr int kNewer = (NS - 2) * (A_G + B_G);  // DMAs issued after the stage needed next
+  static_assert(kNewer < 64, "vmcnt range");
+  constexpr int kWaitNext = 0x0F70 | (kNewer & 15) | ((kNewer >> 4) << 14);
+  // The barrier between steps: this wave's DMA of the next step has landed (vmcnt), every fragment read of
+  // this step has been consumed by an MFMA, and the waves meet.  A __syncthreads() would add a release
+  // fence, which waits for every outstanding DMA (vmcnt(0)) and so drains the whole ring; the raw s_barrier
+  // between compiler-level memory fences keeps the later DMAs in flight.
+  auto ring_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(kWaitNext);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // One K step on stage I: start the DMA of step kt + NS - 1 into the stage consumed last step (every wave
+  // passed the barrier after reading it), run this step's MFMAs, wait until this wave's DMA of step kt + 1
+  // has landed, and meet the other waves at the barrier.
+  auto step = [&](auto I, int kt) {
+    constexpr int i = decltype(I)::value;
+    uint16_t* cur = stage_buf(std::integral_constant<int, i>{});
+    uint16_t* nxt = stage_buf(std::integral_constant<int, (i + NS - 1) % NS>{});
+    dma_stage((kt + NS - 1) * BK, nxt);
     __builtin_amdgcn_sched_barrier(0);  // keep the DMA issue at the top: the scheduler would sink it
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) mma_step(cur, cur + BM * BK, ks);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA into the other buffer has landed
-    __syncthreads();
+    ring_barrier();
   };
-  dma_stage(0, smem0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  for (int kt = 0; kt < KT2; kt += 2) {
-    body(std::integral_constant<int, 0>{}, kt);
-    body(std::integral_constant<int, 1>{}, kt + 1);
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (dma_stage(I * BK, stage_buf(std::integral_constant<int, I>{})), ...);
+  }(std::make_integer_sequence<int, NS - 1>{});
+  ring_barrier();
+  for (int kt = 0; kt < KTS; kt += NS) {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (step(std::integral_constant<int, I>{}, kt + I), ...);
+    }(std::make_integer_sequence<int, NS>{});
   }
+  // The last steps prefetched stages past K (never consumed); drain them before the epilogue reuses LDS.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
 
   // ---- epilogue.  Weights were the MFMA's first operand, so lane holds output row (lane & 31) of its
   // 32-row fragment and, in register 4*jj + r, column 8*jj + 4*(lane >> 5) + r of its 32-column fragment.
   const int col4 = 4 * (lane >> 5);
+  constexpr int TNO = MODE == MODE_SWIGLU ? TN / 2 : TN;        // output columns per wave
+  constexpr int FNO = TNO / 32;                                  // output fragments per wave
+  const int ncol0 = tn * NB_OUT + (wave % WAVES_N) * TNO;        // first output column of the wave tile
+  // Bias of this lane's output columns, read once with clamped indices (columns past Nout are computed but
+  // never stored): per-element loads under branches would each wait a full memory latency.
+  constexpr bool kBias = MODE != MODE_COMBINE;
+  float bias_g[kBias ? FNO : 1][4][4], bias_u[MODE == MODE_SWIGLU ? FNO : 1][4][4];
+  if constexpr (kBias) {
+    const bool has_bias = p.bias != nullptr && (MODE != MODE_ROW || p.Y != nullptr);
+#pragma unroll
+    for (int jo = 0; jo < FNO; ++jo)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = min(ncol0 + 32 * jo + 8 * jj + col4 + r, p.Nout - 1);
+          bias_g[jo][jj][r] = has_bias ? from_bf16(p.bias[c]) : 0.f;
+          if constexpr (MODE == MODE_SWIGLU) bias_u[jo][jj][r] = has_bias ? from_bf16(p.bias[p.up_offset + c]) : 0.f;
+        }
+  }
+  // output value of (fragment row block i, output fragment jo, run jj, element r)
+  auto out_val = [&](int i, int jo, int jj, int r, auto gelu) -> float {
+    if constexpr (MODE == MODE_SWIGLU) {
+      const float g = acc[i][2 * jo][4 * jj + r] + bias_g[jo][jj][r];
+      const float u = acc[i][2 * jo + 1][4 * jj + r] + bias_u[jo][jj][r];
+      return silu(g) * u;
+    } else {
+      const float x = acc[i][jo][4 * jj + r] + bias_g[jo][jj][r];
+      if constexpr (decltype(gelu)::value) return gelu_erf(x);
+      else return x;
+    }
+  };
+  constexpr bool kStaged = MODE == MODE_COL || MODE == MODE_SWIGLU || MODE == MODE_ROW;
+  if (kStaged && (MODE != MODE_ROW || p.Yacc == nullptr)) {
+    // bf16 outputs go through LDS so that the global stores are whole rows: each wave writes its own
+    // TM x TNO tile into a private region (the drain above retired every LDS access of the main loop),
+    // then reads it back row-contiguously; no cross-wave synchronisation is needed.  Regions are row-major
+    // with 8-byte units permuted per row so the 32 lanes of a write (32 rows, one unit) and of a read (2-4
+    // whole rows) hit distinct banks.
+    constexpr int UPR = TNO / 4;  // 8-byte units per row
+    constexpr int RPB = 32 / UPR; // rows sharing one 256-byte bank line
+    static_assert(UPR == 8 || UPR == 16 || UPR == 32, "unit layout");
+    constexpr int WPS = C::STAGE / (TM * TNO);  // wave regions per LDS stage
+    static_assert(WPS >= 1 && (NWAVES + WPS - 1) / WPS <= NS, "staging fits");
+    const int si = wave / WPS;
+    uint16_t* reg = (si == 0 ? lds0 : si == 1 ? lds1 : si == 2 ? lds2 : lds3) + (wave % WPS) * TM * TNO;
+    auto unit_at = [&](int row, int u) { return row * TNO + 4 * (u ^ ((row / RPB) & (UPR - 1))); };
+    auto stage_tile = [&](auto gelu) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jo = 0; jo < FNO; ++jo)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float v0 = out_val(i, jo, jj, 0, gelu), v1 = out_val(i, jo, jj, 1, gelu);
+            const float v2 = out_val(i, jo, jj, 2, gelu), v3 = out_val(i, jo, jj, 3, gelu);
+            *reinterpret_cast<uint2*>(reg + unit_at(32 * i + fr, 8 * jo + 2 * jj + (lane >> 5))) =
+                make_uint2(pack_bf16(v0, v1), pack_bf16(v2, v3));
+          }
+    };
+    if (MODE == MODE_COL && p.act == 1) stage_tile(std::true_type{});
+    else stage_tile(std::false_type{});
+    // read back: 64 lanes cover 64 / UPR whole rows per pass
+    const int u = lane % UPR, rsub = lane / UPR;
+    const int n = ncol0 + 4 * u;
+    const int valid = p.Nout - n;
+#pragma unroll 4
+    for (int r0 = 0; r0 < TM; r0 += 64 / UPR) {
+      const int row = r0 + rsub;
+      const int m = m0 + wm0 + row;
+      const uint2 d = *reinterpret_cast<const uint2*>(reg + unit_at(row, u));
+      if (m < rows && valid > 0) {
+        uint16_t* dst = p.Y + ((int64_t)row_base + m) * p.ldy + n;
+        if (valid >= 4) {
+          *reinterpret_cast<uint2*>(dst) = d;
+        } else {
+          const uint16_t h[4] = {(uint16_t)d.x, (uint16_t)(d.x >> 16), (uint16_t)d.y, (uint16_t)(d.y >> 16)};
+          for (int q = 0; q < valid; ++q) dst[q] = h[q];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int m = m0 + wm0 + 32 * i + fr;
     if (m >= rows) continue;
     const int64_t orow = (int64_t)row_base + m;
-    if constexpr (MODE == MODE_SWIGLU) {
 #pragma unroll
-      for (int j = 0; j < FN; j += 2) {
-        const int g32 = wn0 / 32 + j;  // even: gate rows; g32 + 1: the matching up rows
+    for (int j = 0; j < FN; ++j) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int n = tn * NB_OUT + 32 * (g32 >> 1) + 8 * jj + col4;
-          if (n >= p.Nout) continue;
-          float v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float g = acc[i][j][4 * jj + r], u = acc[i][j + 1][4 * jj + r];
-            if (p.bias && n + r < p.Nout) {
-              g += from_bf16(p.bias[n + r]);
-              u += from_bf16(p.bias[p.up_offset + n + r]);
+      for (int jj = 0; jj < 4; ++jj) {
+        const int n = tn * BN + wn0 + 32 * j + 8 * jj + col4;
+        if (n >= p.Nout) continue;
+        const int valid = p.Nout - n;
+        float v[4] = {acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]};
+        if constexpr (MODE == MODE_ROW) {
+          // fp32 partial of a row-parallel shard (and, on the last shard, the bf16 result)
+          float* dst = p.Yacc + orow * p.ldacc + n;
+          if (valid >= 4) {
+            if (p.accumulate) {
+              const float4 o = *reinterpret_cast<const float4*>(dst);
+              v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
             }
-            v[r] = silu(g) * u;
-          }
-          store4_bf16(p.Y + orow * p.ldy + n, v, p.Nout - n);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int n = tn * BN + wn0 + 32 * j + 8 * jj + col4;
-          if (n >= p.Nout) continue;
-          const int valid = p.Nout - n;
-          float v[4] = {acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]};
-          if constexpr (MODE == MODE_COL) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (p.bias && r < valid) v[r] += from_bf16(p.bias[n + r]);
-              if (p.act == 1) v[r] = gelu_erf(v[r]);
-            }
-            store4_bf16(p.Y + orow * p.ldy + n, v, valid);
-          } else if constexpr (MODE == MODE_ROW) {
-            if (p.Yacc) {
-              float* dst = p.Yacc + orow * p.ldacc + n;
-              if (valid >= 4) {
-                if (p.accumulate) {
-                  const float4 o = *reinterpret_cast<const float4*>(dst);
-                  v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
-                }
-                *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-              } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  if (r < valid) {
-                    if (p.accumulate) v[r] += dst[r];
-                    dst[r] = v[r];
-                  }
-              }
-            }
-            if (p.Y) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (p.bias && r < valid) v[r] += from_bf16(p.bias[n + r]);
-              store4_bf16(p.Y + orow * p.ldy + n, v, valid);
-            }
-          } else {  // MODE_COMBINE
-            const float w = p.row_w[orow];
-            float* dst = p.Yacc + (int64_t)p.out_rows[orow] * p.ldacc + n;
+            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if (r < valid) atomicAdd(dst + r, w * v[r]);
+              if (r < valid) {
+                if (p.accumulate) v[r] += dst[r];
+                dst[r] = v[r];
+              }
           }
+          if (p.Y) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] += bias_g[j][jj][r];
+            store4_bf16(p.Y + orow * p.ldy + n, v, valid);
+          }
+        } else if constexpr (MODE == MODE_COMBINE) {
+          const float w = p.row_w[orow];
+          float* dst = p.Yacc + (int64_t)p.out_rows[orow] * p.ldacc + n;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (r < valid) atomicAdd(dst + r, w * v[r]);
         }
       }
     }
@@ -355,26 +463,27 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
 }
 
 // ------------------------------------------------------------------------------------------ launch
-template <int BM, int BN, int WM, int WN, int MODE, bool GROUPED>
+template <class C, int MODE, bool GROUPED>
 static hipError_t launch_cfg(const GemmParams& p, int grid_rows_upper, hipStream_t st) {
-  const int nb = MODE == MODE_SWIGLU ? BN / 2 : BN;
+  const int nb = MODE == MODE_SWIGLU ? C::BN / 2 : C::BN;
   const int tiles_n = (p.Nout + nb - 1) / nb;
   int64_t tiles;
   if (GROUPED)
-    tiles = (int64_t)((grid_rows_upper + BM - 1) / BM + p.groups) * tiles_n;
+    tiles = (int64_t)((grid_rows_upper + C::BM - 1) / C::BM + p.groups) * tiles_n;
   else
-    tiles = (int64_t)((p.M + BM - 1) / BM) * tiles_n;
+    tiles = (int64_t)((p.M + C::BM - 1) / C::BM) * tiles_n;
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const bool kfull = p.K % (2 * BK) == 0;  // whole chunks and an even number of K steps
+  const bool kfull = p.K % (C::BK * C::NS) == 0;  // whole chunks and a step count that fills the ring
   if (kfull)
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, MODE, GROUPED, true>), dim3((unsigned)tiles), dim3(64 * WM * WN),
-                       0, st, p);
+    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, true>), dim3((unsigned)tiles), dim3(C::NT), 0, st, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, MODE, GROUPED, false>), dim3((unsigned)tiles), dim3(64 * WM * WN),
-                       0, st, p);
+    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, false>), dim3((unsigned)tiles), dim3(C::NT), 0, st, p);
   return hipGetLastError();
 }
+
+using BigTile = Cfg<256, 256, 2, 4, 32, 4>;    // 8 waves, 128 KB LDS ring
+using SmallTile = Cfg<128, 128, 2, 2, 64, 4>;  // 4 waves, 128 KB LDS ring
 
 // Tile choice: the largest tile that still gives every CU work, else the
 // 128 x 128 tile.  (The 256 x 256 tile needs about 256 tiles to fill the chip.)
@@ -382,8 +491,8 @@ template <int MODE>
 static hipError_t dispatch(const GemmParams& p, hipStream_t st) {
   const int64_t nb_big = MODE == MODE_SWIGLU ? 128 : 256;
   const int64_t big_tiles = ((p.M + 255) / 256) * ((p.Nout + nb_big - 1) / nb_big);
-  if (big_tiles >= 192) return launch_cfg<256, 256, 2, 4, MODE, false>(p, 0, st);
-  return launch_cfg<128, 128, 2, 2, MODE, false>(p, 0, st);
+  if (big_tiles >= 192) return launch_cfg<BigTile, MODE, false>(p, 0, st);
+  return launch_cfg<SmallTile, MODE, false>(p, 0, st);
 }
 
 hipError_t gemm(const GemmParams& p, int mode, hipStream_t st) {
@@ -397,8 +506,8 @@ hipError_t gemm(const GemmParams& p, int mode, hipStream_t st) {
 
 hipError_t gemm_grouped(const GemmParams& p, int mode, int rows_upper, hipStream_t st) {
   switch (mode) {
-    case MODE_SWIGLU: return launch_cfg<256, 256, 2, 4, MODE_SWIGLU, true>(p, rows_upper, st);
-    case MODE_COMBINE: return launch_cfg<256, 256, 2, 4, MODE_COMBINE, true>(p, rows_upper, st);
+    case MODE_SWIGLU: return launch_cfg<BigTile, MODE_SWIGLU, true>(p, rows_upper, st);
+    case MODE_COMBINE: return launch_cfg<BigTile, MODE_COMBINE, true>(p, rows_upper, st);
     default: return hipErrorInvalidValue;
   }
 }
