@@ -49,9 +49,13 @@ namespace mtp {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int NS_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int NS_, bool EARLY_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BK = BK_, NS = NS_;
+  // EARLY: the first fragments of step k + 1 are read during the last MFMAs of step k (the barrier ending a
+  // step then makes the stage two steps ahead visible, so the ring needs one more stage for the same lead)
+  static constexpr bool EARLY = EARLY_;
+  static constexpr int LEAD = EARLY ? 2 : 1;
   static constexpr int NWAVES = WAVES_M * WAVES_N, NT = 64 * NWAVES;
   static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;  // wave tile
   static constexpr int FM = TM / 32, FN = TN / 32;             // 32 x 32 MFMA tiles per wave
@@ -62,7 +66,7 @@ struct Cfg {
   static constexpr int B_G = BN / ROWS_PER_DMA / NWAVES;       // (B)
   static constexpr int STAGE = (BM + BN) * BK;                 // elements per LDS stage
   static_assert(BK == 32 || BK == 64, "K step");
-  static_assert(NS >= 2 && NS <= 4, "LDS stages");
+  static_assert(NS >= 2 + LEAD - 1 && NS <= 5, "LDS stages");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "32 x 32 fragments");
   static_assert(BM % (ROWS_PER_DMA * NWAVES) == 0 && BN % (ROWS_PER_DMA * NWAVES) == 0, "DMA split");
   static_assert(NS * STAGE * 2 <= 160 * 1024, "LDS capacity");
@@ -151,12 +155,14 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds1[C::STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t lds2[NS > 2 ? C::STAGE : 8];
   __shared__ __attribute__((aligned(16))) uint16_t lds3[NS > 3 ? C::STAGE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t lds4[NS > 4 ? C::STAGE : 8];
   auto stage_buf = [&](auto I) -> uint16_t* {
     constexpr int i = decltype(I)::value;
     if constexpr (i == 0) return lds0;
     else if constexpr (i == 1) return lds1;
     else if constexpr (i == 2) return lds2;
-    else return lds3;
+    else if constexpr (i == 3) return lds3;
+    else return lds4;
   };
 
   // ---- tile placement
@@ -269,20 +275,29 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  // 32 x 32 x 16 fragments: lane holds row (lane & 31), k = 8 * (lane >> 5) .. +7 of a 16-wide k step
+  // 32 x 32 x 16 fragments: lane holds row (lane & 31), k = 8 * (lane >> 5) .. +7 of a 16-wide k step.
+  // Two fragment sets alternate: the set of the next k step is read while the MFMAs of this one run.
   const int fr = lane & 31, fk = lane >> 5;
-  auto mma_step = [&](const uint16_t* sA, const uint16_t* sB, int ks) {
-    bf16x8 af[FM], bfr[FN];
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto read_frags = [&](const uint16_t* sbuf, int ks, auto SET) {
+    constexpr int q = decltype(SET)::value;
+    const uint16_t* sA = sbuf;
+    const uint16_t* sB = sbuf + BM * BK;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(sA + swz<C>(wm0 + 32 * i + fr, 2 * ks + fk));
+    for (int i = 0; i < FM; ++i) fa[q][i] = *reinterpret_cast<const bf16x8*>(sA + swz<C>(wm0 + 32 * i + fr, 2 * ks + fk));
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(sB + swz<C>(wn0 + 32 * j + fr, 2 * ks + fk));
+    for (int j = 0; j < FN; ++j) fb[q][j] = *reinterpret_cast<const bf16x8*>(sB + swz<C>(wn0 + 32 * j + fr, 2 * ks + fk));
+  };
+  auto mma = [&](auto SET) {
+    constexpr int q = decltype(SET)::value;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[q][j], fa[q][i], acc[i][j], 0, 0, 0);
   };
+  constexpr int KS = BK / 16;  // MFMA k steps per K step
+  static_assert(!C::EARLY || (NS * KS) % 2 == 0, "fragment sets alternate consistently across the ring");
   // K steps, rounded up to a multiple of NS: the loop body covers NS steps (one per LDS stage, each stage a
   // compile-time choice) and has no branches, so the compiler's wait counts stay exact.  With KFULL the
   // step count is a multiple of NS and every chunk is in range; otherwise chunks at or past K read as zero,
@@ -290,13 +305,14 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
   const int KT = (p.K + BK - 1) / BK;
   const int KTS = (KT + NS - 1) / NS * NS;
   // vmcnt(n): wait until at most n of this wave's DMA instructions are outstanding (expcnt, lgkmcnt free).
-  constexpr int kNewer = (NS - 2) * (A_G + B_G);  // DMAs issued after the stage needed next
-  static_assert(kNewer < 64, "vmcnt range");
+  // The barrier ending step kt makes stage kt + LEAD visible: the DMAs newer than that stage may stay out.
+  constexpr int kNewer = (NS - 1 - C::LEAD) * (A_G + B_G);
+  static_assert(kNewer >= 0 && kNewer < 64, "vmcnt range");
   constexpr int kWaitNext = 0x0F70 | (kNewer & 15) | ((kNewer >> 4) << 14);
-  // The barrier between steps: this wave's DMA of the next step has landed (vmcnt), every fragment read of
-  // this step has been consumed by an MFMA, and the waves meet.  A __syncthreads() would add a release
-  // fence, which waits for every outstanding DMA (vmcnt(0)) and so drains the whole ring; the raw s_barrier
-  // between compiler-level memory fences keeps the later DMAs in flight.
+  // The barrier between steps: this wave's DMA of stage kt + LEAD has landed (vmcnt), every fragment read
+  // of the stage about to be overwritten has been consumed by an MFMA, and the waves meet.  A
+  // __syncthreads() would add a release fence, which waits for every outstanding DMA (vmcnt(0)) and so
+  // drains the whole ring; the raw s_barrier between compiler-level memory fences keeps later DMAs in flight.
   auto ring_barrier = [&]() {
     __builtin_amdgcn_s_waitcnt(kWaitNext);
     asm volatile("" ::: "memory");
@@ -304,22 +320,37 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
     asm volatile("" ::: "memory");
   };
   // One K step on stage I: start the DMA of step kt + NS - 1 into the stage consumed last step (every wave
-  // passed the barrier after reading it), run this step's MFMAs, wait until this wave's DMA of step kt + 1
-  // has landed, and meet the other waves at the barrier.
+  // passed the barrier after reading it), run this step's MFMAs (with EARLY, the last k step reads the first
+  // fragments of stage kt + 1, visible since the previous barrier), then the barrier.
   auto step = [&](auto I, int kt) {
     constexpr int i = decltype(I)::value;
     uint16_t* cur = stage_buf(std::integral_constant<int, i>{});
-    uint16_t* nxt = stage_buf(std::integral_constant<int, (i + NS - 1) % NS>{});
-    dma_stage((kt + NS - 1) * BK, nxt);
+    dma_stage((kt + NS - 1) * BK, stage_buf(std::integral_constant<int, (i + NS - 1) % NS>{}));
     __builtin_amdgcn_sched_barrier(0);  // keep the DMA issue at the top: the scheduler would sink it
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) mma_step(cur, cur + BM * BK, ks);
+    [&]<int... S>(std::integer_sequence<int, S...>) {
+      ([&] {
+        constexpr int ks = S;
+        constexpr int g = i * KS + ks;  // k step index within the ring pass: fixes the fragment set
+        if constexpr (C::EARLY) {
+          if constexpr (ks + 1 < KS)
+            read_frags(cur, ks + 1, std::integral_constant<int, (g + 1) & 1>{});
+          else
+            read_frags(stage_buf(std::integral_constant<int, (i + 1) % NS>{}), 0,
+                       std::integral_constant<int, (g + 1) & 1>{});
+          mma(std::integral_constant<int, g & 1>{});
+        } else {
+          read_frags(cur, ks, std::integral_constant<int, 0>{});
+          mma(std::integral_constant<int, 0>{});
+        }
+      }(), ...);
+    }(std::make_integer_sequence<int, KS>{});
     ring_barrier();
   };
   [&]<int... I>(std::integer_sequence<int, I...>) {
     (dma_stage(I * BK, stage_buf(std::integral_constant<int, I>{})), ...);
   }(std::make_integer_sequence<int, NS - 1>{});
   ring_barrier();
+  if constexpr (C::EARLY) read_frags(lds0, 0, std::integral_constant<int, 0>{});
   for (int kt = 0; kt < KTS; kt += NS) {
     [&]<int... I>(std::integer_sequence<int, I...>) {
       (step(std::integral_constant<int, I>{}, kt + I), ...);
@@ -377,7 +408,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
     constexpr int WPS = C::STAGE / (TM * TNO);  // wave regions per LDS stage
     static_assert(WPS >= 1 && (NWAVES + WPS - 1) / WPS <= NS, "staging fits");
     const int si = wave / WPS;
-    uint16_t* reg = (si == 0 ? lds0 : si == 1 ? lds1 : si == 2 ? lds2 : lds3) + (wave % WPS) * TM * TNO;
+    uint16_t* reg = (si == 0 ? lds0 : si == 1 ? lds1 : si == 2 ? lds2 : si == 3 ? lds3 : lds4) + (wave % WPS) * TM * TNO;
     auto unit_at = [&](int row, int u) { return row * TNO + 4 * (u ^ ((row / RPB) & (UPR - 1))); };
     auto stage_tile = [&](auto gelu) {
 #pragma unroll
@@ -482,8 +513,14 @@ static hipError_t launch_cfg(const GemmParams& p, int grid_rows_upper, hipStream
   return hipGetLastError();
 }
 
-using BigTile = Cfg<256, 256, 2, 4, 32, 4>;    // 8 waves, 128 KB LDS ring
-using SmallTile = Cfg<128, 128, 2, 2, 64, 4>;  // 4 waves, 128 KB LDS ring
+#ifndef MTP_BIG_CFG
+#define MTP_BIG_CFG 256, 256, 2, 4, 32, 4, true
+#endif
+#ifndef MTP_SMALL_CFG
+#define MTP_SMALL_CFG 128, 128, 4, 2, 64, 4, true
+#endif
+using BigTile = Cfg<MTP_BIG_CFG>;      // 8 waves, 128 KB LDS ring
+using SmallTile = Cfg<MTP_SMALL_CFG>;  // 8 waves, 128 KB LDS ring
 
 // Tile choice: the largest tile that still gives every CU work, else the
 // 128 x 128 tile.  (The 256 x 256 tile needs about 256 tiles to fill the chip.)

@@ -8,7 +8,7 @@
 // needs a stable scatter: one workgroup walks the tokens in 1024-token
 // chunks, ranks each token within its expert by wave ballots plus an
 // across-wave prefix, and carries the running per-expert base between chunks.
-// The work is O(T * E) and runs in a few microseconds; it is not a GEMM.
+// Each token's logits are read once into registers.  The work is O(T * E); it is not a GEMM.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,11 +26,19 @@ struct Choice {
   float w[kMaxTopK];    // their softmax probabilities
 };
 
-__device__ __forceinline__ void choose(const float* __restrict__ lg, int E, int k, Choice& c) {
+// Softmax + top-k of one token whose logits are in registers (EMAX a compile-time capacity >= E, so every
+// index below is static and nothing spills to scratch).  Selection compares the logits themselves (softmax
+// is monotone); ties go to the lower expert index.
+template <int EMAX>
+__device__ __forceinline__ void choose(const float (&lg)[EMAX], int E, int k, Choice& c) {
   float mx = lg[0];
-  for (int e = 1; e < E; ++e) mx = fmaxf(mx, lg[e]);
+#pragma unroll
+  for (int e = 1; e < EMAX; ++e)
+    if (e < E) mx = fmaxf(mx, lg[e]);
   float sum = 0.f;
-  for (int e = 0; e < E; ++e) sum += expf(lg[e] - mx);
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e)
+    if (e < E) sum += expf(lg[e] - mx);
   c.mask = 0;
 #pragma unroll
   for (int s = 0; s < kMaxTopK; ++s) {
@@ -39,8 +47,9 @@ __device__ __forceinline__ void choose(const float* __restrict__ lg, int E, int 
     if (s < k) {
       int best = -1;
       float bv = 0.f;
-      for (int e = 0; e < E; ++e) {
-        if ((c.mask >> e) & 1ull) continue;
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e) {
+        if (e >= E || ((c.mask >> e) & 1ull)) continue;
         const float v = lg[e];
         if (best < 0 || v > bv) { best = e; bv = v; }
       }
@@ -51,6 +60,22 @@ __device__ __forceinline__ void choose(const float* __restrict__ lg, int E, int 
   }
 }
 
+// The token's E logits into registers, read together (16-byte loads when the row allows).
+template <int EMAX>
+__device__ __forceinline__ void load_logits(const float* __restrict__ row, int E, float (&lg)[EMAX]) {
+  if ((E & 3) == 0 && (reinterpret_cast<uintptr_t>(row) & 15) == 0) {
+#pragma unroll
+    for (int e = 0; e < EMAX; e += 4) {
+      float4 v = e < E ? *reinterpret_cast<const float4*>(row + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      lg[e] = v.x; lg[e + 1] = v.y; lg[e + 2] = v.z; lg[e + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) lg[e] = e < E ? row[e] : 0.f;
+  }
+}
+
+template <int EMAX>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ token_idx,
@@ -63,8 +88,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __res
   __syncthreads();
   // pass 1: tokens per expert (integer sums: order-free)
   for (int t = tid; t < T; t += kRouteThreads) {
+    float lg[EMAX];
+    load_logits(logits + (int64_t)t * E, E, lg);
     Choice c;
-    choose(logits + (int64_t)t * E, E, k, c);
+    choose(lg, E, k, c);
 #pragma unroll
     for (int s = 0; s < kMaxTopK; ++s)
       if (s < k) atomicAdd(&cnt[c.e[s]], 1);
@@ -88,7 +115,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __res
     c.mask = 0;
 #pragma unroll
     for (int s = 0; s < kMaxTopK; ++s) { c.e[s] = -1; c.w[s] = 0.f; }
-    if (t < T) choose(logits + (int64_t)t * E, E, k, c);
+    if (t < T) {
+      float lg[EMAX];
+      load_logits(logits + (int64_t)t * E, E, lg);
+      choose(lg, E, k, c);
+    }
     int rank[kMaxTopK];
 #pragma unroll
     for (int s = 0; s < kMaxTopK; ++s) rank[s] = 0;
@@ -149,7 +180,14 @@ static unsigned grid_for(int64_t n) {
 
 hipError_t moe_route(const float* logits, int T, int E, int k, int32_t* offsets, int32_t* token_idx, float* token_w,
                      hipStream_t st) {
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, st, logits, T, E, k, offsets, token_idx, token_w);
+  if (E <= 8)
+    hipLaunchKernelGGL(route_kernel<8>, dim3(1), dim3(kRouteThreads), 0, st, logits, T, E, k, offsets, token_idx, token_w);
+  else if (E <= 16)
+    hipLaunchKernelGGL(route_kernel<16>, dim3(1), dim3(kRouteThreads), 0, st, logits, T, E, k, offsets, token_idx, token_w);
+  else if (E <= 32)
+    hipLaunchKernelGGL(route_kernel<32>, dim3(1), dim3(kRouteThreads), 0, st, logits, T, E, k, offsets, token_idx, token_w);
+  else
+    hipLaunchKernelGGL(route_kernel<64>, dim3(1), dim3(kRouteThreads), 0, st, logits, T, E, k, offsets, token_idx, token_w);
   return hipGetLastError();
 }
 

@@ -309,3 +309,22 @@ def test_moe_8x_top2_full_size():
     tokens = sample_rows(w.dims["T"], 8, 5)
     _run_moe(w, tokens)
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (1500, 16, 4), (2049, 64, 8), (777, 6, 3), (4096, 8, 2)])
+def test_router_tables(T, E, k):
+    say("router", T, E, k)
+    logits = synth.normal_f32(400 + E, T, E)
+    if T > 2:  # exact ties: equal logits must go to the lower expert index on both sides
+        logits[1, :] = 0.5
+        logits[2, : min(E, 3)] = 2.0
+    lg = torch.from_numpy(logits).cuda()
+    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    idx = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    mtp.mtp_moe_route(lg, k, offs, idx, w)
+    torch.cuda.synchronize()
+    r_offs, r_idx, r_w = oracle.moe_route(logits, k)
+    assert np.array_equal(offs.cpu().numpy(), r_offs)
+    assert np.array_equal(idx.cpu().numpy(), r_idx)
+    assert np.allclose(w.cpu().numpy(), r_w, rtol=2e-6, atol=0)
