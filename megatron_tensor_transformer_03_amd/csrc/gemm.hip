@@ -62,14 +62,18 @@ struct Cfg {
   static constexpr int CPR = BK / 8;                           // 16-byte chunks per LDS row
   static constexpr int RPL = 256 / (2 * BK);                   // LDS rows per 256-byte bank line
   static constexpr int ROWS_PER_DMA = 64 / CPR;                // rows one 64-lane DMA instruction fills
-  static constexpr int A_G = BM / ROWS_PER_DMA / NWAVES;       // DMA instructions per wave per stage (A)
-  static constexpr int B_G = BN / ROWS_PER_DMA / NWAVES;       // (B)
+  static constexpr int GA = BM / ROWS_PER_DMA, GB = BN / ROWS_PER_DMA;  // DMA groups per stage (A, B)
+  // DMA instructions per wave per stage: group g goes to wave g % NWAVES; when the groups do not divide
+  // evenly, the spare slots load nothing (out of range) into a scratch LDS block, so every wave issues the
+  // same number of DMAs and the wait counts stay uniform.
+  static constexpr int D = (GA + GB + NWAVES - 1) / NWAVES;
   static constexpr int STAGE = (BM + BN) * BK;                 // elements per LDS stage
   static_assert(BK == 32 || BK == 64, "K step");
   static_assert(NS >= 2 + LEAD - 1 && NS <= 5, "LDS stages");
+  static_assert(NWAVES % 4 == 0, "whole waves per SIMD");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "32 x 32 fragments");
-  static_assert(BM % (ROWS_PER_DMA * NWAVES) == 0 && BN % (ROWS_PER_DMA * NWAVES) == 0, "DMA split");
-  static_assert(NS * STAGE * 2 <= 160 * 1024, "LDS capacity");
+  static_assert(BM % ROWS_PER_DMA == 0 && BN % ROWS_PER_DMA == 0, "DMA groups");
+  static_assert(NS * STAGE * 2 + 1024 <= 160 * 1024, "LDS capacity");
 };
 
 // Element offset of (row, 16-byte chunk) in an LDS stage: rows of BK elements, chunks permuted by XOR with
@@ -146,7 +150,7 @@ template <class C, int MODE, bool GROUPED, bool KFULL>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NS = C::NS, WAVES_N = C::WAVES_N, NWAVES = C::NWAVES;
   constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, CPR = C::CPR, RPL = C::RPL;
-  constexpr int A_G = C::A_G, B_G = C::B_G, ROWS_PER_DMA = C::ROWS_PER_DMA;
+  constexpr int D = C::D, GA = C::GA, ROWS_PER_DMA = C::ROWS_PER_DMA;
   static_assert(MODE != MODE_SWIGLU || TN % 64 == 0, "gate/up fragment pairs");
   constexpr int NB_OUT = MODE == MODE_SWIGLU ? BN / 2 : BN;  // output columns per tile
 
@@ -156,6 +160,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds2[NS > 2 ? C::STAGE : 8];
   __shared__ __attribute__((aligned(16))) uint16_t lds3[NS > 3 ? C::STAGE : 8];
   __shared__ __attribute__((aligned(16))) uint16_t lds4[NS > 4 ? C::STAGE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_spare[(C::GA + C::GB) % C::NWAVES ? 512 : 8];
   auto stage_buf = [&](auto I) -> uint16_t* {
     constexpr int i = decltype(I)::value;
     if constexpr (i == 0) return lds0;
@@ -216,34 +221,35 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(b_base, 2 * b_extent < (int64_t)kOOB ? 2 * b_extent : (int64_t)kOOB);
   // Direct-to-LDS loads: one buffer_load_dwordx4 ... lds moves 64 lanes x 16 B = ROWS_PER_DMA LDS rows,
   // lane l filling row (l / CPR), chunk (l % CPR) of its group.  The LDS layout is swizzled (see swz), so
-  // each lane loads the global chunk that lands at its slot.
+  // each lane loads the global chunk that lands at its slot.  Groups 0 .. GA-1 are rows of A, the next GB
+  // are rows of B (stored right after A in the stage); slot j of a wave carries group j * NWAVES + wave.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int lrow = lane / CPR;
-  uint32_t a_off[A_G], b_off[B_G];
-  int a_kc[A_G], b_kc[B_G];  // K element offset of each lane's chunk
+  uint32_t d_off[D];
+  int d_kc[D];  // K element offset of each lane's chunk
 #pragma unroll
-  for (int i = 0; i < A_G; ++i) {
-    const int r = ROWS_PER_DMA * (wave_u * A_G + i) + lrow;
+  for (int j = 0; j < D; ++j) {
+    const int g = j * NWAVES + wave_u;
+    const int r = ROWS_PER_DMA * g + lrow - (g < GA ? 0 : BM);  // row within A or within B
     const int c = (lane % CPR) ^ ((r / RPL) & (CPR - 1));
-    a_kc[i] = 8 * c;
-    if (p.a_rows) {
-      const int m = m0 + r;
-      a_off[i] = m < rows ? 2u * (uint32_t)((int64_t)p.a_rows[row_base + m] * p.lda + 8 * c) : kOOB;
+    d_kc[j] = 8 * c;
+    if (g < GA) {
+      if (p.a_rows) {
+        const int m = m0 + r;
+        d_off[j] = m < rows ? 2u * (uint32_t)((int64_t)p.a_rows[row_base + m] * p.lda + 8 * c) : kOOB;
+      } else {
+        d_off[j] = 2u * (uint32_t)(r * p.lda + 8 * c);
+      }
+    } else if (g < GA + C::GB) {
+      int n = r;
+      if constexpr (MODE == MODE_SWIGLU) {
+        const int g32 = r >> 5;
+        n = 32 * (g32 >> 1) + (r & 31) + ((g32 & 1) ? (int)p.up_offset : 0);
+      }
+      d_off[j] = 2u * (uint32_t)(n * p.ldb + 8 * c);
     } else {
-      a_off[i] = 2u * (uint32_t)(r * p.lda + 8 * c);
+      d_off[j] = kOOB;  // spare slot
     }
-  }
-#pragma unroll
-  for (int i = 0; i < B_G; ++i) {
-    const int r = ROWS_PER_DMA * (wave_u * B_G + i) + lrow;
-    const int c = (lane % CPR) ^ ((r / RPL) & (CPR - 1));
-    b_kc[i] = 8 * c;
-    int n = r;
-    if constexpr (MODE == MODE_SWIGLU) {
-      const int g32 = r >> 5;
-      n = 32 * (g32 >> 1) + (r & 31) + ((g32 & 1) ? (int)p.up_offset : 0);
-    }
-    b_off[i] = 2u * (uint32_t)(n * p.ldb + 8 * c);
   }
   typedef __attribute__((address_space(3))) void* lds_ptr;
   // The scalar offset is not part of the hardware range check (only the per-lane offset is), so it stays
@@ -252,18 +258,12 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
   auto dma_stage = [&](int k0, uint16_t* sbuf) {
     const int soff = k0 < p.K ? 2 * k0 : 0;
 #pragma unroll
-    for (int i = 0; i < A_G; ++i) {
-      uint32_t vo = a_off[i];
-      if constexpr (!KFULL) vo = k0 + a_kc[i] < p.K ? vo : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr)(sbuf + (wave_u * A_G + i) * ROWS_PER_DMA * BK), 16,
-                                               vo, soff, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < B_G; ++i) {
-      uint32_t vo = b_off[i];
-      if constexpr (!KFULL) vo = k0 + b_kc[i] < p.K ? vo : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          b_rsrc, (lds_ptr)(sbuf + BM * BK + (wave_u * B_G + i) * ROWS_PER_DMA * BK), 16, vo, soff, 0, 0);
+    for (int j = 0; j < D; ++j) {
+      const int g = j * NWAVES + wave_u;  // uniform
+      uint32_t vo = d_off[j];
+      if constexpr (!KFULL) vo = k0 + d_kc[j] < p.K ? vo : kOOB;
+      uint16_t* dst = g < GA + C::GB ? sbuf + g * ROWS_PER_DMA * BK : lds_spare;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g < GA ? a_rsrc : b_rsrc, (lds_ptr)dst, 16, vo, soff, 0, 0);
     }
   };
 
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
   const int KTS = (KT + NS - 1) / NS * NS;
   // vmcnt(n): wait until at most n of this wave's DMA instructions are outstanding (expcnt, lgkmcnt free).
   // The barrier ending step kt makes stage kt + LEAD visible: the DMAs newer than that stage may stay out.
-  constexpr int kNewer = (NS - 1 - C::LEAD) * (A_G + B_G);
+  constexpr int kNewer = (NS - 1 - C::LEAD) * D;
   static_assert(kNewer >= 0 && kNewer < 64, "vmcnt range");
   constexpr int kWaitNext = 0x0F70 | (kNewer & 15) | ((kNewer >> 4) << 14);
   // The barrier between steps: this wave's DMA of stage kt + LEAD has landed (vmcnt), every fragment read
@@ -402,14 +402,18 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
     // then reads it back row-contiguously; no cross-wave synchronisation is needed.  Regions are row-major
     // with 8-byte units permuted per row so the 32 lanes of a write (32 rows, one unit) and of a read (2-4
     // whole rows) hit distinct banks.
-    constexpr int UPR = TNO / 4;  // 8-byte units per row
-    constexpr int RPB = 32 / UPR; // rows sharing one 256-byte bank line
-    static_assert(UPR == 8 || UPR == 16 || UPR == 32, "unit layout");
+    // UPR 8-byte units per row (a multiple of 8).  A write has 32 lanes store one unit of 32 consecutive
+    // rows; rows whose starts fall on the same bank offset (RP apart) get distinct XOR permutations of the
+    // unit index within blocks of W units, W the largest power of two dividing UPR (at most 32).
+    constexpr int UPR = TNO / 4;
+    constexpr int W = (UPR & -UPR) < 32 ? (UPR & -UPR) : 32;
+    constexpr int RP = 32 / W;
+    static_assert(UPR % 8 == 0 && (TM * UPR) % 64 == 0, "unit layout");
     constexpr int WPS = C::STAGE / (TM * TNO);  // wave regions per LDS stage
     static_assert(WPS >= 1 && (NWAVES + WPS - 1) / WPS <= NS, "staging fits");
     const int si = wave / WPS;
     uint16_t* reg = (si == 0 ? lds0 : si == 1 ? lds1 : si == 2 ? lds2 : si == 3 ? lds3 : lds4) + (wave % WPS) * TM * TNO;
-    auto unit_at = [&](int row, int u) { return row * TNO + 4 * (u ^ ((row / RPB) & (UPR - 1))); };
+    auto unit_at = [&](int row, int u) { return row * TNO + 4 * (u ^ ((row / RP) & (W - 1))); };
     auto stage_tile = [&](auto gelu) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -425,13 +429,13 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
     };
     if (MODE == MODE_COL && p.act == 1) stage_tile(std::true_type{});
     else stage_tile(std::false_type{});
-    // read back: 64 lanes cover 64 / UPR whole rows per pass
-    const int u = lane % UPR, rsub = lane / UPR;
-    const int n = ncol0 + 4 * u;
-    const int valid = p.Nout - n;
+    // read back row-contiguously: pass q covers units 64 q .. 64 q + 63 of the row-major tile
 #pragma unroll 4
-    for (int r0 = 0; r0 < TM; r0 += 64 / UPR) {
-      const int row = r0 + rsub;
+    for (int q = 0; q < TM * UPR / 64; ++q) {
+      const int id = 64 * q + lane;
+      const int row = id / UPR, u = id % UPR;
+      const int n = ncol0 + 4 * u;
+      const int valid = p.Nout - n;
       const int m = m0 + wm0 + row;
       const uint2 d = *reinterpret_cast<const uint2*>(reg + unit_at(row, u));
       if (m < rows && valid > 0) {
@@ -519,17 +523,36 @@ static hipError_t launch_cfg(const GemmParams& p, int grid_rows_upper, hipStream
 #ifndef MTP_SMALL_CFG
 #define MTP_SMALL_CFG 128, 128, 4, 2, 64, 4, true
 #endif
-using BigTile = Cfg<MTP_BIG_CFG>;      // 8 waves, 128 KB LDS ring
-using SmallTile = Cfg<MTP_SMALL_CFG>;  // 8 waves, 128 KB LDS ring
+using BigTile = Cfg<MTP_BIG_CFG>;              // 8 waves (wave tile 128 x 64), 128 KB LDS ring
+using WideTile = Cfg<256, 192, 4, 2, 32, 4, true>;  // 8 waves (64 x 96), 112 KB
+using HalfTile = Cfg<256, 128, 4, 2, 32, 4, true>;  // 8 waves (64 x 64), 96 KB
+using SmallTile = Cfg<MTP_SMALL_CFG>;          // 8 waves (32 x 64), 128 KB
 
-// Tile choice: the largest tile that still gives every CU work, else the
-// 128 x 128 tile.  (The 256 x 256 tile needs about 256 tiles to fill the chip.)
+// Tile choice: the estimated time of a launch is the number of waves of tiles over the 256 CUs times the
+// time of one tile, BM * BN / efficiency (measured relative MFMA efficiency of the tile shapes on large K).
+// Wave quantisation matters at these shard shapes: e.g. 2048 x 4608 is 144 tiles of 256 x 256 (56% of the
+// CUs busy) but 192 tiles of 256 x 192.
 template <int MODE>
 static hipError_t dispatch(const GemmParams& p, hipStream_t st) {
-  const int64_t nb_big = MODE == MODE_SWIGLU ? 128 : 256;
-  const int64_t big_tiles = ((p.M + 255) / 256) * ((p.Nout + nb_big - 1) / nb_big);
-  if (big_tiles >= 192) return launch_cfg<BigTile, MODE, false>(p, 0, st);
-  return launch_cfg<SmallTile, MODE, false>(p, 0, st);
+  struct Opt { int bm, bn; double eff; int id; };
+  const Opt opts[] = {{256, 256, 1.00, 0}, {256, 192, 0.95, 1}, {256, 128, 0.85, 2}, {128, 128, 0.72, 3}};
+  int best = 3;
+  double best_t = 1e300;
+  for (const Opt& o : opts) {
+    if (MODE == MODE_SWIGLU && o.id == 1) continue;  // gate/up pairs need wave tiles of 64 B rows
+    const int64_t nbo = MODE == MODE_SWIGLU ? o.bn / 2 : o.bn;
+    const int64_t tiles = ((p.M + o.bm - 1) / o.bm) * ((p.Nout + nbo - 1) / nbo);
+    const double t = (double)((tiles + 255) / 256) * o.bm * o.bn / o.eff;
+    if (t < best_t * 0.999) { best_t = t; best = o.id; }
+  }
+  switch (best) {
+    case 0: return launch_cfg<BigTile, MODE, false>(p, 0, st);
+    case 1:
+      if constexpr (MODE != MODE_SWIGLU) return launch_cfg<WideTile, MODE, false>(p, 0, st);
+      return hipErrorInvalidValue;
+    case 2: return launch_cfg<HalfTile, MODE, false>(p, 0, st);
+    default: return launch_cfg<SmallTile, MODE, false>(p, 0, st);
+  }
 }
 
 hipError_t gemm(const GemmParams& p, int mode, hipStream_t st) {
