@@ -26,8 +26,15 @@
  *  - bf16 tensors are raw bit patterns (uint16_t), row-major with the given
  *    row pitch (in elements).  Weights are [out x in].  Accumulation is fp32;
  *    every conversion to bf16 rounds to nearest, ties to even.
- *  - Pointers are device pointers owned by the caller.  The library never
- *    allocates, frees, synchronises, or keeps a pointer after returning.
+ *  - Pointers are device pointers owned by the caller; the library keeps none
+ *    after returning.  The one allocation the library makes itself is the
+ *    workspace of the split-K schedule (see mtp_gemm_plan): per device and
+ *    stream, allocated on the first call that needs it (and grown, after a
+ *    synchronisation of that stream, when a later call needs more), at most
+ *    512 MB of fp32 partial tiles plus one int32 per tile, and kept until
+ *    mtp_release_workspaces() or the end of the process.  Calls on one
+ *    stream share its workspace safely; nothing else allocates or
+ *    synchronises.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL is the default stream)
  *    and the call returns at once.  Faults surface at the caller's next sync.
  *  - Every argument is validated before anything is enqueued; on an error
@@ -153,6 +160,26 @@ mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, i
                                const int32_t* expert_offsets, const int32_t* token_idx,
                                const float* token_w, const mtp_bf16* W1t, const mtp_bf16* W2t,
                                mtp_bf16* Z_ws, float* Yacc, mtp_bf16* Y, void* stream);
+
+/*
+ * The launch plan the GEMM calls would use for an [M x K] . [N x K]^T
+ * product with activation act (SWIGLU: N counts gate and up rows): the tile
+ * (*tile_m x *tile_n output elements; the MFMA tiles are 256 x 256,
+ * 256 x 192, 256 x 128 and 128 x 128) and *split_k, 0 for one workgroup per
+ * tile, else the number of K chunks each tile is cut into (split-K: one
+ * workgroup per CU works through the (tile, chunk) units and the tile's last
+ * finisher adds the chunks' fp32 partial sums in chunk order, so results are
+ * deterministic but round differently from the unsplit schedule).  Split-K is
+ * chosen when whole waves of tiles would leave many CUs idle.  The same size
+ * rules as mtp_column_linear apply; nothing is launched.
+ * mtp_row_linear_partial plans as act = NONE.
+ */
+mtp_status mtp_gemm_plan(int64_t M, int64_t N, int64_t K, mtp_act act, int* tile_m, int* tile_n,
+                         int* split_k);
+
+/* Frees the split-K workspaces of the current device after waiting for the
+ * device to finish its work.  Later calls allocate again as needed. */
+mtp_status mtp_release_workspaces(void);
 
 /* Static text for a status code. */
 const char* mtp_status_string(mtp_status s);

@@ -44,6 +44,8 @@ def lib():
             "mtp_qkv_forward": [vp, i64, i64, i64, vp, i64, vp, ci, ci, ci, vp, i64, vp],
             "mtp_moe_route": [vp, i64, ci, ci, vp, vp, vp, vp],
             "mtp_moe_mlp_forward": [vp, i64, i64, ci, i64, ci, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+            "mtp_gemm_plan": [i64, i64, i64, ci, vp, vp, vp],
+            "mtp_release_workspaces": [],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -83,6 +85,19 @@ def _ld(t):
 def _stream(t):
     import torch
     return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def mtp_gemm_plan(M, N, K, act=ACT_NONE):
+    """(tile_m, tile_n, split_k) of the GEMM launch for these sizes (split_k 0: one workgroup per tile; else
+    the number of K chunks per tile of the split-K schedule)."""
+    out = [ctypes.c_int(0) for _ in range(3)]
+    _check("mtp_gemm_plan", lib().mtp_gemm_plan(M, N, K, act, *[ctypes.addressof(o) for o in out]))
+    return tuple(o.value for o in out)
+
+
+def mtp_release_workspaces():
+    """Free the split-K workspaces of the current device (waits for the device first)."""
+    _check("mtp_release_workspaces", lib().mtp_release_workspaces())
 
 
 def mtp_column_linear(X, Wt, bias, Y, act=ACT_NONE):

@@ -115,6 +115,27 @@ const char* mtp_status_string(mtp_status s) {
   return "unknown status";
 }
 
+mtp_status mtp_gemm_plan(int64_t M, int64_t N, int64_t K, mtp_act act, int* tile_m, int* tile_n, int* split_k) {
+  TRY(check_dims(M, N, K));
+  if (act != MTP_ACT_NONE && act != MTP_ACT_GELU && act != MTP_ACT_SWIGLU)
+    return fail(MTP_ERR_SHAPE, "unknown activation %d", (int)act);
+  if (act == MTP_ACT_SWIGLU && N % 2 != 0) return fail(MTP_ERR_SHAPE, "SwiGLU needs an even N (got %lld)", (long long)N);
+  if (!tile_m || !tile_n || !split_k) return fail(MTP_ERR_NULL, "an output pointer is NULL");
+  TRY(check_device());
+  const mtp::GemmPlan pl = mtp::gemm_plan(act == MTP_ACT_SWIGLU ? mtp::MODE_SWIGLU : mtp::MODE_COL, M,
+                                          act == MTP_ACT_SWIGLU ? N / 2 : N, K);
+  *tile_m = pl.bm;
+  *tile_n = pl.bn;
+  *split_k = pl.split_groups > 0 ? pl.split_chunks : 0;
+  g_err[0] = 0;
+  return MTP_OK;
+}
+
+mtp_status mtp_release_workspaces(void) {
+  TRY(check_device());
+  return launched(mtp::release_split_workspaces(), "release workspaces");
+}
+
 mtp_status mtp_column_linear(const mtp_bf16* X, int64_t ldx, const mtp_bf16* Wt, int64_t ldw, const mtp_bf16* bias,
                              mtp_bf16* Y, int64_t ldy, int64_t M, int64_t N, int64_t K, mtp_act act, void* stream) {
   TRY(check_dims(M, N, K));

@@ -33,7 +33,17 @@ struct GemmParams {
   const int32_t* group_offsets = nullptr;  // grouped: [groups + 1] row offsets in device memory
   int groups = 0;
   int64_t group_stride_B = 0;       // grouped: elements between consecutive groups' B
+  float* sk_ws = nullptr;           // split schedule: partial-tile slots (set at launch)
+  int sk_chunks = 0;                // split schedule: K chunks per tile
+  int* sk_cnt = nullptr;            // split schedule: per-tile arrival counters, zero between launches
 };
+
+// Tile and schedule of a launch (split_groups 0: one workgroup per tile).
+struct GemmPlan {
+  int bm = 0, bn = 0, split_groups = 0, id = 0, split_chunks = 0;
+};
+GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K);
+hipError_t release_split_workspaces();
 
 hipError_t gemm(const GemmParams& p, int mode, hipStream_t st);
 // rows_upper: total rows over all groups (an upper bound is enough; spare tiles exit).

@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -67,13 +69,14 @@ struct Cfg {
   // evenly, the spare slots load nothing (out of range) into a scratch LDS block, so every wave issues the
   // same number of DMAs and the wait counts stay uniform.
   static constexpr int D = (GA + GB + NWAVES - 1) / NWAVES;
+  static constexpr bool SPARE = (GA + GB) % NWAVES != 0;
   static constexpr int STAGE = (BM + BN) * BK;                 // elements per LDS stage
   static_assert(BK == 32 || BK == 64, "K step");
   static_assert(NS >= 2 + LEAD - 1 && NS <= 5, "LDS stages");
   static_assert(NWAVES % 4 == 0, "whole waves per SIMD");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "32 x 32 fragments");
   static_assert(BM % ROWS_PER_DMA == 0 && BN % ROWS_PER_DMA == 0, "DMA groups");
-  static_assert(NS * STAGE * 2 + 1024 <= 160 * 1024, "LDS capacity");
+  static_assert(NS * STAGE * 2 + (SPARE ? 1024 : 0) <= 160 * 1024, "LDS capacity");
 };
 
 // Element offset of (row, 16-byte chunk) in an LDS stage: rows of BK elements, chunks permuted by XOR with
@@ -110,11 +113,14 @@ __device__ __forceinline__ float gelu_erf(float x) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
-// Tile coordinates of this workgroup: XCD-aware remap, then GROUP_M row grouping.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
-  int id = blockIdx.x;
-  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+// Workgroup ids alternate over the 8 XCDs (each with its own L2); remapped so that each XCD gets a
+// contiguous range of logical ids.
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  return (total & 7) == 0 ? (id & 7) * (total >> 3) + (id >> 3) : id;
+}
+// Tile of logical id `id`: GROUP_M tile rows at a time, column-major inside the group, so consecutive ids
+// share A and B panels.
+__device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
   constexpr int GROUP_M = 4;
   const int per_group = GROUP_M * tiles_n;
   const int g = id / per_group;
@@ -146,8 +152,11 @@ __device__ __forceinline__ void store4_bf16(uint16_t* dst, const float v[4], int
   }
 }
 
-template <class C, int MODE, bool GROUPED, bool KFULL>
-__global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
+template <class C, int MODE, bool GROUPED, bool KFULL, bool SPLIT>
+__global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
+  // A private copy of the parameters: read once into scalar registers, rather than reloaded from the
+  // kernel argument segment (each reload waits on the LDS/scalar counter) wherever a field is used.
+  GemmParams p = p_arg;
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NS = C::NS, WAVES_N = C::WAVES_N, NWAVES = C::NWAVES;
   constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, CPR = C::CPR, RPL = C::RPL;
   constexpr int D = C::D, GA = C::GA, ROWS_PER_DMA = C::ROWS_PER_DMA;
@@ -160,7 +169,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds2[NS > 2 ? C::STAGE : 8];
   __shared__ __attribute__((aligned(16))) uint16_t lds3[NS > 3 ? C::STAGE : 8];
   __shared__ __attribute__((aligned(16))) uint16_t lds4[NS > 4 ? C::STAGE : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_spare[(C::GA + C::GB) % C::NWAVES ? 512 : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_spare[C::SPARE ? 512 : 8];  // dropped unless used
   auto stage_buf = [&](auto I) -> uint16_t* {
     constexpr int i = decltype(I)::value;
     if constexpr (i == 0) return lds0;
@@ -170,28 +179,26 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
     else return lds4;
   };
 
-  // ---- tile placement
-  int tm, tn;
-  int row_base = 0, rows = p.M;  // rows of this tile's group (all rows when ungrouped)
-  const uint16_t* __restrict__ B = p.B;
-  if constexpr (GROUPED) {
-    // blockIdx.x = row-tile slot * tiles_n + tn; slots are laid over the groups in order.
-    const int tiles_n = (p.Nout + NB_OUT - 1) / NB_OUT;
-    int slot = blockIdx.x / tiles_n;
-    tn = blockIdx.x - slot * tiles_n;
-    int g = 0;
-    for (; g < p.groups; ++g) {
-      const int lo = p.group_offsets[g], hi = p.group_offsets[g + 1];
-      const int nt = (hi - lo + BM - 1) / BM;
-      if (slot < nt) { row_base = lo; rows = hi - lo; break; }
-      slot -= nt;
-    }
-    if (g == p.groups) return;  // spare slot of the upper-bound grid
-    tm = slot;
-    B += (int64_t)g * p.group_stride_B;
-  } else {
-    tile_coords((p.M + BM - 1) / BM, (p.Nout + NB_OUT - 1) / NB_OUT, tm, tn);
-  }
+  __shared__ int sk_flag;
+  // K steps, rounded up to a multiple of NS: the loop body covers NS steps (one per LDS stage, each stage a
+  // compile-time choice) and has no branches, so the compiler's wait counts stay exact.  With KFULL the
+  // step count is a multiple of NS and every chunk is in range; otherwise chunks at or past K read as zero,
+  // so padding steps multiply zeros.
+  const int KT = (p.K + BK - 1) / BK;
+  const int KTS = (KT + NS - 1) / NS * NS;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.Nout + NB_OUT - 1) / NB_OUT;
+  // split schedule (SPLIT only): each tile's RI ring passes in S chunks, partial sums of tile t in slots
+  // t * S .. t * S + S - 1
+  const int RI = KTS / NS;
+  const int G = gridDim.x;
+  const int S = p.sk_chunks;
+  auto slot_of = [&](int c, int t) { return t * S + c; };
+
+  // ---- one tile: rows m0 .. m0 + BM - 1 of the row group at row_base, K steps kt0 .. kt1 - 1.  With
+  // SPLIT and sk_partial, the K range is part of the tile's and the partial sums of all workgroups on the
+  // tile are added before the epilogue (see the split schedule below).
+  auto run_tile = [&](int tm, int tn, int row_base, int rows, const uint16_t* __restrict__ B, int kt0, int kt1,
+                      int sk_tile, int sk_which, int sk_first, int sk_last, bool sk_partial) {
   const int m0 = tm * BM;  // relative to row_base
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave / WAVES_N) * TM, wn0 = (wave % WAVES_N) * TN;
@@ -262,7 +269,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
       const int g = j * NWAVES + wave_u;  // uniform
       uint32_t vo = d_off[j];
       if constexpr (!KFULL) vo = k0 + d_kc[j] < p.K ? vo : kOOB;
-      uint16_t* dst = g < GA + C::GB ? sbuf + g * ROWS_PER_DMA * BK : lds_spare;
+      uint16_t* dst = sbuf + g * ROWS_PER_DMA * BK;
+      if constexpr (C::SPARE) dst = g < GA + C::GB ? dst : lds_spare;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(g < GA ? a_rsrc : b_rsrc, (lds_ptr)dst, 16, vo, soff, 0, 0);
     }
   };
@@ -298,12 +306,6 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
   };
   constexpr int KS = BK / 16;  // MFMA k steps per K step
   static_assert(!C::EARLY || (NS * KS) % 2 == 0, "fragment sets alternate consistently across the ring");
-  // K steps, rounded up to a multiple of NS: the loop body covers NS steps (one per LDS stage, each stage a
-  // compile-time choice) and has no branches, so the compiler's wait counts stay exact.  With KFULL the
-  // step count is a multiple of NS and every chunk is in range; otherwise chunks at or past K read as zero,
-  // so padding steps multiply zeros.
-  const int KT = (p.K + BK - 1) / BK;
-  const int KTS = (KT + NS - 1) / NS * NS;
   // vmcnt(n): wait until at most n of this wave's DMA instructions are outstanding (expcnt, lgkmcnt free).
   // The barrier ending step kt makes stage kt + LEAD visible: the DMAs newer than that stage may stay out.
   constexpr int kNewer = (NS - 1 - C::LEAD) * D;
@@ -346,12 +348,13 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
     }(std::make_integer_sequence<int, KS>{});
     ring_barrier();
   };
+  if constexpr (SPLIT) __syncthreads();  // the previous tile's epilogue may still read the LDS stages
   [&]<int... I>(std::integer_sequence<int, I...>) {
-    (dma_stage(I * BK, stage_buf(std::integral_constant<int, I>{})), ...);
+    (dma_stage((kt0 + I) * BK, stage_buf(std::integral_constant<int, I>{})), ...);
   }(std::make_integer_sequence<int, NS - 1>{});
   ring_barrier();
   if constexpr (C::EARLY) read_frags(lds0, 0, std::integral_constant<int, 0>{});
-  for (int kt = 0; kt < KTS; kt += NS) {
+  for (int kt = kt0; kt < kt1; kt += NS) {
     [&]<int... I>(std::integer_sequence<int, I...>) {
       (step(std::integral_constant<int, I>{}, kt + I), ...);
     }(std::make_integer_sequence<int, NS>{});
@@ -359,6 +362,72 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
   // The last steps prefetched stages past K (never consumed); drain them before the epilogue reuses LDS.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
+
+  if constexpr (SPLIT) {
+    if (sk_partial) {
+      // Every workgroup on the tile stores its partial accumulators to its own workspace slot (float4s in
+      // register order, thread-linear, so the stores and the loads below are contiguous per wave), then
+      // counts itself in on the tile's counter.  The last to arrive adds the slots in workgroup order (a
+      // fixed order, so the sum does not depend on arrival order), resets the counter for the next launch
+      // and runs the epilogue; the others are done with the tile.  Nobody waits on anybody.
+      // The slots and the counter are accessed with device-scope coherent operations (sc1: written through
+      // to, and read from, the point where the XCDs' L2s are coherent) and ordered by waiting for the slot
+      // stores to complete before counting in, so no fence has to write back or invalidate whole L2s
+      // (which would evict the operand panels the other workgroups on the XCD are streaming).
+      constexpr int Q = FM * FN * 4;   // float4 per thread
+      constexpr int kSc1 = 16;         // cache policy: device scope
+      const int64_t slot_bytes = (int64_t)Q * C::NT * 16;
+      const __amdgpu_buffer_rsrc_t ws = make_rsrc(p.sk_ws, (int64_t)tiles_m * tiles_n * S * slot_bytes);
+      typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+      const int mine = (int)(sk_which * slot_bytes) + 16 * tid;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ws,
+                                                   mine + ((i * FN + j) * 4 + q) * C::NT * 16, 0, kSc1);
+          }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's slot stores have completed
+      __syncthreads();
+      if (tid == 0)
+        sk_flag = __hip_atomic_fetch_add(p.sk_cnt + sk_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  sk_last - sk_first;
+      __syncthreads();
+      if (!sk_flag) return;
+      if (tid == 0) __hip_atomic_store(p.sk_cnt + sk_tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // one 32 x 32 fragment at a time (the scheduler barrier keeps the loads of the next fragment from
+      // being hoisted, which would need registers for all of them while the accumulators are live)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int base = ((i * FN + j) * 4) * C::NT * 16 + 16 * tid;
+          float4 v[4];
+          const int s0 = (int)(slot_of(sk_first, sk_tile) * slot_bytes) + base;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            v[q] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ws, s0 + q * C::NT * 16, 0, kSc1));
+          for (int c = sk_first + 1; c <= sk_last; ++c) {
+            const int sc = (int)(slot_of(c, sk_tile) * slot_bytes) + base;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 w =
+                  __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ws, sc + q * C::NT * 16, 0, kSc1));
+              v[q].x += w.x; v[q].y += w.y; v[q].z += w.z; v[q].w += w.w;
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[i][j][4 * q] = v[q].x; acc[i][j][4 * q + 1] = v[q].y;
+            acc[i][j][4 * q + 2] = v[q].z; acc[i][j][4 * q + 3] = v[q].w;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+  }
 
   // ---- epilogue.  Weights were the MFMA's first operand, so lane holds output row (lane & 31) of its
   // 32-row fragment and, in register 4*jj + r, column 8*jj + 4*(lane >> 5) + r of its 32-column fragment.
@@ -371,16 +440,21 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
   constexpr bool kBias = MODE != MODE_COMBINE;
   float bias_g[kBias ? FNO : 1][4][4], bias_u[MODE == MODE_SWIGLU ? FNO : 1][4][4];
   if constexpr (kBias) {
+    // Through a buffer resource that is empty without a bias and ends at the bias's last element: absent
+    // and out-of-range elements read as zero, with no branch per element.
     const bool has_bias = p.bias != nullptr && (MODE != MODE_ROW || p.Y != nullptr);
+    const int64_t blen = MODE == MODE_SWIGLU ? p.up_offset + p.Nout : p.Nout;
+    const __amdgpu_buffer_rsrc_t brs = make_rsrc(p.bias, has_bias ? 2 * blen : 0);
 #pragma unroll
     for (int jo = 0; jo < FNO; ++jo)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int c = min(ncol0 + 32 * jo + 8 * jj + col4 + r, p.Nout - 1);
-          bias_g[jo][jj][r] = has_bias ? from_bf16(p.bias[c]) : 0.f;
-          if constexpr (MODE == MODE_SWIGLU) bias_u[jo][jj][r] = has_bias ? from_bf16(p.bias[p.up_offset + c]) : 0.f;
+          const int c = ncol0 + 32 * jo + 8 * jj + col4 + r;
+          bias_g[jo][jj][r] = from_bf16(__builtin_amdgcn_raw_buffer_load_b16(brs, 2 * c, 0, 0));
+          if constexpr (MODE == MODE_SWIGLU)
+            bias_u[jo][jj][r] = from_bf16(__builtin_amdgcn_raw_buffer_load_b16(brs, 2 * ((int)p.up_offset + c), 0, 0));
         }
   }
   // output value of (fragment row block i, output fragment jo, run jj, element r)
@@ -443,63 +517,183 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p) {
         if (valid >= 4) {
           *reinterpret_cast<uint2*>(dst) = d;
         } else {
-          const uint16_t h[4] = {(uint16_t)d.x, (uint16_t)(d.x >> 16), (uint16_t)d.y, (uint16_t)(d.y >> 16)};
-          for (int q = 0; q < valid; ++q) dst[q] = h[q];
+          // (constant indices: a runtime-indexed local array would be placed in LDS)
+          dst[0] = (uint16_t)d.x;
+          if (valid > 1) dst[1] = (uint16_t)(d.x >> 16);
+          if (valid > 2) dst[2] = (uint16_t)d.y;
         }
       }
     }
     return;
   }
+  // Direct stores: ROW with an fp32 target (the uniform choices are made once, outside the element loops)
+  // and COMBINE.
+  auto direct = [&](auto ACCUM, auto WITH_Y) {
+    constexpr bool accum = decltype(ACCUM)::value, with_y = decltype(WITH_Y)::value;
+    float* const yacc = p.Yacc;
+    const int64_t ldacc = p.ldacc, ldy = p.ldy;
+    uint16_t* const y = p.Y;
+    const int nout = p.Nout;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm0 + 32 * i + fr;
-    if (m >= rows) continue;
-    const int64_t orow = (int64_t)row_base + m;
+    for (int i = 0; i < FM; ++i) {
+      const int m = m0 + wm0 + 32 * i + fr;
+      if (m >= rows) continue;
+      const int64_t orow = (int64_t)row_base + m;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
+      for (int j = 0; j < FN; ++j) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int n = tn * BN + wn0 + 32 * j + 8 * jj + col4;
-        if (n >= p.Nout) continue;
-        const int valid = p.Nout - n;
-        float v[4] = {acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]};
-        if constexpr (MODE == MODE_ROW) {
-          // fp32 partial of a row-parallel shard (and, on the last shard, the bf16 result)
-          float* dst = p.Yacc + orow * p.ldacc + n;
-          if (valid >= 4) {
-            if (p.accumulate) {
-              const float4 o = *reinterpret_cast<const float4*>(dst);
-              v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
+        for (int jj = 0; jj < 4; ++jj) {
+          const int n = tn * BN + wn0 + 32 * j + 8 * jj + col4;
+          if (n >= nout) continue;
+          const int valid = nout - n;
+          float v[4] = {acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]};
+          if constexpr (MODE == MODE_ROW) {
+            // fp32 partial of a row-parallel shard (and, on the last shard, the bf16 result)
+            float* dst = yacc + orow * ldacc + n;
+            if (valid >= 4) {
+              if constexpr (accum) {
+                const float4 o = *reinterpret_cast<const float4*>(dst);
+                v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
+              }
+              *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (r < valid) {
+                  if constexpr (accum) v[r] += dst[r];
+                  dst[r] = v[r];
+                }
             }
-            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-          } else {
+            if constexpr (with_y) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) v[r] += bias_g[j][jj][r];
+              store4_bf16(y + orow * ldy + n, v, valid);
+            }
+          } else if constexpr (MODE == MODE_COMBINE) {
+            const float w = p.row_w[orow];
+            float* dst = yacc + (int64_t)p.out_rows[orow] * ldacc + n;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if (r < valid) {
-                if (p.accumulate) v[r] += dst[r];
-                dst[r] = v[r];
-              }
+              if (r < valid) atomicAdd(dst + r, w * v[r]);
           }
-          if (p.Y) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] += bias_g[j][jj][r];
-            store4_bf16(p.Y + orow * p.ldy + n, v, valid);
-          }
-        } else if constexpr (MODE == MODE_COMBINE) {
-          const float w = p.row_w[orow];
-          float* dst = p.Yacc + (int64_t)p.out_rows[orow] * p.ldacc + n;
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (r < valid) atomicAdd(dst + r, w * v[r]);
         }
       }
     }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if constexpr (MODE == MODE_ROW) {
+    if (p.accumulate) {
+      if (p.Y) direct(T_{}, T_{});
+      else direct(T_{}, F_{});
+    } else {
+      if (p.Y) direct(F_{}, T_{});
+      else direct(F_{}, F_{});
+    }
+  } else {
+    direct(F_{}, F_{});
+  }
+  };
+
+  if constexpr (SPLIT) {
+    // Split schedule: every tile's K range is cut into S chunks of whole ring passes, and the units
+    // (tile, chunk) are dealt out chunk-major, unit u to logical workgroup u mod G, so the units that run at
+    // the same time are the same K chunk of neighbouring tiles: they stream the same K slices of the shared
+    // operand panels, as one-tile-per-workgroup tiles do.  (Contiguous per-workgroup K ranges, as in
+    // stream-K, put concurrent workgroups at unrelated K positions and defeat the L2.)  Logical ids are
+    // XCD-contiguous.
+    const int T = tiles_m * tiles_n;
+    const int U = T * S;
+    for (int u = xcd_remap(blockIdx.x, G); u < U; u += G) {
+      const int c = u / T, t = u - c * T;
+      const int r0 = (int)((int64_t)c * RI / S), r1 = (int)((int64_t)(c + 1) * RI / S);
+      int tm, tn;
+      tile_coords(t, tiles_m, tiles_n, tm, tn);
+      run_tile(tm, tn, 0, p.M, p.B, r0 * NS, r1 * NS, t, slot_of(c, t), 0, S - 1, true);
+    }
+  } else {
+    // ---- tile placement
+      int tm, tn;
+    int row_base = 0, rows = p.M;  // rows of this tile's group (all rows when ungrouped)
+    const uint16_t* __restrict__ B = p.B;
+    if constexpr (GROUPED) {
+      // blockIdx.x = row-tile slot * tiles_n + tn; slots are laid over the groups in order.
+      const int tiles_n = (p.Nout + NB_OUT - 1) / NB_OUT;
+      int slot = blockIdx.x / tiles_n;
+      tn = blockIdx.x - slot * tiles_n;
+      int g = 0;
+      for (; g < p.groups; ++g) {
+        const int lo = p.group_offsets[g], hi = p.group_offsets[g + 1];
+        const int nt = (hi - lo + BM - 1) / BM;
+        if (slot < nt) { row_base = lo; rows = hi - lo; break; }
+        slot -= nt;
+      }
+      if (g == p.groups) return;  // spare slot of the upper-bound grid
+      tm = slot;
+      B += (int64_t)g * p.group_stride_B;
+    } else {
+      tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
+    }
+    run_tile(tm, tn, row_base, rows, B, 0, KTS, 0, 0, 0, 0, false);
   }
 }
 
 // ------------------------------------------------------------------------------------------ launch
+// Workspace of the split schedule, per (device, stream): two partial-tile slots per workgroup and one
+// arrival counter per tile.  Counters are zero between launches (the last arrival on a tile resets its
+// counter), so they are cleared only when allocated.  Launches on one stream are ordered, so they can
+// share the stream's workspace.
+namespace {
+struct SplitWs {
+  float* ws = nullptr;
+  int* cnt = nullptr;
+  size_t ws_bytes = 0;
+  int64_t cnt_n = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, SplitWs> g_ws;
+int g_cus[64] = {0};
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (g_cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    g_cus[dev] = n;
+  }
+  return g_cus[dev];
+}
+
+hipError_t split_workspace(hipStream_t st, size_t ws_bytes, int64_t cnt_n, float** ws, int** cnt) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  SplitWs& w = g_ws[{dev, st}];
+  if (w.ws_bytes < ws_bytes || w.cnt_n < cnt_n) {
+    if (w.ws || w.cnt) {
+      if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;  // earlier launches may still use them
+      if (w.ws) (void)hipFree(w.ws);
+      if (w.cnt) (void)hipFree(w.cnt);
+      w = SplitWs{};
+    }
+    if ((e = hipMalloc(&w.ws, ws_bytes)) != hipSuccess) return e;
+    if ((e = hipMalloc(&w.cnt, cnt_n * sizeof(int))) != hipSuccess) return e;
+    if ((e = fill_zero_f32(reinterpret_cast<float*>(w.cnt), 1, cnt_n, cnt_n, st)) != hipSuccess) return e;
+    w.ws_bytes = ws_bytes;
+    w.cnt_n = cnt_n;
+  }
+  *ws = w.ws;
+  *cnt = w.cnt;
+  return hipSuccess;
+}
+}  // namespace
+
 template <class C, int MODE, bool GROUPED>
-static hipError_t launch_cfg(const GemmParams& p, int grid_rows_upper, hipStream_t st) {
+static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStream_t st, int split_groups = 0,
+                             int split_chunks = 0) {
+  GemmParams p = p0;
   const int nb = MODE == MODE_SWIGLU ? C::BN / 2 : C::BN;
   const int tiles_n = (p.Nout + nb - 1) / nb;
   int64_t tiles;
@@ -510,49 +704,109 @@ static hipError_t launch_cfg(const GemmParams& p, int grid_rows_upper, hipStream
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   const bool kfull = p.K % (C::BK * C::NS) == 0;  // whole chunks and a step count that fills the ring
+  if constexpr (!GROUPED) {
+    if (split_groups > 0 && split_chunks > 1) {
+      const size_t slot = (size_t)C::FM * C::FN * 16 * sizeof(float) * C::NT;
+      p.sk_chunks = split_chunks;
+      hipError_t e = split_workspace(st, (size_t)tiles * split_chunks * slot, tiles, &p.sk_ws, &p.sk_cnt);
+      if (e != hipSuccess) return e;
+      if (kfull)
+        hipLaunchKernelGGL((gemm_kernel<C, MODE, false, true, true>), dim3(split_groups), dim3(C::NT), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm_kernel<C, MODE, false, false, true>), dim3(split_groups), dim3(C::NT), 0, st, p);
+      return hipGetLastError();
+    }
+  }
   if (kfull)
-    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, true>), dim3((unsigned)tiles), dim3(C::NT), 0, st, p);
+    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, true, false>), dim3((unsigned)tiles), dim3(C::NT), 0, st, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, false>), dim3((unsigned)tiles), dim3(C::NT), 0, st, p);
+    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, false, false>), dim3((unsigned)tiles), dim3(C::NT), 0, st, p);
   return hipGetLastError();
 }
 
 #ifndef MTP_BIG_CFG
 #define MTP_BIG_CFG 256, 256, 2, 4, 32, 4, true
 #endif
+#ifndef MTP_WIDE_CFG
+#define MTP_WIDE_CFG 256, 192, 4, 2, 32, 4, true
+#endif
+#ifndef MTP_HALF_CFG
+#define MTP_HALF_CFG 256, 128, 4, 2, 32, 4, true
+#endif
 #ifndef MTP_SMALL_CFG
 #define MTP_SMALL_CFG 128, 128, 4, 2, 64, 4, true
 #endif
 using BigTile = Cfg<MTP_BIG_CFG>;              // 8 waves (wave tile 128 x 64), 128 KB LDS ring
-using WideTile = Cfg<256, 192, 4, 2, 32, 4, true>;  // 8 waves (64 x 96), 112 KB
-using HalfTile = Cfg<256, 128, 4, 2, 32, 4, true>;  // 8 waves (64 x 64), 96 KB
+using WideTile = Cfg<MTP_WIDE_CFG>;            // 8 waves (64 x 96), 112 KB
+using HalfTile = Cfg<MTP_HALF_CFG>;            // 8 waves (64 x 64), 96 KB
 using SmallTile = Cfg<MTP_SMALL_CFG>;          // 8 waves (32 x 64), 128 KB
 
-// Tile choice: the estimated time of a launch is the number of waves of tiles over the 256 CUs times the
-// time of one tile, BM * BN / efficiency (measured relative MFMA efficiency of the tile shapes on large K).
-// Wave quantisation matters at these shard shapes: e.g. 2048 x 4608 is 144 tiles of 256 x 256 (56% of the
-// CUs busy) but 192 tiles of 256 x 192.
-template <int MODE>
-static hipError_t dispatch(const GemmParams& p, hipStream_t st) {
-  struct Opt { int bm, bn; double eff; int id; };
-  const Opt opts[] = {{256, 256, 1.00, 0}, {256, 192, 0.95, 1}, {256, 128, 0.85, 2}, {128, 128, 0.72, 3}};
-  int best = 3;
+// Schedule choice.  One workgroup per tile: the time is the number of waves of tiles over the CUs times
+// the time of one tile (BM * BN / efficiency, the measured relative MFMA efficiency of the tile shapes on
+// large K).  Split-K: every tile's K range in S chunks, one workgroup per CU working through the (tile,
+// chunk) units, each chunk's partial sums added by the tile's last finisher; the time is the number of
+// waves of units times the time of a chunk plus fixed costs.  Wave quantisation is large at the shard
+// shapes of a tensor-parallel layer: 4096 x 1280 is 80 tiles of 256 x 256 (31% of the CUs busy) but 240
+// units in 3 chunks.
+GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K) {
+  struct Opt { int bm, bn; double eff; int id; int ns_bk; int64_t slot_bytes; };
+  const Opt opts[] = {{256, 256, 1.00, 0, 128, 256 << 10}, {256, 192, 0.95, 1, 128, 192 << 10},
+                      {256, 128, 0.85, 2, 128, 128 << 10}, {128, 128, 0.72, 3, 256, 0}};
+  const int cus = cu_count();
+  GemmPlan best;
+  best.bm = 128; best.bn = 128; best.id = 3;
   double best_t = 1e300;
   for (const Opt& o : opts) {
-    if (MODE == MODE_SWIGLU && o.id == 1) continue;  // gate/up pairs need wave tiles of 64 B rows
-    const int64_t nbo = MODE == MODE_SWIGLU ? o.bn / 2 : o.bn;
-    const int64_t tiles = ((p.M + o.bm - 1) / o.bm) * ((p.Nout + nbo - 1) / nbo);
-    const double t = (double)((tiles + 255) / 256) * o.bm * o.bn / o.eff;
-    if (t < best_t * 0.999) { best_t = t; best = o.id; }
+    if (mode == MODE_SWIGLU && o.id == 1) continue;  // gate/up pairs need wave tiles of 64 B rows
+    const int64_t nbo = mode == MODE_SWIGLU ? o.bn / 2 : o.bn;
+    const int64_t tiles = ((M + o.bm - 1) / o.bm) * ((Nout + nbo - 1) / nbo);
+    const double tile_t = o.bm * o.bn / o.eff;
+    const double t_dp = (double)((tiles + cus - 1) / (cus > 0 ? cus : 1)) * tile_t;
+    if (t_dp < best_t * 0.999) { best_t = t_dp; best = GemmPlan{o.bm, (int)nbo, 0, o.id, 0}; }
+    // split-K: S chunks of at least 4 ring passes; per unit a fixed cost of about 1.5 passes (pipeline fill,
+    // partial store), and per tile the reads of its S partial sums
+    const int64_t passes = (K + o.ns_bk - 1) / o.ns_bk;
+    if (o.slot_bytes == 0 || cus < 8 || cus % 8 != 0) continue;
+    for (int S : {2, 3, 4, 5, 6, 8}) {
+      if (passes < 4 * S || tiles * S * o.slot_bytes > ((int64_t)512 << 20)) continue;
+      const int64_t waves = (tiles * S + cus - 1) / cus;
+      const double t_sk = waves * tile_t * (1.0 / S + 1.5 / passes) + tile_t * 0.03 * S;
+      if (t_sk < best_t * 0.95) { best_t = t_sk; best = GemmPlan{o.bm, (int)nbo, cus, o.id, S}; }
+    }
   }
-  switch (best) {
-    case 0: return launch_cfg<BigTile, MODE, false>(p, 0, st);
+  return best;
+}
+
+template <int MODE>
+static hipError_t dispatch(const GemmParams& p, hipStream_t st) {
+  const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K);
+  switch (pl.id) {
+    case 0: return launch_cfg<BigTile, MODE, false>(p, 0, st, pl.split_groups, pl.split_chunks);
     case 1:
-      if constexpr (MODE != MODE_SWIGLU) return launch_cfg<WideTile, MODE, false>(p, 0, st);
+      if constexpr (MODE != MODE_SWIGLU)
+        return launch_cfg<WideTile, MODE, false>(p, 0, st, pl.split_groups, pl.split_chunks);
       return hipErrorInvalidValue;
-    case 2: return launch_cfg<HalfTile, MODE, false>(p, 0, st);
-    default: return launch_cfg<SmallTile, MODE, false>(p, 0, st);
+    case 2: return launch_cfg<HalfTile, MODE, false>(p, 0, st, pl.split_groups, pl.split_chunks);
+    default: return launch_cfg<SmallTile, MODE, false>(p, 0, st);  // (never split)
   }
+}
+
+hipError_t release_split_workspaces() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  for (auto it = g_ws.begin(); it != g_ws.end();) {
+    if (it->first.first == dev) {
+      if (it->second.ws) (void)hipFree(it->second.ws);
+      if (it->second.cnt) (void)hipFree(it->second.cnt);
+      it = g_ws.erase(it);
+    } else {
+      ++it;
+    }
+  }
+  return hipSuccess;
 }
 
 hipError_t gemm(const GemmParams& p, int mode, hipStream_t st) {

@@ -27,7 +27,7 @@ def _gpu_present():
 def test_library_exports_every_header_symbol():
     L = mtp.lib()
     names = mtp.header_symbols()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", mtp.LIB_PATH], capture_output=True, text=True).stdout
@@ -150,6 +150,25 @@ def test_moe_valid_call_reaches_the_device_check():
     L = mtp.lib()
     assert L.mtp_moe_route(P, 16, 8, 2, P, P2, P3, None) == UNSUPPORTED
     assert L.mtp_moe_mlp_forward(P, 64, 64, 8, 128, 2, P2, P3, P4, P, P2, P3, P4, P, None) == UNSUPPORTED
+
+
+def test_gemm_plan_rejects():
+    L = mtp.lib()
+    o = [ctypes.c_int(0) for _ in range(3)]
+    a = [ctypes.addressof(x) for x in o]
+    assert L.mtp_gemm_plan(0, 8, 8, 0, *a) == SHAPE
+    assert L.mtp_gemm_plan(8, 8, 12, 0, *a) == SHAPE      # K not a multiple of 8
+    assert L.mtp_gemm_plan(8, 7, 8, 2, *a) == SHAPE       # SwiGLU with odd N
+    assert L.mtp_gemm_plan(8, 8, 8, 5, *a) == SHAPE       # unknown activation
+    assert L.mtp_gemm_plan(8, 8, 8, 0, a[0], None, a[2]) == NULL
+
+
+@pytest.mark.skipif(_gpu_present(), reason="on a GPU box the plan is computed")
+def test_gemm_plan_and_release_need_a_device():
+    L = mtp.lib()
+    o = [ctypes.c_int(0) for _ in range(3)]
+    assert L.mtp_gemm_plan(4096, 4096, 4096, 0, *[ctypes.addressof(x) for x in o]) == UNSUPPORTED
+    assert L.mtp_release_workspaces() == UNSUPPORTED
 
 
 def test_binding_raises_when_library_refuses(monkeypatch):

@@ -113,6 +113,82 @@ def test_integer_exact_row_partials_and_sum(M, N, Kp, p):
     assert np.array_equal(bits(Y1), oracle.round_bf16(P[0] + widen_bits(bb)[None, :]))
 
 
+# ----------------------------------------------------------------------------- split-K schedule
+# Shapes whose launch plan is split-K (each tile's K range in S chunks, the chunks' fp32 partial sums added
+# in chunk order by the tile's last finisher), one per tile shape, with even and uneven chunks.
+# Integer-valued inputs make the sums exact whatever the split, so the bf16 outputs are bit-exact; rows
+# are sampled for the large cases (each output row depends only on its input row, and every row tile and
+# every column is covered).
+@pytest.mark.parametrize("M,N,K,plan,sampled", [
+    (300, 400, 4096, (256, 128, 6), False),    # 32 ring passes in 6 chunks (5 or 6 each)
+    (777, 190, 8192, (256, 128, 5), False),
+    (4100, 900, 2048, (256, 192, 3), True),
+    (900, 4100, 2048, (256, 256, 3), True),
+])
+def test_split_schedule_integer_exact(M, N, K, plan, sampled):
+    say("split int column", M, N, K)
+    assert mtp.mtp_gemm_plan(M, N, K) == plan
+    Xb, Wb = synth.ternary_bf16(251, M, K), synth.ternary_bf16(252, N, K)
+    bb = synth.ternary_bf16(253, 1, N)[0]
+    X, W, b = to_dev(Xb), to_dev(Wb), to_dev(bb)
+    ldy = ((N + 7) // 8) * 8
+    Y = torch.empty(M, ldy, dtype=torch.bfloat16, device="cuda")[:, :N]
+    mtp.mtp_column_linear(X, W, b, Y)
+    Y2 = torch.empty(M, ldy, dtype=torch.bfloat16, device="cuda")[:, :N]
+    mtp.mtp_column_linear(X, W, b, Y2)  # a second launch reuses the (self-resetting) tile counters
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 96, 254) if sampled else list(range(M))
+    R = oracle.linear(np.ascontiguousarray(Xb[rows]), Wb, bb)
+    G = bits(Y)
+    assert np.array_equal(G[rows], oracle.round_bf16(R))
+    assert np.array_equal(bits(Y2), G), "split schedule is not deterministic"
+    # the row-parallel form: fp32 partials of two shards through the same schedule
+    Kp = K // 2
+    Yacc = torch.empty(M, ((N + 7) // 8) * 8, dtype=torch.float32, device="cuda")[:, :N]
+    Yb = torch.empty(M, ldy, dtype=torch.bfloat16, device="cuda")[:, :N]
+    mtp.mtp_row_linear_partial(X[:, :Kp], W[:, :Kp], Yacc)
+    mtp.mtp_row_linear_partial(X[:, Kp:], W[:, Kp:], Yacc, True, b, Yb)
+    torch.cuda.synchronize()
+    P = oracle.row_parallel_partials([np.ascontiguousarray(Xb[rows][:, :Kp]), np.ascontiguousarray(Xb[rows][:, Kp:])],
+                                     Wb, 2)
+    S = oracle.row_parallel_sum(P)
+    assert np.array_equal(Yacc.cpu().numpy()[rows].astype(np.float64), S)
+    assert np.array_equal(bits(Yb)[rows], oracle.round_bf16(S + widen_bits(bb)[None, :]))
+
+
+@pytest.mark.parametrize("M,F,K,plan", [(300, 200, 4096, (256, 64, 6)), (400, 4100, 2048, (256, 128, 3))])
+def test_split_schedule_swiglu(M, F, K, plan):
+    say("split swiglu", M, F, K)
+    assert mtp.mtp_gemm_plan(M, 2 * F, K, mtp.ACT_SWIGLU) == plan
+    Xb = synth.normal_bf16(261, M, K, 1.0)
+    Wb = synth.normal_bf16(262, 2 * F, K, 0.02)
+    bb = synth.normal_bf16(263, 1, 2 * F, 0.1)[0]
+    Y = torch.empty(M, ((F + 7) // 8) * 8, dtype=torch.bfloat16, device="cuda")[:, :F]
+    mtp.mtp_column_linear(to_dev(Xb), to_dev(Wb), to_dev(bb), Y, mtp.ACT_SWIGLU)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 64, 264)
+    R = oracle.linear(np.ascontiguousarray(Xb[rows]), Wb, bb, oracle.ACT_SWIGLU)
+    G = bits(Y)[rows]
+    _close(widen_bits(G), R, "split swiglu")
+    assert _exact_bits_frac(G, R) >= EXACT_FRAC_MIN
+
+
+def test_split_schedule_gelu_matches_one_tile_per_workgroup():
+    # the same product through both schedules: the split sums the K range in another order, so the two
+    # agree to fp32 rounding (and both with the oracle)
+    M, N, K = 300, 400, 4096
+    assert mtp.mtp_gemm_plan(M, N, K, mtp.ACT_GELU)[2] > 1
+    Xb, Wb = synth.normal_bf16(271, M, K, 1.0), synth.normal_bf16(272, N, K, 0.02)
+    bb = synth.normal_bf16(273, 1, N, 0.1)[0]
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    mtp.mtp_column_linear(to_dev(Xb), to_dev(Wb), to_dev(bb), Y, mtp.ACT_GELU)
+    torch.cuda.synchronize()
+    R = oracle.linear(Xb, Wb, bb, oracle.ACT_GELU)
+    G = bits(Y)
+    _close(widen_bits(G), R, "split gelu")
+    assert _exact_bits_frac(G, R) >= EXACT_FRAC_MIN
+
+
 # ----------------------------------------------------------------------------- activations, small full checks
 @pytest.mark.parametrize("M,N,K", [(200, 300, 136), (64, 64, 64), (513, 1030, 256)])
 def test_gelu_column_linear(M, N, K):
