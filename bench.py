@@ -8,10 +8,12 @@ GeLU (or SwiGLU), fc2 row-parallel GEMM (and for the MoE workload the router
 and the grouped expert GEMMs).  The default workload is the GPT-345M-shaped
 layer at TP=1 with 4096 tokens; --workload picks another.
 
-Prints one JSON line: TFLOP/s (algorithmic 2*M*N*K over the step's GEMMs),
-the dominant kernel's roofline position (HIP events around each GEMM inside
-the timed region, on the stream the kernels are launched on), and the CPU
-oracle timed on a bounded sample of the same workload on this host's cores.
+Prints one JSON line: TFLOP/s (algorithmic 2*M*N*K over the step's GEMMs,
+whole steps timed), the dominant kernel's roofline position (HIP events
+around that kernel in every timed step, on the stream the kernels are
+launched on; events without the system-scope cache fence, so timing does not
+flush the caches), and the CPU oracle timed on a bounded sample of the same
+workload on this host's cores.
 """
 import argparse
 import hashlib
@@ -49,6 +51,39 @@ def measured_traffic(workload, kernel_label):
     if not e or e.get("kernel_source_hash") != kernel_source_hash():
         return None
     return e["hbm_bytes_per_launch"]
+
+
+class _FenceFreeEvents:
+    """HIP events (created with hipEventDisableSystemFence) recorded on one stream, for timing only."""
+    _FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self, stream_handle):
+        import ctypes
+        self._c = ctypes
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self._hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._stream = ctypes.c_void_p(stream_handle)
+
+    def record(self):
+        e = self._c.c_void_p()
+        if self._hip.hipEventCreateWithFlags(self._c.byref(e), self._FLAGS) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        if self._hip.hipEventRecord(e, self._stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+        return e
+
+    def elapsed_ms(self, e0, e1):
+        ms = self._c.c_float()
+        if self._hip.hipEventElapsedTime(self._c.byref(ms), e0, e1) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def release(self, events):
+        for e in events:
+            self._hip.hipEventDestroy(e)
 
 
 def cpu_baseline(w, budget_s):
@@ -149,28 +184,20 @@ def main():
         run.step()
     torch.cuda.synchronize()
 
-    # per-kernel events inside the timed region, on the stream the library launches on
-    ev = []
+    # HIP events without the system-scope fence: a default event record writes back and invalidates the
+    # caches, which costs several microseconds per record and slows the following kernel.
+    timer = _FenceFreeEvents(stream.cuda_stream)
 
-    def mark(label):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(stream)
-        ev[-1].append((label, e))
-
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        ev.append([])
-        run.step(mark)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
-
+    # per-GEMM times from a short pass with an event around every launch (outside the timed region)
     per_kernel = {}
-    for marks in ev:
+    for _ in range(min(5, max(args.steps, 1))):
+        marks = []
+        run.step(lambda label: marks.append((label, timer.record())))
+        torch.cuda.synchronize()
         for (label, e0), (_, e1) in zip(marks[:-1], marks[1:]):
-            per_kernel.setdefault(label, []).append(e0.elapsed_time(e1))
+            per_kernel.setdefault(label, []).append(timer.elapsed_ms(e0, e1))
+        timer.release(e for _, e in marks)
+
     flop_by_label = {}
     for label, m, n, k in w.gemms:
         flop_by_label[label] = flop_by_label.get(label, 0) + 2 * m * n * k
@@ -180,7 +207,31 @@ def main():
         flop_by_label = {"mlp": w.flop}
     avg = {lb: sum(v) / len(v) for lb, v in per_kernel.items()}
     dom = max((lb for lb in avg if lb in flop_by_label), key=lambda lb: avg[lb])
-    achieved = flop_by_label[dom] / (avg[dom] * 1e-3) / 1e12
+
+    # Timed region: K whole steps; the dominant kernel is bracketed by events in every step (on the stream
+    # the library launches on), the only events inside the region.
+    dom_events = []
+    state = {"prev": None}
+
+    def mark_dominant(label):
+        if state["prev"] == dom:
+            dom_events[-1].append(timer.record())
+        if label == dom:
+            dom_events.append([timer.record()])
+        state["prev"] = label
+
+    torch.cuda.synchronize()
+    start = timer.record()
+    for _ in range(args.steps):
+        state["prev"] = None
+        run.step(mark_dominant)
+    stop = timer.record()
+    torch.cuda.synchronize()
+    ms = timer.elapsed_ms(start, stop) / args.steps
+    dom_ms = [timer.elapsed_ms(e0, e1) for e0, e1 in dom_events]
+    timer.release([start, stop] + [e for pair in dom_events for e in pair])
+    dom_avg = sum(dom_ms) / len(dom_ms)
+    achieved = flop_by_label[dom] / (dom_avg * 1e-3) / 1e12
     flop = w.flop
     value = flop / (ms * 1e-3) / 1e12
     traffic = measured_traffic(w.name, dom)
@@ -204,7 +255,8 @@ def main():
                    "per_gemm_us": {lb: round(1000 * v, 2) for lb, v in avg.items()},
                    "per_gemm_tflops": {lb: round(flop_by_label[lb] / (avg[lb] * 1e-3) / 1e12, 1)
                                        for lb in avg if lb in flop_by_label}},
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": dom, "kernel_us": round(1000 * dom_avg, 2),
+                     "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": None,

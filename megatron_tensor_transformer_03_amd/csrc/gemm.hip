@@ -92,23 +92,29 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two floats to packed bf16 (one v_cvt_pk_bf16_f32, round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return (uint32_t)to_bf16(lo) | ((uint32_t)to_bf16(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ float from_bf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // Exact-erf GeLU, gelu(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)).  erf is evaluated with Abramowitz &
 // Stegun 7.1.26 (|error| <= 1.5e-7 absolute, far below bf16 resolution): for z >= 0,
-// 1 - erf(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z).  Written as
-// 1 + erf(z) = 2 - q (z >= 0) or q (z < 0, by symmetry) so there is no cancellation for negative x.
+// 1 - erf(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z).  With z = |x| / sqrt 2
+// and P = (a1 t + .. + a5 t^5) / 2 this gives Phi(x) = 1 - P e (x >= 0) and P e (x < 0), e = exp(-x^2 / 2),
+// so gelu(x) = max(x, 0) - |x| P e for both signs, with no cancellation for negative x.  The constants
+// below are p / sqrt 2, a_i / 2 and -log2(e) / 2 (e via exp2); this is an epilogue that runs once per
+// output element, so every operation counts: 12 VALU operations and 2 transcendentals.
 __device__ __forceinline__ float gelu_erf(float x) {
-  const float z = fabsf(x) * 0.70710678118654752440f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-  const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f), -0.284496736f),
-                              0.254829592f);
-  const float q = poly * __expf(-z * z);
-  return 0.5f * x * (x >= 0.f ? 2.0f - q : q);
+  const float e = __builtin_amdgcn_exp2f(x * x * -0.72134752044448170368f);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.23164188773f, fabsf(x), 1.0f));
+  const float P = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 0.5307027145f, -0.7265760135f), 0.7107068705f),
+                                     -0.142248368f), 0.127414796f);
+  return fmaf(-e, fabsf(x) * P, x > 0.0f ? x : 0.0f);
 }
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
