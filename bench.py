@@ -144,6 +144,9 @@ def main():
     ap.add_argument("--workload", default="gpt345m", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graphs", action="store_true",
+                    help="replay the step as HIP graphs (captured from the same calls) instead of launching each "
+                         "call from Python; on ROCm 7 graph launches cost more than they save at this step size")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -178,7 +181,10 @@ def main():
     inputs = synth.device_inputs(w)
     run = RankForward(w.dims, inputs)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
+    # one side stream for everything (graph capture needs a non-default stream, and the library's split-K
+    # workspace is per stream, so warm-up on this stream allocates it before any capture)
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
 
     for _ in range(args.warmup):
         run.step()
@@ -209,22 +215,40 @@ def main():
     dom = max((lb for lb in avg if lb in flop_by_label), key=lambda lb: avg[lb])
 
     # Timed region: K whole steps; the dominant kernel is bracketed by events in every step (on the stream
-    # the library launches on), the only events inside the region.
+    # the library launches on), the only events inside the region.  With --graphs the launches before the
+    # dominant kernel, the dominant kernel, and the launches after it are replayed as three HIP graphs
+    # (captured from the same C-ABI calls).
+    calls = run.calls()
+    idx = [lb for lb, _ in calls].index(dom)
+    segments = [calls[:idx], calls[idx:idx + 1], calls[idx + 1:]]
+    if not args.graphs:
+        launchers = [(lambda seg=seg: [fn() for _, fn in seg]) for seg in segments]
+    else:
+        launchers = []
+        for seg in segments:
+            if not seg:
+                launchers.append(lambda: None)
+                continue
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for _, fn in seg:
+                    fn()
+            launchers.append(g.replay)
+        torch.cuda.synchronize()
+        for _ in range(2):  # replay once untimed
+            for launch in launchers:
+                launch()
+        torch.cuda.synchronize()
+    pre, dom_launch, post = launchers
     dom_events = []
-    state = {"prev": None}
-
-    def mark_dominant(label):
-        if state["prev"] == dom:
-            dom_events[-1].append(timer.record())
-        if label == dom:
-            dom_events.append([timer.record()])
-        state["prev"] = label
-
     torch.cuda.synchronize()
     start = timer.record()
     for _ in range(args.steps):
-        state["prev"] = None
-        run.step(mark_dominant)
+        pre()
+        e0 = timer.record()
+        dom_launch()
+        dom_events.append((e0, timer.record()))
+        post()
     stop = timer.record()
     torch.cuda.synchronize()
     ms = timer.elapsed_ms(start, stop) / args.steps
@@ -250,6 +274,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "desc": w.desc, "flop_per_step": flop,
+                   "launch": "hip_graph" if args.graphs else "eager",
                    "pct_of_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
                    "gemms": [[lb, m, n, k] for lb, m, n, k in w.gemms],
                    "per_gemm_us": {lb: round(1000 * v, 2) for lb, v in avg.items()},

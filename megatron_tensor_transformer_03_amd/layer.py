@@ -52,43 +52,48 @@ class RankForward:
         else:
             self.out["mlp_partial"] = torch.empty(M, H, dtype=f32, device=dev)
 
-    def step(self, mark=None):
-        """Enqueue one forward.  ``mark(label)``, if given, is called before each launch and once at the end
-        (label None): a caller can record stream events there to time each GEMM."""
+    def calls(self):
+        """The forward's launches in order, as (label, thunk) pairs; each thunk enqueues one C-ABI call on the
+        current stream (so a caller can also capture them into graphs)."""
         d, t, o = self.d, self.t, self.out
-        mark = mark or (lambda label: None)
         if "E" in d:
-            mark("route")
-            mtp.mtp_moe_route(t["logits"], d["k"], o["offsets"], o["token_idx"], o["token_w"])
-            mark("moe_mlp")
-            mtp.mtp_moe_mlp_forward(t["X"], d["E"], d["F"], d["k"], o["offsets"], o["token_idx"], o["token_w"],
-                                    t["W1t"], t["W2t"], o["Z"], o["Yacc"], o["Y"])
-            mark(None)
-            return o
+            return [("route", lambda: mtp.mtp_moe_route(t["logits"], d["k"], o["offsets"], o["token_idx"],
+                                                          o["token_w"])),
+                    ("moe_mlp", lambda: mtp.mtp_moe_mlp_forward(t["X"], d["E"], d["F"], d["k"], o["offsets"],
+                                                                o["token_idx"], o["token_w"], t["W1t"], t["W2t"],
+                                                                o["Z"], o["Yacc"], o["Y"]))]
         p = d["p"]
+        out = []
         if "nq" in d:
-            mark("qkv")
-            mtp.mtp_qkv_forward(t["X"], t["Wqkv_t"], t.get("bqkv"), d["nq"] // p, d["ng"] // p, d["d"], o["qkv"])
+            out.append(("qkv", lambda: mtp.mtp_qkv_forward(t["X"], t["Wqkv_t"], t.get("bqkv"), d["nq"] // p,
+                                                           d["ng"] // p, d["d"], o["qkv"])))
         if "ctx" in t:
-            mark("out_proj")
             if p == 1:  # the whole layer: the all-reduce is the identity, bias added here
-                mtp.mtp_row_linear_partial(t["ctx"], t["Wo_t"], None, False, t.get("bo"), o["attn_out"])
+                out.append(("out_proj", lambda: mtp.mtp_row_linear_partial(t["ctx"], t["Wo_t"], None, False,
+                                                                           t.get("bo"), o["attn_out"])))
             else:       # this rank's fp32 partial of the all-reduce
-                mtp.mtp_row_linear_partial(t["ctx"], t["Wo_t"], o["attn_partial"])
+                out.append(("out_proj", lambda: mtp.mtp_row_linear_partial(t["ctx"], t["Wo_t"], o["attn_partial"])))
         if d["ranks"] == "all" and p > 1:
             # every shard in turn; the all-reduce is the fp32 sum in rank order
-            mark("mlp")
-            mtp.mtp_mlp_forward(t["X"], t["W1t"], t.get("b1"), t["W2t"], t.get("b2"), d["act"], p, 0, p, o["Z"],
-                                o["Yacc"], o["Y"])
+            out.append(("mlp", lambda: mtp.mtp_mlp_forward(t["X"], t["W1t"], t.get("b1"), t["W2t"], t.get("b2"),
+                                                           d["act"], p, 0, p, o["Z"], o["Yacc"], o["Y"])))
         else:
             # one shard (p = 1: the whole MLP): fc1 column linear with bias + activation fused, then fc2 as a
             # row-parallel partial; with p = 1 the sum over shards is the identity and b2 is added in its epilogue
-            mark("fc1")
-            mtp.mtp_column_linear(t["X"], t["W1t"], t.get("b1"), o["Z"], d["act"])
-            mark("fc2")
+            out.append(("fc1", lambda: mtp.mtp_column_linear(t["X"], t["W1t"], t.get("b1"), o["Z"], d["act"])))
             if p == 1:
-                mtp.mtp_row_linear_partial(o["Z"], t["W2t"], None, False, t.get("b2"), o["Y"])
+                out.append(("fc2", lambda: mtp.mtp_row_linear_partial(o["Z"], t["W2t"], None, False, t.get("b2"),
+                                                                      o["Y"])))
             else:
-                mtp.mtp_row_linear_partial(o["Z"], t["W2t"], o["mlp_partial"])
+                out.append(("fc2", lambda: mtp.mtp_row_linear_partial(o["Z"], t["W2t"], o["mlp_partial"])))
+        return out
+
+    def step(self, mark=None):
+        """Enqueue one forward.  ``mark(label)``, if given, is called before each launch and once at the end
+        (label None): a caller can record stream events there to time each GEMM."""
+        mark = mark or (lambda label: None)
+        for label, fn in self.calls():
+            mark(label)
+            fn()
         mark(None)
-        return o
+        return self.out
