@@ -346,6 +346,14 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
             read_frags(stage_buf(std::integral_constant<int, (i + 1) % NS>{}), 0,
                        std::integral_constant<int, (g + 1) & 1>{});
           mma(std::integral_constant<int, g & 1>{});
+          // issue order: one fragment read, then its share of the MFMAs, and so on, so the reads of the next
+          // set are spread over this set's MFMAs instead of being bunched (or sunk next to their first use)
+          [&]<int... R>(std::integer_sequence<int, R...>) {
+            constexpr int NR = FM + FN, NM = FM * FN;
+            ((__builtin_amdgcn_sched_group_barrier(0x100, 1, 0),      // one LDS read
+              __builtin_amdgcn_sched_group_barrier(0x008, (NM * (R + 1)) / NR - (NM * R) / NR, 0)), ...);  // MFMAs
+          }(std::make_integer_sequence<int, FM + FN>{});
+          __builtin_amdgcn_sched_barrier(0);
         } else {
           read_frags(cur, ks, std::integral_constant<int, 0>{});
           mma(std::integral_constant<int, 0>{});
