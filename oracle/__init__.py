@@ -243,3 +243,43 @@ def moe_mlp(X, logits, W1t_list, W2t_list, k: int, tokens=None):
         for n, (j, t) in enumerate(rows):
             out[pos[t]] += w[j] * Ye[n]
     return out, (offsets, idx, w)
+
+
+# ----------------------------------------------------------------------------- rotary position embedding
+def rope_inv_freq(rotary_dim: int, base: float) -> np.ndarray:
+    """theta_i = base^(-2i / rotary_dim), i = 0 .. rotary_dim/2 - 1 (RoFormer's frequencies; the pages name
+    RoPE among the layer's elementwise kernels and its rotary_base / rotary_percent settings)."""
+    i = np.arange(rotary_dim // 2, dtype=np.float64)
+    return base ** (-2.0 * i / rotary_dim)
+
+
+def rope(QKV: np.ndarray, positions, nq_local: int, ng_local: int, head_dim: int, rotary_dim: int,
+         base: float, interleaved: bool) -> np.ndarray:
+    """RoPE applied to the query and key heads of one rank's QKV output (value heads untouched), in fp64.
+
+    Readings: the "Megatron-LM 深度学习与源码分析文档" pages list RoPE as a fused elementwise kernel on the QKV
+    output (part 2 sections 3 and 6: --use-rotary-position-embeddings, --use-fused-rotary-pos-emb,
+    rotary_base, rotary_percent) without its formula; it is taken from RoFormer (cited on the same pages): the
+    pair (x_a, x_b) of frequency theta_i at position m becomes
+        (x_a cos(m theta_i) - x_b sin(m theta_i),  x_b cos(m theta_i) + x_a sin(m theta_i)),
+    with a = i, b = i + rotary_dim/2 ("rotate half", Megatron's default) or a = 2i, b = 2i + 1 (interleaved);
+    dimensions from rotary_dim on (rotary_percent < 1) pass through.  The input is the bf16 QKV output
+    (widened exactly), as the pages' unfused and fused forms both read it.
+    """
+    X = np.array(QKV, dtype=np.float64, copy=True)
+    pos = np.asarray(positions, dtype=np.float64)
+    ang = pos[:, None] * rope_inv_freq(rotary_dim, base)[None, :]          # [rows x rotary_dim/2]
+    c, s = np.cos(ang), np.sin(ang)
+    half = rotary_dim // 2
+    for h in range(nq_local + ng_local):                                    # Q heads, then K heads
+        o = h * head_dim
+        if interleaved:
+            a = o + 2 * np.arange(half)
+            b = a + 1
+        else:
+            a = o + np.arange(half)
+            b = a + half
+        xa, xb = X[:, a].copy(), X[:, b].copy()
+        X[:, a] = xa * c - xb * s
+        X[:, b] = xb * c + xa * s
+    return X

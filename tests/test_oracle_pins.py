@@ -338,3 +338,72 @@ def test_moe_token_subset_matches_full():
     full, _ = oracle.moe_mlp(X, logits, W1, W2, 2)
     sub, _ = oracle.moe_mlp(X, logits, W1, W2, 2, tokens=[3, 7, 11])
     assert np.array_equal(sub, full[[3, 7, 11]])
+
+
+# ----------------------------------------------------------------------------- rotary position embedding
+def test_rope_frequencies_closed_form():
+    # base^(-2i/d): with base 10^4 and d = 8 the frequencies are 10^0, 10^-1, 10^-2, 10^-3
+    np.testing.assert_allclose(oracle.rope_inv_freq(8, 10000.0), [1.0, 0.1, 0.01, 0.001], rtol=1e-15)
+    np.testing.assert_allclose(oracle.rope_inv_freq(4, 16.0), [1.0, 0.25], rtol=1e-15)
+
+
+def test_rope_two_dimensional_rotation_golden():
+    # d = 2: the pair rotates by m radians; expected values from the textbook sines and cosines
+    tab = {int(a): (float(c), float(s)) for a, c, s in _golden("rope_d2.txt")}
+    x = np.array([[0.5, -2.0]] * 3)  # one query head of 2 dims, three rows at positions 1, 2, 3
+    for interleaved in (False, True):
+        X = np.concatenate([x, x, x], axis=1)  # Q head, K head, V head (nq = ng = 1, d = 2)
+        Y = oracle.rope(X, [1, 2, 3], 1, 1, 2, 2, 10000.0, interleaved)
+        for r, m in enumerate((1, 2, 3)):
+            c, s = tab[m]
+            want = [0.5 * c + 2.0 * s, -2.0 * c + 0.5 * s]
+            np.testing.assert_allclose(Y[r, 0:2], want, rtol=0, atol=1e-15)   # Q
+            np.testing.assert_allclose(Y[r, 2:4], want, rtol=0, atol=1e-15)   # K
+            np.testing.assert_array_equal(Y[r, 4:6], x[r])                    # V untouched
+
+
+def _complex_pairs(v, rd, interleaved):
+    half = rd // 2
+    if interleaved:
+        return v[0:rd:2] + 1j * v[1:rd:2]
+    return v[:half] + 1j * v[half:rd]
+
+
+def test_rope_is_multiplication_by_unit_complex_numbers():
+    # RoFormer's complex form: each pair, read as z = x_a + i x_b, is multiplied by exp(i m theta_j)
+    rng = np.random.default_rng(7)
+    d, rd, base = 16, 12, 500.0
+    X = rng.standard_normal((5, 3 * d))
+    pos = [0, 1, 7, 123, 4095]
+    theta = [base ** (-2.0 * j / rd) for j in range(rd // 2)]
+    for interleaved in (False, True):
+        Y = oracle.rope(X, pos, 1, 1, d, rd, base, interleaved)
+        for r, m in enumerate(pos):
+            for h in (0, 1):
+                z = _complex_pairs(X[r, h * d:(h + 1) * d], rd, interleaved)
+                want = z * np.array([complex(math.cos(m * t), math.sin(m * t)) for t in theta])
+                got = _complex_pairs(Y[r, h * d:(h + 1) * d], rd, interleaved)
+                np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+                # dimensions past rotary_dim pass through
+                np.testing.assert_array_equal(Y[r, h * d + rd:(h + 1) * d], X[r, h * d + rd:(h + 1) * d])
+            np.testing.assert_array_equal(Y[r, 2 * d:], X[r, 2 * d:])  # V
+
+
+def test_rope_relative_position_and_norms():
+    # the defining property: <rope(q, m), rope(k, n)> depends only on m - n; each pair keeps its norm;
+    # position 0 is the identity
+    rng = np.random.default_rng(11)
+    d = 64
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    for interleaved in (False, True):
+        def f(v, m):
+            X = np.concatenate([v, np.zeros(d), np.zeros(d)])[None, :]
+            return oracle.rope(X, [m], 1, 1, d, d, 10000.0, interleaved)[0, :d]
+        base_dot = f(q, 5) @ f(k, 2)
+        for shift in (1, 17, 1000):
+            assert abs(f(q, 5 + shift) @ f(k, 2 + shift) - base_dot) < 1e-9
+        assert abs(f(q, 3) @ f(k, 0) - base_dot) < 1e-9
+        y = f(q, 77)
+        zq, zy = _complex_pairs(q, d, interleaved), _complex_pairs(y, d, interleaved)
+        np.testing.assert_allclose(np.abs(zy), np.abs(zq), rtol=1e-13)
+        np.testing.assert_array_equal(f(q, 0), q)
