@@ -260,6 +260,17 @@ def main():
     value = flop / (ms * 1e-3) / 1e12
     traffic = measured_traffic(w.name, dom)
 
+    # non-GEMM kernels of the step, against the HBM roofline: algorithmic bytes per launch / event time
+    aux = {}
+    if "rope" in avg and "rope" in w.dims:
+        dd = w.dims
+        heads = (dd["nq"] + dd["ng"]) // dd["p"]
+        rope_bytes = dd["M"] * heads * dd["rope"]["rotary_dim"] * 2 * 2 + 4 * dd["M"]
+        gbs = rope_bytes / (avg["rope"] * 1e-3) / 1e9
+        aux["rope"] = {"bound": "hbm", "us": round(1000 * avg["rope"], 2), "bytes": rope_bytes,
+                       "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -279,7 +290,8 @@ def main():
                    "gemms": [[lb, m, n, k] for lb, m, n, k in w.gemms],
                    "per_gemm_us": {lb: round(1000 * v, 2) for lb, v in avg.items()},
                    "per_gemm_tflops": {lb: round(flop_by_label[lb] / (avg[lb] * 1e-3) / 1e12, 1)
-                                       for lb in avg if lb in flop_by_label}},
+                                       for lb in avg if lb in flop_by_label},
+                   "aux_kernels": aux},
         "roofline": {"bound": "mfma", "kernel": dom, "kernel_us": round(1000 * dom_avg, 2),
                      "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

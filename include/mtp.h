@@ -132,6 +132,28 @@ mtp_status mtp_qkv_forward(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t H,
                            mtp_bf16* QKV, int64_t ldo, void* stream);
 
 /*
+ * Rotary position embedding of the query and key heads of one rank's QKV
+ * output, in place ("Megatron-LM 深度学习与源码分析文档", part 2 sections 3
+ * and 6: RoPE as a fused elementwise kernel on the QKV output, with
+ * rotary_base and rotary_percent; the rotation is RoFormer's, cited there):
+ * for row i at position m = positions[i] and pair j < rotary_dim/2 of each
+ * of the nq_local query and ng_local key heads (the first nq_local + ng_local
+ * heads of the row; value heads are untouched),
+ *   (x_a, x_b) <- (x_a cos(m t_j) - x_b sin(m t_j), x_b cos(m t_j) + x_a sin(m t_j)),
+ *   t_j = base^(-2j / rotary_dim),
+ * with b = a + rotary_dim/2, a = j ("rotate half", interleaved = 0) or
+ * a = 2j, b = 2j + 1 (interleaved = 1); head dimensions from rotary_dim on
+ * pass through.  Computed in fp32 from the bf16 values (angle reduced in
+ * double precision), rounded to bf16.  QKV is [M x ldo] bf16 as written by
+ * mtp_qkv_forward; positions is an int32 device array [M].  Requires
+ * nq_local % ng_local == 0, head_dim % 8 == 0, rotary_dim % 8 == 0 with
+ * 8 <= rotary_dim <= min(head_dim, 512), base > 1.
+ */
+mtp_status mtp_rope_qk(mtp_bf16* QKV, int64_t ldo, int64_t M, const int32_t* positions, int nq_local,
+                       int ng_local, int head_dim, int rotary_dim, double base, int interleaved,
+                       void* stream);
+
+/*
  * MoE router ("ai阅读megatron", MoELayer forward: router logits, top-k):
  * softmax over the E experts of each token (fp32), then the k most probable
  * experts (ties to the lower index).  Outputs, rows grouped by expert in

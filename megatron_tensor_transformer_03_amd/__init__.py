@@ -45,6 +45,7 @@ def lib():
             "mtp_moe_route": [vp, i64, ci, ci, vp, vp, vp, vp],
             "mtp_moe_mlp_forward": [vp, i64, i64, ci, i64, ci, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "mtp_gemm_plan": [i64, i64, i64, ci, vp, vp, vp],
+            "mtp_rope_qk": [vp, i64, i64, vp, ci, ci, ci, ci, ctypes.c_double, ci, vp],
             "mtp_release_workspaces": [],
         }
         for name, args in sig.items():
@@ -135,6 +136,14 @@ def mtp_qkv_forward(X, Wqkv_t, bias, nq_local, ng_local, head_dim, QKV):
     _check("mtp_qkv_forward", lib().mtp_qkv_forward(
         _ptr(X), _ld(X), M, H, _ptr(Wqkv_t), _ld(Wqkv_t), _ptr(bias), nq_local, ng_local, head_dim, _ptr(QKV),
         _ld(QKV), _stream(X)))
+    return QKV
+
+
+def mtp_rope_qk(QKV, positions, nq_local, ng_local, head_dim, rotary_dim, base, interleaved=False):
+    """In place: RoPE on the query and key heads of QKV [M x ldo] bf16; positions int32 [M] on the device."""
+    M = QKV.shape[0]
+    _check("mtp_rope_qk", lib().mtp_rope_qk(_ptr(QKV), _ld(QKV), M, _ptr(positions), nq_local, ng_local, head_dim,
+                                            rotary_dim, float(base), int(bool(interleaved)), _stream(QKV)))
     return QKV
 
 

@@ -238,6 +238,28 @@ mtp_status mtp_qkv_forward(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t H,
   return mtp_column_linear(X, ldx, Wqkv_t, ldw, bias, QKV, ldo, M, N, H, MTP_ACT_NONE, stream);
 }
 
+mtp_status mtp_rope_qk(mtp_bf16* QKV, int64_t ldo, int64_t M, const int32_t* positions, int nq_local, int ng_local,
+                       int head_dim, int rotary_dim, double base, int interleaved, void* stream) {
+  if (!QKV || !positions) return fail(MTP_ERR_NULL, "QKV or positions is NULL");
+  if (misaligned(QKV)) return fail(MTP_ERR_ALIGN, "QKV is not 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(positions) & 3u) != 0) return fail(MTP_ERR_ALIGN, "positions is not 4-byte aligned");
+  if (M < 1 || M > kIntMax) return fail(MTP_ERR_SHAPE, "M = %lld must be in [1, 2^31-1]", (long long)M);
+  if (nq_local < 1 || ng_local < 1 || nq_local % ng_local != 0)
+    return fail(MTP_ERR_SHAPE, "query heads per rank (%d) must be a positive multiple of key/value groups (%d)",
+                nq_local, ng_local);
+  if (head_dim < 8 || head_dim % 8 != 0) return fail(MTP_ERR_SHAPE, "head_dim %d must be a multiple of 8", head_dim);
+  if (rotary_dim < 8 || rotary_dim % 8 != 0 || rotary_dim > head_dim || rotary_dim > 512)
+    return fail(MTP_ERR_SHAPE, "rotary_dim %d must be a multiple of 8 in [8, min(head_dim, 512)]", rotary_dim);
+  if (!(base > 1.0) || base > 1e300) return fail(MTP_ERR_SHAPE, "rotary base must be a finite number > 1");
+  const int64_t width = ((int64_t)nq_local + 2 * (int64_t)ng_local) * head_dim;
+  if (ldo < width || ldo % 8 != 0)
+    return fail(MTP_ERR_SHAPE, "QKV: pitch %lld must be >= %lld and a multiple of 8", (long long)ldo, (long long)width);
+  TRY(check_device());
+  return launched(mtp::rope_qk(QKV, ldo, (int)M, positions, nq_local + ng_local, head_dim, rotary_dim, base,
+                               interleaved != 0, (hipStream_t)stream),
+                  "rope");
+}
+
 mtp_status mtp_moe_route(const float* logits, int64_t T, int E, int k, int32_t* expert_offsets, int32_t* token_idx,
                          float* token_w, void* stream) {
   if (!logits || !expert_offsets || !token_idx || !token_w) return fail(MTP_ERR_NULL, "a routing pointer is NULL");

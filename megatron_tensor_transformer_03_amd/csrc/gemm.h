@@ -49,6 +49,10 @@ hipError_t gemm(const GemmParams& p, int mode, hipStream_t st);
 // rows_upper: total rows over all groups (an upper bound is enough; spare tiles exit).
 hipError_t gemm_grouped(const GemmParams& p, int mode, int rows_upper, hipStream_t st);
 
+// Rotary position embedding of the first `heads` heads of each row, in place (rope.hip).
+hipError_t rope_qk(uint16_t* qkv, int64_t ldo, int M, const int32_t* positions, int heads, int head_dim,
+                   int rotary_dim, double base, bool interleaved, hipStream_t st);
+
 // MoE helpers (moe.hip).
 hipError_t moe_route(const float* logits, int T, int E, int k, int32_t* offsets, int32_t* token_idx,
                      float* token_w, hipStream_t st);

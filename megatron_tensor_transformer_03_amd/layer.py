@@ -1,7 +1,8 @@
 """One rank's layer forward as a sequence of C-ABI calls (argument marshalling only).
 
 The per-rank hot path of a Megatron-style layer ("Megatron-LM 深度学习与源码分析文档",
-part 2 section 2): the QKV ColumnParallelLinear, the attention out-projection
+part 2 section 2): the QKV ColumnParallelLinear (with RoPE on its Q and K heads
+where the model uses it), the attention out-projection
 RowParallelLinear (its input, the attention context, is an input here: core
 attention is not part of this path), and the MLP with fc1 column-parallel
 (bias + GeLU or SwiGLU fused) and fc2 row-parallel.  For an MoE layer the
@@ -38,6 +39,8 @@ class RankForward:
         if "nq" in dims:
             nq_l, ng_l, d = dims["nq"] // p, dims["ng"] // p, dims["d"]
             self.out["qkv"] = torch.empty(M, (nq_l + 2 * ng_l) * d, dtype=bf, device=dev)
+            if "rope" in dims:  # token positions of the rows (one sequence of M tokens)
+                self.positions = torch.arange(M, dtype=torch.int32, device=dev)
         if "ctx" in inputs:
             if p == 1:
                 self.out["attn_out"] = torch.empty(M, H, dtype=bf, device=dev)
@@ -67,6 +70,10 @@ class RankForward:
         if "nq" in d:
             out.append(("qkv", lambda: mtp.mtp_qkv_forward(t["X"], t["Wqkv_t"], t.get("bqkv"), d["nq"] // p,
                                                            d["ng"] // p, d["d"], o["qkv"])))
+        if "rope" in d:
+            r = d["rope"]
+            out.append(("rope", lambda: mtp.mtp_rope_qk(o["qkv"], self.positions, d["nq"] // p, d["ng"] // p, d["d"],
+                                                        r["rotary_dim"], r["base"], r["interleaved"])))
         if "ctx" in t:
             if p == 1:  # the whole layer: the all-reduce is the identity, bias added here
                 out.append(("out_proj", lambda: mtp.mtp_row_linear_partial(t["ctx"], t["Wo_t"], None, False,

@@ -91,7 +91,9 @@ def llama70b_tp8_rank0() -> Workload:
     M, H, nq, ng, d, p, F = 4096, 8192, 64, 8, 128, 8, 28672
     w = Workload("llama70b_gqa_swiglu_tp8_rank0_4096tok",
                  "70B-class GQA/SwiGLU layer, rank 0 of TP=8: 8 q-heads + 1 kv-group per rank, ffn 28672")
-    w.dims = dict(M=M, H=H, nq=nq, ng=ng, d=d, F=F, p=p, act=ACT_SWIGLU, ranks="rank0")
+    # RoPE on the Q and K heads after the QKV GEMM (rotate half, base 5e5, full head dim), one 4096-token sequence
+    w.dims = dict(M=M, H=H, nq=nq, ng=ng, d=d, F=F, p=p, act=ACT_SWIGLU, ranks="rank0",
+                  rope=dict(base=500000.0, rotary_dim=d, interleaved=False))
     nqkv = (nq // p + 2 * (ng // p)) * d
     F_l = F // p
     w.tensors = dict(X=T((M, H), 4001), Wqkv_t=T((nqkv, H), 4002, W_SIGMA),

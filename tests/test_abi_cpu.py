@@ -27,7 +27,7 @@ def _gpu_present():
 def test_library_exports_every_header_symbol():
     L = mtp.lib()
     names = mtp.header_symbols()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", mtp.LIB_PATH], capture_output=True, text=True).stdout
@@ -169,6 +169,33 @@ def test_gemm_plan_and_release_need_a_device():
     o = [ctypes.c_int(0) for _ in range(3)]
     assert L.mtp_gemm_plan(4096, 4096, 4096, 0, *[ctypes.addressof(x) for x in o]) == UNSUPPORTED
     assert L.mtp_release_workspaces() == UNSUPPORTED
+
+
+def test_rope_rejects():
+    L = mtp.lib()
+    ok = dict(QKV=P, ldo=64, M=4, pos=P2, nq=1, ng=1, d=16, rd=16, base=10000.0, il=0)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.mtp_rope_qk(a["QKV"], a["ldo"], a["M"], a["pos"], a["nq"], a["ng"], a["d"], a["rd"], a["base"],
+                             a["il"], None)
+    assert call(QKV=None) == NULL
+    assert call(pos=None) == NULL
+    assert call(QKV=BAD) == ALIGN
+    assert call(pos=P2 + 2) == ALIGN
+    assert call(M=0) == SHAPE
+    assert call(nq=3, ng=2) == SHAPE
+    assert call(d=12) == SHAPE
+    assert call(rd=12) == SHAPE
+    assert call(rd=32) == SHAPE        # rotary_dim > head_dim
+    assert call(base=1.0) == SHAPE
+    assert call(ldo=40) == SHAPE       # pitch below (nq + 2 ng) d = 48
+
+
+@pytest.mark.skipif(_gpu_present(), reason="on a GPU box a valid call would launch")
+def test_rope_valid_call_reaches_the_device_check():
+    assert mtp.lib().mtp_rope_qk(P, 64, 4, P2, 1, 1, 16, 16, 10000.0, 0, None) == UNSUPPORTED
 
 
 def test_binding_raises_when_library_refuses(monkeypatch):

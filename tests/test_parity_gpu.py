@@ -189,6 +189,39 @@ def test_split_schedule_gelu_matches_one_tile_per_workgroup():
     assert _exact_bits_frac(G, R) >= EXACT_FRAC_MIN
 
 
+# ----------------------------------------------------------------------------- rotary position embedding
+@pytest.mark.parametrize("M,nq,ng,d,rd,interleaved", [
+    (1, 1, 1, 8, 8, False), (37, 4, 2, 64, 64, False), (37, 4, 2, 64, 64, True), (300, 8, 1, 128, 128, False),
+    (130, 6, 3, 96, 32, True), (129, 2, 2, 128, 64, False),
+])
+def test_rope_matches_oracle(M, nq, ng, d, rd, interleaved):
+    say("rope", M, nq, ng, d, rd, interleaved)
+    width = (nq + 2 * ng) * d
+    ld = width + 24  # padded rows: the padding must stay untouched
+    Qb = synth.normal_bf16(281, M, ld, 1.0)
+    pos = (np.arange(M, dtype=np.int64) * 977 + 13) % 70000  # scattered positions up to 7e4
+    Q = to_dev(Qb)
+    P = torch.from_numpy(pos.astype(np.int32)).cuda()
+    mtp.mtp_rope_qk(Q, P, nq, ng, d, rd, 10000.0, interleaved)
+    torch.cuda.synchronize()
+    R = oracle.rope(widen_bits(Qb[:, :width]), pos, nq, ng, d, rd, 10000.0, interleaved)
+    G = bits(Q)
+    assert np.array_equal(G[:, (nq + ng) * d:], Qb[:, (nq + ng) * d:]), "value heads or row padding changed"
+    _close(widen_bits(G[:, :width]), R, "rope")
+    assert _exact_bits_frac(G[:, :width], R) >= 0.99
+
+
+def test_rope_rejects_bad_shapes():
+    Q = torch.zeros(4, 64, dtype=torch.bfloat16, device="cuda")
+    P = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for kw in (dict(rotary_dim=12), dict(rotary_dim=128), dict(head_dim=12), dict(base=1.0)):
+        args = dict(nq_local=1, ng_local=1, head_dim=16, rotary_dim=16, base=10000.0)
+        args.update(kw)
+        with pytest.raises(mtp.MTPError):
+            mtp.mtp_rope_qk(Q, P, **args)
+    assert torch.count_nonzero(Q) == 0
+
+
 # ----------------------------------------------------------------------------- activations, small full checks
 @pytest.mark.parametrize("M,N,K", [(200, 300, 136), (64, 64, 64), (513, 1030, 256)])
 def test_gelu_column_linear(M, N, K):
@@ -296,6 +329,10 @@ def _check_dense_workload(w, nrows, seed):
     act = d["act"]
     nq_l, ng_l = d["nq"] // p, d["ng"] // p
     Rq, _ = oracle.qkv(X, h["Wqkv_t"], h.get("bqkv"), nq_l, ng_l, d["d"])
+    if "rope" in d:  # RoPE on the bf16 QKV output (chained), rows at their positions
+        r = d["rope"]
+        Rq = oracle.rope(widen_bits(oracle.round_bf16(Rq)), rows, nq_l, ng_l, d["d"], r["rotary_dim"], r["base"],
+                         r["interleaved"])
     _close(widen_bits(bits(o["qkv"][rows])), Rq, "qkv")
     if "ctx" in w.tensors:
         C = synth.host_rows(w.tensors["ctx"], rows)
