@@ -283,3 +283,16 @@ def rope(QKV: np.ndarray, positions, nq_local: int, ng_local: int, head_dim: int
         X[:, a] = xa * c - xb * s
         X[:, b] = xb * c + xa * s
     return X
+
+
+# ----------------------------------------------------------------------------- backward of the linears
+def linear_dgrad(dY: np.ndarray, Wt: np.ndarray) -> np.ndarray:
+    """dX = dY . W for Y = X . W (weights stored Wt = W^T, [N x K]): the input gradient of a linear, the
+    backward GEMM the pages pair with each forward one ("Megatron-LM 深度学习与源码分析文档", part 2 section 2:
+    the column-parallel backward all-reduces dX, the row-parallel backward needs no exchange for dX)."""
+    return linear(dY, np.ascontiguousarray(Wt.T))
+
+
+def linear_wgrad(dY: np.ndarray, X: np.ndarray) -> np.ndarray:
+    """dWt = dY^T . X ([N x K], same layout as Wt): the weight gradient of Y = X . Wt^T, summed over the M rows."""
+    return linear(np.ascontiguousarray(dY.T), np.ascontiguousarray(X.T))

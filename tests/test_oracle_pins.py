@@ -407,3 +407,58 @@ def test_rope_relative_position_and_norms():
         zq, zy = _complex_pairs(q, d, interleaved), _complex_pairs(y, d, interleaved)
         np.testing.assert_allclose(np.abs(zy), np.abs(zq), rtol=1e-13)
         np.testing.assert_array_equal(f(q, 0), q)
+
+
+# ----------------------------------------------------------------------------- backward of the linears
+def test_backward_brute_force_exact():
+    # exact rational sums on a rectangular case: dX[m][k] = sum_n dY[m][n] W[n][k], dW[n][k] = sum_m dY[m][n] X[m][k]
+    rng = np.random.default_rng(3)
+    M, N, K = 3, 5, 4
+    dYb = synth.normal_bf16(31, M, N, 1.0)
+    Wb = synth.normal_bf16(32, N, K, 1.0)
+    Xb = synth.normal_bf16(33, M, K, 1.0)
+    dY, W, X = oracle.widen(dYb), oracle.widen(Wb), oracle.widen(Xb)
+    dX = oracle.linear_dgrad(dYb, Wb)
+    dW = oracle.linear_wgrad(dYb, Xb)
+    for m in range(M):
+        for k in range(K):
+            assert dX[m, k] == float(sum(Fraction(dY[m, n]) * Fraction(W[n, k]) for n in range(N)))
+    for n in range(N):
+        for k in range(K):
+            assert dW[n, k] == float(sum(Fraction(dY[m, n]) * Fraction(X[m, k]) for m in range(M)))
+
+
+def test_backward_adjoint_identities():
+    # for Y = X W^T: <dY, Y> = <dX, X> = <dW, W> (the gradients are the adjoints of the forward map); a
+    # transposed operand or a swapped index breaks them on rectangular shapes
+    M, N, K = 6, 9, 7
+    dYb = synth.normal_bf16(41, M, N, 1.0)
+    Wb = synth.normal_bf16(42, N, K, 1.0)
+    Xb = synth.normal_bf16(43, M, K, 1.0)
+    Y = oracle.linear(Xb, Wb)
+    dY, W, X = oracle.widen(dYb), oracle.widen(Wb), oracle.widen(Xb)
+    lhs = float(np.sum(dY * Y))
+    assert abs(float(np.sum(oracle.linear_dgrad(dYb, Wb) * X)) - lhs) < 1e-9 * (1 + abs(lhs))
+    assert abs(float(np.sum(oracle.linear_wgrad(dYb, Xb) * W)) - lhs) < 1e-9 * (1 + abs(lhs))
+
+
+def test_backward_finite_differences():
+    # central differences of L(X, W) = <dY, X W^T> (exactly bilinear, so the differences are exact up to
+    # rounding) reproduce the gradients element by element
+    M, N, K = 4, 3, 5
+    dYb = synth.normal_bf16(51, M, N, 1.0)
+    Wb = synth.normal_bf16(52, N, K, 1.0)
+    Xb = synth.normal_bf16(53, M, K, 1.0)
+    dY, W, X = oracle.widen(dYb), oracle.widen(Wb), oracle.widen(Xb)
+    L = lambda Xv, Wv: float(np.sum(dY * (Xv @ Wv.T)))
+    dX = oracle.linear_dgrad(dYb, Wb)
+    dW = oracle.linear_wgrad(dYb, Xb)
+    h = 0.5
+    for m in range(M):
+        for k in range(K):
+            E = np.zeros_like(X); E[m, k] = h
+            assert abs((L(X + E, W) - L(X - E, W)) / (2 * h) - dX[m, k]) < 1e-12
+    for n in range(N):
+        for k in range(K):
+            E = np.zeros_like(W); E[n, k] = h
+            assert abs((L(X, W + E) - L(X, W - E)) / (2 * h) - dW[n, k]) < 1e-12
