@@ -132,6 +132,37 @@ mtp_status mtp_qkv_forward(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t H,
                            mtp_bf16* QKV, int64_t ldo, void* stream);
 
 /*
+ * Backward GEMMs of a linear Y = X . Wt^T ("Megatron-LM 深度学习与源码分析文档",
+ * part 2 section 2: each parallel linear's backward computes the input and
+ * weight gradients; the column-parallel one all-reduces dX across ranks, the
+ * row-parallel one needs no exchange for dX; "ai阅读megatron": train_step's
+ * backward pass).  fp32 accumulation, bf16 inputs (raw bits).
+ *
+ * mtp_linear_dgrad: dX [M x K] = dY [M x N] . Wt [N x K].  dXacc (fp32,
+ * pitch ldacc) receives dX (accumulate = 0) or adds it (accumulate = 1: the
+ * local form of the column-parallel all-reduce over ranks); if dX != NULL
+ * it also receives bf16(result).  At least one of dXacc, dX is non-NULL;
+ * accumulate needs dXacc.  N (the contraction) % 8 == 0.
+ *
+ * mtp_linear_wgrad: dWt [N x K] = dY^T . X, summed over the M rows
+ * (dY [M x N], X [M x K]), into fp32 dW (pitch lddw): dW = result
+ * (accumulate = 0) or dW += result (accumulate = 1, gradient accumulation).
+ *
+ * Both read their row-major-K operands with the gfx950 LDS transpose load,
+ * so no transposed copy is made.  Same pointer, pitch and alignment rules as
+ * the forward calls, except that only dgrad's N must be a multiple of 8
+ * (K, and wgrad's M, N, K are free).  A row-major-K operand is read in
+ * 8-column chunks, so each of its rows is read up to the next multiple of 8
+ * past its width (inside the pitch; those columns reach no output); each
+ * such operand must span less than 2 GiB.
+ */
+mtp_status mtp_linear_dgrad(const mtp_bf16* dY, int64_t lddy, const mtp_bf16* Wt, int64_t ldw, float* dXacc,
+                            int64_t ldacc, int accumulate, mtp_bf16* dX, int64_t lddx, int64_t M, int64_t N,
+                            int64_t K, void* stream);
+mtp_status mtp_linear_wgrad(const mtp_bf16* dY, int64_t lddy, const mtp_bf16* X, int64_t ldx, float* dW,
+                            int64_t lddw, int accumulate, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * Rotary position embedding of the query and key heads of one rank's QKV
  * output, in place ("Megatron-LM 深度学习与源码分析文档", part 2 sections 3
  * and 6: RoPE as a fused elementwise kernel on the QKV output, with

@@ -46,6 +46,8 @@ def lib():
             "mtp_moe_mlp_forward": [vp, i64, i64, ci, i64, ci, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "mtp_gemm_plan": [i64, i64, i64, ci, vp, vp, vp],
             "mtp_rope_qk": [vp, i64, i64, vp, ci, ci, ci, ci, ctypes.c_double, ci, vp],
+            "mtp_linear_dgrad": [vp, i64, vp, i64, vp, i64, ci, vp, i64, i64, i64, i64, vp],
+            "mtp_linear_wgrad": [vp, i64, vp, i64, vp, i64, ci, i64, i64, i64, vp],
             "mtp_release_workspaces": [],
         }
         for name, args in sig.items():
@@ -137,6 +139,25 @@ def mtp_qkv_forward(X, Wqkv_t, bias, nq_local, ng_local, head_dim, QKV):
         _ptr(X), _ld(X), M, H, _ptr(Wqkv_t), _ld(Wqkv_t), _ptr(bias), nq_local, ng_local, head_dim, _ptr(QKV),
         _ld(QKV), _stream(X)))
     return QKV
+
+
+def mtp_linear_dgrad(dY, Wt, dXacc=None, accumulate=False, dX=None):
+    """dX = dY . Wt (Wt [N x K]) into fp32 dXacc (= or +=) and/or bf16 dX."""
+    M, N = dY.shape
+    K = Wt.shape[1]
+    _check("mtp_linear_dgrad", lib().mtp_linear_dgrad(
+        _ptr(dY), _ld(dY), _ptr(Wt), _ld(Wt), _ptr(dXacc), _ld(dXacc) if dXacc is not None else 0,
+        int(bool(accumulate)), _ptr(dX), _ld(dX) if dX is not None else 0, M, N, K, _stream(dY)))
+    return dX if dX is not None else dXacc
+
+
+def mtp_linear_wgrad(dY, X, dW, accumulate=False):
+    """dW (=|+=) dY^T . X in fp32; dY [M x N], X [M x K], dW [N x K]."""
+    M, N = dY.shape
+    K = X.shape[1]
+    _check("mtp_linear_wgrad", lib().mtp_linear_wgrad(
+        _ptr(dY), _ld(dY), _ptr(X), _ld(X), _ptr(dW), _ld(dW), int(bool(accumulate)), M, N, K, _stream(dY)))
+    return dW
 
 
 def mtp_rope_qk(QKV, positions, nq_local, ng_local, head_dim, rotary_dim, base, interleaved=False):

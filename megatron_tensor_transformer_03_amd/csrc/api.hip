@@ -238,6 +238,54 @@ mtp_status mtp_qkv_forward(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t H,
   return mtp_column_linear(X, ldx, Wqkv_t, ldw, bias, QKV, ldo, M, N, H, MTP_ACT_NONE, stream);
 }
 
+mtp_status mtp_linear_dgrad(const mtp_bf16* dY, int64_t lddy, const mtp_bf16* Wt, int64_t ldw, float* dXacc,
+                            int64_t ldacc, int accumulate, mtp_bf16* dX, int64_t lddx, int64_t M, int64_t N, int64_t K,
+                            void* stream) {
+  // dX [M x K] = dY [M x N] . Wt [N x K]: the product C = A B^T with A = dY (contraction N along its rows'
+  // columns) and B = Wt read row-major-K (its rows are the contraction index)
+  TRY(check_dims(M, K, N));
+  TRY(check_mat(dY, "dY", N, lddy));
+  TRY(check_mat(Wt, "Wt", K, ldw));
+  if (!dXacc && !dX) return fail(MTP_ERR_NULL, "dXacc and dX are both NULL");
+  if (!dXacc && accumulate) return fail(MTP_ERR_NULL, "accumulate needs dXacc");
+  if (dXacc) {
+    if (misaligned(dXacc)) return fail(MTP_ERR_ALIGN, "dXacc is not 16-byte aligned");
+    if (ldacc < K || ldacc % 8 != 0) return fail(MTP_ERR_SHAPE, "dXacc: pitch %lld must be >= %lld and a multiple of 8",
+                                                 (long long)ldacc, (long long)K);
+  }
+  if (dX) TRY(check_mat(dX, "dX", K, lddx));
+  TRY(check_window("dY", 256, lddy));
+  TRY(check_window("Wt", N, ldw));
+  TRY(check_device());
+  mtp::GemmParams p;
+  p.A = dY; p.lda = lddy; p.B = Wt; p.ldb = ldw; p.Y = dX; p.ldy = dX ? lddx : 0; p.Yacc = dXacc;
+  p.ldacc = dXacc ? ldacc : 0; p.accumulate = accumulate ? 1 : 0;
+  p.M = (int)M; p.Nout = (int)K; p.K = (int)N; p.a_src_rows = M;
+  return launched(mtp::gemm_backward(p, false, true, (hipStream_t)stream), "linear dgrad");
+}
+
+mtp_status mtp_linear_wgrad(const mtp_bf16* dY, int64_t lddy, const mtp_bf16* X, int64_t ldx, float* dW, int64_t lddw,
+                            int accumulate, int64_t M, int64_t N, int64_t K, void* stream) {
+  // dWt [N x K] (+)= dY^T [N x M] . X [M x K]: C = A B^T with A = dY and B = X both read row-major-K (their
+  // rows are the contraction index M)
+  if (M < 1 || N < 1 || K < 1) return fail(MTP_ERR_SHAPE, "sizes must be >= 1 (M=%lld N=%lld K=%lld)", (long long)M,
+                                           (long long)N, (long long)K);
+  if (M > kIntMax || N > kIntMax || K > kIntMax) return fail(MTP_ERR_SHAPE, "a size exceeds 2^31-1");
+  TRY(check_mat(dY, "dY", N, lddy));
+  TRY(check_mat(X, "X", K, ldx));
+  if (!dW) return fail(MTP_ERR_NULL, "dW is NULL");
+  if (misaligned(dW)) return fail(MTP_ERR_ALIGN, "dW is not 16-byte aligned");
+  if (lddw < K || lddw % 8 != 0) return fail(MTP_ERR_SHAPE, "dW: pitch %lld must be >= %lld and a multiple of 8",
+                                             (long long)lddw, (long long)K);
+  TRY(check_window("dY", M, lddy));
+  TRY(check_window("X", M, ldx));
+  TRY(check_device());
+  mtp::GemmParams p;
+  p.A = dY; p.lda = lddy; p.B = X; p.ldb = ldx; p.Yacc = dW; p.ldacc = lddw; p.accumulate = accumulate ? 1 : 0;
+  p.M = (int)N; p.Nout = (int)K; p.K = (int)M; p.a_src_rows = N;
+  return launched(mtp::gemm_backward(p, true, true, (hipStream_t)stream), "linear wgrad");
+}
+
 mtp_status mtp_rope_qk(mtp_bf16* QKV, int64_t ldo, int64_t M, const int32_t* positions, int nq_local, int ng_local,
                        int head_dim, int rotary_dim, double base, int interleaved, void* stream) {
   if (!QKV || !positions) return fail(MTP_ERR_NULL, "QKV or positions is NULL");

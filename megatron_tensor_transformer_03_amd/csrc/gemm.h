@@ -42,10 +42,12 @@ struct GemmParams {
 struct GemmPlan {
   int bm = 0, bn = 0, split_groups = 0, id = 0, split_chunks = 0;
 };
-GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K);
+GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, bool row_major_k = false);
 hipError_t release_split_workspaces();
 
 hipError_t gemm(const GemmParams& p, int mode, hipStream_t st);
+// MODE_ROW products whose A (and/or B) operand is stored [K x M] ([K x N]): lda / ldb are those pitches.
+hipError_t gemm_backward(const GemmParams& p, bool a_row_major_k, bool b_row_major_k, hipStream_t st);
 // rows_upper: total rows over all groups (an upper bound is enough; spare tiles exit).
 hipError_t gemm_grouped(const GemmParams& p, int mode, int rows_upper, hipStream_t st);
 

@@ -158,7 +158,12 @@ __device__ __forceinline__ void store4_bf16(uint16_t* dst, const float v[4], int
   }
 }
 
-template <class C, int MODE, bool GROUPED, bool KFULL, bool SPLIT>
+// AT / BT: the operand is stored with the contraction index along its rows ([K x M] for A, [K x N] for B;
+// the backward GEMMs: dX = dY W reads W that way, dW = dY^T X reads both).  Such a tile is kept in LDS as
+// [BK rows][BM or BN columns] and its MFMA fragments are read with ds_read_b64_tr_b16, the gfx950 LDS
+// transpose load: 16 lanes each name 4 consecutive columns of one row, and lane i receives column i of
+// four consecutive rows.
+template <class C, int MODE, bool GROUPED, bool KFULL, bool SPLIT, bool AT = false, bool BT = false>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   // A private copy of the parameters: read once into scalar registers, rather than reloaded from the
   // kernel argument segment (each reload waits on the LDS/scalar counter) wherever a field is used.
@@ -167,6 +172,10 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, CPR = C::CPR, RPL = C::RPL;
   constexpr int D = C::D, GA = C::GA, ROWS_PER_DMA = C::ROWS_PER_DMA;
   static_assert(MODE != MODE_SWIGLU || TN % 64 == 0, "gate/up fragment pairs");
+  static_assert(!(AT || BT) || (BK == 32 && !GROUPED && (MODE == MODE_COL || MODE == MODE_ROW)),
+                "row-major-K operands: K step 32, plain column/row epilogues");
+  static_assert(!AT || BM == 128 || BM == 256, "A rows of 256 or 512 bytes");
+  static_assert(!BT || BN == 128 || BN == 256, "B rows of 256 or 512 bytes");
   constexpr int NB_OUT = MODE == MODE_SWIGLU ? BN / 2 : BN;  // output columns per tile
 
   // one LDS variable per stage (see the design notes); unused ones are a token 16 bytes
@@ -218,7 +227,10 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   constexpr uint32_t kOOB = 0x7FFFFFF0u;
   const uint16_t* a_base;
   int64_t a_extent;
-  if (p.a_rows) {
+  if constexpr (AT) {  // [K x M]: the tile's columns m0 .. m0 + BM - 1 of every row
+    a_base = p.A + m0;
+    a_extent = (int64_t)p.K * p.lda - m0;
+  } else if (p.a_rows) {
     a_base = p.A;
     a_extent = p.a_src_rows * p.lda;
   } else {
@@ -226,8 +238,9 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     a_extent = (p.a_src_rows - (row_base + m0)) * p.lda;
   }
   const int nbase = tn * NB_OUT;
-  const uint16_t* b_base = B + (int64_t)nbase * p.ldb;
-  const int64_t b_extent = ((MODE == MODE_SWIGLU ? p.up_offset : 0) + p.Nout - nbase) * p.ldb;
+  const uint16_t* b_base = BT ? B + nbase : B + (int64_t)nbase * p.ldb;
+  const int64_t b_extent = BT ? (int64_t)p.K * p.ldb - nbase
+                              : ((MODE == MODE_SWIGLU ? p.up_offset : 0) + p.Nout - nbase) * p.ldb;
   // (integer clamps written out: the device min() overload for 64-bit integers goes through double, and a
   // converted value lands in a vector register, which turns every buffer load into a waterfall loop)
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(a_base, 2 * a_extent < (int64_t)kOOB ? 2 * a_extent : (int64_t)kOOB);
@@ -246,7 +259,21 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     const int r = ROWS_PER_DMA * g + lrow - (g < GA ? 0 : BM);  // row within A or within B
     const int c = (lane % CPR) ^ ((r / RPL) & (CPR - 1));
     d_kc[j] = 8 * c;
-    if (g < GA) {
+    // a row-major-K operand: instruction g fills rows RT g .. RT g + RT - 1 of the [BK x BX] tile (RT = 512 /
+    // BX), 16-byte chunk (lane % (BX / 8)) of a row holding global chunk (lane % (BX / 8)) ^ 4 (row % 4); its K
+    // position is the row, and chunks that start past the matrix width load nothing
+    auto t_off = [&](int gg, int BX, int64_t ld, int x0, int width) {
+      const int cpr = BX / 8;
+      const int rk = (512 / BX) * gg + lane / cpr;
+      const int cc = (lane % cpr) ^ (4 * (rk & 3));
+      d_kc[j] = rk;
+      return x0 + 8 * cc < width ? 2u * (uint32_t)(rk * ld + 8 * cc) : kOOB;
+    };
+    if (g < GA && AT) {
+      d_off[j] = t_off(g, BM, p.lda, m0, p.M);
+    } else if (g >= GA && g < GA + C::GB && BT) {
+      d_off[j] = t_off(g - GA, BN, p.ldb, nbase, p.Nout);
+    } else if (g < GA) {
       if (p.a_rows) {
         const int m = m0 + r;
         d_off[j] = m < rows ? 2u * (uint32_t)((int64_t)p.a_rows[row_base + m] * p.lda + 8 * c) : kOOB;
@@ -269,7 +296,9 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   // inside the rows: a prefetch past the last K step re-reads step 0 into a stage that is never consumed
   // (KFULL) or is redirected out of range per lane (!KFULL, reading zeros).
   auto dma_stage = [&](int k0, uint16_t* sbuf) {
-    const int soff = k0 < p.K ? 2 * k0 : 0;
+    // the K position: a column offset for K-major operands, a row offset for row-major-K ones
+    const int soff_a = k0 < p.K ? (AT ? 2 * k0 * (int)p.lda : 2 * k0) : 0;
+    const int soff_b = k0 < p.K ? (BT ? 2 * k0 * (int)p.ldb : 2 * k0) : 0;
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int g = j * NWAVES + wave_u;  // uniform
@@ -277,7 +306,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
       if constexpr (!KFULL) vo = k0 + d_kc[j] < p.K ? vo : kOOB;
       uint16_t* dst = sbuf + g * ROWS_PER_DMA * BK;
       if constexpr (C::SPARE) dst = g < GA + C::GB ? dst : lds_spare;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(g < GA ? a_rsrc : b_rsrc, (lds_ptr)dst, 16, vo, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g < GA ? a_rsrc : b_rsrc, (lds_ptr)dst, 16, vo, g < GA ? soff_a : soff_b,
+                                               0, 0);
     }
   };
 
@@ -293,14 +323,40 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   // Two fragment sets alternate: the set of the next k step is read while the MFMAs of this one run.
   const int fr = lane & 31, fk = lane >> 5;
   bf16x8 fa[2][FM], fb[2][FN];
+  // Fragment of a [BK x BX] row-major-K tile: lane l (16-lane group g = l / 16, i = l % 16) names row
+  // 16 ks + 8 (l / 32) + 4 r + i / 4 and columns x0 + 16 (g % 2) + 4 (i % 4) .. + 3; the transpose load then
+  // gives it column x0 + (l % 32) of rows 16 ks + 8 (l / 32) + 4 r .. + 3, i.e. k = 8 (l / 32) + 4 r .. + 3 of
+  // its MFMA operand row.  Two loads (r = 0, 1) make the 8 k values.  Rows r and r + 1 .. r + 3 use chunks
+  // XOR 4 (row % 4), so the 32 lanes of a half-wave hit 64 distinct banks.
+  typedef short short4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) short4_t* lds_s4;
+  auto read_t = [&](const uint16_t* s, auto BXC, int x0, int ks) -> bf16x8 {
+    constexpr int BX = decltype(BXC)::value;
+    const int i = lane & 15, h = lane >> 5;
+    const int x = x0 + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+    short4_t v[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int k = 16 * ks + 8 * h + 4 * r + (i >> 2);
+      const int off = k * BX + (((x >> 3) ^ (4 * (i >> 2))) << 3) + (x & 7);
+      v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(s + off));
+    }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   auto read_frags = [&](const uint16_t* sbuf, int ks, auto SET) {
     constexpr int q = decltype(SET)::value;
     const uint16_t* sA = sbuf;
     const uint16_t* sB = sbuf + BM * BK;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fa[q][i] = *reinterpret_cast<const bf16x8*>(sA + swz<C>(wm0 + 32 * i + fr, 2 * ks + fk));
+    for (int i = 0; i < FM; ++i) {
+      if constexpr (AT) fa[q][i] = read_t(sA, std::integral_constant<int, BM>{}, wm0 + 32 * i, ks);
+      else fa[q][i] = *reinterpret_cast<const bf16x8*>(sA + swz<C>(wm0 + 32 * i + fr, 2 * ks + fk));
+    }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) fb[q][j] = *reinterpret_cast<const bf16x8*>(sB + swz<C>(wn0 + 32 * j + fr, 2 * ks + fk));
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (BT) fb[q][j] = read_t(sB, std::integral_constant<int, BN>{}, wn0 + 32 * j, ks);
+      else fb[q][j] = *reinterpret_cast<const bf16x8*>(sB + swz<C>(wn0 + 32 * j + fr, 2 * ks + fk));
+    }
   };
   auto mma = [&](auto SET) {
     constexpr int q = decltype(SET)::value;
@@ -704,7 +760,7 @@ hipError_t split_workspace(hipStream_t st, size_t ws_bytes, int64_t cnt_n, float
 }
 }  // namespace
 
-template <class C, int MODE, bool GROUPED>
+template <class C, int MODE, bool GROUPED, bool AT = false, bool BT = false>
 static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStream_t st, int split_groups = 0,
                              int split_chunks = 0) {
   GemmParams p = p0;
@@ -725,16 +781,19 @@ static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStrea
       hipError_t e = split_workspace(st, (size_t)tiles * split_chunks * slot, tiles, &p.sk_ws, &p.sk_cnt);
       if (e != hipSuccess) return e;
       if (kfull)
-        hipLaunchKernelGGL((gemm_kernel<C, MODE, false, true, true>), dim3(split_groups), dim3(C::NT), 0, st, p);
+        hipLaunchKernelGGL((gemm_kernel<C, MODE, false, true, true, AT, BT>), dim3(split_groups), dim3(C::NT), 0, st, p);
       else
-        hipLaunchKernelGGL((gemm_kernel<C, MODE, false, false, true>), dim3(split_groups), dim3(C::NT), 0, st, p);
+        hipLaunchKernelGGL((gemm_kernel<C, MODE, false, false, true, AT, BT>), dim3(split_groups), dim3(C::NT), 0, st,
+                           p);
       return hipGetLastError();
     }
   }
   if (kfull)
-    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, true, false>), dim3((unsigned)tiles), dim3(C::NT), 0, st, p);
+    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, true, false, AT, BT>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
+                       p);
   else
-    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, false, false>), dim3((unsigned)tiles), dim3(C::NT), 0, st, p);
+    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, false, false, AT, BT>), dim3((unsigned)tiles), dim3(C::NT), 0,
+                       st, p);
   return hipGetLastError();
 }
 
@@ -762,7 +821,7 @@ using SmallTile = Cfg<MTP_SMALL_CFG>;          // 8 waves (32 x 64), 128 KB
 // waves of units times the time of a chunk plus fixed costs.  Wave quantisation is large at the shard
 // shapes of a tensor-parallel layer: 4096 x 1280 is 80 tiles of 256 x 256 (31% of the CUs busy) but 240
 // units in 3 chunks.
-GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K) {
+GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, bool row_major_k) {
   struct Opt { int bm, bn; double eff; int id; int ns_bk; int64_t slot_bytes; };
   const Opt opts[] = {{256, 256, 1.00, 0, 128, 256 << 10}, {256, 192, 0.95, 1, 128, 192 << 10},
                       {256, 128, 0.85, 2, 128, 128 << 10}, {128, 128, 0.72, 3, 256, 0}};
@@ -772,6 +831,7 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K) {
   double best_t = 1e300;
   for (const Opt& o : opts) {
     if (mode == MODE_SWIGLU && o.id == 1) continue;  // gate/up pairs need wave tiles of 64 B rows
+    if (row_major_k && (o.id == 1 || o.id == 3)) continue;  // transposed tiles: 256 x 256 and 256 x 128 only
     const int64_t nbo = mode == MODE_SWIGLU ? o.bn / 2 : o.bn;
     const int64_t tiles = ((M + o.bm - 1) / o.bm) * ((Nout + nbo - 1) / nbo);
     const double tile_t = o.bm * o.bn / o.eff;
@@ -793,7 +853,7 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K) {
 
 template <int MODE>
 static hipError_t dispatch(const GemmParams& p, hipStream_t st) {
-  const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K);
+  const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K, false);
   switch (pl.id) {
     case 0: return launch_cfg<BigTile, MODE, false>(p, 0, st, pl.split_groups, pl.split_chunks);
     case 1:
@@ -803,6 +863,20 @@ static hipError_t dispatch(const GemmParams& p, hipStream_t st) {
     case 2: return launch_cfg<HalfTile, MODE, false>(p, 0, st, pl.split_groups, pl.split_chunks);
     default: return launch_cfg<SmallTile, MODE, false>(p, 0, st);  // (never split)
   }
+}
+
+// Backward products: dgrad reads B row-major-K (AT = false, BT = true), wgrad both operands.
+template <bool AT, bool BT>
+static hipError_t dispatch_t(const GemmParams& p, hipStream_t st) {
+  const GemmPlan pl = gemm_plan(MODE_ROW, p.M, p.Nout, p.K, true);
+  if (pl.id == 0) return launch_cfg<BigTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks);
+  return launch_cfg<HalfTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks);
+}
+
+hipError_t gemm_backward(const GemmParams& p, bool a_row_major_k, bool b_row_major_k, hipStream_t st) {
+  if (!a_row_major_k && b_row_major_k) return dispatch_t<false, true>(p, st);
+  if (a_row_major_k && b_row_major_k) return dispatch_t<true, true>(p, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t release_split_workspaces() {

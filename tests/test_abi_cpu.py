@@ -27,7 +27,7 @@ def _gpu_present():
 def test_library_exports_every_header_symbol():
     L = mtp.lib()
     names = mtp.header_symbols()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", mtp.LIB_PATH], capture_output=True, text=True).stdout
@@ -219,3 +219,52 @@ def test_binding_raises_when_library_refuses(monkeypatch):
     with pytest.raises(mtp.MTPError) as e:
         mtp.mtp_column_linear(X, W, None, Y)
     assert e.value.status == SHAPE
+
+
+def dgrad(**kw):
+    a = dict(dY=P, lddy=64, Wt=P2, ldw=40, dXacc=P3, ldacc=40, acc=0, dX=None, lddx=0, M=8, N=64, K=40)
+    a.update(kw)
+    return mtp.lib().mtp_linear_dgrad(a["dY"], a["lddy"], a["Wt"], a["ldw"], a["dXacc"], a["ldacc"], a["acc"],
+                                      a["dX"], a["lddx"], a["M"], a["N"], a["K"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dY=None), NULL), (dict(Wt=None), NULL),
+    (dict(dXacc=None), NULL),                        # neither output
+    (dict(dXacc=None, dX=P4, lddx=40, acc=1), NULL),  # accumulate without dXacc
+    (dict(N=60, lddy=64), SHAPE),                    # the contraction N must be a multiple of 8
+    (dict(ldw=32), SHAPE),                           # Wt pitch below K
+    (dict(lddy=56), SHAPE), (dict(ldacc=36), SHAPE), (dict(dX=P4, lddx=32), SHAPE),
+    (dict(M=0), SHAPE), (dict(K=0), SHAPE),
+    (dict(N=1 << 20, lddy=1 << 20, ldw=1 << 10), SHAPE),  # Wt read along N rows spans 2 GiB
+    (dict(dY=BAD), ALIGN), (dict(dXacc=BAD), ALIGN), (dict(dX=BAD, lddx=40), ALIGN),
+])
+def test_dgrad_rejects(kw, status):
+    assert dgrad(**kw) == status
+
+
+def wgrad(**kw):
+    a = dict(dY=P, lddy=40, X=P2, ldx=24, dW=P3, lddw=24, acc=0, M=13, N=33, K=17)
+    a.update(kw)
+    return mtp.lib().mtp_linear_wgrad(a["dY"], a["lddy"], a["X"], a["ldx"], a["dW"], a["lddw"], a["acc"], a["M"],
+                                      a["N"], a["K"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dY=None), NULL), (dict(X=None), NULL), (dict(dW=None), NULL),
+    (dict(M=0), SHAPE), (dict(N=0), SHAPE), (dict(K=0), SHAPE),
+    (dict(lddy=32), SHAPE), (dict(ldx=16), SHAPE), (dict(lddw=16), SHAPE), (dict(lddw=28), SHAPE),
+    (dict(M=1 << 21, lddy=1 << 9), SHAPE),           # dY read along M rows spans 2 GiB
+    (dict(dY=BAD), ALIGN), (dict(X=BAD), ALIGN), (dict(dW=BAD), ALIGN),
+])
+def test_wgrad_rejects(kw, status):
+    assert wgrad(**kw) == status
+
+
+@pytest.mark.skipif(_gpu_present(), reason="on a GPU box a valid call would launch")
+def test_backward_valid_calls_reach_the_device_check():
+    # ragged sizes are valid: only dgrad's contraction N must be a multiple of 8
+    assert dgrad() == UNSUPPORTED
+    assert dgrad(dXacc=None, ldacc=0, dX=P4, lddx=40, K=37) == UNSUPPORTED
+    assert wgrad() == UNSUPPORTED
+    assert wgrad(acc=1, M=1, N=1, K=1) == UNSUPPORTED

@@ -189,6 +189,131 @@ def test_split_schedule_gelu_matches_one_tile_per_workgroup():
     assert _exact_bits_frac(G, R) >= EXACT_FRAC_MIN
 
 
+# ----------------------------------------------------------------------------- backward GEMMs
+# dX = dY . Wt and dWt = dY^T . X read the row-major-K operands (Wt for dgrad; dY and X for wgrad) in place
+# through the LDS transpose load.  Integer-valued inputs make every sum exact, so fp32 results equal the
+# oracle's and bf16 ones its round-to-nearest-even.  The split cases are shapes the planner splits (the
+# backward plan restricted to the 256 x 256 and 256 x 128 tiles equals the forward one when that picks one
+# of them).
+def _split_plan(M, N, K):
+    pl = mtp.mtp_gemm_plan(M, N, K)
+    assert pl[:2] in ((256, 256), (256, 128)) and pl[2] > 1, pl
+    return pl
+
+
+def _pitch(n):
+    return ((n + 7) // 8) * 8
+
+
+def _dev_pad(b):
+    """bf16 bits -> device view with a pitch of the next multiple of 8 (+8), the padding NaN: a chunk read
+    past the row width must not reach a stored output."""
+    rows, cols = b.shape
+    full = np.full((rows, _pitch(cols) + 8), 0x7FC0, dtype=np.uint16)
+    full[:, :cols] = b
+    return to_dev(full)[:, :cols]
+
+
+@pytest.mark.parametrize("M,N,K,split", [
+    (1, 8, 1, False), (7, 16, 5, False), (130, 96, 200, False), (257, 72, 129, False), (513, 264, 300, False),
+    (4100, 64, 3000, False), (300, 4096, 400, True),
+])
+def test_dgrad_integer_exact(M, N, K, split):
+    say("dgrad int", M, N, K)
+    if split:
+        _split_plan(M, K, N)
+    dYb, Wb = synth.ternary_bf16(291, M, N), synth.ternary_bf16(292, N, K)
+    dY, Wt = _dev_pad(dYb), _dev_pad(Wb)
+    acc = torch.full((M, _pitch(K) + 8), 5.0, dtype=torch.float32, device="cuda")
+    dXacc = acc[:, :K]
+    dX = torch.empty(M, _pitch(K), dtype=torch.bfloat16, device="cuda")[:, :K]
+    mtp.mtp_linear_dgrad(dY, Wt, dXacc, False, dX)
+    torch.cuda.synchronize()
+    R = oracle.linear_dgrad(dYb, Wb)
+    assert np.array_equal(dXacc.cpu().numpy().astype(np.float64), R)
+    assert np.array_equal(bits(dX), oracle.round_bf16(R))
+    assert torch.all(acc[:, K:] == 5.0), "padding of the fp32 target was touched"
+    # accumulate (the column-parallel all-reduce of dX, local form), then a bf16-only call
+    mtp.mtp_linear_dgrad(dY, Wt, dXacc, True, dX)
+    dX2 = torch.empty(M, _pitch(K), dtype=torch.bfloat16, device="cuda")[:, :K]
+    mtp.mtp_linear_dgrad(dY, Wt, None, False, dX2)
+    torch.cuda.synchronize()
+    assert np.array_equal(dXacc.cpu().numpy().astype(np.float64), 2 * R)
+    assert np.array_equal(bits(dX), oracle.round_bf16(2 * R))
+    assert np.array_equal(bits(dX2), oracle.round_bf16(R))
+
+
+@pytest.mark.parametrize("M,N,K,split,sampled", [
+    (1, 1, 1, False, False), (5, 7, 9, False, False), (200, 130, 257, False, False),
+    (1000, 300, 520, False, False), (4096, 256, 1280, False, False), (2048, 900, 4100, True, True),
+])
+def test_wgrad_integer_exact(M, N, K, split, sampled):
+    say("wgrad int", M, N, K)
+    if split:
+        _split_plan(N, K, M)
+    dYb, Xb = synth.ternary_bf16(301, M, N), synth.ternary_bf16(302, M, K)
+    dY, X = _dev_pad(dYb), _dev_pad(Xb)
+    W0 = synth.ternary_bf16(303, N, K)
+    dW = torch.empty(N, _pitch(K), dtype=torch.float32, device="cuda")[:, :K]
+    mtp.mtp_linear_wgrad(dY, X, dW)
+    dWa = torch.empty(N, _pitch(K), dtype=torch.float32, device="cuda")[:, :K]
+    dWa.copy_(to_dev(W0).float())
+    mtp.mtp_linear_wgrad(dY, X, dWa, True)  # gradient accumulation onto existing values
+    torch.cuda.synchronize()
+    rows = sample_rows(N, 96, 304) if sampled else list(range(N))
+    R = oracle.linear_wgrad(np.ascontiguousarray(dYb[:, rows]), Xb)
+    assert np.array_equal(dW.cpu().numpy()[rows].astype(np.float64), R)
+    assert np.array_equal(dWa.cpu().numpy()[rows].astype(np.float64), R + widen_bits(W0[rows]))
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 4096, 400), (520, 136, 1030), (4096, 1024, 1024)])
+def test_dgrad_float(M, N, K):
+    say("dgrad float", M, N, K)
+    dYb, Wb = synth.normal_bf16(311, M, N, 1.0), synth.normal_bf16(312, N, K, 0.02)
+    dX = torch.empty(M, _pitch(K), dtype=torch.bfloat16, device="cuda")[:, :K]
+    dXacc = torch.empty(M, _pitch(K), dtype=torch.float32, device="cuda")[:, :K]
+    mtp.mtp_linear_dgrad(_dev_pad(dYb), _dev_pad(Wb), dXacc, False, dX)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 128, 313)
+    R = oracle.linear_dgrad(np.ascontiguousarray(dYb[rows]), Wb)
+    _close(dXacc.cpu().numpy()[rows], R, "dgrad fp32")
+    G = bits(dX)[rows]
+    _close(widen_bits(G), R, "dgrad bf16")
+    assert _exact_bits_frac(G, R) >= EXACT_FRAC_MIN
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 900, 4100), (37, 264, 136), (4096, 4096, 1024)])
+def test_wgrad_float(M, N, K):
+    say("wgrad float", M, N, K)
+    dYb, Xb = synth.normal_bf16(321, M, N, 1.0), synth.normal_bf16(322, M, K, 1.0)
+    dW = torch.empty(N, _pitch(K), dtype=torch.float32, device="cuda")[:, :K]
+    mtp.mtp_linear_wgrad(_dev_pad(dYb), _dev_pad(Xb), dW)
+    torch.cuda.synchronize()
+    rows = sample_rows(N, 64, 323)
+    R = oracle.linear_wgrad(np.ascontiguousarray(dYb[:, rows]), Xb)
+    _close(dW.cpu().numpy()[rows], R, "wgrad fp32")
+
+
+def test_backward_of_column_linear_matches_forward_identity():
+    # <dY, X . Wt^T> = <dX, X> = <dWt, Wt> (the adjoint identities), with integer inputs so every term is
+    # exact: ties the two backward kernels to the forward one without the oracle
+    M, N, K = 333, 200, 264
+    Xb, Wb, dYb = synth.ternary_bf16(331, M, K), synth.ternary_bf16(332, N, K), synth.ternary_bf16(333, M, N)
+    X, Wt, dY = _dev_pad(Xb), _dev_pad(Wb), _dev_pad(dYb)
+    Yacc = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    mtp.mtp_row_linear_partial(X, Wt, Yacc)
+    dXacc = torch.empty(M, K, dtype=torch.float32, device="cuda")
+    mtp.mtp_linear_dgrad(dY, Wt, dXacc)
+    dW = torch.empty(N, K, dtype=torch.float32, device="cuda")
+    mtp.mtp_linear_wgrad(dY, X, dW)
+    torch.cuda.synchronize()
+    f = lambda t: t.double().cpu()
+    a = float((f(dY.float()) * f(Yacc)).sum())
+    b = float((f(dXacc) * f(X.float())).sum())
+    c = float((f(dW) * f(Wt.float())).sum())
+    assert a == b == c
+
+
 # ----------------------------------------------------------------------------- rotary position embedding
 @pytest.mark.parametrize("M,nq,ng,d,rd,interleaved", [
     (1, 1, 1, 8, 8, False), (37, 4, 2, 64, 64, False), (37, 4, 2, 64, 64, True), (300, 8, 1, 128, 128, False),
