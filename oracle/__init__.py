@@ -50,6 +50,7 @@ def _load():
         lib = ctypes.CDLL(path)
         i64, vp = ctypes.c_int64, ctypes.c_void_p
         lib.oracle_linear.argtypes = [vp, i64, vp, i64, vp, ctypes.c_int, i64, i64, i64, vp, i64]
+        lib.oracle_linear_f64.argtypes = [vp, i64, vp, i64, vp, ctypes.c_int, i64, i64, i64, vp, i64]
         lib.oracle_round_bf16.argtypes = [vp, i64, vp]
         lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_to_f64.restype = ctypes.c_double
@@ -296,3 +297,82 @@ def linear_dgrad(dY: np.ndarray, Wt: np.ndarray) -> np.ndarray:
 def linear_wgrad(dY: np.ndarray, X: np.ndarray) -> np.ndarray:
     """dWt = dY^T . X ([N x K], same layout as Wt): the weight gradient of Y = X . Wt^T, summed over the M rows."""
     return linear(np.ascontiguousarray(dY.T), np.ascontiguousarray(X.T))
+
+
+# ----------------------------------------------------------------------------- norms and the residual epilogue
+NORM_LAYER, NORM_RMS = 0, 1
+
+
+def norm_stats(X: np.ndarray, kind: int, eps: float):
+    """Per-row (mean, rstd) of the bf16 rows X [M x H], in fp64.
+
+    LayerNorm (Ba, Kiros & Hinton 2016): mean = sum(x) / H, var = sum((x - mean)^2) / H (the biased
+    variance), rstd = 1 / sqrt(var + eps).  RMSNorm (Zhang & Sennrich 2019, in the pages' reading list):
+    no centring (mean = 0), rstd = 1 / sqrt(sum(x^2) / H + eps).  The pages name both as the layer's
+    input_layernorm / pre_mlp_layernorm ("快速入门", model implementation: the layer spec and the LLaMA
+    layer tree; "ai阅读megatron": --normalization RMSNorm for the LLaMA shapes) without their formulas.
+    """
+    x = widen(X)
+    H = x.shape[1]
+    if kind == NORM_LAYER:
+        mean = x.sum(axis=1) / H
+        var = ((x - mean[:, None]) ** 2).sum(axis=1) / H
+    elif kind == NORM_RMS:
+        mean = np.zeros(x.shape[0])
+        var = (x * x).sum(axis=1) / H
+    else:
+        raise ValueError("unknown norm kind")
+    return mean, 1.0 / np.sqrt(var + eps)
+
+
+def norm(X, gamma, beta, kind: int, eps: float, one_plus: bool = False) -> np.ndarray:
+    """y = (x - mean) * rstd * g + beta per row, in fp64; g = gamma, or 1 + gamma when the scale is stored
+    zero-centred (the pages' --apply-layernorm-1p); beta may be None (RMSNorm has none)."""
+    mean, rstd = norm_stats(X, kind, eps)
+    g = widen(gamma) + (1.0 if one_plus else 0.0)
+    y = (widen(X) - mean[:, None]) * rstd[:, None] * g[None, :]
+    if beta is not None:
+        y = y + widen(beta)[None, :]
+    return y
+
+
+def norm_linear(X, gamma, beta, kind: int, eps: float, Wt, bias=None, act: int = ACT_NONE,
+                one_plus: bool = False) -> np.ndarray:
+    """act(norm(X) . Wt^T + bias): the norm prologue of a column-parallel linear ("快速入门", model
+    implementation: the QKV projection is a LayerNorm-fused column-parallel linear), the normalized
+    activations kept in fp64 (no intermediate rounding)."""
+    A = np.ascontiguousarray(norm(X, gamma, beta, kind, eps, one_plus))
+    M, K = A.shape
+    N = Wt.shape[0]
+    assert Wt.shape[1] == K
+    nout = N // 2 if act == ACT_SWIGLU else N
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.uint16)
+        assert bias.shape == (N,)
+    Y = np.empty((M, nout), dtype=np.float64)
+    if M and nout:
+        _load().oracle_linear_f64(A.ctypes.data, K, Wt.ctypes.data, _rowpitch(Wt),
+                                  None if bias is None else bias.ctypes.data, act, M, N, K, Y.ctypes.data, nout)
+    return Y
+
+
+def keep_mask(bits: np.ndarray, cols: int) -> np.ndarray:
+    """Packed dropout keep bits -> bool [rows x cols]: column c is bit c % 8 of byte c // 8 of its row."""
+    b = np.asarray(bits, dtype=np.uint8)
+    out = np.zeros((b.shape[0], cols), dtype=bool)
+    for c in range(cols):
+        out[:, c] = (b[:, c // 8] >> (c % 8)) & 1
+    return out
+
+
+def bias_dropout_add(Y: np.ndarray, bias, keep_bits, p: float, residual) -> np.ndarray:
+    """residual + dropout(Y + b): the fused epilogue after a row-parallel sum ("快速入门", model
+    implementation: self_attn_bda / mlp_bda = get_bias_dropout_add; "Megatron-LM 深度学习与源码分析文档",
+    part 3: bias+dropout+add among the layer's elementwise kernels).  Dropout is inverted dropout: a kept
+    element is scaled by 1 / (1 - p), a dropped one is zero; keep_bits None means no dropout (p = 0)."""
+    v = np.array(Y, dtype=np.float64, copy=True)
+    if bias is not None:
+        v = v + widen(bias)[None, :]
+    if keep_bits is not None:
+        v = np.where(keep_mask(keep_bits, v.shape[1]), v / (1.0 - p), 0.0)
+    return widen(residual) + v

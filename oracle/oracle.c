@@ -104,6 +104,31 @@ void oracle_linear(const uint16_t *X, int64_t ldx, const uint16_t *Wt, int64_t l
   }
 }
 
+/* The same product over an fp64 left operand A [M x K] (normalized activations kept in fp64). */
+void oracle_linear_f64(const double *A, int64_t lda, const uint16_t *Wt, int64_t ldw, const uint16_t *bias,
+                       int act, int64_t M, int64_t N, int64_t K, double *Y, int64_t ldy) {
+  const int64_t nout = act == ACT_SWIGLU ? N / 2 : N;
+#pragma omp parallel for collapse(2) schedule(dynamic, 64)
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t j = 0; j < nout; ++j) {
+      double pre = 0.0;
+      for (int64_t k = 0; k < K; ++k) pre += A[i * lda + k] * oracle_bf16_to_f64(Wt[j * ldw + k]);
+      if (bias) pre += oracle_bf16_to_f64(bias[j]);
+      if (act == ACT_NONE) {
+        Y[i * ldy + j] = pre;
+      } else if (act == ACT_GELU) {
+        Y[i * ldy + j] = oracle_gelu(pre);
+      } else {
+        const int64_t ju = nout + j;
+        double up = 0.0;
+        for (int64_t k = 0; k < K; ++k) up += A[i * lda + k] * oracle_bf16_to_f64(Wt[ju * ldw + k]);
+        if (bias) up += oracle_bf16_to_f64(bias[ju]);
+        Y[i * ldy + j] = oracle_silu(pre) * up;
+      }
+    }
+  }
+}
+
 /* Round an fp64 [rows x cols] array to bf16 (the stored precision of the
  * intermediate activation Z between fc1 and fc2). */
 void oracle_round_bf16(const double *src, int64_t n, uint16_t *dst) {

@@ -30,6 +30,8 @@ def _load_host():
         lib.synth_normal_bf16_rows.argtypes = [vp, u64, ctypes.c_double, i64, i64, i64]
         lib.synth_normal_f32_rows.argtypes = [vp, u64, i64, i64, i64]
         lib.synth_ternary_bf16_rows.argtypes = [vp, u64, i64, i64, i64]
+        lib.synth_affine_bf16_rows.argtypes = [vp, u64, ctypes.c_double, ctypes.c_double, i64, i64, i64]
+        lib.synth_keep_bits_rows.argtypes = [vp, i64, u64, ctypes.c_double, i64, i64, i64]
         lib.synth_splitmix64_next.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
         lib.synth_splitmix64_next.restype = ctypes.c_uint64
         _host = lib
@@ -80,6 +82,24 @@ def ternary_bf16(seed: int, rows: int, cols: int, r0: int = 0) -> np.ndarray:
     out = np.empty((rows, cols), dtype=np.uint16)
     if rows:
         _load_host().synth_ternary_bf16_rows(out.ctypes.data, seed, cols, r0, rows)
+    return out
+
+
+def affine_bf16(seed: int, rows: int, cols: int, mean: float, sigma: float, r0: int = 0) -> np.ndarray:
+    """bf16 values (float)(mean + z sigma), z the tensor's N(0,1)-like stream (norm scales near one)."""
+    out = np.empty((rows, cols), dtype=np.uint16)
+    if rows:
+        _load_host().synth_affine_bf16_rows(out.ctypes.data, seed, float(mean), float(sigma), cols, r0, rows)
+    return out
+
+
+def keep_bits(seed: int, rows: int, cols: int, p: float, ldk: int | None = None, r0: int = 0) -> np.ndarray:
+    """Dropout keep mask, kept with probability 1 - p: uint8 [rows x ldk], column c in bit c % 8 of byte c // 8."""
+    ldk = (cols + 7) // 8 if ldk is None else ldk
+    assert ldk >= (cols + 7) // 8 and 0.0 <= p < 1.0
+    out = np.empty((rows, ldk), dtype=np.uint8)
+    if rows:
+        _load_host().synth_keep_bits_rows(out.ctypes.data, ldk, seed, float(p), cols, r0, rows)
     return out
 
 

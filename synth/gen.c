@@ -93,3 +93,33 @@ void synth_ternary_bf16_rows(uint16_t *out, uint64_t seed, int64_t cols, int64_t
       out[r * cols + c] = lut[((h >> 32) * 3) >> 32];
     }
 }
+
+/* Same index space, N(mean, sigma^2)-like bf16 values: (float)(mean + z * sigma) rounded to nearest even
+ * (norm scales near one). */
+void synth_affine_bf16_rows(uint16_t *out, uint64_t seed, double mean, double sigma, int64_t cols,
+                            int64_t r0, int64_t nrows) {
+  const uint64_t key = key_of(seed);
+  for (int64_t r = 0; r < nrows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      uint64_t e = (uint64_t)(r0 + r) * (uint64_t)cols + (uint64_t)c;
+      out[r * cols + c] = f32_to_bf16_rne((float)(mean + irwin_hall_z(key, e) * sigma));
+    }
+}
+
+/* Dropout keep mask (the random draw of dropout, handed to both sides as an input): element e is kept iff
+ * (h_0 >> 11) >= floor(p * 2^53), i.e. a 53-bit uniform at least p (kept with probability 1 - p).  Packed
+ * eight columns to a byte, column c of row r in bit (c % 8) of byte r * ldk + c / 8; padding bytes are zero. */
+void synth_keep_bits_rows(uint8_t *out, int64_t ldk, uint64_t seed, double p, int64_t cols, int64_t r0,
+                          int64_t nrows) {
+  const uint64_t key = key_of(seed);
+  const uint64_t thr = (uint64_t)(p * 9007199254740992.0);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < nrows; ++r) {
+    memset(out + r * ldk, 0, (size_t)ldk);
+    for (int64_t c = 0; c < cols; ++c) {
+      uint64_t e = (uint64_t)(r0 + r) * (uint64_t)cols + (uint64_t)c;
+      uint64_t h = mix64(key + (3 * e + 1) * GAMMA);
+      if ((h >> 11) >= thr) out[r * ldk + c / 8] |= (uint8_t)(1u << (c % 8));
+    }
+  }
+}

@@ -462,3 +462,94 @@ def test_backward_finite_differences():
         for k in range(K):
             E = np.zeros_like(W); E[n, k] = h
             assert abs((L(X, W + E) - L(X, W - E)) / (2 * h) - dW[n, k]) < 1e-12
+
+
+# ----------------------------------------------------------------------------- norms and bias-dropout-add
+def test_norm_golden_rows():
+    rows = _golden("norm_rows.txt")
+    for kind, name in ((oracle.NORM_LAYER, "layer"), (oracle.NORM_RMS, "rms")):
+        xs = [float(x) for k, x, _ in rows if k == name]
+        ys = [float(y) for k, _, y in rows if k == name]
+        X = _bits(xs)[None, :]
+        one = _bits([1.0] * len(xs))
+        got = oracle.norm(X, one, None, kind, 0.0)[0]
+        np.testing.assert_allclose(got, ys, rtol=1e-15, atol=0)
+
+
+def test_norm_row_moments_and_eps():
+    # unit scale, no shift: LayerNorm rows have mean 0 and mean square var / (var + eps); RMSNorm rows have
+    # mean square ms / (ms + eps) (ms the input's mean square)
+    X = synth.normal_bf16(61, 7, 40, 3.0)
+    x = oracle.widen(X)
+    one = _bits([1.0] * 40)
+    for eps in (0.0, 1e-5, 0.5):
+        y = oracle.norm(X, one, None, oracle.NORM_LAYER, eps)
+        var = x.var(axis=1)
+        np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-14)
+        np.testing.assert_allclose((y * y).mean(axis=1), var / (var + eps), rtol=1e-13)
+        z = oracle.norm(X, one, None, oracle.NORM_RMS, eps)
+        ms = (x * x).mean(axis=1)
+        np.testing.assert_allclose((z * z).mean(axis=1), ms / (ms + eps), rtol=1e-13)
+        np.testing.assert_allclose(z / x, (1 / np.sqrt(ms + eps))[:, None] * np.ones_like(x), rtol=1e-13)
+
+
+def test_norm_invariances_and_special_cases():
+    # LayerNorm ignores a positive scale and a shift of the row (eps = 0); RMSNorm ignores a positive scale;
+    # on a zero-mean row the two agree; scale 0 leaves the shift; a zero-centred scale g - 1 with one_plus
+    # equals g
+    xi = np.array([[-3, 5, 1, 0, 2, -1, 4, 7], [2, 2, -6, 1, 0, 3, -1, -1]], dtype=np.float64)
+    X = _bits(xi)
+    Xs = _bits(2 * xi + 3)
+    g = _bits([0.5, 1, 1.5, 2, -1, 0.25, 3, 1])
+    b = _bits([1, -2, 0.5, 0, 4, -0.75, 2, 1])
+    np.testing.assert_allclose(oracle.norm(Xs, g, b, oracle.NORM_LAYER, 0.0),
+                               oracle.norm(X, g, b, oracle.NORM_LAYER, 0.0), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(oracle.norm(_bits(4 * xi), g, None, oracle.NORM_RMS, 0.0),
+                               oracle.norm(X, g, None, oracle.NORM_RMS, 0.0), rtol=1e-14)
+    Z = _bits(np.array([[-3, 5, 1, 0, 2, -1, -4, 0], [2, 2, -6, 1, 0, 3, -1, -1]], dtype=np.float64))
+    np.testing.assert_allclose(oracle.norm(Z, g, None, oracle.NORM_LAYER, 1e-5),
+                               oracle.norm(Z, g, None, oracle.NORM_RMS, 1e-5), rtol=1e-14)
+    zero = _bits([0.0] * 8)
+    np.testing.assert_array_equal(oracle.norm(X, zero, b, oracle.NORM_LAYER, 1e-5),
+                                  np.broadcast_to(oracle.widen(b), (2, 8)))
+    gm1 = _bits(oracle.widen(g) - 1)
+    np.testing.assert_allclose(oracle.norm(X, gm1, b, oracle.NORM_LAYER, 1e-5, one_plus=True),
+                               oracle.norm(X, g, b, oracle.NORM_LAYER, 1e-5), rtol=1e-15)
+
+
+def test_norm_linear_reduces_to_linear_on_normalized_rows():
+    # rows of +-1 with as many of each sign have mean 0 and variance 1, so with eps = 0 the norm is the
+    # identity and norm_linear is the (independently coded) bf16 linear; scale 2 doubles the input and a
+    # +-1 shift adds to it, both exactly in bf16
+    M, H, N = 5, 16, 12
+    signs = np.array([[1, -1] * 8, [-1, 1] * 8, [1, 1, -1, -1] * 4, [1] * 8 + [-1] * 8, [-1] * 8 + [1] * 8],
+                     dtype=np.float64)
+    X = _bits(signs)
+    Wb = synth.normal_bf16(71, N, H, 0.5)
+    bb = synth.normal_bf16(72, 1, N, 0.1)[0]
+    one, two = _bits([1.0] * H), _bits([2.0] * H)
+    shift = _bits(np.where(np.arange(H) % 3 == 0, 1.0, -1.0))
+    for act in (oracle.ACT_NONE, oracle.ACT_GELU, oracle.ACT_SWIGLU):
+        for kind in (oracle.NORM_LAYER, oracle.NORM_RMS):
+            np.testing.assert_array_equal(oracle.norm_linear(X, one, None, kind, 0.0, Wb, bb, act),
+                                          oracle.linear(X, Wb, bb, act))
+            np.testing.assert_array_equal(oracle.norm_linear(X, two, None, kind, 0.0, Wb, bb, act),
+                                          oracle.linear(_bits(2 * signs), Wb, bb, act))
+        np.testing.assert_array_equal(oracle.norm_linear(X, one, shift, oracle.NORM_LAYER, 0.0, Wb, bb, act),
+                                      oracle.linear(_bits(signs + oracle.widen(shift)[None, :]), Wb, bb, act))
+    assert M == X.shape[0]
+
+
+def test_bias_dropout_add_hand_cases_and_bit_order():
+    # residual 1, product 2, bias 0.5, p = 0.5: kept -> 1 + 2.5 / 0.5 = 6, dropped -> 1; byte 0b101 keeps
+    # columns 0 and 2 of its row; no mask -> residual + product + bias
+    Y = np.full((2, 9), 2.0)
+    bias = _bits([0.5] * 9)
+    res = _bits([1.0] * 9)
+    res2 = np.broadcast_to(res, (2, 9))
+    keep = np.array([[0b101, 0b1], [0b11111111, 0]], dtype=np.uint8)
+    out = oracle.bias_dropout_add(Y, bias, keep, 0.5, res2)
+    np.testing.assert_array_equal(out[0], [6, 1, 6, 1, 1, 1, 1, 1, 6])
+    np.testing.assert_array_equal(out[1], [6] * 8 + [1])
+    np.testing.assert_array_equal(oracle.bias_dropout_add(Y, bias, None, 0.0, res2), np.full((2, 9), 3.5))
+    np.testing.assert_array_equal(oracle.bias_dropout_add(Y, None, None, 0.0, res2), np.full((2, 9), 3.0))

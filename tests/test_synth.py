@@ -60,3 +60,22 @@ def test_workload_shapes_match_the_pages_shard_rules():
     c4 = configs.llama70b_tp8_rank0()
     d = c4.dims
     assert (d["nq"] // d["p"]) % (d["ng"] // d["p"]) == 0
+
+
+def test_keep_bits_rate_padding_and_extremes():
+    k = synth.keep_bits(7, 64, 1000, 0.1, ldk=128)
+    assert k.shape == (64, 128)
+    assert np.all(k[:, 125:] == 0), "padding bytes must be zero"
+    frac = np.unpackbits(k[:, :125], axis=1, bitorder="little").mean()
+    n = 64 * 1000
+    assert abs(frac - 0.9) < 4 * np.sqrt(0.09 / n)
+    assert np.all(synth.keep_bits(8, 3, 16, 0.0) == 0xFF)
+    # a row block equals the same rows of the whole tensor
+    assert np.array_equal(synth.keep_bits(7, 10, 1000, 0.1, ldk=128, r0=20), k[20:30])
+
+
+def test_affine_bf16_is_shifted_normal():
+    a = synth.affine_bf16(9, 4, 300, 1.0, 0.0)
+    assert np.all(a == 0x3F80)  # sigma 0: exactly one
+    z = synth.affine_bf16(9, 4, 300, 0.0, 1.0)
+    assert np.array_equal(z, synth.normal_bf16(9, 4, 300, 1.0))
