@@ -69,6 +69,8 @@ typedef enum {
 
 typedef enum { MTP_ACT_NONE = 0, MTP_ACT_GELU = 1, MTP_ACT_SWIGLU = 2 } mtp_act;
 
+typedef enum { MTP_NORM_LAYER = 0, MTP_NORM_RMS = 1 } mtp_norm;
+
 /*
  * ColumnParallelLinear forward of one shard (part 2 section 2, Y_i = X W_i),
  * with its bias and activation fused:
@@ -130,6 +132,61 @@ mtp_status mtp_mlp_forward(const mtp_bf16* X, int64_t M, int64_t H, int64_t F, i
 mtp_status mtp_qkv_forward(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t H, const mtp_bf16* Wqkv_t,
                            int64_t ldw, const mtp_bf16* bias, int nq_local, int ng_local, int head_dim,
                            mtp_bf16* QKV, int64_t ldo, void* stream);
+
+/*
+ * The norm prologue of a column-parallel linear ("快速入门", model
+ * implementation: the layer spec's QKV linear is the LayerNorm-fused
+ * column-parallel linear and pre_mlp_layernorm precedes fc1; the LLaMA layer
+ * tree uses RMSNorm; "Megatron-LM 深度学习与源码分析文档", part 3: LayerNorm
+ * among the layer's elementwise kernels).  LayerNorm: mean and biased
+ * variance over the row, y = (x - mean) / sqrt(var + eps) * g + beta.
+ * RMSNorm: y = x / sqrt(mean(x^2) + eps) * g.  g = gamma, or 1 + gamma when
+ * one_plus (zero-centred storage, the pages' --apply-layernorm-1p).
+ *
+ * The norm is folded through the product instead of materialising the
+ * normalized activations:
+ *   norm(X) . Wt^T + b = rstd * (X . Wf^T - mean * colsum) + bias_f,
+ * Wf = Wt scaled by g along K (bf16, rounded to nearest even),
+ * colsum[n] = sum_k Wf[n][k], bias_f[n] = b[n] + sum_k beta[k] Wt[n][k].
+ *
+ * mtp_norm_stats: per-row (mean, rstd) of X [M x H] into stats[2 M] (fp32,
+ *   8-byte aligned; RMSNorm writes mean = 0).  H % 8 == 0; eps >= 0.
+ * mtp_norm_fold_weights: Wf [N x K] (pitch ldwf), colsum [N] (may be NULL:
+ *   only LayerNorm needs it), bias_f [N] (fp32) from Wt [N x K], gamma [K],
+ *   beta [K] (NULL: none), bias [N] (NULL: none).  Once per weight update.
+ *   A SwiGLU weight [gate ; up] folds as one N = 2F matrix.
+ * mtp_norm_column_linear: Y = act(rstd_m * (X . Wf^T - mean_m * colsum) +
+ *   bias_f) with the same shapes, activations and output rules as
+ *   mtp_column_linear; colsum NULL drops the centring term (RMSNorm),
+ *   bias_f NULL means no bias.
+ */
+mtp_status mtp_norm_stats(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t H, mtp_norm kind, float eps,
+                          float* stats, void* stream);
+mtp_status mtp_norm_fold_weights(const mtp_bf16* Wt, int64_t ldw, int64_t N, int64_t K, const mtp_bf16* gamma,
+                                 const mtp_bf16* beta, const mtp_bf16* bias, int one_plus, mtp_bf16* Wf,
+                                 int64_t ldwf, float* colsum, float* bias_f, void* stream);
+mtp_status mtp_norm_column_linear(const mtp_bf16* X, int64_t ldx, const float* stats, const mtp_bf16* Wf,
+                                  int64_t ldw, const float* colsum, const float* bias_f, mtp_bf16* Y, int64_t ldy,
+                                  int64_t M, int64_t N, int64_t K, mtp_act act, void* stream);
+
+/*
+ * Row-parallel partial with the bias-dropout-add epilogue ("快速入门", model
+ * implementation: self_attn_bda and mlp_bda follow the attention output
+ * projection and fc2; "Megatron-LM 深度学习与源码分析文档", part 3:
+ * bias+dropout+add among the fused elementwise kernels).  As
+ * mtp_row_linear_partial (Yacc optional: NULL for a single shard), and the
+ * bf16 output is the new residual stream:
+ *   Y = bf16(residual + keep * (P + bias) / (1 - p_drop))
+ * (P the fp32 sum of the shards so far).  keep: packed dropout keep bits
+ * (the random draw, made by the caller), column c of row i in bit c % 8 of
+ * byte i * ldk + c / 8, ldk >= ceil(N / 8); NULL means no dropout and then
+ * p_drop must be 0.  residual [M x N] (pitch ldr) is required; Y may not
+ * alias it.  Only the call that finishes the sum should take this form.
+ */
+mtp_status mtp_row_linear_bda(const mtp_bf16* Z, int64_t ldz, const mtp_bf16* Wt, int64_t ldw, float* Yacc,
+                              int64_t ldacc, int accumulate, const mtp_bf16* bias, const mtp_bf16* residual,
+                              int64_t ldr, const uint8_t* keep, int64_t ldk, float p_drop, mtp_bf16* Y, int64_t ldy,
+                              int64_t M, int64_t N, int64_t Kp, void* stream);
 
 /*
  * Backward GEMMs of a linear Y = X . Wt^T ("Megatron-LM 深度学习与源码分析文档",

@@ -14,6 +14,7 @@ import os
 import re
 
 ACT_NONE, ACT_GELU, ACT_SWIGLU = 0, 1, 2
+NORM_LAYER, NORM_RMS = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmtp.so")
@@ -49,6 +50,11 @@ def lib():
             "mtp_linear_dgrad": [vp, i64, vp, i64, vp, i64, ci, vp, i64, i64, i64, i64, vp],
             "mtp_linear_wgrad": [vp, i64, vp, i64, vp, i64, ci, i64, i64, i64, vp],
             "mtp_release_workspaces": [],
+            "mtp_norm_stats": [vp, i64, i64, i64, ci, ctypes.c_float, vp, vp],
+            "mtp_norm_fold_weights": [vp, i64, i64, i64, vp, vp, vp, ci, vp, i64, vp, vp, vp],
+            "mtp_norm_column_linear": [vp, i64, vp, vp, i64, vp, vp, vp, i64, i64, i64, i64, ci, vp],
+            "mtp_row_linear_bda": [vp, i64, vp, i64, vp, i64, ci, vp, vp, i64, vp, i64, ctypes.c_float, vp, i64,
+                                   i64, i64, i64, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -96,6 +102,42 @@ def mtp_gemm_plan(M, N, K, act=ACT_NONE):
     out = [ctypes.c_int(0) for _ in range(3)]
     _check("mtp_gemm_plan", lib().mtp_gemm_plan(M, N, K, act, *[ctypes.addressof(o) for o in out]))
     return tuple(o.value for o in out)
+
+
+def mtp_norm_stats(X, stats, kind=NORM_LAYER, eps=1e-5):
+    """Per-row (mean, rstd) of X [M x H] into fp32 stats [M x 2]."""
+    M, H = X.shape
+    _check("mtp_norm_stats", lib().mtp_norm_stats(_ptr(X), _ld(X), M, H, kind, eps, _ptr(stats), _stream(X)))
+    return stats
+
+
+def mtp_norm_fold_weights(Wt, gamma, beta, bias, Wf, colsum, bias_f, one_plus=False):
+    """Fold the norm's scale (and shift, and the linear's bias) into Wf, colsum, bias_f."""
+    N, K = Wt.shape
+    _check("mtp_norm_fold_weights", lib().mtp_norm_fold_weights(
+        _ptr(Wt), _ld(Wt), N, K, _ptr(gamma), _ptr(beta), _ptr(bias), int(bool(one_plus)), _ptr(Wf), _ld(Wf),
+        _ptr(colsum), _ptr(bias_f), _stream(Wt)))
+
+
+def mtp_norm_column_linear(X, stats, Wf, colsum, bias_f, Y, act=ACT_NONE):
+    """Y = act(norm(X) . Wt^T + b) through the folded weight (Wf [N x K], colsum, bias_f from the fold)."""
+    M, K = X.shape
+    N = Wf.shape[0]
+    _check("mtp_norm_column_linear", lib().mtp_norm_column_linear(
+        _ptr(X), _ld(X), _ptr(stats), _ptr(Wf), _ld(Wf), _ptr(colsum), _ptr(bias_f), _ptr(Y), _ld(Y), M, N, K,
+        act, _stream(X)))
+    return Y
+
+
+def mtp_row_linear_bda(Z, Wt, residual, Y, Yacc=None, accumulate=False, bias=None, keep=None, p_drop=0.0):
+    """Y = bf16(residual + dropout(Yacc (+)= Z . Wt^T, + bias)); keep: uint8 [M x ldk] packed keep bits."""
+    M, Kp = Z.shape
+    N = Wt.shape[0]
+    _check("mtp_row_linear_bda", lib().mtp_row_linear_bda(
+        _ptr(Z), _ld(Z), _ptr(Wt), _ld(Wt), _ptr(Yacc), _ld(Yacc) if Yacc is not None else 0,
+        int(bool(accumulate)), _ptr(bias), _ptr(residual), _ld(residual), _ptr(keep),
+        _ld(keep) if keep is not None else 0, p_drop, _ptr(Y), _ld(Y), M, N, Kp, _stream(Z)))
+    return Y
 
 
 def mtp_release_workspaces():

@@ -178,6 +178,97 @@ mtp_status mtp_row_linear_partial(const mtp_bf16* Z, int64_t ldz, const mtp_bf16
   return launched(mtp::gemm(p, mtp::MODE_ROW, (hipStream_t)stream), "row-parallel partial");
 }
 
+mtp_status mtp_row_linear_bda(const mtp_bf16* Z, int64_t ldz, const mtp_bf16* Wt, int64_t ldw, float* Yacc,
+                              int64_t ldacc, int accumulate, const mtp_bf16* bias, const mtp_bf16* residual,
+                              int64_t ldr, const uint8_t* keep, int64_t ldk, float p_drop, mtp_bf16* Y, int64_t ldy,
+                              int64_t M, int64_t N, int64_t Kp, void* stream) {
+  TRY(check_dims(M, N, Kp));
+  TRY(check_mat(Z, "Z", Kp, ldz));
+  TRY(check_mat(Wt, "Wt", Kp, ldw));
+  if (!Yacc && accumulate) return fail(MTP_ERR_NULL, "accumulate needs Yacc");
+  if (Yacc) TRY(check_mat(Yacc, "Yacc", N, ldacc));
+  TRY(check_mat(Y, "Y", N, ldy));
+  TRY(check_mat(residual, "residual", N, ldr));
+  TRY(check_vec(bias, "bias"));
+  if (!(p_drop >= 0.f && p_drop < 1.f)) return fail(MTP_ERR_SHAPE, "dropout probability %g is not in [0, 1)", (double)p_drop);
+  if (keep) {
+    if (ldk < (N + 7) / 8) return fail(MTP_ERR_SHAPE, "keep: %lld bytes per row < %lld", (long long)ldk, (long long)((N + 7) / 8));
+    if (M * ldk >= kWindow - 64) return fail(MTP_ERR_SHAPE, "keep: the mask exceeds the 2 GiB addressing window");
+  } else if (p_drop != 0.f) {
+    return fail(MTP_ERR_NULL, "dropout probability %g without a keep mask", (double)p_drop);
+  }
+  TRY(check_window("residual", M, ldr));
+  TRY(check_window("Z", 256, ldz));
+  TRY(check_window("Wt", 256, ldw));
+  TRY(check_device());
+  mtp::GemmParams p;
+  p.A = Z; p.lda = ldz; p.B = Wt; p.ldb = ldw; p.Yacc = Yacc; p.ldacc = Yacc ? ldacc : 0;
+  p.accumulate = accumulate ? 1 : 0; p.bias = bias; p.Y = Y; p.ldy = ldy;
+  p.M = (int)M; p.Nout = (int)N; p.K = (int)Kp; p.a_src_rows = M;
+  p.resid = residual; p.ldr = ldr; p.keep = keep; p.ldk = keep ? ldk : 0;
+  p.drop_scale = keep ? 1.f / (1.f - p_drop) : 1.f;
+  return launched(mtp::gemm(p, mtp::MODE_ROW, (hipStream_t)stream, mtp::EPI_BDA), "row-parallel bias-dropout-add");
+}
+
+mtp_status mtp_norm_stats(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t H, mtp_norm kind, float eps,
+                          float* stats, void* stream) {
+  TRY(check_dims(M, 8, H));
+  TRY(check_mat(X, "X", H, ldx));
+  if (kind != MTP_NORM_LAYER && kind != MTP_NORM_RMS) return fail(MTP_ERR_SHAPE, "unknown norm kind %d", (int)kind);
+  if (!(eps >= 0.f && eps < 1e30f)) return fail(MTP_ERR_SHAPE, "eps %g must be finite and >= 0", (double)eps);
+  if (!stats) return fail(MTP_ERR_NULL, "stats is NULL");
+  if (reinterpret_cast<uintptr_t>(stats) & 7u) return fail(MTP_ERR_ALIGN, "stats is not 8-byte aligned");
+  TRY(check_device());
+  return launched(mtp::norm_stats(X, ldx, (int)M, (int)H, (int)kind, eps, stats, (hipStream_t)stream), "norm stats");
+}
+
+mtp_status mtp_norm_fold_weights(const mtp_bf16* Wt, int64_t ldw, int64_t N, int64_t K, const mtp_bf16* gamma,
+                                 const mtp_bf16* beta, const mtp_bf16* bias, int one_plus, mtp_bf16* Wf,
+                                 int64_t ldwf, float* colsum, float* bias_f, void* stream) {
+  TRY(check_dims(N, 8, K));
+  TRY(check_mat(Wt, "Wt", K, ldw));
+  TRY(check_mat(Wf, "Wf", K, ldwf));
+  if (!gamma) return fail(MTP_ERR_NULL, "gamma is NULL");
+  TRY(check_vec(gamma, "gamma"));
+  TRY(check_vec(beta, "beta"));
+  TRY(check_vec(bias, "bias"));
+  if (!bias_f) return fail(MTP_ERR_NULL, "bias_f is NULL");
+  TRY(check_vec(bias_f, "bias_f"));
+  TRY(check_vec(colsum, "colsum"));
+  TRY(check_device());
+  return launched(mtp::norm_fold(Wt, ldw, (int)N, (int)K, gamma, beta, bias, one_plus ? 1 : 0, Wf, ldwf, colsum,
+                                 bias_f, (hipStream_t)stream),
+                  "norm fold");
+}
+
+mtp_status mtp_norm_column_linear(const mtp_bf16* X, int64_t ldx, const float* stats, const mtp_bf16* Wf,
+                                  int64_t ldw, const float* colsum, const float* bias_f, mtp_bf16* Y, int64_t ldy,
+                                  int64_t M, int64_t N, int64_t K, mtp_act act, void* stream) {
+  TRY(check_dims(M, N, K));
+  if (act != MTP_ACT_NONE && act != MTP_ACT_GELU && act != MTP_ACT_SWIGLU)
+    return fail(MTP_ERR_SHAPE, "unknown activation %d", (int)act);
+  if (act == MTP_ACT_SWIGLU && N % 2 != 0) return fail(MTP_ERR_SHAPE, "SwiGLU needs an even N (got %lld)", (long long)N);
+  const int64_t nout = act == MTP_ACT_SWIGLU ? N / 2 : N;
+  TRY(check_mat(X, "X", K, ldx));
+  TRY(check_mat(Wf, "Wf", K, ldw));
+  TRY(check_mat(Y, "Y", nout, ldy));
+  if (!stats) return fail(MTP_ERR_NULL, "stats is NULL");
+  if (reinterpret_cast<uintptr_t>(stats) & 7u) return fail(MTP_ERR_ALIGN, "stats is not 8-byte aligned");
+  TRY(check_vec(colsum, "colsum"));
+  TRY(check_vec(bias_f, "bias_f"));
+  TRY(check_window("X", 256, ldx));
+  TRY(check_window("Wf", (act == MTP_ACT_SWIGLU ? nout : 0) + 256, ldw));
+  TRY(check_device());
+  mtp::GemmParams p;
+  p.A = X; p.lda = ldx; p.B = Wf; p.ldb = ldw; p.Y = Y; p.ldy = ldy;
+  p.M = (int)M; p.Nout = (int)nout; p.K = (int)K; p.up_offset = nout; p.a_src_rows = M;
+  p.act = act == MTP_ACT_GELU ? 1 : 0;
+  p.norm_stats = stats; p.norm_colsum = colsum; p.bias_f32 = bias_f;
+  return launched(mtp::gemm(p, act == MTP_ACT_SWIGLU ? mtp::MODE_SWIGLU : mtp::MODE_COL, (hipStream_t)stream,
+                            mtp::EPI_NORM),
+                  "norm column linear");
+}
+
 mtp_status mtp_mlp_forward(const mtp_bf16* X, int64_t M, int64_t H, int64_t F, int p, int r0, int r1,
                            const mtp_bf16* W1t, const mtp_bf16* b1, const mtp_bf16* W2t, const mtp_bf16* b2,
                            mtp_act act, mtp_bf16* Z_ws, float* Yacc, mtp_bf16* Y, void* stream) {

@@ -33,6 +33,17 @@ struct GemmParams {
   const int32_t* group_offsets = nullptr;  // grouped: [groups + 1] row offsets in device memory
   int groups = 0;
   int64_t group_stride_B = 0;       // grouped: elements between consecutive groups' B
+  // EPI_NORM (COL/SWIGLU): out = act(rstd_m * (acc - mean_m * colsum_n) + bias_f_n), the norm prologue
+  // folded through the product (the scale is already folded into B)
+  const float* norm_stats = nullptr;  // [rows] x (mean, rstd)
+  const float* norm_colsum = nullptr; // [N] (NULL: no centring term)
+  const float* bias_f32 = nullptr;    // [N] fp32 bias (NULL: none)
+  // EPI_BDA (ROW, bf16 output): Y = resid + dropout(P + bias), kept elements scaled by drop_scale
+  const uint16_t* resid = nullptr;
+  int64_t ldr = 0;
+  const uint8_t* keep = nullptr;      // packed keep bits (column c: bit c % 8 of byte c / 8), NULL: no dropout
+  int64_t ldk = 0;                    // bytes per keep row
+  float drop_scale = 1.f;
   float* sk_ws = nullptr;           // split schedule: partial-tile slots (set at launch)
   int sk_chunks = 0;                // split schedule: K chunks per tile
   int* sk_cnt = nullptr;            // split schedule: per-tile arrival counters, zero between launches
@@ -45,7 +56,8 @@ struct GemmPlan {
 GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, bool row_major_k = false);
 hipError_t release_split_workspaces();
 
-hipError_t gemm(const GemmParams& p, int mode, hipStream_t st);
+enum GemmEpilogue { EPI_PLAIN = 0, EPI_NORM = 1, EPI_BDA = 2 };
+hipError_t gemm(const GemmParams& p, int mode, hipStream_t st, int epi = EPI_PLAIN);
 // MODE_ROW products whose A (and/or B) operand is stored [K x M] ([K x N]): lda / ldb are those pitches.
 hipError_t gemm_backward(const GemmParams& p, bool a_row_major_k, bool b_row_major_k, hipStream_t st);
 // rows_upper: total rows over all groups (an upper bound is enough; spare tiles exit).
@@ -54,6 +66,13 @@ hipError_t gemm_grouped(const GemmParams& p, int mode, int rows_upper, hipStream
 // Rotary position embedding of the first `heads` heads of each row, in place (rope.hip).
 hipError_t rope_qk(uint16_t* qkv, int64_t ldo, int M, const int32_t* positions, int heads, int head_dim,
                    int rotary_dim, double base, bool interleaved, hipStream_t st);
+
+// Norm prologue pieces (norm.hip): per-row (mean, rstd), and the scale/shift folded into a weight.
+hipError_t norm_stats(const uint16_t* X, int64_t ldx, int M, int H, int kind, float eps, float* stats,
+                      hipStream_t st);
+hipError_t norm_fold(const uint16_t* Wt, int64_t ldw, int N, int K, const uint16_t* gamma, const uint16_t* beta,
+                     const uint16_t* bias, int one_plus, uint16_t* Wf, int64_t ldwf, float* colsum, float* bias_f,
+                     hipStream_t st);
 
 // MoE helpers (moe.hip).
 hipError_t moe_route(const float* logits, int T, int E, int k, int32_t* offsets, int32_t* token_idx,

@@ -163,7 +163,7 @@ __device__ __forceinline__ void store4_bf16(uint16_t* dst, const float v[4], int
 // [BK rows][BM or BN columns] and its MFMA fragments are read with ds_read_b64_tr_b16, the gfx950 LDS
 // transpose load: 16 lanes each name 4 consecutive columns of one row, and lane i receives column i of
 // four consecutive rows.
-template <class C, int MODE, bool GROUPED, bool KFULL, bool SPLIT, bool AT = false, bool BT = false>
+template <class C, int MODE, bool GROUPED, bool KFULL, bool SPLIT, bool AT = false, bool BT = false, int EPI = EPI_PLAIN>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   // A private copy of the parameters: read once into scalar registers, rather than reloaded from the
   // kernel argument segment (each reload waits on the LDS/scalar counter) wherever a field is used.
@@ -176,6 +176,9 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
                 "row-major-K operands: K step 32, plain column/row epilogues");
   static_assert(!AT || BM == 128 || BM == 256, "A rows of 256 or 512 bytes");
   static_assert(!BT || BN == 128 || BN == 256, "B rows of 256 or 512 bytes");
+  static_assert(EPI == EPI_PLAIN || (!GROUPED && (EPI == EPI_NORM ? (MODE == MODE_COL || MODE == MODE_SWIGLU)
+                                                                    : MODE == MODE_ROW)),
+                "norm epilogue on column products, bias-dropout-add on row products");
   constexpr int NB_OUT = MODE == MODE_SWIGLU ? BN / 2 : BN;  // output columns per tile
 
   // one LDS variable per stage (see the design notes); unused ones are a token 16 bytes
@@ -508,8 +511,38 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   // Bias of this lane's output columns, read once with clamped indices (columns past Nout are computed but
   // never stored): per-element loads under branches would each wait a full memory latency.
   constexpr bool kBias = MODE != MODE_COMBINE;
+  constexpr bool kNorm = EPI == EPI_NORM;
   float bias_g[kBias ? FNO : 1][4][4], bias_u[MODE == MODE_SWIGLU ? FNO : 1][4][4];
-  if constexpr (kBias) {
+  // norm epilogue: column sums of the folded weight (gate and up parts) and each fragment row's statistics
+  float cs_g[kNorm ? FNO : 1][4][4], cs_u[kNorm && MODE == MODE_SWIGLU ? FNO : 1][4][4];
+  float st_mean[kNorm ? FM : 1], st_rstd[kNorm ? FM : 1];
+  if constexpr (kNorm) {
+    const int64_t blen = MODE == MODE_SWIGLU ? p.up_offset + p.Nout : p.Nout;
+    const __amdgpu_buffer_rsrc_t brs = make_rsrc(p.bias_f32, p.bias_f32 ? 4 * blen : 0);
+    const __amdgpu_buffer_rsrc_t crs = make_rsrc(p.norm_colsum, p.norm_colsum ? 4 * blen : 0);
+#pragma unroll
+    for (int jo = 0; jo < FNO; ++jo)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = ncol0 + 32 * jo + 8 * jj + col4 + r;
+          bias_g[jo][jj][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(brs, 4 * c, 0, 0));
+          cs_g[jo][jj][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(crs, 4 * c, 0, 0));
+          if constexpr (MODE == MODE_SWIGLU) {
+            const int cu = (int)p.up_offset + c;
+            bias_u[jo][jj][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(brs, 4 * cu, 0, 0));
+            cs_u[jo][jj][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(crs, 4 * cu, 0, 0));
+          }
+        }
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.norm_stats + 2 * (int64_t)(row_base + m0), 8 * (int64_t)(rows - m0));
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int rr = wm0 + 32 * i + fr;
+      st_mean[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 8 * rr, 0, 0));
+      st_rstd[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 8 * rr + 4, 0, 0));
+    }
+  } else if constexpr (kBias) {
     // Through a buffer resource that is empty without a bias and ends at the bias's last element: absent
     // and out-of-range elements read as zero, with no branch per element.
     const bool has_bias = p.bias != nullptr && (MODE != MODE_ROW || p.Y != nullptr);
@@ -528,15 +561,46 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
         }
   }
   // output value of (fragment row block i, output fragment jo, run jj, element r)
+  auto pre = [&](int i, int j, float a, float b, float cs) -> float {
+    if constexpr (kNorm) return fmaf(st_rstd[i], fmaf(-st_mean[i], cs, a), b);
+    else return a + b;
+  };
   auto out_val = [&](int i, int jo, int jj, int r, auto gelu) -> float {
     if constexpr (MODE == MODE_SWIGLU) {
-      const float g = acc[i][2 * jo][4 * jj + r] + bias_g[jo][jj][r];
-      const float u = acc[i][2 * jo + 1][4 * jj + r] + bias_u[jo][jj][r];
+      const float g = pre(i, jo, acc[i][2 * jo][4 * jj + r], bias_g[jo][jj][r], cs_g[kNorm ? jo : 0][jj][r]);
+      const float u = pre(i, jo, acc[i][2 * jo + 1][4 * jj + r], bias_u[jo][jj][r],
+                          cs_u[kNorm ? jo : 0][jj][r]);
       return silu(g) * u;
     } else {
-      const float x = acc[i][jo][4 * jj + r] + bias_g[jo][jj][r];
+      const float x = pre(i, jo, acc[i][jo][4 * jj + r], bias_g[jo][jj][r], cs_g[kNorm ? jo : 0][jj][r]);
       if constexpr (decltype(gelu)::value) return gelu_erf(x);
       else return x;
+    }
+  };
+  // bias-dropout-add on the bf16 output of a row product: v = resid + (kept ? v * scale : 0) for the four
+  // columns n .. n + 3 of output row orow (n a multiple of 4, so their keep bits share one byte).  Reads go
+  // through buffer resources ending at the last row: rows past it read zeros and are never stored.
+  constexpr bool kBda = EPI == EPI_BDA;
+  [[maybe_unused]] const __amdgpu_buffer_rsrc_t r_rs =
+      make_rsrc(kBda ? p.resid : nullptr, kBda ? 2 * (int64_t)(row_base + rows) * p.ldr : 0);
+  [[maybe_unused]] const __amdgpu_buffer_rsrc_t k_rs =
+      make_rsrc(kBda ? p.keep : nullptr, kBda && p.keep ? (int64_t)(row_base + rows) * p.ldk : 0);
+  auto bda4 = [&](int64_t orow, int n, float* v) {
+    if constexpr (EPI == EPI_BDA) {
+      const uint32_t roff = 2u * (uint32_t)(orow * p.ldr + n);
+      const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(r_rs, roff, 0, 0);
+      const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(r_rs, roff + 4, 0, 0);
+      const float res[4] = {__builtin_bit_cast(float, lo << 16), __builtin_bit_cast(float, lo & 0xFFFF0000u),
+                            __builtin_bit_cast(float, hi << 16), __builtin_bit_cast(float, hi & 0xFFFF0000u)};
+      if (p.keep) {
+        const uint32_t kb = __builtin_amdgcn_raw_buffer_load_b8(k_rs, (uint32_t)(orow * p.ldk + (n >> 3)), 0, 0) >>
+                            (n & 7);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = res[r] + (((kb >> r) & 1u) ? v[r] * p.drop_scale : 0.f);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = res[r] + v[r];
+      }
     }
   };
   constexpr bool kStaged = MODE == MODE_COL || MODE == MODE_SWIGLU || MODE == MODE_ROW;
@@ -565,10 +629,12 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
         for (int jo = 0; jo < FNO; ++jo)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const float v0 = out_val(i, jo, jj, 0, gelu), v1 = out_val(i, jo, jj, 1, gelu);
-            const float v2 = out_val(i, jo, jj, 2, gelu), v3 = out_val(i, jo, jj, 3, gelu);
+            float v[4] = {out_val(i, jo, jj, 0, gelu), out_val(i, jo, jj, 1, gelu), out_val(i, jo, jj, 2, gelu),
+                          out_val(i, jo, jj, 3, gelu)};
+            if constexpr (EPI == EPI_BDA)
+              bda4((int64_t)row_base + m0 + wm0 + 32 * i + fr, ncol0 + 32 * jo + 8 * jj + col4, v);
             *reinterpret_cast<uint2*>(reg + unit_at(32 * i + fr, 8 * jo + 2 * jj + (lane >> 5))) =
-                make_uint2(pack_bf16(v0, v1), pack_bf16(v2, v3));
+                make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
           }
     };
     if (MODE == MODE_COL && p.act == 1) stage_tile(std::true_type{});
@@ -637,6 +703,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
             if constexpr (with_y) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) v[r] += bias_g[j][jj][r];
+              bda4(orow, n, v);
               store4_bf16(y + orow * ldy + n, v, valid);
             }
           } else if constexpr (MODE == MODE_COMBINE) {
@@ -760,7 +827,7 @@ hipError_t split_workspace(hipStream_t st, size_t ws_bytes, int64_t cnt_n, float
 }
 }  // namespace
 
-template <class C, int MODE, bool GROUPED, bool AT = false, bool BT = false>
+template <class C, int MODE, bool GROUPED, bool AT = false, bool BT = false, int EPI = EPI_PLAIN>
 static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStream_t st, int split_groups = 0,
                              int split_chunks = 0) {
   GemmParams p = p0;
@@ -781,18 +848,18 @@ static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStrea
       hipError_t e = split_workspace(st, (size_t)tiles * split_chunks * slot, tiles, &p.sk_ws, &p.sk_cnt);
       if (e != hipSuccess) return e;
       if (kfull)
-        hipLaunchKernelGGL((gemm_kernel<C, MODE, false, true, true, AT, BT>), dim3(split_groups), dim3(C::NT), 0, st, p);
+        hipLaunchKernelGGL((gemm_kernel<C, MODE, false, true, true, AT, BT, EPI>), dim3(split_groups), dim3(C::NT), 0, st, p);
       else
-        hipLaunchKernelGGL((gemm_kernel<C, MODE, false, false, true, AT, BT>), dim3(split_groups), dim3(C::NT), 0, st,
+        hipLaunchKernelGGL((gemm_kernel<C, MODE, false, false, true, AT, BT, EPI>), dim3(split_groups), dim3(C::NT), 0, st,
                            p);
       return hipGetLastError();
     }
   }
   if (kfull)
-    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, true, false, AT, BT>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
+    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, true, false, AT, BT, EPI>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
                        p);
   else
-    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, false, false, AT, BT>), dim3((unsigned)tiles), dim3(C::NT), 0,
+    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, false, false, AT, BT, EPI>), dim3((unsigned)tiles), dim3(C::NT), 0,
                        st, p);
   return hipGetLastError();
 }
@@ -851,17 +918,17 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, bool row_major_
   return best;
 }
 
-template <int MODE>
+template <int MODE, int EPI = EPI_PLAIN>
 static hipError_t dispatch(const GemmParams& p, hipStream_t st) {
   const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K, false);
   switch (pl.id) {
-    case 0: return launch_cfg<BigTile, MODE, false>(p, 0, st, pl.split_groups, pl.split_chunks);
+    case 0: return launch_cfg<BigTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks);
     case 1:
       if constexpr (MODE != MODE_SWIGLU)
-        return launch_cfg<WideTile, MODE, false>(p, 0, st, pl.split_groups, pl.split_chunks);
+        return launch_cfg<WideTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks);
       return hipErrorInvalidValue;
-    case 2: return launch_cfg<HalfTile, MODE, false>(p, 0, st, pl.split_groups, pl.split_chunks);
-    default: return launch_cfg<SmallTile, MODE, false>(p, 0, st);  // (never split)
+    case 2: return launch_cfg<HalfTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks);
+    default: return launch_cfg<SmallTile, MODE, false, false, false, EPI>(p, 0, st);  // (never split)
   }
 }
 
@@ -897,7 +964,13 @@ hipError_t release_split_workspaces() {
   return hipSuccess;
 }
 
-hipError_t gemm(const GemmParams& p, int mode, hipStream_t st) {
+hipError_t gemm(const GemmParams& p, int mode, hipStream_t st, int epi) {
+  if (epi == EPI_NORM) {
+    if (mode == MODE_COL) return dispatch<MODE_COL, EPI_NORM>(p, st);
+    if (mode == MODE_SWIGLU) return dispatch<MODE_SWIGLU, EPI_NORM>(p, st);
+    return hipErrorInvalidValue;
+  }
+  if (epi == EPI_BDA) return mode == MODE_ROW ? dispatch<MODE_ROW, EPI_BDA>(p, st) : hipErrorInvalidValue;
   switch (mode) {
     case MODE_COL: return dispatch<MODE_COL>(p, st);
     case MODE_SWIGLU: return dispatch<MODE_SWIGLU>(p, st);

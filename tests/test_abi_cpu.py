@@ -27,7 +27,7 @@ def _gpu_present():
 def test_library_exports_every_header_symbol():
     L = mtp.lib()
     names = mtp.header_symbols()
-    assert len(names) == 14
+    assert len(names) == 18
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", mtp.LIB_PATH], capture_output=True, text=True).stdout
@@ -268,3 +268,58 @@ def test_backward_valid_calls_reach_the_device_check():
     assert dgrad(dXacc=None, ldacc=0, dX=P4, lddx=40, K=37) == UNSUPPORTED
     assert wgrad() == UNSUPPORTED
     assert wgrad(acc=1, M=1, N=1, K=1) == UNSUPPORTED
+
+
+def test_norm_entry_points_reject():
+    L = mtp.lib()
+    st = lambda **kw: L.mtp_norm_stats(kw.get("X", P), kw.get("ldx", 64), kw.get("M", 4), kw.get("H", 64),
+                                       kw.get("kind", 0), kw.get("eps", 1e-5), kw.get("stats", P2), None)
+    assert st(X=None) == NULL and st(stats=None) == NULL
+    assert st(X=BAD) == ALIGN and st(stats=P2 + 4) == ALIGN
+    assert st(H=60, ldx=64) == SHAPE and st(ldx=56) == SHAPE and st(M=0) == SHAPE
+    assert st(kind=2) == SHAPE and st(eps=-1.0) == SHAPE and st(eps=float("nan")) == SHAPE
+
+    fold = lambda **kw: L.mtp_norm_fold_weights(
+        kw.get("Wt", P), kw.get("ldw", 64), kw.get("N", 16), kw.get("K", 64), kw.get("gamma", P2),
+        kw.get("beta", None), kw.get("bias", None), 0, kw.get("Wf", P3), kw.get("ldwf", 64), kw.get("colsum", P4),
+        kw.get("bias_f", P4 + 256), None)
+    assert fold(Wt=None) == NULL and fold(gamma=None) == NULL and fold(bias_f=None) == NULL and fold(Wf=None) == NULL
+    assert fold(gamma=BAD) == ALIGN and fold(beta=BAD) == ALIGN and fold(colsum=BAD) == ALIGN
+    assert fold(K=60, ldw=64, ldwf=64) == SHAPE and fold(ldwf=32) == SHAPE
+
+    ncl = lambda **kw: L.mtp_norm_column_linear(
+        kw.get("X", P), kw.get("ldx", 64), kw.get("stats", P2), kw.get("Wf", P3), kw.get("ldw", 64),
+        kw.get("colsum", None), kw.get("bias_f", None), kw.get("Y", P4), kw.get("ldy", 32), kw.get("M", 8),
+        kw.get("N", 32), kw.get("K", 64), kw.get("act", 0), None)
+    assert ncl(stats=None) == NULL and ncl(X=None) == NULL and ncl(Y=None) == NULL
+    assert ncl(stats=P2 + 4) == ALIGN and ncl(colsum=BAD) == ALIGN
+    assert ncl(act=2, N=31) == SHAPE and ncl(act=7) == SHAPE and ncl(ldy=16) == SHAPE
+
+
+def bda(**kw):
+    a = dict(Z=P, ldz=64, Wt=P2, ldw=64, Yacc=None, ldacc=0, acc=0, bias=None, res=P3, ldr=40, keep=P4, ldk=5,
+             p=0.5, Y=P, ldy=40, M=8, N=40, Kp=64)
+    a.update(kw)
+    return mtp.lib().mtp_row_linear_bda(a["Z"], a["ldz"], a["Wt"], a["ldw"], a["Yacc"], a["ldacc"], a["acc"],
+                                        a["bias"], a["res"], a["ldr"], a["keep"], a["ldk"], a["p"], a["Y"], a["ldy"],
+                                        a["M"], a["N"], a["Kp"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(res=None), NULL), (dict(Y=None), NULL), (dict(acc=1), NULL),   # accumulate without Yacc
+    (dict(keep=None), NULL),                                              # p > 0 without a mask
+    (dict(ldk=4), SHAPE), (dict(p=1.0), SHAPE), (dict(p=-0.1), SHAPE), (dict(ldr=32), SHAPE),
+    (dict(Kp=60), SHAPE), (dict(res=BAD), ALIGN), (dict(bias=BAD), ALIGN),
+])
+def test_row_bda_rejects(kw, status):
+    assert bda(**kw) == status
+
+
+@pytest.mark.skipif(_gpu_present(), reason="on a GPU box a valid call would launch")
+def test_norm_and_bda_valid_calls_reach_the_device_check():
+    L = mtp.lib()
+    assert L.mtp_norm_stats(P, 64, 4, 64, 1, 1e-6, P2, None) == UNSUPPORTED
+    assert L.mtp_norm_fold_weights(P, 64, 16, 64, P2, None, None, 1, P3, 64, None, P4, None) == UNSUPPORTED
+    assert L.mtp_norm_column_linear(P, 64, P2, P3, 64, None, None, P4, 32, 8, 64, 64, 2, None) == UNSUPPORTED
+    assert bda() == UNSUPPORTED
+    assert bda(keep=None, p=0.0, Yacc=P2, ldacc=40, acc=1) == UNSUPPORTED

@@ -314,6 +314,114 @@ def test_backward_of_column_linear_matches_forward_identity():
     assert a == b == c
 
 
+# ----------------------------------------------------------------------------- norm prologue, bias-dropout-add
+# Inputs with a non-zero row mean exercise the centring term; scales near one, small shifts and biases.
+def _norm_inputs(seed, M, N, K):
+    Xb = synth.affine_bf16(seed, M, K, 0.5, 1.5)
+    Wb = synth.normal_bf16(seed + 1, N, K, 0.05)
+    gb = synth.affine_bf16(seed + 2, 1, K, 1.0, 0.1)[0]
+    betab = synth.normal_bf16(seed + 3, 1, K, 0.1)[0]
+    bb = synth.normal_bf16(seed + 4, 1, N, 0.1)[0]
+    return Xb, Wb, gb, betab, bb
+
+
+@pytest.mark.parametrize("M,H,kind", [(1, 8, 0), (37, 264, 0), (300, 1024, 1), (129, 12288, 0), (64, 8192, 1)])
+def test_norm_stats_match_oracle(M, H, kind):
+    say("norm stats", M, H, kind)
+    Xb = synth.affine_bf16(341, M, H, 0.5, 1.5)
+    stats = torch.empty(M, 2, dtype=torch.float32, device="cuda")
+    mtp.mtp_norm_stats(_dev_pad(Xb), stats, kind, 1e-5)
+    torch.cuda.synchronize()
+    mean, rstd = oracle.norm_stats(Xb, kind, 1e-5)
+    g = stats.cpu().numpy().astype(np.float64)
+    # fp32 sums over H terms: a few ulps of the row scale
+    assert np.max(np.abs(g[:, 0] - mean)) <= 1e-5
+    assert np.max(np.abs(g[:, 1] / rstd - 1)) <= 1e-5
+
+
+@pytest.mark.parametrize("M,N,K,act,kind,one_plus", [
+    (200, 300, 136, 1, 0, False), (64, 64, 64, 0, 1, False), (513, 1030, 256, 0, 0, True),
+    (200, 272, 200, 2, 1, False), (300, 400, 4096, 1, 0, False),   # the last one takes the split schedule
+    (4096, 3072, 1024, 0, 0, False),
+])
+def test_norm_column_linear_matches_oracle(M, N, K, act, kind, one_plus):
+    say("norm column linear", M, N, K, act, kind, one_plus)
+    Xb, Wb, gb, betab, bb = _norm_inputs(351, M, N, K)
+    if kind == oracle.NORM_RMS:
+        betab = None
+    gstore = oracle.round_bf16(oracle.widen(gb) - 1) if one_plus else gb
+    X, W = _dev_pad(Xb), _dev_pad(Wb)
+    Wf = torch.empty(N, _pitch(K), dtype=torch.bfloat16, device="cuda")[:, :K]
+    colsum = torch.empty(N, dtype=torch.float32, device="cuda") if kind == oracle.NORM_LAYER else None
+    bias_f = torch.empty(N, dtype=torch.float32, device="cuda")
+    mtp.mtp_norm_fold_weights(W, to_dev(gstore), None if betab is None else to_dev(betab), to_dev(bb), Wf, colsum,
+                              bias_f, one_plus)
+    stats = torch.empty(M, 2, dtype=torch.float32, device="cuda")
+    mtp.mtp_norm_stats(X, stats, kind, 1e-5)
+    nout = N // 2 if act == mtp.ACT_SWIGLU else N
+    Y = torch.empty(M, _pitch(nout), dtype=torch.bfloat16, device="cuda")[:, :nout]
+    mtp.mtp_norm_column_linear(X, stats, Wf, colsum, bias_f, Y, act)
+    torch.cuda.synchronize()
+    # the fold: Wf is the scale times the weight rounded once, and colsum sums Wf's rows
+    g_eff = oracle.widen(gstore) + (1.0 if one_plus else 0.0)
+    assert np.array_equal(bits(Wf), oracle.round_bf16(oracle.widen(Wb) * g_eff[None, :]))
+    if colsum is not None:
+        np.testing.assert_allclose(colsum.cpu().numpy(), widen_bits(bits(Wf)).sum(axis=1), rtol=1e-5, atol=1e-4)
+    rows = sample_rows(M, 128, 352)
+    R = oracle.norm_linear(np.ascontiguousarray(Xb[rows]), gstore, betab, kind, 1e-5, Wb, bb, act, one_plus)
+    G = bits(Y)[rows]
+    _close(widen_bits(G), R, "norm column linear")
+    say(f"exact-bits fraction {_exact_bits_frac(G, R):.3f}")
+
+
+@pytest.mark.parametrize("M,N,Kp,shards,p_drop", [
+    (77, 130, 64, 1, 0.5), (256, 256, 64, 2, 0.5), (300, 400, 4096, 1, 0.5), (513, 1000, 136, 3, 0.0),
+    (1, 8, 8, 1, 0.5),
+])
+def test_row_bda_integer_exact(M, N, Kp, shards, p_drop):
+    # integer inputs and p = 1/2 (scale 2) keep every value exact: bits must equal the oracle's rounding
+    say("row bda int", M, N, Kp, shards, p_drop)
+    Zb, Wb = synth.ternary_bf16(361, M, shards * Kp), synth.ternary_bf16(362, N, shards * Kp)
+    bb, Rb = synth.ternary_bf16(363, 1, N)[0], synth.ternary_bf16(364, M, N)
+    kb = synth.keep_bits(365, M, N, p_drop, ldk=(N + 7) // 8 + 3) if p_drop > 0 else None
+    Z, W, R = to_dev(Zb), to_dev(Wb), _dev_pad(Rb)
+    keep = None if kb is None else torch.from_numpy(kb).cuda()
+    Y = torch.empty(M, _pitch(N), dtype=torch.bfloat16, device="cuda")[:, :N]
+    Yacc = torch.empty(M, _pitch(N), dtype=torch.float32, device="cuda")[:, :N] if shards > 1 else None
+    for r in range(shards):
+        Zr, Wr = Z[:, r * Kp:(r + 1) * Kp], W[:, r * Kp:(r + 1) * Kp]
+        if r < shards - 1:
+            mtp.mtp_row_linear_partial(Zr, Wr, Yacc, r > 0)
+        else:
+            mtp.mtp_row_linear_bda(Zr, Wr, R, Y, Yacc, r > 0, to_dev(bb), keep, p_drop)
+    torch.cuda.synchronize()
+    P = oracle.row_parallel_partials([np.ascontiguousarray(Zb[:, r * Kp:(r + 1) * Kp]) for r in range(shards)],
+                                     Wb, shards)
+    S = oracle.row_parallel_sum(P)
+    ref = oracle.bias_dropout_add(S, bb, kb, p_drop, Rb)
+    assert np.array_equal(bits(Y), oracle.round_bf16(ref))
+    if Yacc is not None:
+        assert np.array_equal(Yacc.cpu().numpy().astype(np.float64), S), "the fp32 sum must stay the plain sum"
+
+
+def test_row_bda_float_dropout():
+    M, N, Kp = 600, 1024, 4096
+    say("row bda float", M, N, Kp)
+    Zb, Wb = synth.normal_bf16(371, M, Kp, 1.0), synth.normal_bf16(372, N, Kp, 0.02)
+    bb, Rb = synth.normal_bf16(373, 1, N, 0.1)[0], synth.normal_bf16(374, M, N, 1.0)
+    kb = synth.keep_bits(375, M, N, 0.1)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    mtp.mtp_row_linear_bda(to_dev(Zb), to_dev(Wb), to_dev(Rb), Y, None, False, to_dev(bb),
+                           torch.from_numpy(kb).cuda(), 0.1)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 96, 376)
+    P = oracle.linear(np.ascontiguousarray(Zb[rows]), Wb)
+    ref = oracle.bias_dropout_add(P, bb, kb[rows], 0.1, Rb[rows])
+    G = bits(Y)[rows]
+    _close(widen_bits(G), ref, "row bda")
+    assert _exact_bits_frac(G, ref) >= EXACT_FRAC_MIN
+
+
 # ----------------------------------------------------------------------------- rotary position embedding
 @pytest.mark.parametrize("M,nq,ng,d,rd,interleaved", [
     (1, 1, 1, 8, 8, False), (37, 4, 2, 64, 64, False), (37, 4, 2, 64, 64, True), (300, 8, 1, 128, 128, False),
