@@ -86,6 +86,116 @@ class _FenceFreeEvents:
             self._hip.hipEventDestroy(e)
 
 
+def backward_gemms(w, timer, reps=5):
+    """The backward GEMMs of the workload's linears (dgrad dX = dY . Wt, wgrad dWt = dY^T . X into fp32),
+    on synthetic operands of the same shapes: event time per launch (median of reps) and TFLOP/s."""
+    import torch
+    import megatron_tensor_transformer_03_amd as mtp
+    import synth
+    per, flop_total, us_total = {}, 0, 0.0
+    for i, (label, M, N, K) in enumerate(w.gemms):
+        if label in per:  # shards of one linear: the same shapes
+            continue
+        X = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        Wt = torch.empty(N, K, dtype=torch.bfloat16, device="cuda")
+        dY = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        synth.gpu_normal_bf16_(X, 9001 + 3 * i, 1.0)
+        synth.gpu_normal_bf16_(Wt, 9002 + 3 * i, 0.02)
+        synth.gpu_normal_bf16_(dY, 9003 + 3 * i, 1.0)
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        dW = torch.zeros(N, K, dtype=torch.float32, device="cuda")
+        res = {}
+        for name, fn in (("dgrad", lambda: mtp.mtp_linear_dgrad(dY, Wt, None, False, dX)),
+                         ("wgrad", lambda: mtp.mtp_linear_wgrad(dY, X, dW, True))):
+            fn()
+            torch.cuda.synchronize()
+            ev = []
+            for _ in range(reps):
+                e0 = timer.record()
+                fn()
+                ev.append((e0, timer.record()))
+            torch.cuda.synchronize()
+            t = sorted(timer.elapsed_ms(a, b) for a, b in ev)[reps // 2]
+            timer.release([e for pair in ev for e in pair])
+            res[name + "_us"] = round(1000 * t, 2)
+            res[name + "_tflops"] = round(2 * M * N * K / (t * 1e-3) / 1e12, 1)
+            flop_total += 2 * M * N * K
+            us_total += 1000 * t
+        per[label] = res
+        del X, Wt, dY, dX, dW
+    tf = flop_total / (us_total * 1e-6) / 1e12
+    return {"per_linear": per, "flop": flop_total, "us": round(us_total, 2), "achieved": round(tf, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+def _median_us(timer, fn, reps=5):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        e0 = timer.record()
+        fn()
+        ev.append((e0, timer.record()))
+    torch.cuda.synchronize()
+    t = sorted(timer.elapsed_ms(a, b) for a, b in ev)[reps // 2]
+    timer.release([e for pair in ev for e in pair])
+    return 1000 * t
+
+
+def norm_and_bda(w, timer):
+    """The norm prologue and the bias-dropout-add epilogue at the workload's shapes (synthetic operands):
+    the row-statistics kernel against the HBM roofline, and the fused GEMMs beside the plain ones."""
+    import torch
+    import megatron_tensor_transformer_03_amd as mtp
+    import synth
+    shapes = {label: (M, N, K) for label, M, N, K in w.gemms}
+    if "qkv" not in shapes or "fc2" not in shapes:
+        return None
+    kind = mtp.NORM_RMS if w.dims.get("act") == mtp.ACT_SWIGLU else mtp.NORM_LAYER
+    M, N, H = shapes["qkv"]
+    X = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
+    Wt = torch.empty(N, H, dtype=torch.bfloat16, device="cuda")
+    g = torch.empty(1, H, dtype=torch.bfloat16, device="cuda")
+    synth.gpu_normal_bf16_(X, 9101, 1.0)
+    synth.gpu_normal_bf16_(Wt, 9102, 0.02)
+    synth.gpu_normal_bf16_(g, 9103, 0.1)
+    g.add_(1.0)
+    stats = torch.empty(M, 2, dtype=torch.float32, device="cuda")
+    Wf = torch.empty_like(Wt)
+    colsum = torch.empty(N, dtype=torch.float32, device="cuda")
+    bias_f = torch.empty(N, dtype=torch.float32, device="cuda")
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    beta = None if kind == mtp.NORM_RMS else g
+    cs = None if kind == mtp.NORM_RMS else colsum
+    t_stats = _median_us(timer, lambda: mtp.mtp_norm_stats(X, stats, kind, 1e-5))
+    t_fold = _median_us(timer, lambda: mtp.mtp_norm_fold_weights(Wt, g[0], None if beta is None else beta[0], None,
+                                                                 Wf, cs, bias_f))
+    t_fused = _median_us(timer, lambda: mtp.mtp_norm_column_linear(X, stats, Wf, cs, bias_f, Y))
+    t_plain = _median_us(timer, lambda: mtp.mtp_column_linear(X, Wt, None, Y))
+    stat_bytes = M * H * 2 + 8 * M
+    gbs = stat_bytes / (t_stats * 1e-6) / 1e9
+    del Wt, Wf, Y
+    # fc2 with the bias-dropout-add epilogue (p = 0.1, a synthetic keep mask) beside the plain bf16 epilogue
+    M2, N2, K2 = shapes["fc2"]
+    Z = torch.empty(M2, K2, dtype=torch.bfloat16, device="cuda")
+    W2 = torch.empty(N2, K2, dtype=torch.bfloat16, device="cuda")
+    R = torch.empty(M2, N2, dtype=torch.bfloat16, device="cuda")
+    synth.gpu_normal_bf16_(Z, 9104, 1.0)
+    synth.gpu_normal_bf16_(W2, 9105, 0.02)
+    synth.gpu_normal_bf16_(R, 9106, 1.0)
+    keep = torch.from_numpy(synth.keep_bits(9107, M2, N2, 0.1)).cuda()
+    Y2 = torch.empty(M2, N2, dtype=torch.bfloat16, device="cuda")
+    t_bda = _median_us(timer, lambda: mtp.mtp_row_linear_bda(Z, W2, R, Y2, keep=keep, p_drop=0.1))
+    t_row = _median_us(timer, lambda: mtp.mtp_row_linear_partial(Z, W2, None, False, None, Y2))
+    return {"norm": "rmsnorm" if kind == mtp.NORM_RMS else "layernorm",
+            "stats_kernel": {"bound": "hbm", "us": round(t_stats, 2), "bytes": stat_bytes, "achieved": round(gbs, 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "fold_us_once_per_weight_update": round(t_fold, 2),
+            "qkv_norm_epilogue_us": round(t_fused, 2), "qkv_plain_us": round(t_plain, 2),
+            "fc2_bias_dropout_add_us": round(t_bda, 2), "fc2_plain_us": round(t_row, 2)}
+
+
 def cpu_baseline(w, budget_s):
     """The oracle on a bounded row sample of the same workload; TFLOP/s of algorithmic work done."""
     import numpy as np
@@ -144,6 +254,8 @@ def main():
     ap.add_argument("--workload", default="gpt345m", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-GEMM and norm/bias-dropout-add measurements")
     ap.add_argument("--graphs", action="store_true",
                     help="replay the step as HIP graphs (captured from the same calls) instead of launching each "
                          "call from Python; on ROCm 7 graph launches cost more than they save at this step size")
@@ -271,6 +383,10 @@ def main():
                        "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
+    # the backward GEMMs of the same linears (outside the timed region; dense layers only)
+    bwd = None if ("E" in w.dims or args.no_backward) else backward_gemms(w, timer)
+    nb = None if ("E" in w.dims or args.no_backward) else norm_and_bda(w, timer)
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -291,7 +407,7 @@ def main():
                    "per_gemm_us": {lb: round(1000 * v, 2) for lb, v in avg.items()},
                    "per_gemm_tflops": {lb: round(flop_by_label[lb] / (avg[lb] * 1e-3) / 1e12, 1)
                                        for lb in avg if lb in flop_by_label},
-                   "aux_kernels": aux},
+                   "aux_kernels": aux, "backward_gemms": bwd, "norm_and_bda": nb},
         "roofline": {"bound": "mfma", "kernel": dom, "kernel_us": round(1000 * dom_avg, 2),
                      "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -15,6 +15,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gemm.h"
 
 namespace mtp {
@@ -31,10 +33,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Per-row (mean, rstd): LayerNorm takes two passes over the row (the mean, then the centred squares: the
-// second pass reads the row back from the cache), RMSNorm one pass over the squares.  Each lane sums its
-// 8-element chunks in order, then the wave adds the lanes' sums in a fixed butterfly: deterministic.
-template <bool RMS>
+// Per-row (mean, rstd).  A wave holds its row in registers (CPL 16-byte chunks per lane, every load issued
+// before the first use), so LayerNorm's second pass over the centred squares reads registers, not memory;
+// rows wider than 24 chunks per lane (H > 12288) take the streaming form, which re-reads the row from the
+// cache.  Each lane
+// sums its chunks in order, then the wave adds the lanes' sums in a fixed butterfly: deterministic.
+template <bool RMS, int CPL>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void stats_kernel(const uint16_t* __restrict__ X, int64_t ldx,
                                                                     int M, int H, float eps,
                                                                     float* __restrict__ stats) {
@@ -43,19 +47,11 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void stats_kernel(const uint16_
   if (row >= M) return;
   const uint4* x = reinterpret_cast<const uint4*>(X + (int64_t)row * ldx);
   const int chunks = H / 8;
-  float mean = 0.f;
-  if constexpr (!RMS) {
-    float s = 0.f;
-    for (int c = lane; c < chunks; c += 64) {
-      const uint4 v = x[c];
-      s += (lo_bf16(v.x) + hi_bf16(v.x)) + (lo_bf16(v.y) + hi_bf16(v.y)) + (lo_bf16(v.z) + hi_bf16(v.z)) +
+  auto chunk_sum = [](const uint4& v) {
+    return (lo_bf16(v.x) + hi_bf16(v.x)) + (lo_bf16(v.y) + hi_bf16(v.y)) + (lo_bf16(v.z) + hi_bf16(v.z)) +
            (lo_bf16(v.w) + hi_bf16(v.w));
-    }
-    mean = wave_sum(s) / (float)H;
-  }
-  float q = 0.f;
-  for (int c = lane; c < chunks; c += 64) {
-    const uint4 v = x[c];
+  };
+  auto chunk_sq = [](const uint4& v, float mean, float q) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -63,6 +59,32 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void stats_kernel(const uint16_
       q = fmaf(a, a, q);
       q = fmaf(b, b, q);
     }
+    return q;
+  };
+  float mean = 0.f, q = 0.f;
+  if constexpr (CPL > 0) {
+    uint4 v[CPL];
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      const int c = lane + 64 * t;
+      v[t] = c < chunks ? x[c] : make_uint4(0, 0, 0, 0);  // zero chunks add nothing to the sums
+    }
+    if constexpr (!RMS) {
+      float s = 0.f;
+#pragma unroll
+      for (int t = 0; t < CPL; ++t) s += chunk_sum(v[t]);
+      mean = wave_sum(s) / (float)H;
+    }
+#pragma unroll
+    for (int t = 0; t < CPL; ++t)
+      if (lane + 64 * t < chunks) q = chunk_sq(v[t], mean, q);
+  } else {
+    if constexpr (!RMS) {
+      float s = 0.f;
+      for (int c = lane; c < chunks; c += 64) s += chunk_sum(x[c]);
+      mean = wave_sum(s) / (float)H;
+    }
+    for (int c = lane; c < chunks; c += 64) q = chunk_sq(x[c], mean, q);
   }
   const float var = wave_sum(q) / (float)H;
   if (lane == 0) {
@@ -130,10 +152,22 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void fold_kernel(const uint16_t
 hipError_t norm_stats(const uint16_t* X, int64_t ldx, int M, int H, int kind, float eps, float* stats,
                       hipStream_t st) {
   const dim3 grid((M + kRowsPerBlock - 1) / kRowsPerBlock), block(64 * kRowsPerBlock);
-  if (kind == 1)
-    hipLaunchKernelGGL(stats_kernel<true>, grid, block, 0, st, X, ldx, M, H, eps, stats);
-  else
-    hipLaunchKernelGGL(stats_kernel<false>, grid, block, 0, st, X, ldx, M, H, eps, stats);
+  const int cpl = (H / 8 + 63) / 64;  // 16-byte chunks per lane
+  auto go = [&](auto RMSC, auto CPLC) {
+    hipLaunchKernelGGL((stats_kernel<decltype(RMSC)::value, decltype(CPLC)::value>), grid, block, 0, st, X, ldx, M,
+                       H, eps, stats);
+  };
+  auto by_width = [&](auto RMSC) {
+    if (cpl <= 1) go(RMSC, std::integral_constant<int, 1>{});
+    else if (cpl <= 2) go(RMSC, std::integral_constant<int, 2>{});
+    else if (cpl <= 4) go(RMSC, std::integral_constant<int, 4>{});
+    else if (cpl <= 8) go(RMSC, std::integral_constant<int, 8>{});
+    else if (cpl <= 16) go(RMSC, std::integral_constant<int, 16>{});
+    else if (cpl <= 24) go(RMSC, std::integral_constant<int, 24>{});
+    else go(RMSC, std::integral_constant<int, 0>{});
+  };
+  if (kind == 1) by_width(std::true_type{});
+  else by_width(std::false_type{});
   return hipGetLastError();
 }
 

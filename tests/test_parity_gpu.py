@@ -325,7 +325,8 @@ def _norm_inputs(seed, M, N, K):
     return Xb, Wb, gb, betab, bb
 
 
-@pytest.mark.parametrize("M,H,kind", [(1, 8, 0), (37, 264, 0), (300, 1024, 1), (129, 12288, 0), (64, 8192, 1)])
+@pytest.mark.parametrize("M,H,kind", [(1, 8, 0), (37, 264, 0), (300, 1024, 1), (129, 12288, 0), (64, 8192, 1),
+                                      (9, 2992, 0), (5, 16384, 0), (6, 20480, 1)])
 def test_norm_stats_match_oracle(M, H, kind):
     say("norm stats", M, H, kind)
     Xb = synth.affine_bf16(341, M, H, 0.5, 1.5)
