@@ -376,3 +376,87 @@ def bias_dropout_add(Y: np.ndarray, bias, keep_bits, p: float, residual) -> np.n
     if keep_bits is not None:
         v = np.where(keep_mask(keep_bits, v.shape[1]), v / (1.0 - p), 0.0)
     return widen(residual) + v
+
+
+# ----------------------------------------------------------------------------- FP8 (E4M3) forward GEMMs
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """E4M3 codes -> fp64 values, from the format definition (Micikevicius et al., "FP8 Formats for Deep
+    Learning", 2022, in the pages' reading list): sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+    exponent 0 holds the subnormals m/8 * 2^-6; S.1111.111 is NaN; no infinities (max 448)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * 2.0 ** (e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return s * mag
+
+
+def e4m3_encode(values) -> np.ndarray:
+    """Values -> E4M3 codes, rounding to nearest with ties to the even code, saturating at +-448 (the
+    saturating cast the FP8 recipes use for E4M3); NaN -> S.1111.111."""
+    v = np.asarray(values, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint8)
+    flat_v, flat_o = v.reshape(-1), out.reshape(-1)
+    for i, x in enumerate(flat_v):
+        sign = 0x80 if math.copysign(1.0, x) < 0 else 0
+        a = abs(x)
+        if math.isnan(x):
+            flat_o[i] = sign | 0x7F
+            continue
+        if a >= E4M3_MAX:
+            flat_o[i] = sign | 0x7E
+            continue
+        # quantum of the binade of a (subnormal quantum 2^-9 below 2^-6), then round half to even
+        e = math.frexp(a)[1] - 1 if a > 0 else -7
+        quantum = 2.0 ** (max(e, -6) - 3)
+        q = a / quantum                      # exact: division by a power of two
+        n = math.floor(q)
+        if q - n > 0.5 or (q - n == 0.5 and n % 2 == 1):
+            n += 1
+        r = n * quantum
+        if r >= E4M3_MAX:
+            flat_o[i] = sign | 0x7E
+            continue
+        if r < 2.0 ** -6:
+            flat_o[i] = sign | int(round(r / 2.0 ** -9))
+        else:
+            er = math.frexp(r)[1] - 1
+            flat_o[i] = sign | ((er + 7) << 3) | int(round((r / 2.0 ** er - 1) * 8))
+    return out
+
+
+def fp8_quantize(X: np.ndarray):
+    """Per-tensor scaled E4M3 quantization of a bf16 tensor, the pages' FP8 recipe (\"快速入门\", FP8 training:
+    an amax-based scaling factor per tensor, E4M3 in the forward pass; --fp8-amax-compute-algo max).
+    Reading: the current tensor's amax (history of length one).  The scaling decisions are made in fp32, the
+    precision the GPU takes them in, so the codes are unique: amax = max |x| (exact), s = fp32(448 / amax)
+    (1 when amax is 0), code = E4M3(fp32(x * s)), and the dequantization factor is fp32(1 / s).
+    Returns (codes uint8 [same shape], scale_inv as a Python float)."""
+    x = widen(X).astype(np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    s = np.float32(E4M3_MAX) / amax if amax > 0 else np.float32(1)
+    codes = e4m3_encode((x * np.float32(s)).astype(np.float32))
+    return codes, float(np.float32(1) / np.float32(s))
+
+
+def fp8_linear(Xq, x_scale_inv: float, Wq, w_scale_inv: float, bias=None, act: int = ACT_NONE) -> np.ndarray:
+    """act(x_scale_inv * w_scale_inv * (dec(Xq) . dec(Wq)^T) + bias) in fp64: the FP8 form of the column or row
+    linear (the product of the decoded codes, then the two dequantization factors)."""
+    A = e4m3_decode(Xq)
+    W = e4m3_decode(Wq)
+    M, K = A.shape
+    N = W.shape[0]
+    nout = N // 2 if act == ACT_SWIGLU else N
+    P = (A @ W.T) * (x_scale_inv * w_scale_inv)
+    if bias is not None:
+        P = P + widen(bias)[None, :]
+    if act == ACT_NONE:
+        return P
+    if act == ACT_GELU:
+        return np.vectorize(gelu)(P)
+    g, u = P[:, :nout], P[:, nout:]
+    return np.vectorize(silu)(g) * u

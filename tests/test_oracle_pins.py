@@ -553,3 +553,67 @@ def test_bias_dropout_add_hand_cases_and_bit_order():
     np.testing.assert_array_equal(out[1], [6] * 8 + [1])
     np.testing.assert_array_equal(oracle.bias_dropout_add(Y, bias, None, 0.0, res2), np.full((2, 9), 3.5))
     np.testing.assert_array_equal(oracle.bias_dropout_add(Y, None, None, 0.0, res2), np.full((2, 9), 3.0))
+
+
+# ----------------------------------------------------------------------------- FP8 (E4M3)
+def test_e4m3_golden_codes():
+    for v, c in _golden("e4m3.txt"):
+        assert int(oracle.e4m3_encode([float(v)])[0]) == int(c, 16), v
+        assert oracle.e4m3_decode([int(c, 16)])[0] == float(v), c
+
+
+def test_e4m3_table_shape():
+    vals = oracle.e4m3_decode(np.arange(256))
+    assert np.isnan(vals).sum() == 2 and np.isnan(vals[0x7F]) and np.isnan(vals[0xFF])
+    pos = vals[:0x7F]
+    assert np.all(np.diff(pos) > 0), "codes 0..0x7e must increase"
+    assert pos[-1] == 448.0 and pos[1] == 2.0 ** -9 and pos[8] == 2.0 ** -6
+    np.testing.assert_array_equal(vals[0x80:0xFF], -pos)
+
+
+def test_e4m3_encode_is_nearest_with_ties_to_even_by_brute_force():
+    table = oracle.e4m3_decode(np.arange(0x7F))           # non-negative finite values, codes 0..0x7e
+    rng = np.random.default_rng(5)
+    xs = np.concatenate([rng.normal(0, 1, 300) * 2.0 ** rng.integers(-12, 10, 300),
+                         (table[:-1] + table[1:]) / 2,      # exact midpoints: the tie cases
+                         [500.0, -1e6, 449.0, 464.0, 0.0, -0.0]]).astype(np.float32).astype(np.float64)
+    codes = oracle.e4m3_encode(xs)
+    for x, c in zip(xs, codes):
+        a = abs(x)
+        if a >= 448:
+            assert c & 0x7F == 0x7E
+            continue
+        d = np.abs(table - a)
+        best = np.flatnonzero(d == d.min())
+        want = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        assert c & 0x7F == want, (x, c, want)
+        if a > 0:
+            assert (c >> 7) == (x < 0)
+
+
+def test_fp8_quantize_maps_amax_to_448_and_zero_tensor():
+    X = synth.normal_bf16(81, 6, 40, 3.0)
+    codes, sinv = oracle.fp8_quantize(X)
+    x = oracle.widen(X)
+    i = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert codes[i] & 0x7F == 0x7E
+    assert abs(sinv * 448 / np.abs(x).max() - 1) < 1e-6
+    # the dequantized tensor is within half an E4M3 step (relative 1/16) of the input, above the subnormals
+    deq = oracle.e4m3_decode(codes) * sinv
+    big = np.abs(x) > 2.0 ** -6 * sinv
+    assert np.all(np.abs(deq - x)[big] <= np.abs(x)[big] / 16 * (1 + 1e-6))
+    z, s0 = oracle.fp8_quantize(np.zeros((2, 8), np.uint16))
+    assert np.all(z == 0) and s0 == 1.0
+
+
+def test_fp8_linear_reduces_to_the_bf16_linear_on_exact_values():
+    # codes of -1, 0, +1 with unit (and power-of-two) factors: the product equals the independently coded
+    # bf16 linear of the same values
+    M, N, K = 5, 12, 24
+    Xb, Wb = synth.ternary_bf16(91, M, K), synth.ternary_bf16(92, N, K)
+    bb = synth.normal_bf16(93, 1, N, 0.1)[0]
+    Xq, Wq = oracle.e4m3_encode(oracle.widen(Xb)), oracle.e4m3_encode(oracle.widen(Wb))
+    for act in (oracle.ACT_NONE, oracle.ACT_GELU, oracle.ACT_SWIGLU):
+        np.testing.assert_allclose(oracle.fp8_linear(Xq, 1.0, Wq, 1.0, bb, act), oracle.linear(Xb, Wb, bb, act),
+                                   rtol=1e-15, atol=1e-15)
+    np.testing.assert_array_equal(oracle.fp8_linear(Xq, 2.0, Wq, 0.25, None), oracle.linear(Xb, Wb) * 0.5)
