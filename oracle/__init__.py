@@ -397,36 +397,31 @@ def e4m3_decode(codes) -> np.ndarray:
 
 def e4m3_encode(values) -> np.ndarray:
     """Values -> E4M3 codes, rounding to nearest with ties to the even code, saturating at +-448 (the
-    saturating cast the FP8 recipes use for E4M3); NaN -> S.1111.111."""
+    saturating cast the FP8 recipes use for E4M3); NaN -> S.1111.111.  Elementwise over an array: the
+    quantum of each value's binade (2^-9 below 2^-6), round half to even on the multiple of it, then the
+    fields."""
     v = np.asarray(values, dtype=np.float64)
-    out = np.empty(v.shape, dtype=np.uint8)
-    flat_v, flat_o = v.reshape(-1), out.reshape(-1)
-    for i, x in enumerate(flat_v):
-        sign = 0x80 if math.copysign(1.0, x) < 0 else 0
-        a = abs(x)
-        if math.isnan(x):
-            flat_o[i] = sign | 0x7F
-            continue
-        if a >= E4M3_MAX:
-            flat_o[i] = sign | 0x7E
-            continue
-        # quantum of the binade of a (subnormal quantum 2^-9 below 2^-6), then round half to even
-        e = math.frexp(a)[1] - 1 if a > 0 else -7
-        quantum = 2.0 ** (max(e, -6) - 3)
-        q = a / quantum                      # exact: division by a power of two
-        n = math.floor(q)
-        if q - n > 0.5 or (q - n == 0.5 and n % 2 == 1):
-            n += 1
-        r = n * quantum
-        if r >= E4M3_MAX:
-            flat_o[i] = sign | 0x7E
-            continue
-        if r < 2.0 ** -6:
-            flat_o[i] = sign | int(round(r / 2.0 ** -9))
-        else:
-            er = math.frexp(r)[1] - 1
-            flat_o[i] = sign | ((er + 7) << 3) | int(round((r / 2.0 ** er - 1) * 8))
-    return out
+    sign = np.where(np.signbit(v), 0x80, 0).astype(np.int64)
+    a = np.abs(v)
+    nan = np.isnan(v)
+    a0 = np.where(nan, 0.0, a)
+    e = np.frexp(a0)[1].astype(np.int64) - 1                 # a = f 2^e with f in [1, 2) (a > 0)
+    e = np.where(a0 > 0, e, -7)
+    quantum = np.ldexp(1.0, np.maximum(e, -6) - 3)
+    q = a0 / quantum                                          # exact: division by a power of two
+    n = np.floor(q)
+    frac = q - n
+    n = n + ((frac > 0.5) | ((frac == 0.5) & (np.mod(n, 2) == 1)))
+    r = n * quantum
+    sub = r < 2.0 ** -6
+    er = np.frexp(np.where(sub, 1.0, r))[1].astype(np.int64) - 1
+    mant = np.where(sub, 0, np.rint((r / np.ldexp(1.0, er) - 1) * 8)).astype(np.int64)
+    normal_code = ((er + 7) << 3) | mant
+    sub_code = np.rint(r / 2.0 ** -9).astype(np.int64)
+    code = np.where(sub, sub_code, normal_code)
+    code = np.where((a0 >= E4M3_MAX) | (r >= E4M3_MAX), 0x7E, code)
+    code = np.where(nan, 0x7F, code)
+    return (sign | code).astype(np.uint8)
 
 
 def fp8_quantize(X: np.ndarray):
