@@ -189,6 +189,38 @@ mtp_status mtp_row_linear_bda(const mtp_bf16* Z, int64_t ldz, const mtp_bf16* Wt
                               int64_t M, int64_t N, int64_t Kp, void* stream);
 
 /*
+ * FP8 (E4M3) forward GEMMs with per-tensor scaling ("快速入门", FP8 training:
+ * E4M3 in the forward pass, an amax-derived scaling factor per tensor;
+ * "Megatron-LM 深度学习与源码分析文档", part 5: FP8 quant/dequant and scaling
+ * among the kernel priorities).  E4M3 as defined by the FP8 formats paper
+ * (OCP): bias 7, max 448, S.1111.111 = NaN, no infinities.
+ *
+ * mtp_fp8_quantize: Xq = E4M3(fp32(x * s)), nearest with ties to even,
+ *   saturating; s = fp32(448 / amax) (1 if amax = 0), amax = max |x| of X
+ *   [M x K]; *scale_inv = fp32(1 / s) (the dequantization factor).  amax_ws
+ *   and scale_inv are one fp32 each in device memory; amax_ws is scratch
+ *   (cleared and reduced by the call, on the stream).  K % 8 == 0; Xq pitch
+ *   ldq (bytes) >= K and a multiple of 8; X and Xq 16-byte aligned.
+ * mtp_fp8_column_linear: Y = act(x_scale_inv * w_scale_inv * (Xq . Wq^T) +
+ *   bias), shapes, activations and output rules as mtp_column_linear; Wq
+ *   [N x K] codes (weights quantized once per update); the scale factors are
+ *   device pointers (as mtp_fp8_quantize writes them).
+ * mtp_fp8_row_linear_partial: as mtp_row_linear_partial with the product
+ *   x_scale_inv * w_scale_inv * (Zq . Wq^T) (fp32 partials, bf16 last shard).
+ * For both GEMMs: K and the code pitches (bytes) are multiples of 16; fp32
+ * accumulation; code matrices 16-byte aligned and under 2 GiB per 256 rows.
+ */
+mtp_status mtp_fp8_quantize(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t K, uint8_t* Xq, int64_t ldq,
+                            float* amax_ws, float* scale_inv, void* stream);
+mtp_status mtp_fp8_column_linear(const uint8_t* Xq, int64_t ldx, const float* x_scale_inv, const uint8_t* Wq,
+                                 int64_t ldw, const float* w_scale_inv, const mtp_bf16* bias, mtp_bf16* Y,
+                                 int64_t ldy, int64_t M, int64_t N, int64_t K, mtp_act act, void* stream);
+mtp_status mtp_fp8_row_linear_partial(const uint8_t* Zq, int64_t ldz, const float* z_scale_inv, const uint8_t* Wq,
+                                      int64_t ldw, const float* w_scale_inv, float* Yacc, int64_t ldacc,
+                                      int accumulate, const mtp_bf16* bias, mtp_bf16* Y, int64_t ldy, int64_t M,
+                                      int64_t N, int64_t Kp, void* stream);
+
+/*
  * Backward GEMMs of a linear Y = X . Wt^T ("Megatron-LM 深度学习与源码分析文档",
  * part 2 section 2: each parallel linear's backward computes the input and
  * weight gradients; the column-parallel one all-reduces dX across ranks, the

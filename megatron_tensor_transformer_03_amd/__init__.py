@@ -51,6 +51,9 @@ def lib():
             "mtp_linear_wgrad": [vp, i64, vp, i64, vp, i64, ci, i64, i64, i64, vp],
             "mtp_release_workspaces": [],
             "mtp_norm_stats": [vp, i64, i64, i64, ci, ctypes.c_float, vp, vp],
+            "mtp_fp8_quantize": [vp, i64, i64, i64, vp, i64, vp, vp, vp],
+            "mtp_fp8_column_linear": [vp, i64, vp, vp, i64, vp, vp, vp, i64, i64, i64, i64, ci, vp],
+            "mtp_fp8_row_linear_partial": [vp, i64, vp, vp, i64, vp, vp, i64, ci, vp, vp, i64, i64, i64, i64, vp],
             "mtp_norm_fold_weights": [vp, i64, i64, i64, vp, vp, vp, ci, vp, i64, vp, vp, vp],
             "mtp_norm_column_linear": [vp, i64, vp, vp, i64, vp, vp, vp, i64, i64, i64, i64, ci, vp],
             "mtp_row_linear_bda": [vp, i64, vp, i64, vp, i64, ci, vp, vp, i64, vp, i64, ctypes.c_float, vp, i64,
@@ -138,6 +141,37 @@ def mtp_row_linear_bda(Z, Wt, residual, Y, Yacc=None, accumulate=False, bias=Non
         int(bool(accumulate)), _ptr(bias), _ptr(residual), _ld(residual), _ptr(keep),
         _ld(keep) if keep is not None else 0, p_drop, _ptr(Y), _ld(Y), M, N, Kp, _stream(Z)))
     return Y
+
+
+def mtp_fp8_quantize(X, Xq, amax_ws, scale_inv):
+    """Per-tensor E4M3 codes of X into Xq (uint8, same shape); scale_inv (1 fp32 on the device) receives the
+    dequantization factor; amax_ws is one fp32 of device scratch."""
+    M, K = X.shape
+    _check("mtp_fp8_quantize", lib().mtp_fp8_quantize(_ptr(X), _ld(X), M, K, _ptr(Xq), _ld(Xq), _ptr(amax_ws),
+                                                      _ptr(scale_inv), _stream(X)))
+    return Xq
+
+
+def mtp_fp8_column_linear(Xq, x_scale_inv, Wq, w_scale_inv, bias, Y, act=ACT_NONE):
+    """Y = act(sx * sw * (Xq . Wq^T) + bias) from E4M3 codes (uint8) and device scale factors."""
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    _check("mtp_fp8_column_linear", lib().mtp_fp8_column_linear(
+        _ptr(Xq), _ld(Xq), _ptr(x_scale_inv), _ptr(Wq), _ld(Wq), _ptr(w_scale_inv), _ptr(bias), _ptr(Y), _ld(Y),
+        M, N, K, act, _stream(Y)))
+    return Y
+
+
+def mtp_fp8_row_linear_partial(Zq, z_scale_inv, Wq, w_scale_inv, Yacc=None, accumulate=False, bias=None, Y=None):
+    """Yacc (=|+=) sz * sw * (Zq . Wq^T) in fp32; if Y is given, Y = bf16(Yacc + bias)."""
+    M, Kp = Zq.shape
+    N = Wq.shape[0]
+    out = Y if Y is not None else Yacc
+    _check("mtp_fp8_row_linear_partial", lib().mtp_fp8_row_linear_partial(
+        _ptr(Zq), _ld(Zq), _ptr(z_scale_inv), _ptr(Wq), _ld(Wq), _ptr(w_scale_inv), _ptr(Yacc),
+        _ld(Yacc) if Yacc is not None else 0, int(bool(accumulate)), _ptr(bias), _ptr(Y),
+        _ld(Y) if Y is not None else 0, M, N, Kp, _stream(out)))
+    return out
 
 
 def mtp_release_workspaces():

@@ -9,7 +9,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmtp.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["gemm.hip", "moe.hip", "rope.hip", "norm.hip", "api.hip"]
+SOURCES = ["gemm.hip", "gemm_f8.hip", "fp8.hip", "moe.hip", "rope.hip", "norm.hip", "api.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++20", "-munsafe-fp-atomics",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
 

@@ -269,6 +269,83 @@ mtp_status mtp_norm_column_linear(const mtp_bf16* X, int64_t ldx, const float* s
                   "norm column linear");
 }
 
+mtp_status mtp_fp8_quantize(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t K, uint8_t* Xq, int64_t ldq,
+                            float* amax_ws, float* scale_inv, void* stream) {
+  TRY(check_dims(M, 8, K));
+  TRY(check_mat(X, "X", K, ldx));
+  TRY(check_mat(Xq, "Xq", K, ldq));
+  if (!amax_ws || !scale_inv) return fail(MTP_ERR_NULL, "amax_ws and scale_inv are required");
+  if ((reinterpret_cast<uintptr_t>(amax_ws) | reinterpret_cast<uintptr_t>(scale_inv)) & 3u)
+    return fail(MTP_ERR_ALIGN, "amax_ws / scale_inv are not 4-byte aligned");
+  TRY(check_device());
+  return launched(mtp::fp8_quantize(X, ldx, (int)M, (int)K, Xq, ldq, amax_ws, scale_inv, (hipStream_t)stream),
+                  "fp8 quantize");
+}
+
+// E4M3 operands: K, and the pitches in bytes, multiples of 16 (the kernels count pairs of codes)
+static mtp_status check_f8(const void* p, const char* name, int64_t K, int64_t ld, const float* sinv,
+                           const char* sname) {
+  if (!p) return fail(MTP_ERR_NULL, "%s is NULL", name);
+  if (misaligned(p)) return fail(MTP_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  if (ld < K || ld % 16 != 0) return fail(MTP_ERR_SHAPE, "%s: pitch %lld must be >= %lld and a multiple of 16", name,
+                                          (long long)ld, (long long)K);
+  if (!sinv) return fail(MTP_ERR_NULL, "%s is NULL", sname);
+  if (reinterpret_cast<uintptr_t>(sinv) & 3u) return fail(MTP_ERR_ALIGN, "%s is not 4-byte aligned", sname);
+  return MTP_OK;
+}
+
+mtp_status mtp_fp8_column_linear(const uint8_t* Xq, int64_t ldx, const float* x_scale_inv, const uint8_t* Wq,
+                                 int64_t ldw, const float* w_scale_inv, const mtp_bf16* bias, mtp_bf16* Y,
+                                 int64_t ldy, int64_t M, int64_t N, int64_t K, mtp_act act, void* stream) {
+  TRY(check_dims(M, N, K));
+  if (K % 16 != 0) return fail(MTP_ERR_SHAPE, "the inner dimension %lld is not a multiple of 16", (long long)K);
+  if (act != MTP_ACT_NONE && act != MTP_ACT_GELU && act != MTP_ACT_SWIGLU)
+    return fail(MTP_ERR_SHAPE, "unknown activation %d", (int)act);
+  if (act == MTP_ACT_SWIGLU && N % 2 != 0) return fail(MTP_ERR_SHAPE, "SwiGLU needs an even N (got %lld)", (long long)N);
+  const int64_t nout = act == MTP_ACT_SWIGLU ? N / 2 : N;
+  TRY(check_f8(Xq, "Xq", K, ldx, x_scale_inv, "x_scale_inv"));
+  TRY(check_f8(Wq, "Wq", K, ldw, w_scale_inv, "w_scale_inv"));
+  TRY(check_mat(Y, "Y", nout, ldy));
+  TRY(check_vec(bias, "bias"));
+  TRY(check_window("Xq", 128, ldx));
+  TRY(check_window("Wq", ((act == MTP_ACT_SWIGLU ? nout : 0) + 256) / 2 + 1, ldw));
+  TRY(check_device());
+  mtp::GemmParams p;
+  p.A = reinterpret_cast<const uint16_t*>(Xq); p.lda = ldx / 2;
+  p.B = reinterpret_cast<const uint16_t*>(Wq); p.ldb = ldw / 2;
+  p.bias = bias; p.Y = Y; p.ldy = ldy;
+  p.M = (int)M; p.Nout = (int)nout; p.K = (int)(K / 2); p.up_offset = nout; p.a_src_rows = M;
+  p.act = act == MTP_ACT_GELU ? 1 : 0;
+  p.f8_scale_a = x_scale_inv; p.f8_scale_b = w_scale_inv;
+  return launched(mtp::gemm_f8(p, act == MTP_ACT_SWIGLU ? mtp::MODE_SWIGLU : mtp::MODE_COL, (hipStream_t)stream),
+                  "fp8 column linear");
+}
+
+mtp_status mtp_fp8_row_linear_partial(const uint8_t* Zq, int64_t ldz, const float* z_scale_inv, const uint8_t* Wq,
+                                      int64_t ldw, const float* w_scale_inv, float* Yacc, int64_t ldacc,
+                                      int accumulate, const mtp_bf16* bias, mtp_bf16* Y, int64_t ldy, int64_t M,
+                                      int64_t N, int64_t Kp, void* stream) {
+  TRY(check_dims(M, N, Kp));
+  if (Kp % 16 != 0) return fail(MTP_ERR_SHAPE, "the inner dimension %lld is not a multiple of 16", (long long)Kp);
+  TRY(check_f8(Zq, "Zq", Kp, ldz, z_scale_inv, "z_scale_inv"));
+  TRY(check_f8(Wq, "Wq", Kp, ldw, w_scale_inv, "w_scale_inv"));
+  if (!Yacc && !Y) return fail(MTP_ERR_NULL, "Yacc and Y are both NULL");
+  if (!Yacc && accumulate) return fail(MTP_ERR_NULL, "accumulate needs Yacc");
+  if (Yacc) TRY(check_mat(Yacc, "Yacc", N, ldacc));
+  if (Y) TRY(check_mat(Y, "Y", N, ldy));
+  TRY(check_vec(bias, "bias"));
+  TRY(check_window("Zq", 128, ldz));
+  TRY(check_window("Wq", 128, ldw));
+  TRY(check_device());
+  mtp::GemmParams p;
+  p.A = reinterpret_cast<const uint16_t*>(Zq); p.lda = ldz / 2;
+  p.B = reinterpret_cast<const uint16_t*>(Wq); p.ldb = ldw / 2;
+  p.Yacc = Yacc; p.ldacc = Yacc ? ldacc : 0; p.accumulate = accumulate ? 1 : 0;
+  p.bias = bias; p.Y = Y; p.ldy = Y ? ldy : 0; p.M = (int)M; p.Nout = (int)N; p.K = (int)(Kp / 2); p.a_src_rows = M;
+  p.f8_scale_a = z_scale_inv; p.f8_scale_b = w_scale_inv;
+  return launched(mtp::gemm_f8(p, mtp::MODE_ROW, (hipStream_t)stream), "fp8 row-parallel partial");
+}
+
 mtp_status mtp_mlp_forward(const mtp_bf16* X, int64_t M, int64_t H, int64_t F, int p, int r0, int r1,
                            const mtp_bf16* W1t, const mtp_bf16* b1, const mtp_bf16* W2t, const mtp_bf16* b2,
                            mtp_act act, mtp_bf16* Z_ws, float* Yacc, mtp_bf16* Y, void* stream) {

@@ -44,6 +44,10 @@ struct GemmParams {
   const uint8_t* keep = nullptr;      // packed keep bits (column c: bit c % 8 of byte c / 8), NULL: no dropout
   int64_t ldk = 0;                    // bytes per keep row
   float drop_scale = 1.f;
+  // E4M3 products: device pointers to the two operands' dequantization factors (the product is scaled by
+  // both before the epilogue); K, lda and ldb then count pairs of one-byte codes
+  const float* f8_scale_a = nullptr;
+  const float* f8_scale_b = nullptr;
   float* sk_ws = nullptr;           // split schedule: partial-tile slots (set at launch)
   int sk_chunks = 0;                // split schedule: K chunks per tile
   int* sk_cnt = nullptr;            // split schedule: per-tile arrival counters, zero between launches
@@ -53,13 +57,19 @@ struct GemmParams {
 struct GemmPlan {
   int bm = 0, bn = 0, split_groups = 0, id = 0, split_chunks = 0;
 };
-GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, bool row_major_k = false);
+GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, bool row_major_k = false, bool allow_small = true);
 hipError_t release_split_workspaces();
 
 enum GemmEpilogue { EPI_PLAIN = 0, EPI_NORM = 1, EPI_BDA = 2 };
 hipError_t gemm(const GemmParams& p, int mode, hipStream_t st, int epi = EPI_PLAIN);
 // MODE_ROW products whose A (and/or B) operand is stored [K x M] ([K x N]): lda / ldb are those pitches.
 hipError_t gemm_backward(const GemmParams& p, bool a_row_major_k, bool b_row_major_k, hipStream_t st);
+// E4M3 x E4M3 products (gemm_f8.hip): COL (none / GeLU), SWIGLU and ROW epilogues.
+hipError_t gemm_f8(const GemmParams& p, int mode, hipStream_t st);
+// Per-tensor E4M3 quantization (fp8.hip): amax of X, then codes = E4M3(fp32(x * s)), s = fp32(448 / amax),
+// and scale_inv = fp32(1 / s).  amax_ws: one fp32 of device scratch.
+hipError_t fp8_quantize(const uint16_t* X, int64_t ldx, int M, int K, uint8_t* Xq, int64_t ldq, float* amax_ws,
+                        float* scale_inv, hipStream_t st);
 // rows_upper: total rows over all groups (an upper bound is enough; spare tiles exit).
 hipError_t gemm_grouped(const GemmParams& p, int mode, int rows_upper, hipStream_t st);
 

@@ -1,41 +1,5 @@
-// bf16 MFMA GEMM family for gfx950 with fused tensor-parallel epilogues.
-//
-// Every linear of the layer is C = A . B^T with both operands K-contiguous:
-// A = activations [M x K], B = weights stored [out x in] = [N x K] (the
-// F.linear layout of the pages' ColumnParallelLinear / RowParallelLinear
-// pseudo-code, "ai阅读megatron").  One kernel template covers
-//   MODE_COL    : column-parallel output, bf16(act(acc + bias)), act in {none, erf-GeLU}
-//   MODE_SWIGLU : column-parallel gate+up, bf16(silu(gate + bg) * (up + bu))
-//   MODE_ROW    : row-parallel partial in fp32 (Yacc = P or Yacc += P), and on the
-//                 last shard bf16(Yacc + bias): the local form of Y = sum_i Y_i
-//   MODE_COMBINE: MoE expert output, Yacc[token] += w * acc (fp32 atomics)
-// and a grouped variant (MoE experts) whose row tiles are laid over the
-// ragged per-expert row ranges read from device memory.
-//
-// Design (gfx950, CDNA4):
-//  * A tile configuration (Cfg) fixes the block tile BM x BN, the wave grid, the
-//    K step BK and the number NS of LDS stages.  Each wave owns a
-//    (BM/WAVES_M) x (BN/WAVES_N) tile of v_mfma_f32_32x32x16_bf16 fragments
-//    accumulated in fp32 (the 32x32x16 form sustains ~97% of the dense bf16
-//    rate on gfx950; the 16x16x32 form measured ~85%).  The large tile is
-//    256 x 256 with 8 waves (two per SIMD, 128 accumulators each).
-//  * Operands are swapped in the MFMA (weights as the first operand) so a
-//    lane's accumulators hold runs of 4 consecutive output columns of one row.
-//  * Global -> LDS: buffer_load_dwordx4 ... lds (direct to LDS, no VGPR round
-//    trip, no ds_write) into an NS-deep ring of LDS stages, NS - 1 K steps
-//    ahead of the MFMAs, one barrier per K step.  Each stage is its own LDS
-//    variable so the compiler sees that a DMA into one stage does not alias
-//    the fragment reads of another.  Buffer resources make out-of-range rows
-//    read as zero without faulting, and the K position is a scalar offset, so
-//    the loop has no vector address arithmetic.  (With one step of lead the
-//    DMA latency, ~2-3K cycles under load, was exposed on every step.)
-//  * LDS rows are BK * 2 bytes; 16-byte chunks are XOR-swizzled per row so the
-//    fragment reads (16 lanes read one chunk of 16 consecutive rows) hit
-//    distinct banks of the 64-bank (256 B per cycle) LDS.
-//  * bf16 epilogues stage each wave's tile through LDS and store whole rows.
-//  * Tile order is XCD-aware: consecutive workgroup ids land on different XCDs
-//    (8 L2 slices), so ids are remapped to give each XCD a contiguous band of
-//    tiles, grouped GROUP_M rows at a time for A/B panel reuse in its L2.
+// Launch planning and dispatch of the bf16 GEMM kernels (the kernel template is in gemm_kernel.h), the
+// split-K workspace, and the backward products.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -44,736 +8,9 @@
 #include <type_traits>
 #include <utility>
 
-#include "gemm.h"
+#include "gemm_kernel.h"
 
 namespace mtp {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int NS_, bool EARLY_>
-struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BK = BK_, NS = NS_;
-  // EARLY: the first fragments of step k + 1 are read during the last MFMAs of step k (the barrier ending a
-  // step then makes the stage two steps ahead visible, so the ring needs one more stage for the same lead)
-  static constexpr bool EARLY = EARLY_;
-  static constexpr int LEAD = EARLY ? 2 : 1;
-  static constexpr int NWAVES = WAVES_M * WAVES_N, NT = 64 * NWAVES;
-  static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;  // wave tile
-  static constexpr int FM = TM / 32, FN = TN / 32;             // 32 x 32 MFMA tiles per wave
-  static constexpr int CPR = BK / 8;                           // 16-byte chunks per LDS row
-  static constexpr int RPL = 256 / (2 * BK);                   // LDS rows per 256-byte bank line
-  static constexpr int ROWS_PER_DMA = 64 / CPR;                // rows one 64-lane DMA instruction fills
-  static constexpr int GA = BM / ROWS_PER_DMA, GB = BN / ROWS_PER_DMA;  // DMA groups per stage (A, B)
-  // DMA instructions per wave per stage: group g goes to wave g % NWAVES; when the groups do not divide
-  // evenly, the spare slots load nothing (out of range) into a scratch LDS block, so every wave issues the
-  // same number of DMAs and the wait counts stay uniform.
-  static constexpr int D = (GA + GB + NWAVES - 1) / NWAVES;
-  static constexpr bool SPARE = (GA + GB) % NWAVES != 0;
-  static constexpr int STAGE = (BM + BN) * BK;                 // elements per LDS stage
-  static_assert(BK == 32 || BK == 64, "K step");
-  static_assert(NS >= 2 + LEAD - 1 && NS <= 5, "LDS stages");
-  static_assert(NWAVES % 4 == 0, "whole waves per SIMD");
-  static_assert(TM % 32 == 0 && TN % 32 == 0, "32 x 32 fragments");
-  static_assert(BM % ROWS_PER_DMA == 0 && BN % ROWS_PER_DMA == 0, "DMA groups");
-  static_assert(NS * STAGE * 2 + (SPARE ? 1024 : 0) <= 160 * 1024, "LDS capacity");
-};
-
-// Element offset of (row, 16-byte chunk) in an LDS stage: rows of BK elements, chunks permuted by XOR with
-// (row / RPL) & (CPR - 1).  A fragment read has 16 lanes read one chunk of 16 consecutive rows; the RPL rows
-// that share a 256-byte bank line differ in their permutation, so those 16 reads hit 16 distinct bank groups.
-template <class C>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * C::BK + ((chunk ^ ((row / C::RPL) & (C::CPR - 1))) << 3);
-}
-
-__device__ __forceinline__ uint16_t to_bf16(float x) {
-  __bf16 h = (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
-  return __builtin_bit_cast(uint16_t, h);
-}
-
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-// Two floats to packed bf16 (one v_cvt_pk_bf16_f32, round to nearest even).
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const f32x2_t v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
-__device__ __forceinline__ float from_bf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-// Exact-erf GeLU, gelu(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)).  erf is evaluated with Abramowitz &
-// Stegun 7.1.26 (|error| <= 1.5e-7 absolute, far below bf16 resolution): for z >= 0,
-// 1 - erf(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z).  With z = |x| / sqrt 2
-// and P = (a1 t + .. + a5 t^5) / 2 this gives Phi(x) = 1 - P e (x >= 0) and P e (x < 0), e = exp(-x^2 / 2),
-// so gelu(x) = max(x, 0) - |x| P e for both signs, with no cancellation for negative x.  The constants
-// below are p / sqrt 2, a_i / 2 and -log2(e) / 2 (e via exp2); this is an epilogue that runs once per
-// output element, so every operation counts: 12 VALU operations and 2 transcendentals.
-__device__ __forceinline__ float gelu_erf(float x) {
-  const float e = __builtin_amdgcn_exp2f(x * x * -0.72134752044448170368f);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.23164188773f, fabsf(x), 1.0f));
-  const float P = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 0.5307027145f, -0.7265760135f), 0.7107068705f),
-                                     -0.142248368f), 0.127414796f);
-  return fmaf(-e, fabsf(x) * P, x > 0.0f ? x : 0.0f);
-}
-
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
-
-// Workgroup ids alternate over the 8 XCDs (each with its own L2); remapped so that each XCD gets a
-// contiguous range of logical ids.
-__device__ __forceinline__ int xcd_remap(int id, int total) {
-  return (total & 7) == 0 ? (id & 7) * (total >> 3) + (id >> 3) : id;
-}
-// Tile of logical id `id`: GROUP_M tile rows at a time, column-major inside the group, so consecutive ids
-// share A and B panels.
-__device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int GROUP_M = 4;
-  const int per_group = GROUP_M * tiles_n;
-  const int g = id / per_group;
-  const int first_m = g * GROUP_M;
-  const int gm = min(tiles_m - first_m, GROUP_M);
-  const int r = id - g * per_group;
-  tm = first_m + r % gm;
-  tn = r / gm;
-}
-
-// Buffer resource (raw, stride 0) over `bytes` bytes at `base`.  The fields are made explicitly uniform:
-// a resource the compiler cannot prove uniform is wrapped in a per-lane "waterfall" loop at every load.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
-}
-
-// Store 4 consecutive bf16 outputs (8 bytes) or the in-range part of them.
-__device__ __forceinline__ void store4_bf16(uint16_t* dst, const float v[4], int valid) {
-  if (valid >= 4) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (r < valid) dst[r] = to_bf16(v[r]);
-  }
-}
-
-// AT / BT: the operand is stored with the contraction index along its rows ([K x M] for A, [K x N] for B;
-// the backward GEMMs: dX = dY W reads W that way, dW = dY^T X reads both).  Such a tile is kept in LDS as
-// [BK rows][BM or BN columns] and its MFMA fragments are read with ds_read_b64_tr_b16, the gfx950 LDS
-// transpose load: 16 lanes each name 4 consecutive columns of one row, and lane i receives column i of
-// four consecutive rows.
-template <class C, int MODE, bool GROUPED, bool KFULL, bool SPLIT, bool AT = false, bool BT = false, int EPI = EPI_PLAIN>
-__global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
-  // A private copy of the parameters: read once into scalar registers, rather than reloaded from the
-  // kernel argument segment (each reload waits on the LDS/scalar counter) wherever a field is used.
-  GemmParams p = p_arg;
-  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NS = C::NS, WAVES_N = C::WAVES_N, NWAVES = C::NWAVES;
-  constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, CPR = C::CPR, RPL = C::RPL;
-  constexpr int D = C::D, GA = C::GA, ROWS_PER_DMA = C::ROWS_PER_DMA;
-  static_assert(MODE != MODE_SWIGLU || TN % 64 == 0, "gate/up fragment pairs");
-  static_assert(!(AT || BT) || (BK == 32 && !GROUPED && (MODE == MODE_COL || MODE == MODE_ROW)),
-                "row-major-K operands: K step 32, plain column/row epilogues");
-  static_assert(!AT || BM == 128 || BM == 256, "A rows of 256 or 512 bytes");
-  static_assert(!BT || BN == 128 || BN == 256, "B rows of 256 or 512 bytes");
-  static_assert(EPI == EPI_PLAIN || (!GROUPED && (EPI == EPI_NORM ? (MODE == MODE_COL || MODE == MODE_SWIGLU)
-                                                                    : MODE == MODE_ROW)),
-                "norm epilogue on column products, bias-dropout-add on row products");
-  constexpr int NB_OUT = MODE == MODE_SWIGLU ? BN / 2 : BN;  // output columns per tile
-
-  // one LDS variable per stage (see the design notes); unused ones are a token 16 bytes
-  __shared__ __attribute__((aligned(16))) uint16_t lds0[C::STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t lds1[C::STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t lds2[NS > 2 ? C::STAGE : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t lds3[NS > 3 ? C::STAGE : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t lds4[NS > 4 ? C::STAGE : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_spare[C::SPARE ? 512 : 8];  // dropped unless used
-  auto stage_buf = [&](auto I) -> uint16_t* {
-    constexpr int i = decltype(I)::value;
-    if constexpr (i == 0) return lds0;
-    else if constexpr (i == 1) return lds1;
-    else if constexpr (i == 2) return lds2;
-    else if constexpr (i == 3) return lds3;
-    else return lds4;
-  };
-
-  __shared__ int sk_flag;
-  // K steps, rounded up to a multiple of NS: the loop body covers NS steps (one per LDS stage, each stage a
-  // compile-time choice) and has no branches, so the compiler's wait counts stay exact.  With KFULL the
-  // step count is a multiple of NS and every chunk is in range; otherwise chunks at or past K read as zero,
-  // so padding steps multiply zeros.
-  const int KT = (p.K + BK - 1) / BK;
-  const int KTS = (KT + NS - 1) / NS * NS;
-  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.Nout + NB_OUT - 1) / NB_OUT;
-  // split schedule (SPLIT only): each tile's RI ring passes in S chunks, partial sums of tile t in slots
-  // t * S .. t * S + S - 1
-  const int RI = KTS / NS;
-  const int G = gridDim.x;
-  const int S = p.sk_chunks;
-  auto slot_of = [&](int c, int t) { return t * S + c; };
-
-  // ---- one tile: rows m0 .. m0 + BM - 1 of the row group at row_base, K steps kt0 .. kt1 - 1.  With
-  // SPLIT and sk_partial, the K range is part of the tile's and the partial sums of all workgroups on the
-  // tile are added before the epilogue (see the split schedule below).
-  auto run_tile = [&](int tm, int tn, int row_base, int rows, const uint16_t* __restrict__ B, int kt0, int kt1,
-                      int sk_tile, int sk_which, int sk_first, int sk_last, bool sk_partial) {
-  const int m0 = tm * BM;  // relative to row_base
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm0 = (wave / WAVES_N) * TM, wn0 = (wave % WAVES_N) * TN;
-
-  // ---- global sources: raw buffer loads.  Each operand gets a buffer resource whose base is this tile's
-  // first row (the whole gather source for gathered rows) and whose size ends at the operand's last row:
-  // a load past it returns zero and cannot fault.  Per-lane byte offsets are fixed across K; the K position
-  // is a scalar offset, so the loop issues loads with no vector address arithmetic.  Rows past the end of
-  // a tile only feed outputs that are never stored, so they need no masking; only K chunks at or past K
-  // must read as zero (the KFULL = false variant redirects them out of range).
-  constexpr uint32_t kOOB = 0x7FFFFFF0u;
-  const uint16_t* a_base;
-  int64_t a_extent;
-  if constexpr (AT) {  // [K x M]: the tile's columns m0 .. m0 + BM - 1 of every row
-    a_base = p.A + m0;
-    a_extent = (int64_t)p.K * p.lda - m0;
-  } else if (p.a_rows) {
-    a_base = p.A;
-    a_extent = p.a_src_rows * p.lda;
-  } else {
-    a_base = p.A + (int64_t)(row_base + m0) * p.lda;
-    a_extent = (p.a_src_rows - (row_base + m0)) * p.lda;
-  }
-  const int nbase = tn * NB_OUT;
-  const uint16_t* b_base = BT ? B + nbase : B + (int64_t)nbase * p.ldb;
-  const int64_t b_extent = BT ? (int64_t)p.K * p.ldb - nbase
-                              : ((MODE == MODE_SWIGLU ? p.up_offset : 0) + p.Nout - nbase) * p.ldb;
-  // (integer clamps written out: the device min() overload for 64-bit integers goes through double, and a
-  // converted value lands in a vector register, which turns every buffer load into a waterfall loop)
-  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(a_base, 2 * a_extent < (int64_t)kOOB ? 2 * a_extent : (int64_t)kOOB);
-  const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(b_base, 2 * b_extent < (int64_t)kOOB ? 2 * b_extent : (int64_t)kOOB);
-  // Direct-to-LDS loads: one buffer_load_dwordx4 ... lds moves 64 lanes x 16 B = ROWS_PER_DMA LDS rows,
-  // lane l filling row (l / CPR), chunk (l % CPR) of its group.  The LDS layout is swizzled (see swz), so
-  // each lane loads the global chunk that lands at its slot.  Groups 0 .. GA-1 are rows of A, the next GB
-  // are rows of B (stored right after A in the stage); slot j of a wave carries group j * NWAVES + wave.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int lrow = lane / CPR;
-  uint32_t d_off[D];
-  int d_kc[D];  // K element offset of each lane's chunk
-#pragma unroll
-  for (int j = 0; j < D; ++j) {
-    const int g = j * NWAVES + wave_u;
-    const int r = ROWS_PER_DMA * g + lrow - (g < GA ? 0 : BM);  // row within A or within B
-    const int c = (lane % CPR) ^ ((r / RPL) & (CPR - 1));
-    d_kc[j] = 8 * c;
-    // a row-major-K operand: instruction g fills rows RT g .. RT g + RT - 1 of the [BK x BX] tile (RT = 512 /
-    // BX), 16-byte chunk (lane % (BX / 8)) of a row holding global chunk (lane % (BX / 8)) ^ 4 (row % 4); its K
-    // position is the row, and chunks that start past the matrix width load nothing
-    auto t_off = [&](int gg, int BX, int64_t ld, int x0, int width) {
-      const int cpr = BX / 8;
-      const int rk = (512 / BX) * gg + lane / cpr;
-      const int cc = (lane % cpr) ^ (4 * (rk & 3));
-      d_kc[j] = rk;
-      return x0 + 8 * cc < width ? 2u * (uint32_t)(rk * ld + 8 * cc) : kOOB;
-    };
-    if (g < GA && AT) {
-      d_off[j] = t_off(g, BM, p.lda, m0, p.M);
-    } else if (g >= GA && g < GA + C::GB && BT) {
-      d_off[j] = t_off(g - GA, BN, p.ldb, nbase, p.Nout);
-    } else if (g < GA) {
-      if (p.a_rows) {
-        const int m = m0 + r;
-        d_off[j] = m < rows ? 2u * (uint32_t)((int64_t)p.a_rows[row_base + m] * p.lda + 8 * c) : kOOB;
-      } else {
-        d_off[j] = 2u * (uint32_t)(r * p.lda + 8 * c);
-      }
-    } else if (g < GA + C::GB) {
-      int n = r;
-      if constexpr (MODE == MODE_SWIGLU) {
-        const int g32 = r >> 5;
-        n = 32 * (g32 >> 1) + (r & 31) + ((g32 & 1) ? (int)p.up_offset : 0);
-      }
-      d_off[j] = 2u * (uint32_t)(n * p.ldb + 8 * c);
-    } else {
-      d_off[j] = kOOB;  // spare slot
-    }
-  }
-  typedef __attribute__((address_space(3))) void* lds_ptr;
-  // The scalar offset is not part of the hardware range check (only the per-lane offset is), so it stays
-  // inside the rows: a prefetch past the last K step re-reads step 0 into a stage that is never consumed
-  // (KFULL) or is redirected out of range per lane (!KFULL, reading zeros).
-  auto dma_stage = [&](int k0, uint16_t* sbuf) {
-    // the K position: a column offset for K-major operands, a row offset for row-major-K ones
-    const int soff_a = k0 < p.K ? (AT ? 2 * k0 * (int)p.lda : 2 * k0) : 0;
-    const int soff_b = k0 < p.K ? (BT ? 2 * k0 * (int)p.ldb : 2 * k0) : 0;
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-      const int g = j * NWAVES + wave_u;  // uniform
-      uint32_t vo = d_off[j];
-      if constexpr (!KFULL) vo = k0 + d_kc[j] < p.K ? vo : kOOB;
-      uint16_t* dst = sbuf + g * ROWS_PER_DMA * BK;
-      if constexpr (C::SPARE) dst = g < GA + C::GB ? dst : lds_spare;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(g < GA ? a_rsrc : b_rsrc, (lds_ptr)dst, 16, vo, g < GA ? soff_a : soff_b,
-                                               0, 0);
-    }
-  };
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-  // 32 x 32 x 16 fragments: lane holds row (lane & 31), k = 8 * (lane >> 5) .. +7 of a 16-wide k step.
-  // Two fragment sets alternate: the set of the next k step is read while the MFMAs of this one run.
-  const int fr = lane & 31, fk = lane >> 5;
-  bf16x8 fa[2][FM], fb[2][FN];
-  // Fragment of a [BK x BX] row-major-K tile: lane l (16-lane group g = l / 16, i = l % 16) names row
-  // 16 ks + 8 (l / 32) + 4 r + i / 4 and columns x0 + 16 (g % 2) + 4 (i % 4) .. + 3; the transpose load then
-  // gives it column x0 + (l % 32) of rows 16 ks + 8 (l / 32) + 4 r .. + 3, i.e. k = 8 (l / 32) + 4 r .. + 3 of
-  // its MFMA operand row.  Two loads (r = 0, 1) make the 8 k values.  Rows r and r + 1 .. r + 3 use chunks
-  // XOR 4 (row % 4), so the 32 lanes of a half-wave hit 64 distinct banks.
-  typedef short short4_t __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) short4_t* lds_s4;
-  auto read_t = [&](const uint16_t* s, auto BXC, int x0, int ks) -> bf16x8 {
-    constexpr int BX = decltype(BXC)::value;
-    const int i = lane & 15, h = lane >> 5;
-    const int x = x0 + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
-    short4_t v[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int k = 16 * ks + 8 * h + 4 * r + (i >> 2);
-      const int off = k * BX + (((x >> 3) ^ (4 * (i >> 2))) << 3) + (x & 7);
-      v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(s + off));
-    }
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-  auto read_frags = [&](const uint16_t* sbuf, int ks, auto SET) {
-    constexpr int q = decltype(SET)::value;
-    const uint16_t* sA = sbuf;
-    const uint16_t* sB = sbuf + BM * BK;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if constexpr (AT) fa[q][i] = read_t(sA, std::integral_constant<int, BM>{}, wm0 + 32 * i, ks);
-      else fa[q][i] = *reinterpret_cast<const bf16x8*>(sA + swz<C>(wm0 + 32 * i + fr, 2 * ks + fk));
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      if constexpr (BT) fb[q][j] = read_t(sB, std::integral_constant<int, BN>{}, wn0 + 32 * j, ks);
-      else fb[q][j] = *reinterpret_cast<const bf16x8*>(sB + swz<C>(wn0 + 32 * j + fr, 2 * ks + fk));
-    }
-  };
-  auto mma = [&](auto SET) {
-    constexpr int q = decltype(SET)::value;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[q][j], fa[q][i], acc[i][j], 0, 0, 0);
-  };
-  constexpr int KS = BK / 16;  // MFMA k steps per K step
-  static_assert(!C::EARLY || (NS * KS) % 2 == 0, "fragment sets alternate consistently across the ring");
-  // vmcnt(n): wait until at most n of this wave's DMA instructions are outstanding (expcnt, lgkmcnt free).
-  // The barrier ending step kt makes stage kt + LEAD visible: the DMAs newer than that stage may stay out.
-  constexpr int kNewer = (NS - 1 - C::LEAD) * D;
-  static_assert(kNewer >= 0 && kNewer < 64, "vmcnt range");
-  constexpr int kWaitNext = 0x0F70 | (kNewer & 15) | ((kNewer >> 4) << 14);
-  // The barrier between steps: this wave's DMA of stage kt + LEAD has landed (vmcnt), every fragment read
-  // of the stage about to be overwritten has been consumed by an MFMA, and the waves meet.  A
-  // __syncthreads() would add a release fence, which waits for every outstanding DMA (vmcnt(0)) and so
-  // drains the whole ring; the raw s_barrier between compiler-level memory fences keeps later DMAs in flight.
-  auto ring_barrier = [&]() {
-    __builtin_amdgcn_s_waitcnt(kWaitNext);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-  // One K step on stage I: start the DMA of step kt + NS - 1 into the stage consumed last step (every wave
-  // passed the barrier after reading it), run this step's MFMAs (with EARLY, the last k step reads the first
-  // fragments of stage kt + 1, visible since the previous barrier), then the barrier.
-  auto step = [&](auto I, int kt) {
-    constexpr int i = decltype(I)::value;
-    uint16_t* cur = stage_buf(std::integral_constant<int, i>{});
-    dma_stage((kt + NS - 1) * BK, stage_buf(std::integral_constant<int, (i + NS - 1) % NS>{}));
-    __builtin_amdgcn_sched_barrier(0);  // keep the DMA issue at the top: the scheduler would sink it
-    [&]<int... S>(std::integer_sequence<int, S...>) {
-      ([&] {
-        constexpr int ks = S;
-        constexpr int g = i * KS + ks;  // k step index within the ring pass: fixes the fragment set
-        if constexpr (C::EARLY) {
-          if constexpr (ks + 1 < KS)
-            read_frags(cur, ks + 1, std::integral_constant<int, (g + 1) & 1>{});
-          else
-            read_frags(stage_buf(std::integral_constant<int, (i + 1) % NS>{}), 0,
-                       std::integral_constant<int, (g + 1) & 1>{});
-          mma(std::integral_constant<int, g & 1>{});
-          // issue order: one fragment read, then its share of the MFMAs, and so on, so the reads of the next
-          // set are spread over this set's MFMAs instead of being bunched (or sunk next to their first use)
-          [&]<int... R>(std::integer_sequence<int, R...>) {
-            constexpr int NR = FM + FN, NM = FM * FN;
-            ((__builtin_amdgcn_sched_group_barrier(0x100, 1, 0),      // one LDS read
-              __builtin_amdgcn_sched_group_barrier(0x008, (NM * (R + 1)) / NR - (NM * R) / NR, 0)), ...);  // MFMAs
-          }(std::make_integer_sequence<int, FM + FN>{});
-          __builtin_amdgcn_sched_barrier(0);
-        } else {
-          read_frags(cur, ks, std::integral_constant<int, 0>{});
-          mma(std::integral_constant<int, 0>{});
-        }
-      }(), ...);
-    }(std::make_integer_sequence<int, KS>{});
-    ring_barrier();
-  };
-  if constexpr (SPLIT) __syncthreads();  // the previous tile's epilogue may still read the LDS stages
-  [&]<int... I>(std::integer_sequence<int, I...>) {
-    (dma_stage((kt0 + I) * BK, stage_buf(std::integral_constant<int, I>{})), ...);
-  }(std::make_integer_sequence<int, NS - 1>{});
-  ring_barrier();
-  if constexpr (C::EARLY) read_frags(lds0, 0, std::integral_constant<int, 0>{});
-  for (int kt = kt0; kt < kt1; kt += NS) {
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      (step(std::integral_constant<int, I>{}, kt + I), ...);
-    }(std::make_integer_sequence<int, NS>{});
-  }
-  // The last steps prefetched stages past K (never consumed); drain them before the epilogue reuses LDS.
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
-
-  if constexpr (SPLIT) {
-    if (sk_partial) {
-      // Every workgroup on the tile stores its partial accumulators to its own workspace slot (float4s in
-      // register order, thread-linear, so the stores and the loads below are contiguous per wave), then
-      // counts itself in on the tile's counter.  The last to arrive adds the slots in workgroup order (a
-      // fixed order, so the sum does not depend on arrival order), resets the counter for the next launch
-      // and runs the epilogue; the others are done with the tile.  Nobody waits on anybody.
-      // The slots and the counter are accessed with device-scope coherent operations (sc1: written through
-      // to, and read from, the point where the XCDs' L2s are coherent) and ordered by waiting for the slot
-      // stores to complete before counting in, so no fence has to write back or invalidate whole L2s
-      // (which would evict the operand panels the other workgroups on the XCD are streaming).
-      constexpr int Q = FM * FN * 4;   // float4 per thread
-      constexpr int kSc1 = 16;         // cache policy: device scope
-      const int64_t slot_bytes = (int64_t)Q * C::NT * 16;
-      const __amdgpu_buffer_rsrc_t ws = make_rsrc(p.sk_ws, (int64_t)tiles_m * tiles_n * S * slot_bytes);
-      typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-      const int mine = (int)(sk_which * slot_bytes) + 16 * tid;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ws,
-                                                   mine + ((i * FN + j) * 4 + q) * C::NT * 16, 0, kSc1);
-          }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's slot stores have completed
-      __syncthreads();
-      if (tid == 0)
-        sk_flag = __hip_atomic_fetch_add(p.sk_cnt + sk_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                  sk_last - sk_first;
-      __syncthreads();
-      if (!sk_flag) return;
-      if (tid == 0) __hip_atomic_store(p.sk_cnt + sk_tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // one 32 x 32 fragment at a time (the scheduler barrier keeps the loads of the next fragment from
-      // being hoisted, which would need registers for all of them while the accumulators are live)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int base = ((i * FN + j) * 4) * C::NT * 16 + 16 * tid;
-          float4 v[4];
-          const int s0 = (int)(slot_of(sk_first, sk_tile) * slot_bytes) + base;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            v[q] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ws, s0 + q * C::NT * 16, 0, kSc1));
-          for (int c = sk_first + 1; c <= sk_last; ++c) {
-            const int sc = (int)(slot_of(c, sk_tile) * slot_bytes) + base;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float4 w =
-                  __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ws, sc + q * C::NT * 16, 0, kSc1));
-              v[q].x += w.x; v[q].y += w.y; v[q].z += w.z; v[q].w += w.w;
-            }
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[i][j][4 * q] = v[q].x; acc[i][j][4 * q + 1] = v[q].y;
-            acc[i][j][4 * q + 2] = v[q].z; acc[i][j][4 * q + 3] = v[q].w;
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-  }
-
-  // ---- epilogue.  Weights were the MFMA's first operand, so lane holds output row (lane & 31) of its
-  // 32-row fragment and, in register 4*jj + r, column 8*jj + 4*(lane >> 5) + r of its 32-column fragment.
-  const int col4 = 4 * (lane >> 5);
-  constexpr int TNO = MODE == MODE_SWIGLU ? TN / 2 : TN;        // output columns per wave
-  constexpr int FNO = TNO / 32;                                  // output fragments per wave
-  const int ncol0 = tn * NB_OUT + (wave % WAVES_N) * TNO;        // first output column of the wave tile
-  // Bias of this lane's output columns, read once with clamped indices (columns past Nout are computed but
-  // never stored): per-element loads under branches would each wait a full memory latency.
-  constexpr bool kBias = MODE != MODE_COMBINE;
-  constexpr bool kNorm = EPI == EPI_NORM;
-  float bias_g[kBias ? FNO : 1][4][4], bias_u[MODE == MODE_SWIGLU ? FNO : 1][4][4];
-  // norm epilogue: column sums of the folded weight (gate and up parts) and each fragment row's statistics
-  float cs_g[kNorm ? FNO : 1][4][4], cs_u[kNorm && MODE == MODE_SWIGLU ? FNO : 1][4][4];
-  float st_mean[kNorm ? FM : 1], st_rstd[kNorm ? FM : 1];
-  if constexpr (kNorm) {
-    const int64_t blen = MODE == MODE_SWIGLU ? p.up_offset + p.Nout : p.Nout;
-    const __amdgpu_buffer_rsrc_t brs = make_rsrc(p.bias_f32, p.bias_f32 ? 4 * blen : 0);
-    const __amdgpu_buffer_rsrc_t crs = make_rsrc(p.norm_colsum, p.norm_colsum ? 4 * blen : 0);
-#pragma unroll
-    for (int jo = 0; jo < FNO; ++jo)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int c = ncol0 + 32 * jo + 8 * jj + col4 + r;
-          bias_g[jo][jj][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(brs, 4 * c, 0, 0));
-          cs_g[jo][jj][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(crs, 4 * c, 0, 0));
-          if constexpr (MODE == MODE_SWIGLU) {
-            const int cu = (int)p.up_offset + c;
-            bias_u[jo][jj][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(brs, 4 * cu, 0, 0));
-            cs_u[jo][jj][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(crs, 4 * cu, 0, 0));
-          }
-        }
-    const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.norm_stats + 2 * (int64_t)(row_base + m0), 8 * (int64_t)(rows - m0));
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int rr = wm0 + 32 * i + fr;
-      st_mean[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 8 * rr, 0, 0));
-      st_rstd[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 8 * rr + 4, 0, 0));
-    }
-  } else if constexpr (kBias) {
-    // Through a buffer resource that is empty without a bias and ends at the bias's last element: absent
-    // and out-of-range elements read as zero, with no branch per element.
-    const bool has_bias = p.bias != nullptr && (MODE != MODE_ROW || p.Y != nullptr);
-    const int64_t blen = MODE == MODE_SWIGLU ? p.up_offset + p.Nout : p.Nout;
-    const __amdgpu_buffer_rsrc_t brs = make_rsrc(p.bias, has_bias ? 2 * blen : 0);
-#pragma unroll
-    for (int jo = 0; jo < FNO; ++jo)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int c = ncol0 + 32 * jo + 8 * jj + col4 + r;
-          bias_g[jo][jj][r] = from_bf16(__builtin_amdgcn_raw_buffer_load_b16(brs, 2 * c, 0, 0));
-          if constexpr (MODE == MODE_SWIGLU)
-            bias_u[jo][jj][r] = from_bf16(__builtin_amdgcn_raw_buffer_load_b16(brs, 2 * ((int)p.up_offset + c), 0, 0));
-        }
-  }
-  // output value of (fragment row block i, output fragment jo, run jj, element r)
-  auto pre = [&](int i, int j, float a, float b, float cs) -> float {
-    if constexpr (kNorm) return fmaf(st_rstd[i], fmaf(-st_mean[i], cs, a), b);
-    else return a + b;
-  };
-  auto out_val = [&](int i, int jo, int jj, int r, auto gelu) -> float {
-    if constexpr (MODE == MODE_SWIGLU) {
-      const float g = pre(i, jo, acc[i][2 * jo][4 * jj + r], bias_g[jo][jj][r], cs_g[kNorm ? jo : 0][jj][r]);
-      const float u = pre(i, jo, acc[i][2 * jo + 1][4 * jj + r], bias_u[jo][jj][r],
-                          cs_u[kNorm ? jo : 0][jj][r]);
-      return silu(g) * u;
-    } else {
-      const float x = pre(i, jo, acc[i][jo][4 * jj + r], bias_g[jo][jj][r], cs_g[kNorm ? jo : 0][jj][r]);
-      if constexpr (decltype(gelu)::value) return gelu_erf(x);
-      else return x;
-    }
-  };
-  // bias-dropout-add on the bf16 output of a row product: v = resid + (kept ? v * scale : 0) for the four
-  // columns n .. n + 3 of output row orow (n a multiple of 4, so their keep bits share one byte).  Reads go
-  // through buffer resources ending at the last row: rows past it read zeros and are never stored.
-  constexpr bool kBda = EPI == EPI_BDA;
-  [[maybe_unused]] const __amdgpu_buffer_rsrc_t r_rs =
-      make_rsrc(kBda ? p.resid : nullptr, kBda ? 2 * (int64_t)(row_base + rows) * p.ldr : 0);
-  [[maybe_unused]] const __amdgpu_buffer_rsrc_t k_rs =
-      make_rsrc(kBda ? p.keep : nullptr, kBda && p.keep ? (int64_t)(row_base + rows) * p.ldk : 0);
-  auto bda4 = [&](int64_t orow, int n, float* v) {
-    if constexpr (EPI == EPI_BDA) {
-      const uint32_t roff = 2u * (uint32_t)(orow * p.ldr + n);
-      const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(r_rs, roff, 0, 0);
-      const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(r_rs, roff + 4, 0, 0);
-      const float res[4] = {__builtin_bit_cast(float, lo << 16), __builtin_bit_cast(float, lo & 0xFFFF0000u),
-                            __builtin_bit_cast(float, hi << 16), __builtin_bit_cast(float, hi & 0xFFFF0000u)};
-      if (p.keep) {
-        const uint32_t kb = __builtin_amdgcn_raw_buffer_load_b8(k_rs, (uint32_t)(orow * p.ldk + (n >> 3)), 0, 0) >>
-                            (n & 7);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = res[r] + (((kb >> r) & 1u) ? v[r] * p.drop_scale : 0.f);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = res[r] + v[r];
-      }
-    }
-  };
-  constexpr bool kStaged = MODE == MODE_COL || MODE == MODE_SWIGLU || MODE == MODE_ROW;
-  if (kStaged && (MODE != MODE_ROW || p.Yacc == nullptr)) {
-    // bf16 outputs go through LDS so that the global stores are whole rows: each wave writes its own
-    // TM x TNO tile into a private region (the drain above retired every LDS access of the main loop),
-    // then reads it back row-contiguously; no cross-wave synchronisation is needed.  Regions are row-major
-    // with 8-byte units permuted per row so the 32 lanes of a write (32 rows, one unit) and of a read (2-4
-    // whole rows) hit distinct banks.
-    // UPR 8-byte units per row (a multiple of 8).  A write has 32 lanes store one unit of 32 consecutive
-    // rows; rows whose starts fall on the same bank offset (RP apart) get distinct XOR permutations of the
-    // unit index within blocks of W units, W the largest power of two dividing UPR (at most 32).
-    constexpr int UPR = TNO / 4;
-    constexpr int W = (UPR & -UPR) < 32 ? (UPR & -UPR) : 32;
-    constexpr int RP = 32 / W;
-    static_assert(UPR % 8 == 0 && (TM * UPR) % 64 == 0, "unit layout");
-    constexpr int WPS = C::STAGE / (TM * TNO);  // wave regions per LDS stage
-    static_assert(WPS >= 1 && (NWAVES + WPS - 1) / WPS <= NS, "staging fits");
-    const int si = wave / WPS;
-    uint16_t* reg = (si == 0 ? lds0 : si == 1 ? lds1 : si == 2 ? lds2 : si == 3 ? lds3 : lds4) + (wave % WPS) * TM * TNO;
-    auto unit_at = [&](int row, int u) { return row * TNO + 4 * (u ^ ((row / RP) & (W - 1))); };
-    auto stage_tile = [&](auto gelu) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int jo = 0; jo < FNO; ++jo)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            float v[4] = {out_val(i, jo, jj, 0, gelu), out_val(i, jo, jj, 1, gelu), out_val(i, jo, jj, 2, gelu),
-                          out_val(i, jo, jj, 3, gelu)};
-            if constexpr (EPI == EPI_BDA)
-              bda4((int64_t)row_base + m0 + wm0 + 32 * i + fr, ncol0 + 32 * jo + 8 * jj + col4, v);
-            *reinterpret_cast<uint2*>(reg + unit_at(32 * i + fr, 8 * jo + 2 * jj + (lane >> 5))) =
-                make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
-          }
-    };
-    if (MODE == MODE_COL && p.act == 1) stage_tile(std::true_type{});
-    else stage_tile(std::false_type{});
-    // read back row-contiguously: pass q covers units 64 q .. 64 q + 63 of the row-major tile
-#pragma unroll 4
-    for (int q = 0; q < TM * UPR / 64; ++q) {
-      const int id = 64 * q + lane;
-      const int row = id / UPR, u = id % UPR;
-      const int n = ncol0 + 4 * u;
-      const int valid = p.Nout - n;
-      const int m = m0 + wm0 + row;
-      const uint2 d = *reinterpret_cast<const uint2*>(reg + unit_at(row, u));
-      if (m < rows && valid > 0) {
-        uint16_t* dst = p.Y + ((int64_t)row_base + m) * p.ldy + n;
-        if (valid >= 4) {
-          *reinterpret_cast<uint2*>(dst) = d;
-        } else {
-          // (constant indices: a runtime-indexed local array would be placed in LDS)
-          dst[0] = (uint16_t)d.x;
-          if (valid > 1) dst[1] = (uint16_t)(d.x >> 16);
-          if (valid > 2) dst[2] = (uint16_t)d.y;
-        }
-      }
-    }
-    return;
-  }
-  // Direct stores: ROW with an fp32 target (the uniform choices are made once, outside the element loops)
-  // and COMBINE.
-  auto direct = [&](auto ACCUM, auto WITH_Y) {
-    constexpr bool accum = decltype(ACCUM)::value, with_y = decltype(WITH_Y)::value;
-    float* const yacc = p.Yacc;
-    const int64_t ldacc = p.ldacc, ldy = p.ldy;
-    uint16_t* const y = p.Y;
-    const int nout = p.Nout;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int m = m0 + wm0 + 32 * i + fr;
-      if (m >= rows) continue;
-      const int64_t orow = (int64_t)row_base + m;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int n = tn * BN + wn0 + 32 * j + 8 * jj + col4;
-          if (n >= nout) continue;
-          const int valid = nout - n;
-          float v[4] = {acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]};
-          if constexpr (MODE == MODE_ROW) {
-            // fp32 partial of a row-parallel shard (and, on the last shard, the bf16 result)
-            float* dst = yacc + orow * ldacc + n;
-            if (valid >= 4) {
-              if constexpr (accum) {
-                const float4 o = *reinterpret_cast<const float4*>(dst);
-                v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
-              }
-              *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-            } else {
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (r < valid) {
-                  if constexpr (accum) v[r] += dst[r];
-                  dst[r] = v[r];
-                }
-            }
-            if constexpr (with_y) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r) v[r] += bias_g[j][jj][r];
-              bda4(orow, n, v);
-              store4_bf16(y + orow * ldy + n, v, valid);
-            }
-          } else if constexpr (MODE == MODE_COMBINE) {
-            const float w = p.row_w[orow];
-            float* dst = yacc + (int64_t)p.out_rows[orow] * ldacc + n;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (r < valid) atomicAdd(dst + r, w * v[r]);
-          }
-        }
-      }
-    }
-  };
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-  if constexpr (MODE == MODE_ROW) {
-    if (p.accumulate) {
-      if (p.Y) direct(T_{}, T_{});
-      else direct(T_{}, F_{});
-    } else {
-      if (p.Y) direct(F_{}, T_{});
-      else direct(F_{}, F_{});
-    }
-  } else {
-    direct(F_{}, F_{});
-  }
-  };
-
-  if constexpr (SPLIT) {
-    // Split schedule: every tile's K range is cut into S chunks of whole ring passes, and the units
-    // (tile, chunk) are dealt out chunk-major, unit u to logical workgroup u mod G, so the units that run at
-    // the same time are the same K chunk of neighbouring tiles: they stream the same K slices of the shared
-    // operand panels, as one-tile-per-workgroup tiles do.  (Contiguous per-workgroup K ranges, as in
-    // stream-K, put concurrent workgroups at unrelated K positions and defeat the L2.)  Logical ids are
-    // XCD-contiguous.
-    const int T = tiles_m * tiles_n;
-    const int U = T * S;
-    for (int u = xcd_remap(blockIdx.x, G); u < U; u += G) {
-      const int c = u / T, t = u - c * T;
-      const int r0 = (int)((int64_t)c * RI / S), r1 = (int)((int64_t)(c + 1) * RI / S);
-      int tm, tn;
-      tile_coords(t, tiles_m, tiles_n, tm, tn);
-      run_tile(tm, tn, 0, p.M, p.B, r0 * NS, r1 * NS, t, slot_of(c, t), 0, S - 1, true);
-    }
-  } else {
-    // ---- tile placement
-      int tm, tn;
-    int row_base = 0, rows = p.M;  // rows of this tile's group (all rows when ungrouped)
-    const uint16_t* __restrict__ B = p.B;
-    if constexpr (GROUPED) {
-      // blockIdx.x = row-tile slot * tiles_n + tn; slots are laid over the groups in order.
-      const int tiles_n = (p.Nout + NB_OUT - 1) / NB_OUT;
-      int slot = blockIdx.x / tiles_n;
-      tn = blockIdx.x - slot * tiles_n;
-      int g = 0;
-      for (; g < p.groups; ++g) {
-        const int lo = p.group_offsets[g], hi = p.group_offsets[g + 1];
-        const int nt = (hi - lo + BM - 1) / BM;
-        if (slot < nt) { row_base = lo; rows = hi - lo; break; }
-        slot -= nt;
-      }
-      if (g == p.groups) return;  // spare slot of the upper-bound grid
-      tm = slot;
-      B += (int64_t)g * p.group_stride_B;
-    } else {
-      tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
-    }
-    run_tile(tm, tn, row_base, rows, B, 0, KTS, 0, 0, 0, 0, false);
-  }
-}
 
 // ------------------------------------------------------------------------------------------ launch
 // Workspace of the split schedule, per (device, stream): two partial-tile slots per workgroup and one
@@ -790,6 +27,7 @@ struct SplitWs {
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, SplitWs> g_ws;
 int g_cus[64] = {0};
+}  // namespace
 
 int cu_count() {
   int dev = 0;
@@ -825,61 +63,6 @@ hipError_t split_workspace(hipStream_t st, size_t ws_bytes, int64_t cnt_n, float
   *cnt = w.cnt;
   return hipSuccess;
 }
-}  // namespace
-
-template <class C, int MODE, bool GROUPED, bool AT = false, bool BT = false, int EPI = EPI_PLAIN>
-static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStream_t st, int split_groups = 0,
-                             int split_chunks = 0) {
-  GemmParams p = p0;
-  const int nb = MODE == MODE_SWIGLU ? C::BN / 2 : C::BN;
-  const int tiles_n = (p.Nout + nb - 1) / nb;
-  int64_t tiles;
-  if (GROUPED)
-    tiles = (int64_t)((grid_rows_upper + C::BM - 1) / C::BM + p.groups) * tiles_n;
-  else
-    tiles = (int64_t)((p.M + C::BM - 1) / C::BM) * tiles_n;
-  if (tiles <= 0) return hipSuccess;
-  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const bool kfull = p.K % (C::BK * C::NS) == 0;  // whole chunks and a step count that fills the ring
-  if constexpr (!GROUPED) {
-    if (split_groups > 0 && split_chunks > 1) {
-      const size_t slot = (size_t)C::FM * C::FN * 16 * sizeof(float) * C::NT;
-      p.sk_chunks = split_chunks;
-      hipError_t e = split_workspace(st, (size_t)tiles * split_chunks * slot, tiles, &p.sk_ws, &p.sk_cnt);
-      if (e != hipSuccess) return e;
-      if (kfull)
-        hipLaunchKernelGGL((gemm_kernel<C, MODE, false, true, true, AT, BT, EPI>), dim3(split_groups), dim3(C::NT), 0, st, p);
-      else
-        hipLaunchKernelGGL((gemm_kernel<C, MODE, false, false, true, AT, BT, EPI>), dim3(split_groups), dim3(C::NT), 0, st,
-                           p);
-      return hipGetLastError();
-    }
-  }
-  if (kfull)
-    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, true, false, AT, BT, EPI>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
-                       p);
-  else
-    hipLaunchKernelGGL((gemm_kernel<C, MODE, GROUPED, false, false, AT, BT, EPI>), dim3((unsigned)tiles), dim3(C::NT), 0,
-                       st, p);
-  return hipGetLastError();
-}
-
-#ifndef MTP_BIG_CFG
-#define MTP_BIG_CFG 256, 256, 2, 4, 32, 4, true
-#endif
-#ifndef MTP_WIDE_CFG
-#define MTP_WIDE_CFG 256, 192, 4, 2, 32, 4, true
-#endif
-#ifndef MTP_HALF_CFG
-#define MTP_HALF_CFG 256, 128, 4, 2, 32, 4, true
-#endif
-#ifndef MTP_SMALL_CFG
-#define MTP_SMALL_CFG 128, 128, 4, 2, 64, 4, true
-#endif
-using BigTile = Cfg<MTP_BIG_CFG>;              // 8 waves (wave tile 128 x 64), 128 KB LDS ring
-using WideTile = Cfg<MTP_WIDE_CFG>;            // 8 waves (64 x 96), 112 KB
-using HalfTile = Cfg<MTP_HALF_CFG>;            // 8 waves (64 x 64), 96 KB
-using SmallTile = Cfg<MTP_SMALL_CFG>;          // 8 waves (32 x 64), 128 KB
 
 // Schedule choice.  One workgroup per tile: the time is the number of waves of tiles over the CUs times
 // the time of one tile (BM * BN / efficiency, the measured relative MFMA efficiency of the tile shapes on
@@ -888,7 +71,7 @@ using SmallTile = Cfg<MTP_SMALL_CFG>;          // 8 waves (32 x 64), 128 KB
 // waves of units times the time of a chunk plus fixed costs.  Wave quantisation is large at the shard
 // shapes of a tensor-parallel layer: 4096 x 1280 is 80 tiles of 256 x 256 (31% of the CUs busy) but 240
 // units in 3 chunks.
-GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, bool row_major_k) {
+GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, bool row_major_k, bool allow_small) {
   struct Opt { int bm, bn; double eff; int id; int ns_bk; int64_t slot_bytes; };
   const Opt opts[] = {{256, 256, 1.00, 0, 128, 256 << 10}, {256, 192, 0.95, 1, 128, 192 << 10},
                       {256, 128, 0.85, 2, 128, 128 << 10}, {128, 128, 0.72, 3, 256, 0}};
@@ -899,6 +82,7 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, bool row_major_
   for (const Opt& o : opts) {
     if (mode == MODE_SWIGLU && o.id == 1) continue;  // gate/up pairs need wave tiles of 64 B rows
     if (row_major_k && (o.id == 1 || o.id == 3)) continue;  // transposed tiles: 256 x 256 and 256 x 128 only
+    if (!allow_small && o.id == 3) continue;                 // (its K step is 64 two-byte units)
     const int64_t nbo = mode == MODE_SWIGLU ? o.bn / 2 : o.bn;
     const int64_t tiles = ((M + o.bm - 1) / o.bm) * ((Nout + nbo - 1) / nbo);
     const double tile_t = o.bm * o.bn / o.eff;

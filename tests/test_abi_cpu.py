@@ -27,7 +27,7 @@ def _gpu_present():
 def test_library_exports_every_header_symbol():
     L = mtp.lib()
     names = mtp.header_symbols()
-    assert len(names) == 18
+    assert len(names) == 21
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", mtp.LIB_PATH], capture_output=True, text=True).stdout
@@ -323,3 +323,34 @@ def test_norm_and_bda_valid_calls_reach_the_device_check():
     assert L.mtp_norm_column_linear(P, 64, P2, P3, 64, None, None, P4, 32, 8, 64, 64, 2, None) == UNSUPPORTED
     assert bda() == UNSUPPORTED
     assert bda(keep=None, p=0.0, Yacc=P2, ldacc=40, acc=1) == UNSUPPORTED
+
+
+def test_fp8_entry_points_reject():
+    L = mtp.lib()
+    q = lambda **kw: L.mtp_fp8_quantize(kw.get("X", P), kw.get("ldx", 64), kw.get("M", 4), kw.get("K", 64),
+                                        kw.get("Xq", P2), kw.get("ldq", 64), kw.get("amax", P3), kw.get("sinv", P4),
+                                        None)
+    assert q(X=None) == NULL and q(Xq=None) == NULL and q(amax=None) == NULL and q(sinv=None) == NULL
+    assert q(K=60, ldx=64, ldq=64) == SHAPE and q(ldq=56) == SHAPE and q(X=BAD) == ALIGN and q(sinv=P4 + 2) == ALIGN
+    col = lambda **kw: L.mtp_fp8_column_linear(
+        kw.get("Xq", P), kw.get("ldx", 64), kw.get("xs", P2), kw.get("Wq", P3), kw.get("ldw", 64), kw.get("ws", P4),
+        kw.get("bias", None), kw.get("Y", P), kw.get("ldy", 32), kw.get("M", 8), kw.get("N", 32), kw.get("K", 64),
+        kw.get("act", 0), None)
+    assert col(xs=None) == NULL and col(ws=None) == NULL and col(Wq=None) == NULL
+    assert col(K=56, ldx=64, ldw=64) == SHAPE          # K % 16
+    assert col(ldx=72) == SHAPE and col(ldw=48) == SHAPE  # code pitches: multiples of 16, >= K
+    assert col(act=2, N=31) == SHAPE and col(Xq=BAD) == ALIGN and col(xs=P2 + 2) == ALIGN
+    row = lambda **kw: L.mtp_fp8_row_linear_partial(
+        kw.get("Zq", P), kw.get("ldz", 64), kw.get("zs", P2), kw.get("Wq", P3), kw.get("ldw", 64), kw.get("ws", P4),
+        kw.get("Yacc", P), kw.get("ldacc", 32), kw.get("acc", 0), None, kw.get("Y", None), kw.get("ldy", 0),
+        kw.get("M", 8), kw.get("N", 32), kw.get("Kp", 64), None)
+    assert row(Yacc=None) == NULL and row(Yacc=None, Y=P2, ldy=32, acc=1) == NULL and row(zs=None) == NULL
+    assert row(Kp=40, ldz=48, ldw=48) == SHAPE and row(ldacc=30) == SHAPE
+
+
+@pytest.mark.skipif(_gpu_present(), reason="on a GPU box a valid call would launch")
+def test_fp8_valid_calls_reach_the_device_check():
+    L = mtp.lib()
+    assert L.mtp_fp8_quantize(P, 64, 4, 64, P2, 64, P3, P4, None) == UNSUPPORTED
+    assert L.mtp_fp8_column_linear(P, 64, P2, P3, 64, P4, None, P, 32, 8, 32, 64, 1, None) == UNSUPPORTED
+    assert L.mtp_fp8_row_linear_partial(P, 64, P2, P3, 64, P4, P, 32, 1, None, None, 0, 8, 32, 64, None) == UNSUPPORTED

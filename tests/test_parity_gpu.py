@@ -423,6 +423,113 @@ def test_row_bda_float_dropout():
     assert _exact_bits_frac(G, ref) >= EXACT_FRAC_MIN
 
 
+# ----------------------------------------------------------------------------- FP8 (E4M3)
+def _codes_dev(codes, pitch=None):
+    """uint8 codes -> device view with a pitch that is a multiple of 16 (the padding 0x7f, an E4M3 NaN: a
+    read past the row width would poison a stored output)."""
+    rows, cols = codes.shape
+    pitch = pitch or ((cols + 15) // 16) * 16 + 16
+    full = np.full((rows, pitch), 0x7F, dtype=np.uint8)
+    full[:, :cols] = codes
+    return torch.from_numpy(full).cuda()[:, :cols]
+
+
+def _scalar(v):
+    return torch.tensor([v], dtype=torch.float32, device="cuda")
+
+
+@pytest.mark.parametrize("M,K,sigma", [(1, 8, 1.0), (37, 136, 3.0), (300, 1024, 0.02), (129, 4104, 50.0)])
+def test_fp8_quantize_codes_bit_exact(M, K, sigma):
+    say("fp8 quantize", M, K, sigma)
+    Xb = synth.normal_bf16(381, M, K, sigma)
+    Xq = torch.zeros(M, ((K + 15) // 16) * 16, dtype=torch.uint8, device="cuda")[:, :K]
+    amax, sinv = _scalar(123.0), _scalar(0.0)
+    mtp.mtp_fp8_quantize(_dev_pad(Xb), Xq, amax, sinv)
+    torch.cuda.synchronize()
+    codes, ref_sinv = oracle.fp8_quantize(Xb)
+    assert np.array_equal(Xq.cpu().numpy(), codes)
+    assert float(sinv.item()) == ref_sinv
+    # all zeros: scale 1, zero codes
+    Z = torch.zeros(4, 16, dtype=torch.bfloat16, device="cuda")
+    Zq = torch.full((4, 16), 5, dtype=torch.uint8, device="cuda")
+    mtp.mtp_fp8_quantize(Z, Zq, amax, sinv)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(Zq) == 0 and float(sinv.item()) == 1.0
+
+
+@pytest.mark.parametrize("M,N,K,act", [
+    (1, 8, 16, 0), (130, 200, 96, 0), (257, 129, 80, 1), (4100, 3000, 64, 0), (300, 400, 4096, 0),
+    (900, 4100, 2048, 0), (200, 272, 160, 2),
+])
+def test_fp8_column_linear_integer_exact(M, N, K, act):
+    # codes of -1, 0, +1 and power-of-two factors keep every sum exact (GeLU/SwiGLU: within the bar)
+    say("fp8 int column", M, N, K, act)
+    Xc = oracle.e4m3_encode(oracle.widen(synth.ternary_bf16(391, M, K)))
+    Wc = oracle.e4m3_encode(oracle.widen(synth.ternary_bf16(392, N, K)))
+    bb = synth.ternary_bf16(393, 1, N)[0]
+    nout = N // 2 if act == mtp.ACT_SWIGLU else N
+    Y = torch.empty(M, _pitch(nout), dtype=torch.bfloat16, device="cuda")[:, :nout]
+    mtp.mtp_fp8_column_linear(_codes_dev(Xc), _scalar(0.5), _codes_dev(Wc), _scalar(0.25), to_dev(bb), Y, act)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 128, 394) if M > 1000 else list(range(M))
+    R = oracle.fp8_linear(np.ascontiguousarray(Xc[rows]), 0.5, Wc, 0.25, bb, act)
+    G = bits(Y)[rows]
+    if act == mtp.ACT_NONE:
+        assert np.array_equal(G, oracle.round_bf16(R))
+    else:
+        _close(widen_bits(G), R, "fp8 int column act")
+        assert _exact_bits_frac(G, R) >= EXACT_FRAC_MIN
+
+
+@pytest.mark.parametrize("M,N,Kp,p", [(77, 130, 64, 3), (256, 256, 2048, 2), (1, 8, 16, 1)])
+def test_fp8_row_partials_integer_exact(M, N, Kp, p):
+    say("fp8 int row", M, N, Kp, p)
+    Zc = oracle.e4m3_encode(oracle.widen(synth.ternary_bf16(401, M, p * Kp)))
+    Wc = oracle.e4m3_encode(oracle.widen(synth.ternary_bf16(402, N, p * Kp)))
+    bb = synth.ternary_bf16(403, 1, N)[0]
+    Zd, Wd = _codes_dev(Zc), _codes_dev(Wc)
+    one = _scalar(1.0)
+    Yacc = torch.empty(M, _pitch(N), dtype=torch.float32, device="cuda")[:, :N]
+    Y = torch.empty(M, _pitch(N), dtype=torch.bfloat16, device="cuda")[:, :N]
+    for r in range(p):
+        last = r == p - 1
+        mtp.mtp_fp8_row_linear_partial(Zd[:, r * Kp:(r + 1) * Kp], one, Wd[:, r * Kp:(r + 1) * Kp], one, Yacc, r > 0,
+                                       to_dev(bb) if last else None, Y if last else None)
+    torch.cuda.synchronize()
+    S = sum(oracle.fp8_linear(np.ascontiguousarray(Zc[:, r * Kp:(r + 1) * Kp]), 1.0,
+                              np.ascontiguousarray(Wc[:, r * Kp:(r + 1) * Kp]), 1.0) for r in range(p))
+    assert np.array_equal(Yacc.cpu().numpy().astype(np.float64), S)
+    assert np.array_equal(bits(Y), oracle.round_bf16(S + widen_bits(bb)[None, :]))
+
+
+@pytest.mark.parametrize("M,N,K,act", [(300, 400, 1024, 1), (4096, 4096, 1024, 1), (512, 7168 // 4, 2048, 2),
+                                       (2048, 1024, 4096, 0)])
+def test_fp8_end_to_end_matches_oracle(M, N, K, act):
+    # quantize both operands on the GPU (codes checked bit for bit), then the GEMM against the oracle's
+    # product of the same codes
+    say("fp8 end to end", M, N, K, act)
+    Xb, Wb = synth.normal_bf16(411, M, K, 1.0), synth.normal_bf16(412, N, K, 0.02)
+    bb = synth.normal_bf16(413, 1, N, 0.1)[0]
+    Xq = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    Wq = torch.empty(N, K, dtype=torch.uint8, device="cuda")
+    amax, sx, sw = _scalar(0.0), _scalar(0.0), _scalar(0.0)
+    mtp.mtp_fp8_quantize(to_dev(Xb), Xq, amax, sx)
+    mtp.mtp_fp8_quantize(to_dev(Wb), Wq, amax, sw)
+    nout = N // 2 if act == mtp.ACT_SWIGLU else N
+    Y = torch.empty(M, nout, dtype=torch.bfloat16, device="cuda")
+    mtp.mtp_fp8_column_linear(Xq, sx, Wq, sw, to_dev(bb), Y, act)
+    torch.cuda.synchronize()
+    xc, xs = oracle.fp8_quantize(Xb)
+    wc, ws = oracle.fp8_quantize(Wb)
+    rows = sample_rows(M, 96, 414)
+    assert np.array_equal(Xq.cpu().numpy()[rows], xc[rows]) and np.array_equal(Wq.cpu().numpy(), wc)
+    assert float(sx.item()) == xs and float(sw.item()) == ws
+    R = oracle.fp8_linear(np.ascontiguousarray(xc[rows]), xs, wc, ws, bb, act)
+    G = bits(Y)[rows]
+    _close(widen_bits(G), R, "fp8 end to end")
+    assert _exact_bits_frac(G, R) >= EXACT_FRAC_MIN
+
+
 # ----------------------------------------------------------------------------- rotary position embedding
 @pytest.mark.parametrize("M,nq,ng,d,rd,interleaved", [
     (1, 1, 1, 8, 8, False), (37, 4, 2, 64, 64, False), (37, 4, 2, 64, 64, True), (300, 8, 1, 128, 128, False),
