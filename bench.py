@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 FLOP/clk
+MFMA_FP8_PEAK_TFLOPS = 5033.2    # dense fp8 MFMA: twice the bf16 rate
 HBM_PEAK_GBS = 8000.0
 METRIC = "TFLOP/s per TP-rank QKV+MLP forward (bf16) and % of MI355X MFMA peak"
 WORKLOADS = {"gpt345m": 1, "gpt3_175b_rank0": 2, "llama70b_rank0": 3, "moe": 4, "tiny": 0}
@@ -33,7 +34,7 @@ WORKLOADS = {"gpt345m": 1, "gpt3_175b_rank0": 2, "llama70b_rank0": 3, "moe": 4, 
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("gemm.hip", "gemm.h"):
+    for f in ("gemm_kernel.h", "gemm.hip", "gemm.h"):
         with open(os.path.join(ROOT, "megatron_tensor_transformer_03_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -196,6 +197,44 @@ def norm_and_bda(w, timer):
             "fc2_bias_dropout_add_us": round(t_bda, 2), "fc2_plain_us": round(t_row, 2)}
 
 
+def fp8_gemms(w, timer):
+    """The workload's linears as E4M3 GEMMs (per-tensor scaled codes of synthetic operands): the GEMM against
+    the dense fp8 MFMA peak beside the bf16 one, and the activation quantization against the HBM roofline."""
+    import torch
+    import megatron_tensor_transformer_03_amd as mtp
+    import synth
+    per, flop_total, us_total, q_total = {}, 0, 0.0, 0.0
+    for i, (label, M, N, K) in enumerate(w.gemms):
+        if label in per:
+            continue
+        act = mtp.ACT_SWIGLU if (label == "fc1" and w.dims.get("act") == mtp.ACT_SWIGLU) else mtp.ACT_NONE
+        X = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        Wt = torch.empty(N, K, dtype=torch.bfloat16, device="cuda")
+        synth.gpu_normal_bf16_(X, 9201 + 2 * i, 1.0)
+        synth.gpu_normal_bf16_(Wt, 9202 + 2 * i, 0.02)
+        Xq = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+        Wq = torch.empty(N, K, dtype=torch.uint8, device="cuda")
+        amax = torch.zeros(mtp.FP8_WS_FLOATS, dtype=torch.float32, device="cuda")
+        sx = torch.zeros(1, dtype=torch.float32, device="cuda")
+        sw = torch.zeros(1, dtype=torch.float32, device="cuda")
+        mtp.mtp_fp8_quantize(Wt, Wq, amax, sw)
+        nout = N // 2 if act == mtp.ACT_SWIGLU else N
+        Y = torch.empty(M, nout, dtype=torch.bfloat16, device="cuda")
+        t_q = _median_us(timer, lambda: mtp.mtp_fp8_quantize(X, Xq, amax, sx))
+        t_g = _median_us(timer, lambda: mtp.mtp_fp8_column_linear(Xq, sx, Wq, sw, None, Y, act))
+        fl = 2 * M * N * K
+        per[label] = {"gemm_us": round(t_g, 2), "tflops": round(fl / (t_g * 1e-6) / 1e12, 1),
+                      "quantize_us": round(t_q, 2)}
+        flop_total += fl
+        us_total += t_g
+        q_total += t_q
+        del X, Wt, Xq, Wq, Y
+    tf = flop_total / (us_total * 1e-6) / 1e12
+    return {"per_linear": per, "achieved": round(tf, 1), "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_FP8_PEAK_TFLOPS, 4), "gemm_us": round(us_total, 2),
+            "quantize_us": round(q_total, 2)}
+
+
 def cpu_baseline(w, budget_s):
     """The oracle on a bounded row sample of the same workload; TFLOP/s of algorithmic work done."""
     import numpy as np
@@ -255,7 +294,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip the backward-GEMM and norm/bias-dropout-add measurements")
+                    help="skip the backward-GEMM, norm/bias-dropout-add and FP8 measurements")
     ap.add_argument("--graphs", action="store_true",
                     help="replay the step as HIP graphs (captured from the same calls) instead of launching each "
                          "call from Python; on ROCm 7 graph launches cost more than they save at this step size")
@@ -386,6 +425,7 @@ def main():
     # the backward GEMMs of the same linears (outside the timed region; dense layers only)
     bwd = None if ("E" in w.dims or args.no_backward) else backward_gemms(w, timer)
     nb = None if ("E" in w.dims or args.no_backward) else norm_and_bda(w, timer)
+    f8 = None if ("E" in w.dims or args.no_backward) else fp8_gemms(w, timer)
 
     out = {
         "metric": METRIC,
@@ -407,7 +447,7 @@ def main():
                    "per_gemm_us": {lb: round(1000 * v, 2) for lb, v in avg.items()},
                    "per_gemm_tflops": {lb: round(flop_by_label[lb] / (avg[lb] * 1e-3) / 1e12, 1)
                                        for lb in avg if lb in flop_by_label},
-                   "aux_kernels": aux, "backward_gemms": bwd, "norm_and_bda": nb},
+                   "aux_kernels": aux, "backward_gemms": bwd, "norm_and_bda": nb, "fp8_gemms": f8},
         "roofline": {"bound": "mfma", "kernel": dom, "kernel_us": round(1000 * dom_avg, 2),
                      "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

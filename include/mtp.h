@@ -71,6 +71,8 @@ typedef enum { MTP_ACT_NONE = 0, MTP_ACT_GELU = 1, MTP_ACT_SWIGLU = 2 } mtp_act;
 
 typedef enum { MTP_NORM_LAYER = 0, MTP_NORM_RMS = 1 } mtp_norm;
 
+#define MTP_FP8_WS_FLOATS 1024 /* scratch of mtp_fp8_quantize, in fp32 elements */
+
 /*
  * ColumnParallelLinear forward of one shard (part 2 section 2, Y_i = X W_i),
  * with its bias and activation fused:
@@ -197,9 +199,10 @@ mtp_status mtp_row_linear_bda(const mtp_bf16* Z, int64_t ldz, const mtp_bf16* Wt
  *
  * mtp_fp8_quantize: Xq = E4M3(fp32(x * s)), nearest with ties to even,
  *   saturating; s = fp32(448 / amax) (1 if amax = 0), amax = max |x| of X
- *   [M x K]; *scale_inv = fp32(1 / s) (the dequantization factor).  amax_ws
- *   and scale_inv are one fp32 each in device memory; amax_ws is scratch
- *   (cleared and reduced by the call, on the stream).  K % 8 == 0; Xq pitch
+ *   [M x K]; *scale_inv = fp32(1 / s) (the dequantization factor), one
+ *   fp32 in device memory.  amax_ws: MTP_FP8_WS_FLOATS fp32 of device
+ *   scratch (per-block partial maxima; calls sharing it on one stream are
+ *   ordered, on different streams they race).  M K < 2^34.  K % 8 == 0; Xq pitch
  *   ldq (bytes) >= K and a multiple of 8; X and Xq 16-byte aligned.
  * mtp_fp8_column_linear: Y = act(x_scale_inv * w_scale_inv * (Xq . Wq^T) +
  *   bias), shapes, activations and output rules as mtp_column_linear; Wq

@@ -15,6 +15,7 @@ import re
 
 ACT_NONE, ACT_GELU, ACT_SWIGLU = 0, 1, 2
 NORM_LAYER, NORM_RMS = 0, 1
+FP8_WS_FLOATS = 1024  # scratch of mtp_fp8_quantize (fp32 elements)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmtp.so")
@@ -145,7 +146,7 @@ def mtp_row_linear_bda(Z, Wt, residual, Y, Yacc=None, accumulate=False, bias=Non
 
 def mtp_fp8_quantize(X, Xq, amax_ws, scale_inv):
     """Per-tensor E4M3 codes of X into Xq (uint8, same shape); scale_inv (1 fp32 on the device) receives the
-    dequantization factor; amax_ws is one fp32 of device scratch."""
+    dequantization factor; amax_ws is FP8_WS_FLOATS fp32 of device scratch."""
     M, K = X.shape
     _check("mtp_fp8_quantize", lib().mtp_fp8_quantize(_ptr(X), _ld(X), M, K, _ptr(Xq), _ld(Xq), _ptr(amax_ws),
                                                       _ptr(scale_inv), _stream(X)))

@@ -277,6 +277,7 @@ mtp_status mtp_fp8_quantize(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t K
   if (!amax_ws || !scale_inv) return fail(MTP_ERR_NULL, "amax_ws and scale_inv are required");
   if ((reinterpret_cast<uintptr_t>(amax_ws) | reinterpret_cast<uintptr_t>(scale_inv)) & 3u)
     return fail(MTP_ERR_ALIGN, "amax_ws / scale_inv are not 4-byte aligned");
+  if (M * (K / 8) >= ((int64_t)1 << 31)) return fail(MTP_ERR_SHAPE, "X has 2^34 or more elements");
   TRY(check_device());
   return launched(mtp::fp8_quantize(X, ldx, (int)M, (int)K, Xq, ldq, amax_ws, scale_inv, (hipStream_t)stream),
                   "fp8 quantize");

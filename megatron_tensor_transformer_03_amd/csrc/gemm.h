@@ -67,8 +67,9 @@ hipError_t gemm_backward(const GemmParams& p, bool a_row_major_k, bool b_row_maj
 // E4M3 x E4M3 products (gemm_f8.hip): COL (none / GeLU), SWIGLU and ROW epilogues.
 hipError_t gemm_f8(const GemmParams& p, int mode, hipStream_t st);
 // Per-tensor E4M3 quantization (fp8.hip): amax of X, then codes = E4M3(fp32(x * s)), s = fp32(448 / amax),
-// and scale_inv = fp32(1 / s).  amax_ws: one fp32 of device scratch.
-hipError_t fp8_quantize(const uint16_t* X, int64_t ldx, int M, int K, uint8_t* Xq, int64_t ldq, float* amax_ws,
+// and scale_inv = fp32(1 / s).  ws: kFp8QuantBlocks fp32 of device scratch (per-block partial maxima).
+constexpr int kFp8QuantBlocks = 1024;
+hipError_t fp8_quantize(const uint16_t* X, int64_t ldx, int M, int K, uint8_t* Xq, int64_t ldq, float* ws,
                         float* scale_inv, hipStream_t st);
 // rows_upper: total rows over all groups (an upper bound is enough; spare tiles exit).
 hipError_t gemm_grouped(const GemmParams& p, int mode, int rows_upper, hipStream_t st);

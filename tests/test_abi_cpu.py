@@ -354,3 +354,10 @@ def test_fp8_valid_calls_reach_the_device_check():
     assert L.mtp_fp8_quantize(P, 64, 4, 64, P2, 64, P3, P4, None) == UNSUPPORTED
     assert L.mtp_fp8_column_linear(P, 64, P2, P3, 64, P4, None, P, 32, 8, 32, 64, 1, None) == UNSUPPORTED
     assert L.mtp_fp8_row_linear_partial(P, 64, P2, P3, 64, P4, P, 32, 1, None, None, 0, 8, 32, 64, None) == UNSUPPORTED
+
+
+def test_fp8_scratch_size_matches_header():
+    import re
+    with open(mtp.HEADER) as f:
+        m = re.search(r"#define MTP_FP8_WS_FLOATS (\d+)", f.read())
+    assert m and int(m.group(1)) == mtp.FP8_WS_FLOATS

@@ -443,7 +443,7 @@ def test_fp8_quantize_codes_bit_exact(M, K, sigma):
     say("fp8 quantize", M, K, sigma)
     Xb = synth.normal_bf16(381, M, K, sigma)
     Xq = torch.zeros(M, ((K + 15) // 16) * 16, dtype=torch.uint8, device="cuda")[:, :K]
-    amax, sinv = _scalar(123.0), _scalar(0.0)
+    amax, sinv = torch.full((mtp.FP8_WS_FLOATS,), 123.0, device="cuda"), _scalar(0.0)
     mtp.mtp_fp8_quantize(_dev_pad(Xb), Xq, amax, sinv)
     torch.cuda.synchronize()
     codes, ref_sinv = oracle.fp8_quantize(Xb)
@@ -512,7 +512,7 @@ def test_fp8_end_to_end_matches_oracle(M, N, K, act):
     bb = synth.normal_bf16(413, 1, N, 0.1)[0]
     Xq = torch.empty(M, K, dtype=torch.uint8, device="cuda")
     Wq = torch.empty(N, K, dtype=torch.uint8, device="cuda")
-    amax, sx, sw = _scalar(0.0), _scalar(0.0), _scalar(0.0)
+    amax, sx, sw = torch.zeros(mtp.FP8_WS_FLOATS, device="cuda"), _scalar(0.0), _scalar(0.0)
     mtp.mtp_fp8_quantize(to_dev(Xb), Xq, amax, sx)
     mtp.mtp_fp8_quantize(to_dev(Wb), Wq, amax, sw)
     nout = N // 2 if act == mtp.ACT_SWIGLU else N
