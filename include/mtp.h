@@ -253,6 +253,11 @@ mtp_status mtp_linear_dgrad(const mtp_bf16* dY, int64_t lddy, const mtp_bf16* Wt
                             int64_t K, void* stream);
 mtp_status mtp_linear_wgrad(const mtp_bf16* dY, int64_t lddy, const mtp_bf16* X, int64_t ldx, float* dW,
                             int64_t lddw, int accumulate, int64_t M, int64_t N, int64_t K, void* stream);
+/* The launch plan of a backward product with output [M x N] and contraction K (dgrad: M, K_out, N; wgrad:
+ * N, K, M in the names above; wgrad != 0 selects mtp_linear_wgrad's plan), as mtp_gemm_plan; launches
+ * nothing. */
+mtp_status mtp_gemm_plan_backward(int64_t M, int64_t N, int64_t K, int wgrad, int* tile_m, int* tile_n,
+                                  int* split_k);
 
 /*
  * Rotary position embedding of the query and key heads of one rank's QKV

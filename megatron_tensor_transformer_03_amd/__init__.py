@@ -47,6 +47,7 @@ def lib():
             "mtp_moe_route": [vp, i64, ci, ci, vp, vp, vp, vp],
             "mtp_moe_mlp_forward": [vp, i64, i64, ci, i64, ci, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "mtp_gemm_plan": [i64, i64, i64, ci, vp, vp, vp],
+            "mtp_gemm_plan_backward": [i64, i64, i64, ci, vp, vp, vp],
             "mtp_rope_qk": [vp, i64, i64, vp, ci, ci, ci, ci, ctypes.c_double, ci, vp],
             "mtp_linear_dgrad": [vp, i64, vp, i64, vp, i64, ci, vp, i64, i64, i64, i64, vp],
             "mtp_linear_wgrad": [vp, i64, vp, i64, vp, i64, ci, i64, i64, i64, vp],
@@ -173,6 +174,14 @@ def mtp_fp8_row_linear_partial(Zq, z_scale_inv, Wq, w_scale_inv, Yacc=None, accu
         _ld(Yacc) if Yacc is not None else 0, int(bool(accumulate)), _ptr(bias), _ptr(Y),
         _ld(Y) if Y is not None else 0, M, N, Kp, _stream(out)))
     return out
+
+
+def mtp_gemm_plan_backward(M, N, K, wgrad=False):
+    """(tile_m, tile_n, split_k) of a backward product (dgrad, or wgrad) with output [M x N] and contraction K."""
+    out = [ctypes.c_int(0) for _ in range(3)]
+    _check("mtp_gemm_plan_backward", lib().mtp_gemm_plan_backward(M, N, K, int(bool(wgrad)),
+                                                                  *[ctypes.addressof(o) for o in out]))
+    return tuple(o.value for o in out)
 
 
 def mtp_release_workspaces():

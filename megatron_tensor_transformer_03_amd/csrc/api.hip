@@ -131,6 +131,21 @@ mtp_status mtp_gemm_plan(int64_t M, int64_t N, int64_t K, mtp_act act, int* tile
   return MTP_OK;
 }
 
+mtp_status mtp_gemm_plan_backward(int64_t M, int64_t N, int64_t K, int wgrad, int* tile_m, int* tile_n,
+                                  int* split_k) {
+  if (M < 1 || N < 1 || K < 1 || M > kIntMax || N > kIntMax || K > kIntMax)
+    return fail(MTP_ERR_SHAPE, "sizes must be in [1, 2^31-1] (M=%lld N=%lld K=%lld)", (long long)M, (long long)N,
+                (long long)K);
+  if (!tile_m || !tile_n || !split_k) return fail(MTP_ERR_NULL, "an output pointer is NULL");
+  TRY(check_device());
+  const mtp::GemmPlan pl = mtp::gemm_plan(mtp::MODE_ROW, M, N, K, wgrad ? 2 : 1);
+  *tile_m = pl.bm;
+  *tile_n = pl.bn;
+  *split_k = pl.split_groups > 0 ? pl.split_chunks : 0;
+  g_err[0] = 0;
+  return MTP_OK;
+}
+
 mtp_status mtp_release_workspaces(void) {
   TRY(check_device());
   return launched(mtp::release_split_workspaces(), "release workspaces");

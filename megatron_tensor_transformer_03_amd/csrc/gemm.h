@@ -57,7 +57,8 @@ struct GemmParams {
 struct GemmPlan {
   int bm = 0, bn = 0, split_groups = 0, id = 0, split_chunks = 0;
 };
-GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, bool row_major_k = false, bool allow_small = true);
+// row_major_k: 0 both operands K-contiguous; 1 B row-major-K (dgrad); 2 both row-major-K (wgrad)
+GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k = 0, bool allow_small = true);
 hipError_t release_split_workspaces();
 
 enum GemmEpilogue { EPI_PLAIN = 0, EPI_NORM = 1, EPI_BDA = 2 };

@@ -71,17 +71,23 @@ hipError_t split_workspace(hipStream_t st, size_t ws_bytes, int64_t cnt_n, float
 // waves of units times the time of a chunk plus fixed costs.  Wave quantisation is large at the shard
 // shapes of a tensor-parallel layer: 4096 x 1280 is 80 tiles of 256 x 256 (31% of the CUs busy) but 240
 // units in 3 chunks.
-GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, bool row_major_k, bool allow_small) {
+GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k, bool allow_small) {
   struct Opt { int bm, bn; double eff; int id; int ns_bk; int64_t slot_bytes; };
   const Opt opts[] = {{256, 256, 1.00, 0, 128, 256 << 10}, {256, 192, 0.95, 1, 128, 192 << 10},
-                      {256, 128, 0.85, 2, 128, 128 << 10}, {128, 128, 0.72, 3, 256, 0}};
+                      {256, 128, 0.85, 2, 128, 128 << 10}, {128, 128, 0.72, 3, 256, 0},
+                      {128, 128, 0.72, 4, 128, 64 << 10}};
   const int cus = cu_count();
   GemmPlan best;
   best.bm = 128; best.bn = 128; best.id = 3;
   double best_t = 1e300;
   for (const Opt& o : opts) {
     if (mode == MODE_SWIGLU && o.id == 1) continue;  // gate/up pairs need wave tiles of 64 B rows
-    if (row_major_k && (o.id == 1 || o.id == 3)) continue;  // transposed tiles: 256 x 256 and 256 x 128 only
+    // transposed operands: every tile but the 128 x 128 one with the 64-deep K step (id 3), and its 32-deep
+    // form (id 4), which serves only them
+    if (row_major_k ? o.id == 3 : o.id == 4) continue;
+    // with both operands transposed the 192-wide tile measured slower than the 256 x 256 one (wgrad of the
+    // 175B fc1: 411 against 372 us), so it is left out there
+    if (row_major_k == 2 && o.id == 1) continue;
     if (!allow_small && o.id == 3) continue;                 // (its K step is 64 two-byte units)
     const int64_t nbo = mode == MODE_SWIGLU ? o.bn / 2 : o.bn;
     const int64_t tiles = ((M + o.bm - 1) / o.bm) * ((Nout + nbo - 1) / nbo);
@@ -104,7 +110,7 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, bool row_major_
 
 template <int MODE, int EPI = EPI_PLAIN>
 static hipError_t dispatch(const GemmParams& p, hipStream_t st) {
-  const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K, false);
+  const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K, 0);
   switch (pl.id) {
     case 0: return launch_cfg<BigTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks);
     case 1:
@@ -119,8 +125,10 @@ static hipError_t dispatch(const GemmParams& p, hipStream_t st) {
 // Backward products: dgrad reads B row-major-K (AT = false, BT = true), wgrad both operands.
 template <bool AT, bool BT>
 static hipError_t dispatch_t(const GemmParams& p, hipStream_t st) {
-  const GemmPlan pl = gemm_plan(MODE_ROW, p.M, p.Nout, p.K, true);
+  const GemmPlan pl = gemm_plan(MODE_ROW, p.M, p.Nout, p.K, AT ? 2 : 1);
   if (pl.id == 0) return launch_cfg<BigTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks);
+  if (pl.id == 4) return launch_cfg<SmallTTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks);
+  if (pl.id == 1) return launch_cfg<WideTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks);
   return launch_cfg<HalfTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks);
 }
 

@@ -169,6 +169,17 @@ __device__ __forceinline__ void store4_bf16(uint16_t* dst, const float v[4], int
 // [BK rows][BM or BN columns] and its MFMA fragments are read with ds_read_b64_tr_b16, the gfx950 LDS
 // transpose load: 16 lanes each name 4 consecutive columns of one row, and lane i receives column i of
 // four consecutive rows.
+// LDS slot of global 16-byte chunk c in row r of a row-major-K tile [BK x BX]: rows r and r + 1 .. r + 3
+// place their chunks 4 slots apart (XOR for a power-of-two number of chunks per row, rotation otherwise),
+// so the 32 lanes of a half-wave of transpose reads (four rows, 64 contiguous bytes each) hit 64 distinct
+// banks for row pitches of 256, 384 and 512 bytes.
+template <int BX>
+__device__ __forceinline__ int t_slot(int c, int r) {
+  constexpr int cpr = BX / 8;
+  if constexpr ((cpr & (cpr - 1)) == 0) return c ^ (4 * r);
+  else return (c + 4 * r) % cpr;
+}
+
 template <class C, int MODE, bool GROUPED, bool KFULL, bool SPLIT, bool AT = false, bool BT = false, int EPI = EPI_PLAIN,
           bool F8 = false>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
@@ -182,7 +193,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   static_assert(!(AT || BT) || (BK == 32 && !GROUPED && (MODE == MODE_COL || MODE == MODE_ROW)),
                 "row-major-K operands: K step 32, plain column/row epilogues");
   static_assert(!AT || BM == 128 || BM == 256, "A rows of 256 or 512 bytes");
-  static_assert(!BT || BN == 128 || BN == 256, "B rows of 256 or 512 bytes");
+  static_assert(!BT || BN == 128 || BN == 192 || BN == 256, "B rows of 256, 384 or 512 bytes");
   static_assert(EPI == EPI_PLAIN || (!GROUPED && (EPI == EPI_NORM ? (MODE == MODE_COL || MODE == MODE_SWIGLU)
                                                                     : MODE == MODE_ROW)),
                 "norm epilogue on column products, bias-dropout-add on row products");
@@ -272,20 +283,21 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     const int r = ROWS_PER_DMA * g + lrow - (g < GA ? 0 : BM);  // row within A or within B
     const int c = (lane % CPR) ^ ((r / RPL) & (CPR - 1));
     d_kc[j] = 8 * c;
-    // a row-major-K operand: instruction g fills rows RT g .. RT g + RT - 1 of the [BK x BX] tile (RT = 512 /
-    // BX), 16-byte chunk (lane % (BX / 8)) of a row holding global chunk (lane % (BX / 8)) ^ 4 (row % 4); its K
-    // position is the row, and chunks that start past the matrix width load nothing
-    auto t_off = [&](int gg, int BX, int64_t ld, int x0, int width) {
-      const int cpr = BX / 8;
-      const int rk = (512 / BX) * gg + lane / cpr;
-      const int cc = (lane % cpr) ^ (4 * (rk & 3));
+    // a row-major-K operand: instruction g fills elements 512 g .. 512 g + 511 of the row-major [BK x BX] tile,
+    // lane l the 16-byte slot at element 512 g + 8 l: row rk, slot s, holding global chunk t_chunk(s, rk) (see
+    // t_slot); its K position is the row, and chunks that start past the matrix width load nothing
+    auto t_off = [&](int gg, auto BXC, int64_t ld, int x0, int width) {
+      constexpr int BX = decltype(BXC)::value, cpr = BX / 8;
+      const int e = 512 * gg + 8 * lane;
+      const int rk = e / BX, slot = (e % BX) / 8;
+      const int cc = (cpr & (cpr - 1)) == 0 ? slot ^ (4 * (rk & 3)) : (slot + cpr - 4 * (rk & 3)) % cpr;
       d_kc[j] = rk;
       return x0 + 8 * cc < width ? 2u * (uint32_t)(rk * ld + 8 * cc) : kOOB;
     };
     if (g < GA && AT) {
-      d_off[j] = t_off(g, BM, p.lda, m0, p.M);
+      d_off[j] = t_off(g, std::integral_constant<int, BM>{}, p.lda, m0, p.M);
     } else if (g >= GA && g < GA + C::GB && BT) {
-      d_off[j] = t_off(g - GA, BN, p.ldb, nbase, p.Nout);
+      d_off[j] = t_off(g - GA, std::integral_constant<int, BN>{}, p.ldb, nbase, p.Nout);
     } else if (g < GA) {
       if (p.a_rows) {
         const int m = m0 + r;
@@ -352,7 +364,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int k = 16 * ks + 8 * h + 4 * r + (i >> 2);
-      const int off = k * BX + (((x >> 3) ^ (4 * (i >> 2))) << 3) + (x & 7);
+      const int off = k * BX + (t_slot<BX>(x >> 3, i >> 2) << 3) + (x & 7);
       v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(s + off));
     }
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -870,5 +882,6 @@ using BigTile = Cfg<MTP_BIG_CFG>;              // 8 waves (wave tile 128 x 64), 
 using WideTile = Cfg<MTP_WIDE_CFG>;            // 8 waves (64 x 96), 112 KB
 using HalfTile = Cfg<MTP_HALF_CFG>;            // 8 waves (64 x 64), 96 KB
 using SmallTile = Cfg<MTP_SMALL_CFG>;          // 8 waves (32 x 64), 128 KB
+using SmallTTile = Cfg<128, 128, 4, 2, 32, 4, true>;  // row-major-K operands: 8 waves (32 x 64), 64 KB
 
 }  // namespace mtp

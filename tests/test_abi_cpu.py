@@ -27,7 +27,7 @@ def _gpu_present():
 def test_library_exports_every_header_symbol():
     L = mtp.lib()
     names = mtp.header_symbols()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", mtp.LIB_PATH], capture_output=True, text=True).stdout
@@ -361,3 +361,13 @@ def test_fp8_scratch_size_matches_header():
     with open(mtp.HEADER) as f:
         m = re.search(r"#define MTP_FP8_WS_FLOATS (\d+)", f.read())
     assert m and int(m.group(1)) == mtp.FP8_WS_FLOATS
+
+
+def test_gemm_plan_backward_rejects_and_needs_a_device():
+    L = mtp.lib()
+    o = [ctypes.c_int(0) for _ in range(3)]
+    ptrs = [ctypes.addressof(x) for x in o]
+    assert L.mtp_gemm_plan_backward(0, 8, 8, 0, *ptrs) == SHAPE
+    assert L.mtp_gemm_plan_backward(8, 8, 8, 1, None, ptrs[1], ptrs[2]) == NULL
+    if not _gpu_present():
+        assert L.mtp_gemm_plan_backward(8, 8, 8, 0, *ptrs) == UNSUPPORTED

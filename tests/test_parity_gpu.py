@@ -192,13 +192,24 @@ def test_split_schedule_gelu_matches_one_tile_per_workgroup():
 # ----------------------------------------------------------------------------- backward GEMMs
 # dX = dY . Wt and dWt = dY^T . X read the row-major-K operands (Wt for dgrad; dY and X for wgrad) in place
 # through the LDS transpose load.  Integer-valued inputs make every sum exact, so fp32 results equal the
-# oracle's and bf16 ones its round-to-nearest-even.  The split cases are shapes the planner splits (the
-# backward plan restricted to the 256 x 256 and 256 x 128 tiles equals the forward one when that picks one
-# of them).
-def _split_plan(M, N, K):
-    pl = mtp.mtp_gemm_plan(M, N, K)
-    assert pl[:2] in ((256, 256), (256, 128)) and pl[2] > 1, pl
+# oracle's and bf16 ones its round-to-nearest-even.  The split cases are shapes whose backward plan is
+# split-K.
+def _split_plan(M, N, K, wgrad=False):
+    pl = mtp.mtp_gemm_plan_backward(M, N, K, wgrad)
+    assert pl[2] > 1, pl
     return pl
+
+
+def test_backward_plans_cover_every_transposed_tile():
+    # (output rows, output columns, contraction) -> (tile_m, tile_n, split): one-tile-per-workgroup and
+    # split-K plans of each of the three transposed tiles
+    seen = {mtp.mtp_gemm_plan_backward(*s, wg) for s in [(8192, 8192, 1024), (4096, 1024, 3072), (300, 400, 4096),
+                                                          (2048, 12288, 6144), (1024, 4096, 4096), (512, 512, 512),
+                                                          (4096, 3072, 4096), (2048, 1536, 12288)]
+            for wg in (False, True)}
+    tiles = {(a, b) for a, b, _ in seen}
+    assert {(256, 256), (256, 192), (128, 128)} <= tiles, seen
+    assert any(sp > 1 for *_, sp in seen) and any(sp == 0 for *_, sp in seen), seen
 
 
 def _pitch(n):
@@ -250,7 +261,7 @@ def test_dgrad_integer_exact(M, N, K, split):
 def test_wgrad_integer_exact(M, N, K, split, sampled):
     say("wgrad int", M, N, K)
     if split:
-        _split_plan(N, K, M)
+        _split_plan(N, K, M, True)
     dYb, Xb = synth.ternary_bf16(301, M, N), synth.ternary_bf16(302, M, K)
     dY, X = _dev_pad(dYb), _dev_pad(Xb)
     W0 = synth.ternary_bf16(303, N, K)
@@ -264,6 +275,26 @@ def test_wgrad_integer_exact(M, N, K, split, sampled):
     R = oracle.linear_wgrad(np.ascontiguousarray(dYb[:, rows]), Xb)
     assert np.array_equal(dW.cpu().numpy()[rows].astype(np.float64), R)
     assert np.array_equal(dWa.cpu().numpy()[rows].astype(np.float64), R + widen_bits(W0[rows]))
+
+
+@pytest.mark.parametrize("Mo,No,Kc,plan", [(4096, 3072, 1024, (256, 192, 0)), (2048, 1536, 8192, (256, 192, 4))])
+def test_backward_wide_tile_integer_exact(Mo, No, Kc, plan):
+    # the 256 x 192 tile's transposed form (rows of 24 chunks, rotated slots), one tile per workgroup and
+    # split-K: dgrad with output [Mo x No] and contraction Kc (that tile), and wgrad of the same output shape
+    # (its own plan)
+    say("backward wide", Mo, No, Kc)
+    assert mtp.mtp_gemm_plan_backward(Mo, No, Kc) == plan
+    dYb, Wb = synth.ternary_bf16(421, Mo, Kc), synth.ternary_bf16(422, Kc, No)
+    dX = torch.empty(Mo, No, dtype=torch.bfloat16, device="cuda")
+    mtp.mtp_linear_dgrad(_dev_pad(dYb), _dev_pad(Wb), None, False, dX)
+    gY, gX = synth.ternary_bf16(423, Kc, Mo), synth.ternary_bf16(424, Kc, No)
+    dW = torch.empty(Mo, No, dtype=torch.float32, device="cuda")
+    mtp.mtp_linear_wgrad(_dev_pad(gY), _dev_pad(gX), dW)
+    torch.cuda.synchronize()
+    rows = sample_rows(Mo, 48, 425)
+    assert np.array_equal(bits(dX)[rows], oracle.round_bf16(oracle.linear_dgrad(np.ascontiguousarray(dYb[rows]), Wb)))
+    R = oracle.linear_wgrad(np.ascontiguousarray(gY[:, rows]), gX)
+    assert np.array_equal(dW.cpu().numpy()[rows].astype(np.float64), R)
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 4096, 400), (520, 136, 1030), (4096, 1024, 1024)])
@@ -527,6 +558,123 @@ def test_fp8_end_to_end_matches_oracle(M, N, K, act):
     R = oracle.fp8_linear(np.ascontiguousarray(xc[rows]), xs, wc, ws, bb, act)
     G = bits(Y)[rows]
     _close(widen_bits(G), R, "fp8 end to end")
+    assert _exact_bits_frac(G, R) >= EXACT_FRAC_MIN
+
+
+# ----------------------------------------------------------------------------- NEXT rows at the workloads' sizes
+# The dense workloads' linears at full size, with the operands the benchmark's measurement uses (same
+# generator keys, hence the same launch plans), checked on sampled rows the oracle computes one by one.
+def _rows_of(seed, rows, cols, sigma):
+    return np.concatenate([synth.normal_bf16(seed, 1, cols, sigma, r0=r) for r in rows])
+
+
+@pytest.mark.parametrize("index", [1, 2, 3])
+def test_backward_full_size(index):
+    w = configs.by_index(index)
+    seen = set()
+    for i, (label, M, N, K) in enumerate(w.gemms):
+        if label in seen:
+            continue
+        seen.add(label)
+        say("backward full size", w.name, label, M, N, K)
+        X = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        Wt = torch.empty(N, K, dtype=torch.bfloat16, device="cuda")
+        dY = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        synth.gpu_normal_bf16_(X, 9001 + 3 * i, 1.0)
+        synth.gpu_normal_bf16_(Wt, 9002 + 3 * i, 0.02)
+        synth.gpu_normal_bf16_(dY, 9003 + 3 * i, 1.0)
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        dW = torch.zeros(N, K, dtype=torch.float32, device="cuda")
+        mtp.mtp_linear_dgrad(dY, Wt, None, False, dX)
+        mtp.mtp_linear_wgrad(dY, X, dW, True)
+        torch.cuda.synchronize()
+        Wh = synth.normal_bf16(9002 + 3 * i, N, K, 0.02)
+        rows = sample_rows(M, 24, 500 + i)
+        R = oracle.linear_dgrad(_rows_of(9003 + 3 * i, rows, N, 1.0), Wh)
+        G = bits(dX)[rows]
+        _close(widen_bits(G), R, f"{label} dgrad")
+        assert _exact_bits_frac(G, R) >= EXACT_FRAC_MIN
+        del Wh
+        cols = sample_rows(N, 24, 600 + i)
+        dYh = synth.normal_bf16(9003 + 3 * i, M, N, 1.0)
+        R = oracle.linear_wgrad(np.ascontiguousarray(dYh[:, cols]), synth.normal_bf16(9001 + 3 * i, M, K, 1.0))
+        _close(dW.cpu().numpy()[cols], R, f"{label} wgrad")
+        del X, Wt, dY, dX, dW, dYh
+
+
+@pytest.mark.parametrize("index", [1, 2, 3])
+def test_norm_and_bda_full_size(index):
+    w = configs.by_index(index)
+    shapes = {label: (M, N, K) for label, M, N, K in w.gemms}
+    kind = oracle.NORM_RMS if w.dims.get("act") == oracle.ACT_SWIGLU else oracle.NORM_LAYER
+    M, N, H = shapes["qkv"]
+    say("norm full size", w.name, M, N, H, kind)
+    Wb = synth.normal_bf16(9102, N, H, 0.02)
+    gb = synth.affine_bf16(9103, 1, H, 1.0, 0.1)[0]
+    betab = None if kind == oracle.NORM_RMS else synth.normal_bf16(9104, 1, H, 0.1)[0]
+    X = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
+    synth.gpu_normal_bf16_(X, 9101, 1.0)
+    Wf = torch.empty(N, H, dtype=torch.bfloat16, device="cuda")
+    colsum = torch.empty(N, dtype=torch.float32, device="cuda") if kind == oracle.NORM_LAYER else None
+    bias_f = torch.empty(N, dtype=torch.float32, device="cuda")
+    stats = torch.empty(M, 2, dtype=torch.float32, device="cuda")
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    mtp.mtp_norm_fold_weights(to_dev(Wb), to_dev(gb), None if betab is None else to_dev(betab), None, Wf, colsum,
+                              bias_f)
+    mtp.mtp_norm_stats(X, stats, kind, 1e-5)
+    mtp.mtp_norm_column_linear(X, stats, Wf, colsum, bias_f, Y)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 32, 700 + index)
+    R = oracle.norm_linear(_rows_of(9101, rows, H, 1.0), gb, betab, kind, 1e-5, Wb)
+    _close(widen_bits(bits(Y)[rows]), R, "norm qkv")
+    del X, Wf, Y, Wb
+    M2, N2, K2 = shapes["fc2"]
+    say("bda full size", w.name, M2, N2, K2)
+    Z = torch.empty(M2, K2, dtype=torch.bfloat16, device="cuda")
+    W2 = torch.empty(N2, K2, dtype=torch.bfloat16, device="cuda")
+    Rs = torch.empty(M2, N2, dtype=torch.bfloat16, device="cuda")
+    synth.gpu_normal_bf16_(Z, 9105, 1.0)
+    synth.gpu_normal_bf16_(W2, 9106, 0.02)
+    synth.gpu_normal_bf16_(Rs, 9107, 1.0)
+    kb = synth.keep_bits(9108, M2, N2, 0.1)
+    Y2 = torch.empty(M2, N2, dtype=torch.bfloat16, device="cuda")
+    mtp.mtp_row_linear_bda(Z, W2, Rs, Y2, keep=torch.from_numpy(kb).cuda(), p_drop=0.1)
+    torch.cuda.synchronize()
+    rows = sample_rows(M2, 32, 800 + index)
+    P = oracle.linear(_rows_of(9105, rows, K2, 1.0), synth.normal_bf16(9106, N2, K2, 0.02))
+    ref = oracle.bias_dropout_add(P, None, kb[rows], 0.1, _rows_of(9107, rows, N2, 1.0))
+    G = bits(Y2)[rows]
+    _close(widen_bits(G), ref, "bda fc2")
+    assert _exact_bits_frac(G, ref) >= EXACT_FRAC_MIN
+
+
+@pytest.mark.parametrize("index", [1, 2, 3])
+def test_fp8_fc1_full_size(index):
+    w = configs.by_index(index)
+    i, (label, M, N, K) = next((j, g) for j, g in enumerate(w.gemms) if g[0] == "fc1")
+    act = mtp.ACT_SWIGLU if w.dims.get("act") == mtp.ACT_SWIGLU else mtp.ACT_NONE
+    say("fp8 full size", w.name, label, M, N, K, act)
+    X = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    Wt = torch.empty(N, K, dtype=torch.bfloat16, device="cuda")
+    synth.gpu_normal_bf16_(X, 9201 + 2 * i, 1.0)
+    synth.gpu_normal_bf16_(Wt, 9202 + 2 * i, 0.02)
+    Xq = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    Wq = torch.empty(N, K, dtype=torch.uint8, device="cuda")
+    ws, sx, sw = torch.zeros(mtp.FP8_WS_FLOATS, device="cuda"), _scalar(0.0), _scalar(0.0)
+    mtp.mtp_fp8_quantize(Wt, Wq, ws, sw)
+    mtp.mtp_fp8_quantize(X, Xq, ws, sx)
+    nout = N // 2 if act == mtp.ACT_SWIGLU else N
+    Y = torch.empty(M, nout, dtype=torch.bfloat16, device="cuda")
+    mtp.mtp_fp8_column_linear(Xq, sx, Wq, sw, None, Y, act)
+    torch.cuda.synchronize()
+    xc, xs = oracle.fp8_quantize(synth.normal_bf16(9201 + 2 * i, M, K, 1.0))
+    wc, wsv = oracle.fp8_quantize(synth.normal_bf16(9202 + 2 * i, N, K, 0.02))
+    rows = sample_rows(M, 32, 900 + index)
+    assert float(sx.item()) == xs and float(sw.item()) == wsv
+    assert np.array_equal(Xq.cpu().numpy()[rows], xc[rows]) and np.array_equal(Wq.cpu().numpy(), wc)
+    R = oracle.fp8_linear(np.ascontiguousarray(xc[rows]), xs, wc, wsv, None, act)
+    G = bits(Y)[rows]
+    _close(widen_bits(G), R, "fp8 fc1")
     assert _exact_bits_frac(G, R) >= EXACT_FRAC_MIN
 
 
