@@ -455,3 +455,18 @@ def fp8_linear(Xq, x_scale_inv: float, Wq, w_scale_inv: float, bias=None, act: i
         return np.vectorize(gelu)(P)
     g, u = P[:, :nout], P[:, nout:]
     return np.vectorize(silu)(g) * u
+
+
+def fp8_quantize_delayed(X: np.ndarray, history, step: int):
+    """Delayed scaling (the pages' FP8 recipe: an amax history of configurable length, reduced by max; the
+    scale of this step comes from earlier steps' amaxes): s = fp32(448 / max(history)) (1 if that is 0),
+    codes = E4M3(fp32(x * s)) (saturating: values above the history's max clip to +-448), and this step's
+    amax = max |x| is recorded in slot step % len(history).  Returns (codes, scale_inv, new history)."""
+    h = np.asarray(history, dtype=np.float32)
+    x = widen(X).astype(np.float32)
+    hmax = np.float32(h.max()) if h.size else np.float32(0)
+    s = np.float32(E4M3_MAX) / hmax if hmax > 0 else np.float32(1)
+    codes = e4m3_encode((x * np.float32(s)).astype(np.float32))
+    new = h.copy()
+    new[step % len(h)] = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    return codes, float(np.float32(1) / np.float32(s)), new

@@ -617,3 +617,22 @@ def test_fp8_linear_reduces_to_the_bf16_linear_on_exact_values():
         np.testing.assert_allclose(oracle.fp8_linear(Xq, 1.0, Wq, 1.0, bb, act), oracle.linear(Xb, Wb, bb, act),
                                    rtol=1e-15, atol=1e-15)
     np.testing.assert_array_equal(oracle.fp8_linear(Xq, 2.0, Wq, 0.25, None), oracle.linear(Xb, Wb) * 0.5)
+
+
+def test_fp8_delayed_scaling_reduces_to_current_scaling_and_records_amax():
+    X = synth.normal_bf16(95, 5, 48, 2.0)
+    amax = np.abs(oracle.widen(X)).max()
+    codes, sinv = oracle.fp8_quantize(X)
+    # a history holding only this tensor's amax gives the current-scaling result
+    c2, s2, h2 = oracle.fp8_quantize_delayed(X, [amax, 0.0, amax / 2], step=4)
+    np.testing.assert_array_equal(c2, codes)
+    assert s2 == sinv and h2[1] == np.float32(amax) and h2[0] == np.float32(amax)
+    # a history max below the tensor's amax saturates the largest values at +-448
+    c3, s3, _ = oracle.fp8_quantize_delayed(X, [amax / 4], step=0)
+    assert s3 == float(np.float32(1) / (np.float32(448) / np.float32(amax / 4)))
+    big = np.abs(oracle.widen(X)) >= amax / 4
+    assert np.all(c3[big] & 0x7F == 0x7E) and big.sum() > 0
+    # an all-zero history means scale 1
+    c4, s4, _ = oracle.fp8_quantize_delayed(X, np.zeros(8), step=9)
+    assert s4 == 1.0
+    np.testing.assert_array_equal(c4, oracle.e4m3_encode(oracle.widen(X)))
