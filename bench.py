@@ -221,10 +221,17 @@ def fp8_gemms(w, timer):
         nout = N // 2 if act == mtp.ACT_SWIGLU else N
         Y = torch.empty(M, nout, dtype=torch.bfloat16, device="cuda")
         t_q = _median_us(timer, lambda: mtp.mtp_fp8_quantize(X, Xq, amax, sx))
+        hist = torch.full((16,), 4.5, dtype=torch.float32, device="cuda")
+        t_qd = _median_us(timer, lambda: mtp.mtp_fp8_quantize_delayed(X, Xq, hist, 3, amax, sx))
         t_g = _median_us(timer, lambda: mtp.mtp_fp8_column_linear(Xq, sx, Wq, sw, None, Y, act))
         fl = 2 * M * N * K
+        # HBM bytes: current scaling reads X twice (amax, then codes) and writes the codes; delayed scaling
+        # reads it once
+        qb, qdb = 5 * M * K, 3 * M * K
         per[label] = {"gemm_us": round(t_g, 2), "tflops": round(fl / (t_g * 1e-6) / 1e12, 1),
-                      "quantize_us": round(t_q, 2)}
+                      "quantize_us": round(t_q, 2), "quantize_gbs": round(qb / (t_q * 1e-6) / 1e9, 1),
+                      "quantize_delayed_us": round(t_qd, 2),
+                      "quantize_delayed_gbs": round(qdb / (t_qd * 1e-6) / 1e9, 1)}
         flop_total += fl
         us_total += t_g
         q_total += t_q

@@ -215,6 +215,13 @@ mtp_status mtp_row_linear_bda(const mtp_bf16* Z, int64_t ldz, const mtp_bf16* Wt
  */
 mtp_status mtp_fp8_quantize(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t K, uint8_t* Xq, int64_t ldq,
                             float* amax_ws, float* scale_inv, void* stream);
+/* Delayed scaling (the pages' recipe: an amax history, reduced by max): s = fp32(448 / max(amax_history[0 ..
+ * history_len-1])) (1 if 0), codes as mtp_fp8_quantize (values past the history's max saturate at +-448),
+ * one pass over X; afterwards this tensor's amax is stored in amax_history[step % history_len].  The history
+ * (device fp32, 1 <= history_len <= 4096) is the caller's; ws as in mtp_fp8_quantize. */
+mtp_status mtp_fp8_quantize_delayed(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t K, uint8_t* Xq, int64_t ldq,
+                                    float* amax_history, int history_len, int64_t step, float* ws, float* scale_inv,
+                                    void* stream);
 mtp_status mtp_fp8_column_linear(const uint8_t* Xq, int64_t ldx, const float* x_scale_inv, const uint8_t* Wq,
                                  int64_t ldw, const float* w_scale_inv, const mtp_bf16* bias, mtp_bf16* Y,
                                  int64_t ldy, int64_t M, int64_t N, int64_t K, mtp_act act, void* stream);

@@ -54,6 +54,7 @@ def lib():
             "mtp_release_workspaces": [],
             "mtp_norm_stats": [vp, i64, i64, i64, ci, ctypes.c_float, vp, vp],
             "mtp_fp8_quantize": [vp, i64, i64, i64, vp, i64, vp, vp, vp],
+            "mtp_fp8_quantize_delayed": [vp, i64, i64, i64, vp, i64, vp, ci, i64, vp, vp, vp],
             "mtp_fp8_column_linear": [vp, i64, vp, vp, i64, vp, vp, vp, i64, i64, i64, i64, ci, vp],
             "mtp_fp8_row_linear_partial": [vp, i64, vp, vp, i64, vp, vp, i64, ci, vp, vp, i64, i64, i64, i64, vp],
             "mtp_norm_fold_weights": [vp, i64, i64, i64, vp, vp, vp, ci, vp, i64, vp, vp, vp],
@@ -151,6 +152,15 @@ def mtp_fp8_quantize(X, Xq, amax_ws, scale_inv):
     M, K = X.shape
     _check("mtp_fp8_quantize", lib().mtp_fp8_quantize(_ptr(X), _ld(X), M, K, _ptr(Xq), _ld(Xq), _ptr(amax_ws),
                                                       _ptr(scale_inv), _stream(X)))
+    return Xq
+
+
+def mtp_fp8_quantize_delayed(X, Xq, amax_history, step, ws, scale_inv):
+    """E4M3 codes of X with the scale from max(amax_history); records X's amax in slot step % len."""
+    M, K = X.shape
+    _check("mtp_fp8_quantize_delayed", lib().mtp_fp8_quantize_delayed(
+        _ptr(X), _ld(X), M, K, _ptr(Xq), _ld(Xq), _ptr(amax_history), amax_history.numel(), step, _ptr(ws),
+        _ptr(scale_inv), _stream(X)))
     return Xq
 
 

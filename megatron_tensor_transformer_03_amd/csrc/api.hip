@@ -298,6 +298,25 @@ mtp_status mtp_fp8_quantize(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t K
                   "fp8 quantize");
 }
 
+mtp_status mtp_fp8_quantize_delayed(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t K, uint8_t* Xq, int64_t ldq,
+                                    float* amax_history, int history_len, int64_t step, float* ws, float* scale_inv,
+                                    void* stream) {
+  TRY(check_dims(M, 8, K));
+  TRY(check_mat(X, "X", K, ldx));
+  TRY(check_mat(Xq, "Xq", K, ldq));
+  if (!amax_history || !ws || !scale_inv) return fail(MTP_ERR_NULL, "amax_history, ws and scale_inv are required");
+  if ((reinterpret_cast<uintptr_t>(amax_history) | reinterpret_cast<uintptr_t>(ws) |
+       reinterpret_cast<uintptr_t>(scale_inv)) & 3u)
+    return fail(MTP_ERR_ALIGN, "amax_history / ws / scale_inv are not 4-byte aligned");
+  if (history_len < 1 || history_len > 4096) return fail(MTP_ERR_SHAPE, "history_len %d is not in [1, 4096]", history_len);
+  if (step < 0) return fail(MTP_ERR_SHAPE, "step %lld is negative", (long long)step);
+  if (M * (K / 8) >= ((int64_t)1 << 31)) return fail(MTP_ERR_SHAPE, "X has 2^34 or more elements");
+  TRY(check_device());
+  return launched(mtp::fp8_quantize_delayed(X, ldx, (int)M, (int)K, Xq, ldq, amax_history, history_len, step, ws,
+                                            scale_inv, (hipStream_t)stream),
+                  "fp8 quantize (delayed scaling)");
+}
+
 // E4M3 operands: K, and the pitches in bytes, multiples of 16 (the kernels count pairs of codes)
 static mtp_status check_f8(const void* p, const char* name, int64_t K, int64_t ld, const float* sinv,
                            const char* sname) {

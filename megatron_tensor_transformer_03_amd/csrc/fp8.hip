@@ -108,6 +108,68 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
   }
 }
 
+// Delayed scaling: the scale comes from the max of an amax history (earlier steps), so one pass quantizes and
+// takes this tensor's max |x| at once (per-block maxima into the scratch; record_kernel then writes their
+// max into the history slot, after every block has read the history).
+__global__ __launch_bounds__(256) void quant_delayed_kernel(const uint16_t* __restrict__ X, int64_t ldx, int cpr,
+                                                            uint32_t total, const float* __restrict__ hist, int hlen,
+                                                            uint8_t* __restrict__ Q, int64_t ldq, float* scale_inv,
+                                                            float* __restrict__ part) {
+  float hm = 0.f;
+  for (int b = threadIdx.x; b < hlen; b += 256) hm = fmaxf(hm, hist[b]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) hm = fmaxf(hm, __shfl_xor(hm, o, 64));
+  __shared__ float red[4], red2[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = hm;
+  __syncthreads();
+  const float hmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = hmax > 0.f ? __fdiv_rn(448.f, hmax) : 1.f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale_inv = __fdiv_rn(1.f, s);
+  float m = 0.f;
+  const uint32_t stride = gridDim.x * 256u;
+  for (uint32_t c0 = blockIdx.x * 256u + threadIdx.x; c0 < total; c0 += kU * stride) {
+    uint4 v[kU];
+    uint32_t rr[kU], kk[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const uint32_t c = c0 + u * stride;
+      rr[u] = c / (uint32_t)cpr;
+      kk[u] = 8 * (c - rr[u] * (uint32_t)cpr);
+      v[u] = c < total ? *reinterpret_cast<const uint4*>(X + (int64_t)rr[u] * ldx + kk[u]) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (c0 + u * stride >= total) break;
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      uint32_t o[2] = {0, 0};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float lo = lo_bf16(w[t]), hi = hi_bf16(w[t]);
+        m = fmaxf(m, fmaxf(fabsf(lo), fabsf(hi)));
+        const uint32_t a = e4m3_rne(__fmul_rn(lo, s)), b = e4m3_rne(__fmul_rn(hi, s));
+        o[t >> 1] |= (a | (b << 8)) << (16 * (t & 1));
+      }
+      *reinterpret_cast<uint2*>(Q + (int64_t)rr[u] * ldq + kk[u]) = make_uint2(o[0], o[1]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) red2[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red2[0], red2[1]), fmaxf(red2[2], red2[3]));
+}
+
+__global__ __launch_bounds__(256) void record_kernel(const float* __restrict__ part, int n, float* slot) {
+  float m = 0.f;
+  for (int b = threadIdx.x; b < n; b += 256) m = fmaxf(m, part[b]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) *slot = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
 }  // namespace
 
 hipError_t fp8_quantize(const uint16_t* X, int64_t ldx, int M, int K, uint8_t* Xq, int64_t ldq, float* ws,
@@ -117,6 +179,17 @@ hipError_t fp8_quantize(const uint16_t* X, int64_t ldx, int M, int K, uint8_t* X
   const int grid = (int)(blocks < (uint32_t)kFp8QuantBlocks ? blocks : (uint32_t)kFp8QuantBlocks);
   hipLaunchKernelGGL(amax_kernel, dim3(grid), dim3(256), 0, st, X, ldx, K / 8, total, ws);
   hipLaunchKernelGGL(quant_kernel, dim3(grid), dim3(256), 0, st, X, ldx, K / 8, total, ws, Xq, ldq, scale_inv);
+  return hipGetLastError();
+}
+
+hipError_t fp8_quantize_delayed(const uint16_t* X, int64_t ldx, int M, int K, uint8_t* Xq, int64_t ldq, float* hist,
+                                int hlen, int64_t step, float* ws, float* scale_inv, hipStream_t st) {
+  const uint32_t total = (uint32_t)((int64_t)M * (K / 8));
+  const uint32_t blocks = (total + 255) / 256;
+  const int grid = (int)(blocks < (uint32_t)kFp8QuantBlocks ? blocks : (uint32_t)kFp8QuantBlocks);
+  hipLaunchKernelGGL(quant_delayed_kernel, dim3(grid), dim3(256), 0, st, X, ldx, K / 8, total, hist, hlen, Xq, ldq,
+                     scale_inv, ws);
+  hipLaunchKernelGGL(record_kernel, dim3(1), dim3(256), 0, st, ws, grid, hist + step % hlen);
   return hipGetLastError();
 }
 

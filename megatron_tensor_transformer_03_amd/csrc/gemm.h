@@ -72,6 +72,9 @@ hipError_t gemm_f8(const GemmParams& p, int mode, hipStream_t st);
 constexpr int kFp8QuantBlocks = 1024;
 hipError_t fp8_quantize(const uint16_t* X, int64_t ldx, int M, int K, uint8_t* Xq, int64_t ldq, float* ws,
                         float* scale_inv, hipStream_t st);
+// Delayed scaling: s from the max of hist[0 .. hlen-1]; this tensor's amax then goes to hist[step % hlen].
+hipError_t fp8_quantize_delayed(const uint16_t* X, int64_t ldx, int M, int K, uint8_t* Xq, int64_t ldq, float* hist,
+                                int hlen, int64_t step, float* ws, float* scale_inv, hipStream_t st);
 // rows_upper: total rows over all groups (an upper bound is enough; spare tiles exit).
 hipError_t gemm_grouped(const GemmParams& p, int mode, int rows_upper, hipStream_t st);
 

@@ -27,7 +27,7 @@ def _gpu_present():
 def test_library_exports_every_header_symbol():
     L = mtp.lib()
     names = mtp.header_symbols()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", mtp.LIB_PATH], capture_output=True, text=True).stdout
@@ -371,3 +371,15 @@ def test_gemm_plan_backward_rejects_and_needs_a_device():
     assert L.mtp_gemm_plan_backward(8, 8, 8, 1, None, ptrs[1], ptrs[2]) == NULL
     if not _gpu_present():
         assert L.mtp_gemm_plan_backward(8, 8, 8, 0, *ptrs) == UNSUPPORTED
+
+
+def test_fp8_delayed_rejects():
+    L = mtp.lib()
+    q = lambda **kw: L.mtp_fp8_quantize_delayed(kw.get("X", P), 64, 4, kw.get("K", 64), kw.get("Xq", P2), 64,
+                                                kw.get("h", P3), kw.get("hl", 16), kw.get("step", 0), kw.get("ws", P4),
+                                                kw.get("sinv", P4 + 4096), None)
+    assert q(h=None) == NULL and q(ws=None) == NULL and q(sinv=None) == NULL
+    assert q(hl=0) == SHAPE and q(hl=5000) == SHAPE and q(step=-1) == SHAPE and q(K=60) == SHAPE
+    assert q(h=P3 + 2) == ALIGN
+    if not _gpu_present():
+        assert q() == UNSUPPORTED

@@ -488,6 +488,24 @@ def test_fp8_quantize_codes_bit_exact(M, K, sigma):
     assert torch.count_nonzero(Zq) == 0 and float(sinv.item()) == 1.0
 
 
+def test_fp8_delayed_scaling_matches_oracle():
+    # three steps over a history of length 2: codes and factors bit-exact, the history updated in place
+    M, K = 300, 1024
+    hist = torch.zeros(2, dtype=torch.float32, device="cuda")
+    hist_host = np.zeros(2, dtype=np.float32)
+    ws, sinv = torch.zeros(mtp.FP8_WS_FLOATS, device="cuda"), _scalar(0.0)
+    for step, sigma in enumerate((1.0, 4.0, 0.5)):
+        say("fp8 delayed", step, sigma)
+        Xb = synth.normal_bf16(431 + step, M, K, sigma)
+        Xq = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+        mtp.mtp_fp8_quantize_delayed(to_dev(Xb), Xq, hist, step, ws, sinv)
+        torch.cuda.synchronize()
+        codes, ref_sinv, hist_host = oracle.fp8_quantize_delayed(Xb, hist_host, step)
+        assert np.array_equal(Xq.cpu().numpy(), codes)
+        assert float(sinv.item()) == ref_sinv
+        assert np.array_equal(hist.cpu().numpy(), hist_host)
+
+
 @pytest.mark.parametrize("M,N,K,act", [
     (1, 8, 16, 0), (130, 200, 96, 0), (257, 129, 80, 1), (4100, 3000, 64, 0), (300, 400, 4096, 0),
     (900, 4100, 2048, 0), (200, 272, 160, 2),
