@@ -50,22 +50,13 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
   if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// fp32 -> E4M3, nearest with ties to even, saturating at +-448; NaN -> S.1111.111.
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return sign | 0x7Fu;
-  if (a >= 0x43E00000u) return sign | 0x7Eu;  // |v| >= 448
-  if (a < 0x3C800000u) {                      // |v| < 2^-6: multiples of 2^-9 (8 -> the first normal, code 8)
-    return sign | (uint32_t)rintf(__uint_as_float(a) * 512.f);
-  }
-  int e = (int)(a >> 23) - 127;               // -6 .. 8
-  uint32_t keep = (a >> 20) & 7u;
-  const uint32_t rest = a & 0xFFFFFu;
-  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ++keep;
-  if (keep == 8u) { keep = 0; ++e; }          // (448 <= |v| is excluded above, so e stays <= 8 here)
-  return sign | ((uint32_t)(e + 7) << 3) | keep;
+// Two fp32 -> E4M3 codes (nearest, ties to even: gfx950's v_cvt_pk_fp8_f32 in the default round mode) into
+// half `hi` of `old`; values are clamped to +-448 first, so the cast saturates (a value in (448, 464) rounds
+// to 448 either way).  X must be finite.
+__device__ __forceinline__ int cvt2(float a, float b, int old, int hi) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  return hi ? __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, true) : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
 }
 
 __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__ X, int64_t ldx, int cpr,
@@ -97,13 +88,10 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
     for (int u = 0; u < kU; ++u) {
       if (c0 + u * stride >= total) break;
       const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      uint32_t o[2] = {0, 0};
+      int o[2] = {0, 0};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t a = e4m3_rne(__fmul_rn(lo_bf16(w[t]), s)), b = e4m3_rne(__fmul_rn(hi_bf16(w[t]), s));
-        o[t >> 1] |= (a | (b << 8)) << (16 * (t & 1));
-      }
-      *reinterpret_cast<uint2*>(Q + (int64_t)rr[u] * ldq + kk[u]) = make_uint2(o[0], o[1]);
+      for (int t = 0; t < 4; ++t) o[t >> 1] = cvt2(__fmul_rn(lo_bf16(w[t]), s), __fmul_rn(hi_bf16(w[t]), s), o[t >> 1], t & 1);
+      *reinterpret_cast<uint2*>(Q + (int64_t)rr[u] * ldq + kk[u]) = make_uint2((uint32_t)o[0], (uint32_t)o[1]);
     }
   }
 }
@@ -141,15 +129,14 @@ __global__ __launch_bounds__(256) void quant_delayed_kernel(const uint16_t* __re
     for (int u = 0; u < kU; ++u) {
       if (c0 + u * stride >= total) break;
       const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      uint32_t o[2] = {0, 0};
+      int o[2] = {0, 0};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const float lo = lo_bf16(w[t]), hi = hi_bf16(w[t]);
         m = fmaxf(m, fmaxf(fabsf(lo), fabsf(hi)));
-        const uint32_t a = e4m3_rne(__fmul_rn(lo, s)), b = e4m3_rne(__fmul_rn(hi, s));
-        o[t >> 1] |= (a | (b << 8)) << (16 * (t & 1));
+        o[t >> 1] = cvt2(__fmul_rn(lo, s), __fmul_rn(hi, s), o[t >> 1], t & 1);
       }
-      *reinterpret_cast<uint2*>(Q + (int64_t)rr[u] * ldq + kk[u]) = make_uint2(o[0], o[1]);
+      *reinterpret_cast<uint2*>(Q + (int64_t)rr[u] * ldq + kk[u]) = make_uint2((uint32_t)o[0], (uint32_t)o[1]);
     }
   }
 #pragma unroll
