@@ -242,6 +242,45 @@ def fp8_gemms(w, timer):
             "quantize_us": round(q_total, 2)}
 
 
+def prenorm_layer(w, timer, steps=10):
+    """The composed TP = 1 pre-norm layer (norm-folded QKV, attention bias-dropout-add, norm-folded fc1, MLP
+    bias-dropout-add; core attention aside): microseconds per step and per launch."""
+    import torch
+    import megatron_tensor_transformer_03_amd as mtp
+    from megatron_tensor_transformer_03_amd.layer import PreNormLayer
+    import synth
+    if w.dims.get("p", 1) != 1 or "nq" not in w.dims or "E" in w.dims:
+        return None
+    hx = synth.prenorm_inputs(w)
+    dev = lambda a: torch.from_numpy(a.view("int16")).cuda().view(torch.bfloat16)
+    ex = {k: dev(hx[k]) for k in ("g1", "beta1", "g2", "beta2")}
+    ex.update(keep1=torch.from_numpy(hx["keep1"]).cuda(), keep2=torch.from_numpy(hx["keep2"]).cuda(),
+              p_drop=hx["p_drop"])
+    kind = mtp.NORM_RMS if w.dims.get("act") == mtp.ACT_SWIGLU else mtp.NORM_LAYER
+    layer = PreNormLayer(w.dims, synth.device_inputs(w), ex, kind)
+    for _ in range(3):
+        layer.step()
+    torch.cuda.synchronize()
+    per = {}
+    for _ in range(3):
+        marks = []
+        layer.step(lambda label: marks.append((label, timer.record())))
+        torch.cuda.synchronize()
+        for (label, e0), (_, e1) in zip(marks[:-1], marks[1:]):
+            per.setdefault(label, []).append(1000 * timer.elapsed_ms(e0, e1))
+        timer.release(e for _, e in marks)
+    e0 = timer.record()
+    for _ in range(steps):
+        layer.step()
+    e1 = timer.record()
+    torch.cuda.synchronize()
+    us = 1000 * timer.elapsed_ms(e0, e1) / steps
+    timer.release([e0, e1])
+    gemm_flop = sum(2 * m * n * k for _, m, n, k in w.gemms)
+    return {"us_per_step": round(us, 2), "gemm_tflops": round(gemm_flop / (us * 1e-6) / 1e12, 1),
+            "per_launch_us": {k: round(sum(v) / len(v), 2) for k, v in per.items()}}
+
+
 def cpu_baseline(w, budget_s):
     """The oracle on a bounded row sample of the same workload; TFLOP/s of algorithmic work done."""
     import numpy as np
@@ -433,6 +472,7 @@ def main():
     bwd = None if ("E" in w.dims or args.no_backward) else backward_gemms(w, timer)
     nb = None if ("E" in w.dims or args.no_backward) else norm_and_bda(w, timer)
     f8 = None if ("E" in w.dims or args.no_backward) else fp8_gemms(w, timer)
+    pre = None if args.no_backward else prenorm_layer(w, timer)
 
     out = {
         "metric": METRIC,
@@ -454,7 +494,8 @@ def main():
                    "per_gemm_us": {lb: round(1000 * v, 2) for lb, v in avg.items()},
                    "per_gemm_tflops": {lb: round(flop_by_label[lb] / (avg[lb] * 1e-3) / 1e12, 1)
                                        for lb in avg if lb in flop_by_label},
-                   "aux_kernels": aux, "backward_gemms": bwd, "norm_and_bda": nb, "fp8_gemms": f8},
+                   "aux_kernels": aux, "backward_gemms": bwd, "norm_and_bda": nb, "fp8_gemms": f8,
+                   "prenorm_layer": pre},
         "roofline": {"bound": "mfma", "kernel": dom, "kernel_us": round(1000 * dom_avg, 2),
                      "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -104,3 +104,70 @@ class RankForward:
             fn()
         mark(None)
         return self.out
+
+
+class PreNormLayer:
+    """A whole pre-norm layer at TP = 1, core attention aside (its context is an input): the layer spec of the
+    pages ("快速入门", model implementation: input norm fused into the QKV linear, self_attn_bda,
+    pre_mlp_layernorm, MLP, mlp_bda) as C-ABI calls:
+        stats1 = norm(X);  qkv = norm-folded QKV linear (+ RoPE);  h1 = X + dropout(ctx . Wo^T + bo)
+        stats2 = norm(h1); Z = act(norm-folded fc1(h1));           out = h1 + dropout(Z . W2^T + b2)
+    The norms' scales and shifts are folded into copies of the column weights once, at construction
+    (mtp_norm_fold_weights), as after each weight update.  ``extra`` holds device tensors g1, beta1, g2,
+    beta2 (beta None for RMSNorm), keep1, keep2 (packed keep bits) and the float p_drop; ``kind`` is
+    mtp.NORM_LAYER or mtp.NORM_RMS."""
+
+    def __init__(self, dims: dict, inputs: dict, extra: dict, kind: int = mtp.NORM_LAYER, eps: float = 1e-5):
+        import torch
+        if dims.get("p", 1) != 1 or "ctx" not in inputs or "nq" not in dims:
+            raise ValueError("the composed layer needs a TP = 1 dense workload with attention context")
+        self.d, self.t, self.x, self.kind, self.eps = dims, inputs, extra, kind, eps
+        dev = inputs["X"].device
+        bf, f32 = torch.bfloat16, torch.float32
+        M, H = dims["M"], dims["H"]
+        ln = kind == mtp.NORM_LAYER
+
+        def fold(Wt, g, beta, bias):
+            Wf = torch.empty_like(Wt)
+            cs = torch.empty(Wt.shape[0], dtype=f32, device=dev) if ln else None
+            bf_ = torch.empty(Wt.shape[0], dtype=f32, device=dev)
+            mtp.mtp_norm_fold_weights(Wt, g, beta if ln else None, bias, Wf, cs, bf_)
+            return Wf, cs, bf_
+
+        self.qkv_w = fold(inputs["Wqkv_t"], extra["g1"], extra["beta1"], inputs.get("bqkv"))
+        self.fc1_w = fold(inputs["W1t"], extra["g2"], extra["beta2"], inputs.get("b1"))
+        nq, ng, d = dims["nq"], dims["ng"], dims["d"]
+        act = dims["act"]
+        F = dims["F"]
+        self.out = dict(stats1=torch.empty(M, 2, dtype=f32, device=dev), stats2=torch.empty(M, 2, dtype=f32, device=dev),
+                        qkv=torch.empty(M, (nq + 2 * ng) * d, dtype=bf, device=dev),
+                        h1=torch.empty(M, H, dtype=bf, device=dev),
+                        Z=torch.empty(M, F, dtype=bf, device=dev),
+                        out=torch.empty(M, H, dtype=bf, device=dev))
+        if "rope" in dims:
+            self.positions = torch.arange(M, dtype=torch.int32, device=dev)
+        self.act = act
+
+    def calls(self):
+        d, t, x, o = self.d, self.t, self.x, self.out
+        out = [("norm1", lambda: mtp.mtp_norm_stats(t["X"], o["stats1"], self.kind, self.eps)),
+               ("qkv", lambda: mtp.mtp_norm_column_linear(t["X"], o["stats1"], *self.qkv_w, o["qkv"]))]
+        if "rope" in d:
+            r = d["rope"]
+            out.append(("rope", lambda: mtp.mtp_rope_qk(o["qkv"], self.positions, d["nq"], d["ng"], d["d"],
+                                                        r["rotary_dim"], r["base"], r["interleaved"])))
+        out += [("attn_bda", lambda: mtp.mtp_row_linear_bda(t["ctx"], t["Wo_t"], t["X"], o["h1"], bias=t.get("bo"),
+                                                             keep=x["keep1"], p_drop=x["p_drop"])),
+                ("norm2", lambda: mtp.mtp_norm_stats(o["h1"], o["stats2"], self.kind, self.eps)),
+                ("fc1", lambda: mtp.mtp_norm_column_linear(o["h1"], o["stats2"], *self.fc1_w, o["Z"], self.act)),
+                ("mlp_bda", lambda: mtp.mtp_row_linear_bda(o["Z"], t["W2t"], o["h1"], o["out"], bias=t.get("b2"),
+                                                           keep=x["keep2"], p_drop=x["p_drop"]))]
+        return out
+
+    def step(self, mark=None):
+        mark = mark or (lambda label: None)
+        for label, fn in self.calls():
+            mark(label)
+            fn()
+        mark(None)
+        return self.out

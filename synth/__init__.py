@@ -176,3 +176,15 @@ def host_rows(spec, rows=None):
     else:
         out = np.concatenate([gen(r, 1) for r in rows], axis=0)
     return out if len(spec.shape) == 2 else out.reshape(-1)
+
+
+def prenorm_inputs(workload, p_drop: float = 0.1) -> dict:
+    """Host inputs of the pre-norm layer composition of a TP = 1 workload, beyond its GEMM operands: the
+    two norms' scales (bf16 near one) and shifts, and the two dropout keep masks (the random draws of the
+    attention and MLP bias-dropout-add).  Keys 1000 * workload + 50 .. 55."""
+    d = workload.dims
+    M, H = d["M"], d["H"]
+    base = 1000 * (2 if workload.name.startswith("gpt345m") else 9) + 50
+    return dict(g1=affine_bf16(base, 1, H, 1.0, 0.1)[0], beta1=normal_bf16(base + 1, 1, H, 0.1)[0],
+                g2=affine_bf16(base + 2, 1, H, 1.0, 0.1)[0], beta2=normal_bf16(base + 3, 1, H, 0.1)[0],
+                keep1=keep_bits(base + 4, M, H, p_drop), keep2=keep_bits(base + 5, M, H, p_drop), p_drop=p_drop)
