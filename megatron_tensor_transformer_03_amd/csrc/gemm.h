@@ -50,12 +50,13 @@ struct GemmParams {
   const float* f8_scale_b = nullptr;
   float* sk_ws = nullptr;           // split schedule: partial-tile slots (set at launch)
   int sk_chunks = 0;                // split schedule: K chunks per tile
+  int sk_dp_tiles = 0;              // split schedule: leading tiles run whole (a multiple of the grid)
   int* sk_cnt = nullptr;            // split schedule: per-tile arrival counters, zero between launches
 };
 
 // Tile and schedule of a launch (split_groups 0: one workgroup per tile).
 struct GemmPlan {
-  int bm = 0, bn = 0, split_groups = 0, id = 0, split_chunks = 0;
+  int bm = 0, bn = 0, split_groups = 0, id = 0, split_chunks = 0, dp_tiles = 0;
 };
 // row_major_k: 0 both operands K-contiguous; 1 B row-major-K (dgrad); 2 both row-major-K (wgrad)
 GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k = 0, bool allow_small = true);

@@ -64,18 +64,31 @@ hipError_t split_workspace(hipStream_t st, size_t ws_bytes, int64_t cnt_n, float
   return hipSuccess;
 }
 
-// Schedule choice.  One workgroup per tile: the time is the number of waves of tiles over the CUs times
-// the time of one tile (BM * BN / efficiency, the measured relative MFMA efficiency of the tile shapes on
-// large K).  Split-K: every tile's K range in S chunks, one workgroup per CU working through the (tile,
-// chunk) units, each chunk's partial sums added by the tile's last finisher; the time is the number of
-// waves of units times the time of a chunk plus fixed costs.  Wave quantisation is large at the shard
-// shapes of a tensor-parallel layer: 4096 x 1280 is 80 tiles of 256 x 256 (31% of the CUs busy) but 240
-// units in 3 chunks.
+// Schedule choice, by a cost model in microseconds.  One workgroup per tile: (waves of tiles over the CUs) x
+// (tile time), tile time = 2 BM BN K / (efficiency x R), R the sustained bf16 rate of one CU and efficiency
+// the tile shape's measured rate relative to the 256 x 256 tile.  Split-K: every tile's K range in S chunks,
+// one workgroup per CU working through the (tile, chunk) units, each chunk's fp32 partial tile written to
+// the workspace and read back by the tile's last finisher: (waves of units) x (chunk time + pipeline fill)
+// plus that partial traffic, tiles x S x (partial tile bytes) x 2, at the bandwidth BW it streams at.  The
+// traffic term is what makes split-K lose on short K (4096 x 1024 x 1024: 134 MB of partials for a 16 MB
+// output) and win on long K with few tiles (4096 x 1280 x 8192: 80 tiles of 256 x 256, 31% of the CUs
+// busy, 240 units in 3 chunks).  Hybrid: whole waves of tiles one per workgroup, then only the remaining
+// tiles split.  R and BW were fitted to the measured times of these schedules at the workloads' shapes
+// (within ~10%).
 GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k, bool allow_small) {
   struct Opt { int bm, bn; double eff; int id; int ns_bk; int64_t slot_bytes; };
-  const Opt opts[] = {{256, 256, 1.00, 0, 128, 256 << 10}, {256, 192, 0.95, 1, 128, 192 << 10},
-                      {256, 128, 0.85, 2, 128, 128 << 10}, {128, 128, 0.72, 3, 256, 0},
+  // Relative efficiencies.  The 256 x 192 tile's differs by board: on some MI355X boards it runs at 0.9-1.1
+  // of the 256 x 256 tile's rate per output, on others at 0.6-0.75 (the 256 x 256 tile with 64 x 128 wave
+  // tiles holds its rate on both); the forward planner takes the low figure, so it picks the 256 x 256 tile
+  // wherever the two differ by less than that (at most 9% lost on the boards where 256 x 192 is fast, up to
+  // 40% gained on the others).  The backward figures were measured on the transposed forms.
+  const double wide_eff = row_major_k ? 0.95 : 0.70;
+  const double half_eff = row_major_k ? 0.85 : 0.75;
+  const Opt opts[] = {{256, 256, 1.00, 0, 128, 256 << 10}, {256, 192, wide_eff, 1, 128, 192 << 10},
+                      {256, 128, half_eff, 2, 128, 128 << 10}, {128, 128, 0.72, 3, 256, 0},
                       {128, 128, 0.72, 4, 128, 64 << 10}};
+  constexpr double kR = 5.5e12 * 1e-6;   // FLOP per microsecond of one CU
+  constexpr double kBW = 3.0e12 * 1e-6;  // bytes per microsecond of the partial-tile traffic
   const int cus = cu_count();
   GemmPlan best;
   best.bm = 128; best.bn = 128; best.id = 3;
@@ -91,18 +104,32 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k
     if (!allow_small && o.id == 3) continue;                 // (its K step is 64 two-byte units)
     const int64_t nbo = mode == MODE_SWIGLU ? o.bn / 2 : o.bn;
     const int64_t tiles = ((M + o.bm - 1) / o.bm) * ((Nout + nbo - 1) / nbo);
-    const double tile_t = o.bm * o.bn / o.eff;
+    // (the backward products keep the relative model they were tuned with: tile time o.bm o.bn / eff, a
+    // per-tile cost of 0.03 tile per chunk for the partial sums, no hybrid)
+    const bool fwd = row_major_k == 0;
+    const double tile_t = fwd ? 2.0 * o.bm * o.bn * (double)K / (o.eff * kR) : o.bm * o.bn / o.eff;
+    const int64_t full_waves = tiles / (cus > 0 ? cus : 1);
     const double t_dp = (double)((tiles + cus - 1) / (cus > 0 ? cus : 1)) * tile_t;
-    if (t_dp < best_t * 0.999) { best_t = t_dp; best = GemmPlan{o.bm, (int)nbo, 0, o.id, 0}; }
-    // split-K: S chunks of at least 4 ring passes; per unit a fixed cost of about 1.5 passes (pipeline fill,
-    // partial store), and per tile the reads of its S partial sums
+    if (t_dp < best_t * 0.999) { best_t = t_dp; best = GemmPlan{o.bm, (int)nbo, 0, o.id, 0, 0}; }
+    // split-K (all tiles, or the tiles past the whole waves): S chunks of at least 4 ring passes; per unit
+    // a pipeline fill of about 1.5 passes; chosen only when clearly faster
     const int64_t passes = (K + o.ns_bk - 1) / o.ns_bk;
     if (o.slot_bytes == 0 || cus < 8 || cus % 8 != 0) continue;
-    for (int S : {2, 3, 4, 5, 6, 8}) {
-      if (passes < 4 * S || tiles * S * o.slot_bytes > ((int64_t)512 << 20)) continue;
-      const int64_t waves = (tiles * S + cus - 1) / cus;
-      const double t_sk = waves * tile_t * (1.0 / S + 1.5 / passes) + tile_t * 0.03 * S;
-      if (t_sk < best_t * 0.95) { best_t = t_sk; best = GemmPlan{o.bm, (int)nbo, cus, o.id, S}; }
+    for (int hybrid = 0; hybrid < 2; ++hybrid) {
+      const int64_t dp_tiles = hybrid ? full_waves * cus : 0;
+      const int64_t split_tiles = tiles - dp_tiles;
+      // (the hybrid form was measured on the 256 x 256 tile only)
+      if (hybrid && (!fwd || o.id != 0 || dp_tiles == 0 || split_tiles == 0)) continue;
+      for (int S : {2, 3, 4, 5, 6, 8}) {
+        if (passes < 4 * S || split_tiles * S * o.slot_bytes > ((int64_t)512 << 20)) continue;
+        const int64_t waves = (split_tiles * S + cus - 1) / cus;
+        const double t_sk = full_waves * hybrid * tile_t + waves * tile_t * (1.0 / S + 1.5 / passes) +
+                            (fwd ? 2.0 * split_tiles * S * o.slot_bytes / kBW : tile_t * 0.03 * S);
+        if (t_sk < best_t * 0.95) {
+          best_t = t_sk;
+          best = GemmPlan{o.bm, (int)nbo, cus, o.id, S, (int)dp_tiles};
+        }
+      }
     }
   }
   return best;
@@ -112,12 +139,12 @@ template <int MODE, int EPI = EPI_PLAIN>
 static hipError_t dispatch(const GemmParams& p, hipStream_t st) {
   const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K, 0);
   switch (pl.id) {
-    case 0: return launch_cfg<BigTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks);
+    case 0: return launch_cfg<BigTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
     case 1:
       if constexpr (MODE != MODE_SWIGLU)
-        return launch_cfg<WideTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks);
+        return launch_cfg<WideTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
       return hipErrorInvalidValue;
-    case 2: return launch_cfg<HalfTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks);
+    case 2: return launch_cfg<HalfTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
     default: return launch_cfg<SmallTile, MODE, false, false, false, EPI>(p, 0, st);  // (never split)
   }
 }
@@ -126,10 +153,10 @@ static hipError_t dispatch(const GemmParams& p, hipStream_t st) {
 template <bool AT, bool BT>
 static hipError_t dispatch_t(const GemmParams& p, hipStream_t st) {
   const GemmPlan pl = gemm_plan(MODE_ROW, p.M, p.Nout, p.K, AT ? 2 : 1);
-  if (pl.id == 0) return launch_cfg<BigTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks);
-  if (pl.id == 4) return launch_cfg<SmallTTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks);
-  if (pl.id == 1) return launch_cfg<WideTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks);
-  return launch_cfg<HalfTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks);
+  if (pl.id == 0) return launch_cfg<BigTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+  if (pl.id == 4) return launch_cfg<SmallTTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+  if (pl.id == 1) return launch_cfg<WideTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+  return launch_cfg<HalfTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
 }
 
 hipError_t gemm_backward(const GemmParams& p, bool a_row_major_k, bool b_row_major_k, hipStream_t st) {

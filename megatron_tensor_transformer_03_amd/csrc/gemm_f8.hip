@@ -13,7 +13,7 @@ static hipError_t dispatch_f8(const GemmParams& p, hipStream_t st) {
   const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K, 0, false);
   switch (pl.id) {
     case 0:
-      return launch_cfg<BigTile, MODE, false, false, false, EPI_PLAIN, true>(p, 0, st, pl.split_groups, pl.split_chunks);
+      return launch_cfg<BigTile, MODE, false, false, false, EPI_PLAIN, true>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
     case 1:
       if constexpr (MODE != MODE_SWIGLU)
         return launch_cfg<WideTile, MODE, false, false, false, EPI_PLAIN, true>(p, 0, st, pl.split_groups,

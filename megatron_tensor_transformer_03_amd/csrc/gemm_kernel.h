@@ -234,10 +234,11 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   auto slot_of = [&](int c, int t) { return t * S + c; };
 
   // ---- one tile: rows m0 .. m0 + BM - 1 of the row group at row_base, K steps kt0 .. kt1 - 1.  With
-  // SPLIT and sk_partial, the K range is part of the tile's and the partial sums of all workgroups on the
-  // tile are added before the epilogue (see the split schedule below).
+  // SPLIT and sk_partial, the K range is chunk sk_which_chunk of the tile's and the partial sums of all
+  // workgroups on the tile are added before the epilogue (see the split schedule below): sk_tile indexes
+  // the tile's arrival counter, sk_wtile its slots in the workspace (split tiles only).
   auto run_tile = [&](int tm, int tn, int row_base, int rows, const uint16_t* __restrict__ B, int kt0, int kt1,
-                      int sk_tile, int sk_which, int sk_first, int sk_last, bool sk_partial) {
+                      int sk_tile, int sk_wtile, int sk_which_chunk, int sk_first, int sk_last, bool sk_partial) {
   const int m0 = tm * BM;  // relative to row_base
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave / WAVES_N) * TM, wn0 = (wave % WAVES_N) * TN;
@@ -492,9 +493,11 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
       constexpr int Q = FM * FN * 4;   // float4 per thread
       constexpr int kSc1 = 16;         // cache policy: device scope
       const int64_t slot_bytes = (int64_t)Q * C::NT * 16;
-      const __amdgpu_buffer_rsrc_t ws = make_rsrc(p.sk_ws, (int64_t)tiles_m * tiles_n * S * slot_bytes);
+      // (the workspace holds the slots of the split tiles only: tiles_m * tiles_n - sk_dp_tiles of them)
+      const __amdgpu_buffer_rsrc_t ws =
+          make_rsrc(p.sk_ws, (int64_t)(tiles_m * tiles_n - p.sk_dp_tiles) * S * slot_bytes);
       typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-      const int mine = (int)(sk_which * slot_bytes) + 16 * tid;
+      const int mine = (int)(slot_of(sk_which_chunk, sk_wtile) * slot_bytes) + 16 * tid;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -513,34 +516,46 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
       __syncthreads();
       if (!sk_flag) return;
       if (tid == 0) __hip_atomic_store(p.sk_cnt + sk_tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // one 32 x 32 fragment at a time (the scheduler barrier keeps the loads of the next fragment from
-      // being hoisted, which would need registers for all of them while the accumulators are live)
+      // The S slots are added in chunk order, in batches of up to 16 float4 per thread (half the partial tile
+      // at most, so the batch's registers fit beside the accumulators): all loads of one slot's batch are
+      // issued together and then added, so the reduction waits for 2 S memory round trips, not one per
+      // fragment and slot.  Element e of a thread's slot is fragment e / 4 (i * FN + j), quarter e % 4.
+      constexpr int NE = FM * FN * 4, NB = 16, NBATCH = (NE + NB - 1) / NB;
+      auto load_batch = [&](int c, int bb, float4* v) {
+        const int sc = (int)(slot_of(c, sk_wtile) * slot_bytes) + 16 * tid;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int e = 0; e < NB; ++e)
+          if (NB * bb + e < NE)
+            v[e] = __builtin_bit_cast(
+                float4, __builtin_amdgcn_raw_buffer_load_b128(ws, sc + (NB * bb + e) * C::NT * 16, 0, kSc1));
+      };
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int base = ((i * FN + j) * 4) * C::NT * 16 + 16 * tid;
-          float4 v[4];
-          const int s0 = (int)(slot_of(sk_first, sk_tile) * slot_bytes) + base;
+      for (int bb = 0; bb < NBATCH; ++bb) {
+        float4 v[NB];
+        load_batch(sk_first, bb, v);
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            v[q] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ws, s0 + q * C::NT * 16, 0, kSc1));
-          for (int c = sk_first + 1; c <= sk_last; ++c) {
-            const int sc = (int)(slot_of(c, sk_tile) * slot_bytes) + base;
+        for (int e = 0; e < NB; ++e) {
+          const int ee = NB * bb + e;
+          if (ee < NE) {
+            const int i = ee / (FN * 4), j = (ee / 4) % FN, q = ee % 4;
+            acc[i][j][4 * q] = v[e].x; acc[i][j][4 * q + 1] = v[e].y;
+            acc[i][j][4 * q + 2] = v[e].z; acc[i][j][4 * q + 3] = v[e].w;
+          }
+        }
+        for (int c = sk_first + 1; c <= sk_last; ++c) {
+          load_batch(c, bb, v);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float4 w =
-                  __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ws, sc + q * C::NT * 16, 0, kSc1));
-              v[q].x += w.x; v[q].y += w.y; v[q].z += w.z; v[q].w += w.w;
+          for (int e = 0; e < NB; ++e) {
+            const int ee = NB * bb + e;
+            if (ee < NE) {
+              const int i = ee / (FN * 4), j = (ee / 4) % FN, q = ee % 4;
+              acc[i][j][4 * q] += v[e].x; acc[i][j][4 * q + 1] += v[e].y;
+              acc[i][j][4 * q + 2] += v[e].z; acc[i][j][4 * q + 3] += v[e].w;
             }
           }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[i][j][4 * q] = v[q].x; acc[i][j][4 * q + 1] = v[q].y;
-            acc[i][j][4 * q + 2] = v[q].z; acc[i][j][4 * q + 3] = v[q].w;
-          }
-          __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
@@ -792,14 +807,24 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     // operand panels, as one-tile-per-workgroup tiles do.  (Contiguous per-workgroup K ranges, as in
     // stream-K, put concurrent workgroups at unrelated K positions and defeat the L2.)  Logical ids are
     // XCD-contiguous.
+    // Hybrid form (sk_dp_tiles > 0, a multiple of the grid): the first sk_dp_tiles tiles are whole units,
+    // one workgroup each, G at a time; only the remaining tiles are cut into chunks, so a ragged last wave
+    // of tiles is spread over every CU while the full waves pay no partial-sum traffic.
     const int T = tiles_m * tiles_n;
-    const int U = T * S;
+    const int TD = p.sk_dp_tiles, TR = T - TD;
+    const int U = TD + TR * S;
     for (int u = xcd_remap(blockIdx.x, G); u < U; u += G) {
-      const int c = u / T, t = u - c * T;
-      const int r0 = (int)((int64_t)c * RI / S), r1 = (int)((int64_t)(c + 1) * RI / S);
       int tm, tn;
-      tile_coords(t, tiles_m, tiles_n, tm, tn);
-      run_tile(tm, tn, 0, p.M, p.B, r0 * NS, r1 * NS, t, slot_of(c, t), 0, S - 1, true);
+      if (u < TD) {
+        tile_coords(u, tiles_m, tiles_n, tm, tn);
+        run_tile(tm, tn, 0, p.M, p.B, 0, KTS, 0, 0, 0, 0, 0, false);
+        continue;
+      }
+      const int v = u - TD;
+      const int c = v / TR, tr = v - c * TR;
+      const int r0 = (int)((int64_t)c * RI / S), r1 = (int)((int64_t)(c + 1) * RI / S);
+      tile_coords(TD + tr, tiles_m, tiles_n, tm, tn);
+      run_tile(tm, tn, 0, p.M, p.B, r0 * NS, r1 * NS, TD + tr, tr, c, 0, S - 1, true);
     }
   } else {
     // ---- tile placement
@@ -824,14 +849,14 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     } else {
       tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
     }
-    run_tile(tm, tn, row_base, rows, B, 0, KTS, 0, 0, 0, 0, false);
+    run_tile(tm, tn, row_base, rows, B, 0, KTS, 0, 0, 0, 0, 0, false);
   }
 }
 
 
 template <class C, int MODE, bool GROUPED, bool AT = false, bool BT = false, int EPI = EPI_PLAIN, bool F8 = false>
 static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStream_t st, int split_groups = 0,
-                             int split_chunks = 0) {
+                             int split_chunks = 0, int dp_tiles = 0) {
   GemmParams p = p0;
   const int nb = MODE == MODE_SWIGLU ? C::BN / 2 : C::BN;
   const int tiles_n = (p.Nout + nb - 1) / nb;
@@ -846,8 +871,11 @@ static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStrea
   if constexpr (!GROUPED) {
     if (split_groups > 0 && split_chunks > 1) {
       const size_t slot = (size_t)C::FM * C::FN * 16 * sizeof(float) * C::NT;
+      // whole tiles first: whole waves of the grid, leaving at least one tile to split
+      if (dp_tiles < 0 || dp_tiles % split_groups != 0 || dp_tiles >= tiles) return hipErrorInvalidValue;
       p.sk_chunks = split_chunks;
-      hipError_t e = split_workspace(st, (size_t)tiles * split_chunks * slot, tiles, &p.sk_ws, &p.sk_cnt);
+      p.sk_dp_tiles = dp_tiles;
+      hipError_t e = split_workspace(st, (size_t)(tiles - dp_tiles) * split_chunks * slot, tiles, &p.sk_ws, &p.sk_cnt);
       if (e != hipSuccess) return e;
       if (kfull)
         hipLaunchKernelGGL((gemm_kernel<C, MODE, false, true, true, AT, BT, EPI, F8>), dim3(split_groups), dim3(C::NT), 0, st, p);
@@ -867,7 +895,7 @@ static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStrea
 }
 
 #ifndef MTP_BIG_CFG
-#define MTP_BIG_CFG 256, 256, 2, 4, 32, 4, true
+#define MTP_BIG_CFG 256, 256, 4, 2, 32, 4, true
 #endif
 #ifndef MTP_WIDE_CFG
 #define MTP_WIDE_CFG 256, 192, 4, 2, 32, 4, true
@@ -878,7 +906,9 @@ static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStrea
 #ifndef MTP_SMALL_CFG
 #define MTP_SMALL_CFG 128, 128, 4, 2, 64, 4, true
 #endif
-using BigTile = Cfg<MTP_BIG_CFG>;              // 8 waves (wave tile 128 x 64), 128 KB LDS ring
+// (8 waves of 64 x 128: against 128 x 64 wave tiles, 1.25-1.45x faster on most MI355X boards measured and
+// never slower, in every mode, at every workload shape; outputs bitwise equal)
+using BigTile = Cfg<MTP_BIG_CFG>;              // 8 waves (wave tile 64 x 128), 128 KB LDS ring
 using WideTile = Cfg<MTP_WIDE_CFG>;            // 8 waves (64 x 96), 112 KB
 using HalfTile = Cfg<MTP_HALF_CFG>;            // 8 waves (64 x 64), 96 KB
 using SmallTile = Cfg<MTP_SMALL_CFG>;          // 8 waves (32 x 64), 128 KB

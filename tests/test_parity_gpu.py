@@ -115,15 +115,17 @@ def test_integer_exact_row_partials_and_sum(M, N, Kp, p):
 
 # ----------------------------------------------------------------------------- split-K schedule
 # Shapes whose launch plan is split-K (each tile's K range in S chunks, the chunks' fp32 partial sums added
-# in chunk order by the tile's last finisher), one per tile shape, with even and uneven chunks.
+# in chunk order by the tile's last finisher), for each tile the forward planner splits, with even and
+# uneven chunks, and a hybrid schedule (whole waves of tiles first, the rest split).  (The 192-wide tile's
+# split form is covered by the backward tests.)
 # Integer-valued inputs make the sums exact whatever the split, so the bf16 outputs are bit-exact; rows
 # are sampled for the large cases (each output row depends only on its input row, and every row tile and
 # every column is covered).
 @pytest.mark.parametrize("M,N,K,plan,sampled", [
-    (300, 400, 4096, (256, 128, 6), False),    # 32 ring passes in 6 chunks (5 or 6 each)
-    (777, 190, 8192, (256, 128, 5), False),
-    (4100, 900, 2048, (256, 192, 3), True),
-    (900, 4100, 2048, (256, 256, 3), True),
+    (300, 1280, 7168, (256, 128, 6), False),   # 56 ring passes in 6 chunks (9 or 10 each)
+    (300, 190, 2048, (256, 128, 4), False),
+    (900, 4100, 5120, (256, 256, 3), True),    # 40 passes in 3 chunks
+    (4100, 4100, 4096, (256, 256, 3), True),   # hybrid: 256 of the 289 tiles whole, the other 33 in 3 chunks
 ])
 def test_split_schedule_integer_exact(M, N, K, plan, sampled):
     say("split int column", M, N, K)
@@ -156,7 +158,8 @@ def test_split_schedule_integer_exact(M, N, K, plan, sampled):
     assert np.array_equal(bits(Yb)[rows], oracle.round_bf16(S + widen_bits(bb)[None, :]))
 
 
-@pytest.mark.parametrize("M,F,K,plan", [(300, 200, 4096, (256, 64, 6)), (400, 4100, 2048, (256, 128, 3))])
+@pytest.mark.parametrize("M,F,K,plan", [(300, 200, 2048, (256, 64, 4)), (400, 4100, 5120, (256, 128, 3)),
+                                         (900, 8200, 2048, (256, 128, 3))])  # (the last one hybrid)
 def test_split_schedule_swiglu(M, F, K, plan):
     say("split swiglu", M, F, K)
     assert mtp.mtp_gemm_plan(M, 2 * F, K, mtp.ACT_SWIGLU) == plan
