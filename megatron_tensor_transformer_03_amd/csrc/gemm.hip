@@ -139,7 +139,7 @@ template <int MODE, int EPI = EPI_PLAIN>
 static hipError_t dispatch(const GemmParams& p, hipStream_t st) {
   const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K, 0);
   switch (pl.id) {
-    case 0: return launch_cfg<BigTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+    case 0: return launch_cfg<BigFwdTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
     case 1:
       if constexpr (MODE != MODE_SWIGLU)
         return launch_cfg<WideTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
@@ -200,8 +200,8 @@ hipError_t gemm(const GemmParams& p, int mode, hipStream_t st, int epi) {
 
 hipError_t gemm_grouped(const GemmParams& p, int mode, int rows_upper, hipStream_t st) {
   switch (mode) {
-    case MODE_SWIGLU: return launch_cfg<BigTile, MODE_SWIGLU, true>(p, rows_upper, st);
-    case MODE_COMBINE: return launch_cfg<BigTile, MODE_COMBINE, true>(p, rows_upper, st);
+    case MODE_SWIGLU: return launch_cfg<BigFwdTile, MODE_SWIGLU, true>(p, rows_upper, st);
+    case MODE_COMBINE: return launch_cfg<BigFwdTile, MODE_COMBINE, true>(p, rows_upper, st);
     default: return hipErrorInvalidValue;
   }
 }
