@@ -346,6 +346,10 @@ def main():
                          "call from Python; on ROCm 7 graph launches cost more than they save at this step size")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--vs-hipblaslt", action="store_true",
+                    help="only time two plain column GEMMs (8192^3 and 4096x7168x8192, no bias or activation) "
+                         "through this library and through torch's linear (hipBLASLt), 5 launches each, for a "
+                         "side-by-side counter run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
@@ -372,6 +376,26 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": 5}), flush=True)
+        return
+
+    if args.vs_hipblaslt:
+        res = {}
+        for (M, N, K) in [(8192, 8192, 8192), (4096, 7168, 8192)]:
+            X = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+            W = (torch.randn(N, K, device="cuda") * 0.02).to(torch.bfloat16)
+            Y = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+            for name, fn in [("mtp", lambda: mtp.mtp_column_linear(X, W, None, Y)),
+                             ("hipblaslt", lambda: torch.nn.functional.linear(X, W))]:
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                fn()
+                a.record()
+                for _ in range(4):
+                    fn()
+                b.record()
+                b.synchronize()
+                res[f"{name} {M}x{N}x{K}"] = round(a.elapsed_time(b) / 4 * 1000, 1)
+        print(json.dumps({"us_per_launch": res}), flush=True)
         return
 
     w = configs.by_index(WORKLOADS[args.workload])
