@@ -327,8 +327,12 @@ mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, i
  * workgroup per CU works through the (tile, chunk) units and the tile's last
  * finisher adds the chunks' fp32 partial sums in chunk order, so results are
  * deterministic but round differently from the unsplit schedule).  Split-K is
- * chosen when whole waves of tiles would leave many CUs idle.  The same size
- * rules as mtp_column_linear apply; nothing is launched.
+ * chosen when whole waves of tiles would leave many CUs idle and the K range
+ * is long enough to pay for the partial sums' traffic; when whole waves fill
+ * the CUs and a ragged last wave does not, the whole waves may run one tile
+ * per workgroup and only the remaining tiles split (*split_k is then their
+ * chunk count).  The same size rules as mtp_column_linear apply; nothing is
+ * launched.
  * mtp_row_linear_partial plans as act = NONE.
  */
 mtp_status mtp_gemm_plan(int64_t M, int64_t N, int64_t K, mtp_act act, int* tile_m, int* tile_n,
