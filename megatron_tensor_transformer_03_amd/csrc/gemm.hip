@@ -77,12 +77,12 @@ hipError_t split_workspace(hipStream_t st, size_t ws_bytes, int64_t cnt_n, float
 // (within ~10%).
 GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k, bool allow_small) {
   struct Opt { int bm, bn; double eff; int id; int ns_bk; int64_t slot_bytes; };
-  // Relative efficiencies.  The 256 x 192 tile's differs by board: on some MI355X boards it runs at 0.9-1.1
-  // of the 256 x 256 tile's rate per output, on others at 0.6-0.75 (the 256 x 256 tile with 64 x 128 wave
-  // tiles holds its rate on both); the forward planner takes the low figure, so it picks the 256 x 256 tile
-  // wherever the two differ by less than that (at most 9% lost on the boards where 256 x 192 is fast, up to
-  // 40% gained on the others).  The backward figures were measured on the transposed forms.
-  const double wide_eff = row_major_k ? 0.95 : 0.70;
+  // Relative efficiencies per output, against the 256 x 256 tile.  The forward products run both large
+  // tiles with a 64-deep K step in two stages, where the 256 x 192 tile measured 0.80-0.86 at the workload
+  // shapes.  (Its 32-deep four-stage form, used by the backward products, ranged from 0.6 to 1.1 of the
+  // 256 x 256 tile's rate depending on the board; the backward figures were measured on the transposed
+  // forms.)
+  const double wide_eff = row_major_k ? 0.95 : 0.85;
   const double half_eff = row_major_k ? 0.85 : 0.75;
   const Opt opts[] = {{256, 256, 1.00, 0, 128, 256 << 10}, {256, 192, wide_eff, 1, 128, 192 << 10},
                       {256, 128, half_eff, 2, 128, 128 << 10}, {128, 128, 0.72, 3, 256, 0},
@@ -142,7 +142,7 @@ static hipError_t dispatch(const GemmParams& p, hipStream_t st) {
     case 0: return launch_cfg<BigFwdTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
     case 1:
       if constexpr (MODE != MODE_SWIGLU)
-        return launch_cfg<WideTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+        return launch_cfg<WideFwdTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
       return hipErrorInvalidValue;
     case 2: return launch_cfg<HalfTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
     default: return launch_cfg<SmallTile, MODE, false, false, false, EPI>(p, 0, st);  // (never split)

@@ -17,11 +17,11 @@ static hipError_t dispatch_f8(const GemmParams& p, hipStream_t st) {
     case 1:
       if constexpr (MODE != MODE_SWIGLU)
         return launch_cfg<WideTile, MODE, false, false, false, EPI_PLAIN, true>(p, 0, st, pl.split_groups,
-                                                                                pl.split_chunks);
+                                                                                pl.split_chunks, pl.dp_tiles);
       return hipErrorInvalidValue;
     default:
       return launch_cfg<HalfTile, MODE, false, false, false, EPI_PLAIN, true>(p, 0, st, pl.split_groups,
-                                                                              pl.split_chunks);
+                                                                              pl.split_chunks, pl.dp_tiles);
   }
 }
 

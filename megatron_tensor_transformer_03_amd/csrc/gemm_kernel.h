@@ -913,6 +913,10 @@ using BigTile = Cfg<MTP_BIG_CFG>;              // 8 waves (wave tile 64 x 128), 
 // in two stages: 128-byte rows per DMA instead of 64, 2-4% faster at the workload shapes.  The row-major-K
 // (backward) and E4M3 forms keep the 32-deep ring their layouts are built on.
 using BigFwdTile = Cfg<256, 256, 4, 2, 64, 2, false>;  // 8 waves (64 x 128), 2 x 64 KB LDS stages
+// Likewise the 256 x 192 tile: in this form it runs at 0.80-0.86 of the 256 x 256 tile's rate per output and
+// beats it where its tile count fills whole waves (175B-shard out-projection 98.5 against 113 us, fc2 295
+// against 326, QKV 211 against 237; 345M QKV 30.9 against 33.0).
+using WideFwdTile = Cfg<256, 192, 4, 2, 64, 2, false>;  // 8 waves (64 x 96), 2 x 56 KB LDS stages
 using WideTile = Cfg<MTP_WIDE_CFG>;            // 8 waves (64 x 96), 112 KB
 using HalfTile = Cfg<MTP_HALF_CFG>;            // 8 waves (64 x 64), 96 KB
 using SmallTile = Cfg<MTP_SMALL_CFG>;          // 8 waves (32 x 64), 128 KB

@@ -116,8 +116,7 @@ def test_integer_exact_row_partials_and_sum(M, N, Kp, p):
 # ----------------------------------------------------------------------------- split-K schedule
 # Shapes whose launch plan is split-K (each tile's K range in S chunks, the chunks' fp32 partial sums added
 # in chunk order by the tile's last finisher), for each tile the forward planner splits, with even and
-# uneven chunks, and a hybrid schedule (whole waves of tiles first, the rest split).  (The 192-wide tile's
-# split form is covered by the backward tests.)
+# uneven chunks, and a hybrid schedule (whole waves of tiles first, the rest split).
 # Integer-valued inputs make the sums exact whatever the split, so the bf16 outputs are bit-exact; rows
 # are sampled for the large cases (each output row depends only on its input row, and every row tile and
 # every column is covered).
@@ -126,6 +125,7 @@ def test_integer_exact_row_partials_and_sum(M, N, Kp, p):
     (300, 190, 2048, (256, 128, 4), False),
     (900, 4100, 5120, (256, 256, 3), True),    # 40 passes in 3 chunks
     (4100, 4100, 4096, (256, 256, 3), True),   # hybrid: 256 of the 289 tiles whole, the other 33 in 3 chunks
+    (640, 3000, 12288, (256, 192, 5), True),   # 96 passes in 5 chunks (19 or 20 each)
 ])
 def test_split_schedule_integer_exact(M, N, K, plan, sampled):
     say("split int column", M, N, K)
