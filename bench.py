@@ -415,10 +415,13 @@ def main():
     # caches, which costs several microseconds per record and slows the following kernel.
     timer = _FenceFreeEvents(stream.cuda_stream)
 
-    # per-GEMM times from a short pass with an event around every launch (outside the timed region)
+    # per-GEMM times from a short pass with an event around every launch (outside the timed region); an
+    # unmarked step is enqueued first so the GPU is busy while the marked launches are issued (otherwise the
+    # first interval would include the host's launch time on an idle GPU)
     per_kernel = {}
     for _ in range(min(5, max(args.steps, 1))):
         marks = []
+        run.step()
         run.step(lambda label: marks.append((label, timer.record())))
         torch.cuda.synchronize()
         for (label, e0), (_, e1) in zip(marks[:-1], marks[1:]):
