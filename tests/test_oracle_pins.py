@@ -329,6 +329,40 @@ def test_moe_single_expert_top1_is_dense_swiglu_mlp():
     assert np.array_equal(out, dense)
 
 
+def _moe_by_dense_mlps(X, logits, W1, W2, k):
+    """Each token's output built from the dense MLP path, one token row at a time: the expert choice and
+    weights come from a 50-digit softmax and a full sort (not from oracle.moe_route), and token t's output
+    is sum over its k experts e of w[t, e] * mlp(x_t; W1_e, W2_e)."""
+    T, E = logits.shape
+    out = np.zeros((T, W2[0].shape[0]))
+    for t in range(T):
+        probs = _softmax_decimal(logits[t])
+        chosen = sorted(sorted(range(E), key=lambda e: (-probs[e], e))[:k])
+        for e in chosen:
+            y = oracle.mlp(X[t:t + 1], W1[e], None, W2[e], None, oracle.ACT_SWIGLU, p=1)["Y"][0]
+            out[t] += probs[e] * y
+    return out
+
+
+@pytest.mark.parametrize("E,k", [(3, 2), (5, 2), (4, 3)])
+def test_moe_distinct_experts_bind_each_row_to_its_own_expert(E, k):
+    # Experts with different weights and very different output scales (expert e's fc2 is scaled by 4^e), so
+    # a row computed with another expert's weights, a combine weight taken from the wrong slot or a row
+    # dropped from an expert's range moves the output far beyond rounding.
+    T, H, F = 23, 16, 8
+    X = synth.normal_bf16(171, T, H, 1.0)
+    logits = synth.normal_f32(172, T, E)
+    W1 = [synth.normal_bf16(180 + e, 2 * F, H, 0.3) for e in range(E)]
+    W2 = [synth.normal_bf16(190 + e, H, F, 0.3 * 4.0 ** e) for e in range(E)]
+    out, (offsets, idx, w) = oracle.moe_mlp(X, logits, W1, W2, k)
+    ref = _moe_by_dense_mlps(X, logits, W1, W2, k)
+    assert np.all(np.diff(offsets) > 0), "every expert receives rows in this case"
+    assert np.allclose(out, ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
+    # reversing the expert order must change the result (the case is sensitive to the binding)
+    rev = _moe_by_dense_mlps(X, logits, W1[::-1], W2[::-1], k)
+    assert not np.allclose(rev, ref, rtol=1e-3)
+
+
 def test_moe_token_subset_matches_full():
     T, H, F, E = 12, 8, 4, 3
     X = synth.normal_bf16(141, T, H, 1.0)
