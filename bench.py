@@ -105,9 +105,10 @@ def backward_gemms(w, timer, reps=5):
         synth.gpu_normal_bf16_(dY, 9003 + 3 * i, 1.0)
         dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
         dW = torch.zeros(N, K, dtype=torch.float32, device="cuda")
+        ws = mtp.workspace_for([(M, K, N, "dgrad"), (N, K, M, "wgrad")])
         res = {}
-        for name, fn in (("dgrad", lambda: mtp.mtp_linear_dgrad(dY, Wt, None, False, dX)),
-                         ("wgrad", lambda: mtp.mtp_linear_wgrad(dY, X, dW, True))):
+        for name, fn in (("dgrad", lambda: mtp.mtp_linear_dgrad(dY, Wt, None, False, dX, workspace=ws)),
+                         ("wgrad", lambda: mtp.mtp_linear_wgrad(dY, X, dW, True, workspace=ws))):
             fn()
             torch.cuda.synchronize()
             ev = []
@@ -172,8 +173,9 @@ def norm_and_bda(w, timer):
     t_stats = _median_us(timer, lambda: mtp.mtp_norm_stats(X, stats, kind, 1e-5))
     t_fold = _median_us(timer, lambda: mtp.mtp_norm_fold_weights(Wt, g[0], None if beta is None else beta[0], None,
                                                                  Wf, cs, bias_f))
-    t_fused = _median_us(timer, lambda: mtp.mtp_norm_column_linear(X, stats, Wf, cs, bias_f, Y))
-    t_plain = _median_us(timer, lambda: mtp.mtp_column_linear(X, Wt, None, Y))
+    ws = mtp.workspace_for([(M, N, H, mtp.ACT_NONE)])
+    t_fused = _median_us(timer, lambda: mtp.mtp_norm_column_linear(X, stats, Wf, cs, bias_f, Y, workspace=ws))
+    t_plain = _median_us(timer, lambda: mtp.mtp_column_linear(X, Wt, None, Y, workspace=ws))
     stat_bytes = M * H * 2 + 8 * M
     gbs = stat_bytes / (t_stats * 1e-6) / 1e9
     del Wt, Wf, Y
@@ -187,8 +189,9 @@ def norm_and_bda(w, timer):
     synth.gpu_normal_bf16_(R, 9106, 1.0)
     keep = torch.from_numpy(synth.keep_bits(9107, M2, N2, 0.1)).cuda()
     Y2 = torch.empty(M2, N2, dtype=torch.bfloat16, device="cuda")
-    t_bda = _median_us(timer, lambda: mtp.mtp_row_linear_bda(Z, W2, R, Y2, keep=keep, p_drop=0.1))
-    t_row = _median_us(timer, lambda: mtp.mtp_row_linear_partial(Z, W2, None, False, None, Y2))
+    ws2 = mtp.workspace_for([(M2, N2, K2, mtp.ACT_NONE)])
+    t_bda = _median_us(timer, lambda: mtp.mtp_row_linear_bda(Z, W2, R, Y2, keep=keep, p_drop=0.1, workspace=ws2))
+    t_row = _median_us(timer, lambda: mtp.mtp_row_linear_partial(Z, W2, None, False, None, Y2, workspace=ws2))
     return {"norm": "rmsnorm" if kind == mtp.NORM_RMS else "layernorm",
             "stats_kernel": {"bound": "hbm", "us": round(t_stats, 2), "bytes": stat_bytes, "achieved": round(gbs, 1),
                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
@@ -223,7 +226,8 @@ def fp8_gemms(w, timer):
         t_q = _median_us(timer, lambda: mtp.mtp_fp8_quantize(X, Xq, amax, sx))
         hist = torch.full((16,), 4.5, dtype=torch.float32, device="cuda")
         t_qd = _median_us(timer, lambda: mtp.mtp_fp8_quantize_delayed(X, Xq, hist, 3, amax, sx))
-        t_g = _median_us(timer, lambda: mtp.mtp_fp8_column_linear(Xq, sx, Wq, sw, None, Y, act))
+        ws = mtp.workspace_for([(M, N, K, ("fp8", act))])
+        t_g = _median_us(timer, lambda: mtp.mtp_fp8_column_linear(Xq, sx, Wq, sw, None, Y, act, workspace=ws))
         fl = 2 * M * N * K
         # HBM bytes: current scaling reads X twice (amax, then codes) and writes the codes; delayed scaling
         # reads it once
@@ -384,7 +388,8 @@ def main():
             X = torch.randn(M, K, device="cuda").to(torch.bfloat16)
             W = (torch.randn(N, K, device="cuda") * 0.02).to(torch.bfloat16)
             Y = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
-            for name, fn in [("mtp", lambda: mtp.mtp_column_linear(X, W, None, Y)),
+            ws = mtp.workspace_for([(M, N, K, mtp.ACT_NONE)])
+            for name, fn in [("mtp", lambda: mtp.mtp_column_linear(X, W, None, Y, workspace=ws)),
                              ("hipblaslt", lambda: torch.nn.functional.linear(X, W))]:
                 torch.cuda.synchronize()
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -402,8 +407,7 @@ def main():
     inputs = synth.device_inputs(w)
     run = RankForward(w.dims, inputs)
     torch.cuda.synchronize()
-    # one side stream for everything (graph capture needs a non-default stream, and the library's split-K
-    # workspace is per stream, so warm-up on this stream allocates it before any capture)
+    # one side stream for everything (graph capture needs a non-default stream)
     stream = torch.cuda.Stream()
     torch.cuda.set_stream(stream)
 

@@ -27,14 +27,20 @@
  *    row pitch (in elements).  Weights are [out x in].  Accumulation is fp32;
  *    every conversion to bf16 rounds to nearest, ties to even.
  *  - Pointers are device pointers owned by the caller; the library keeps none
- *    after returning.  The one allocation the library makes itself is the
- *    workspace of the split-K schedule (see mtp_gemm_plan): per device and
- *    stream, allocated on the first call that needs it (and grown, after a
- *    synchronisation of that stream, when a later call needs more), at most
- *    512 MB of fp32 partial tiles plus one int32 per tile, and kept until
- *    mtp_release_workspaces() or the end of the process.  Calls on one
- *    stream share its workspace safely; nothing else allocates or
- *    synchronises.
+ *    after returning, and it never allocates, frees or synchronises.
+ *  - Workspace.  The GEMM calls take `workspace` (device memory, 16-byte
+ *    aligned, or NULL) and its size `workspace_bytes`.  It is used only by
+ *    the split-K schedule (see mtp_gemm_plan, which reports the bytes a plan
+ *    needs): a call whose best plan needs more workspace than it is given
+ *    takes the best plan that fits (one workgroup per tile needs none), so
+ *    NULL / 0 is always valid.  Its first 16 KiB hold int32 arrival counters
+ *    (one per output tile of a split launch; such launches have at most 4096
+ *    tiles): they must be zero before the workspace is first used (allocate
+ *    it zero-filled), and every call that completes leaves them zero again;
+ *    the partial sums follow them.  Calls that may run at the same time (on
+ *    different streams, or in graphs replayed concurrently) need distinct
+ *    workspaces; calls ordered on one stream may share one, whatever their
+ *    shapes.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL is the default stream)
  *    and the call returns at once.  Faults surface at the caller's next sync.
  *  - Every argument is validated before anything is enqueued; on an error
@@ -43,18 +49,20 @@
  *    pitch multiples of 8; pitches at least the row width; bf16/fp32 pointers
  *    16-byte aligned; the current device a gfx950.
  *  - Outputs must not alias inputs.  Calls are reentrant; the only shared
- *    state is an immutable per-device property cache filled on first use.
+ *    state is an immutable per-device property cache (architecture, CU count)
+ *    filled on first use.
  */
 #ifndef MTP_H_
 #define MTP_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define MTP_ABI_VERSION 1
+#define MTP_ABI_VERSION 2
 
 typedef uint16_t mtp_bf16;
 
@@ -85,7 +93,7 @@ typedef enum { MTP_NORM_LAYER = 0, MTP_NORM_RMS = 1 } mtp_norm;
  */
 mtp_status mtp_column_linear(const mtp_bf16* X, int64_t ldx, const mtp_bf16* Wt, int64_t ldw,
                              const mtp_bf16* bias, mtp_bf16* Y, int64_t ldy, int64_t M, int64_t N,
-                             int64_t K, mtp_act act, void* stream);
+                             int64_t K, mtp_act act, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * RowParallelLinear partial product of one shard (Y_i = X_i W_i) and the
@@ -102,7 +110,7 @@ mtp_status mtp_column_linear(const mtp_bf16* X, int64_t ldx, const mtp_bf16* Wt,
 mtp_status mtp_row_linear_partial(const mtp_bf16* Z, int64_t ldz, const mtp_bf16* Wt, int64_t ldw,
                                   float* Yacc, int64_t ldacc, int accumulate, const mtp_bf16* bias,
                                   mtp_bf16* Y, int64_t ldy, int64_t M, int64_t N, int64_t Kp,
-                                  void* stream);
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Tensor-parallel MLP, Z = phi(X W_1), Y = Z W_2, for shards r0..r1-1 of a
@@ -120,7 +128,7 @@ mtp_status mtp_row_linear_partial(const mtp_bf16* Z, int64_t ldz, const mtp_bf16
 mtp_status mtp_mlp_forward(const mtp_bf16* X, int64_t M, int64_t H, int64_t F, int p, int r0, int r1,
                            const mtp_bf16* W1t, const mtp_bf16* b1, const mtp_bf16* W2t,
                            const mtp_bf16* b2, mtp_act act, mtp_bf16* Z_ws, float* Yacc, mtp_bf16* Y,
-                           void* stream);
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * QKV projection of one rank (part 2 section 2, [Q,K,V] = X W_qkv, heads/TP
@@ -133,7 +141,7 @@ mtp_status mtp_mlp_forward(const mtp_bf16* X, int64_t M, int64_t H, int64_t F, i
  */
 mtp_status mtp_qkv_forward(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t H, const mtp_bf16* Wqkv_t,
                            int64_t ldw, const mtp_bf16* bias, int nq_local, int ng_local, int head_dim,
-                           mtp_bf16* QKV, int64_t ldo, void* stream);
+                           mtp_bf16* QKV, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The norm prologue of a column-parallel linear ("快速入门", model
@@ -169,7 +177,8 @@ mtp_status mtp_norm_fold_weights(const mtp_bf16* Wt, int64_t ldw, int64_t N, int
                                  int64_t ldwf, float* colsum, float* bias_f, void* stream);
 mtp_status mtp_norm_column_linear(const mtp_bf16* X, int64_t ldx, const float* stats, const mtp_bf16* Wf,
                                   int64_t ldw, const float* colsum, const float* bias_f, mtp_bf16* Y, int64_t ldy,
-                                  int64_t M, int64_t N, int64_t K, mtp_act act, void* stream);
+                                  int64_t M, int64_t N, int64_t K, mtp_act act, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * Row-parallel partial with the bias-dropout-add epilogue ("快速入门", model
@@ -188,7 +197,8 @@ mtp_status mtp_norm_column_linear(const mtp_bf16* X, int64_t ldx, const float* s
 mtp_status mtp_row_linear_bda(const mtp_bf16* Z, int64_t ldz, const mtp_bf16* Wt, int64_t ldw, float* Yacc,
                               int64_t ldacc, int accumulate, const mtp_bf16* bias, const mtp_bf16* residual,
                               int64_t ldr, const uint8_t* keep, int64_t ldk, float p_drop, mtp_bf16* Y, int64_t ldy,
-                              int64_t M, int64_t N, int64_t Kp, void* stream);
+                              int64_t M, int64_t N, int64_t Kp, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
  * FP8 (E4M3) forward GEMMs with per-tensor scaling ("快速入门", FP8 training:
@@ -224,11 +234,18 @@ mtp_status mtp_fp8_quantize_delayed(const mtp_bf16* X, int64_t ldx, int64_t M, i
                                     void* stream);
 mtp_status mtp_fp8_column_linear(const uint8_t* Xq, int64_t ldx, const float* x_scale_inv, const uint8_t* Wq,
                                  int64_t ldw, const float* w_scale_inv, const mtp_bf16* bias, mtp_bf16* Y,
-                                 int64_t ldy, int64_t M, int64_t N, int64_t K, mtp_act act, void* stream);
+                                 int64_t ldy, int64_t M, int64_t N, int64_t K, mtp_act act, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 mtp_status mtp_fp8_row_linear_partial(const uint8_t* Zq, int64_t ldz, const float* z_scale_inv, const uint8_t* Wq,
                                       int64_t ldw, const float* w_scale_inv, float* Yacc, int64_t ldacc,
                                       int accumulate, const mtp_bf16* bias, mtp_bf16* Y, int64_t ldy, int64_t M,
-                                      int64_t N, int64_t Kp, void* stream);
+                                      int64_t N, int64_t Kp, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+/* The launch plan and workspace of an E4M3 GEMM (mtp_fp8_column_linear with activation act, or
+ * mtp_fp8_row_linear_partial with act = NONE), as mtp_gemm_plan reports them for the bf16 calls; launches
+ * nothing. */
+mtp_status mtp_fp8_gemm_plan(int64_t M, int64_t N, int64_t K, mtp_act act, int* tile_m, int* tile_n, int* split_k,
+                             size_t* workspace_bytes);
 
 /*
  * Backward GEMMs of a linear Y = X . Wt^T ("Megatron-LM 深度学习与源码分析文档",
@@ -257,14 +274,15 @@ mtp_status mtp_fp8_row_linear_partial(const uint8_t* Zq, int64_t ldz, const floa
  */
 mtp_status mtp_linear_dgrad(const mtp_bf16* dY, int64_t lddy, const mtp_bf16* Wt, int64_t ldw, float* dXacc,
                             int64_t ldacc, int accumulate, mtp_bf16* dX, int64_t lddx, int64_t M, int64_t N,
-                            int64_t K, void* stream);
+                            int64_t K, void* workspace, size_t workspace_bytes, void* stream);
 mtp_status mtp_linear_wgrad(const mtp_bf16* dY, int64_t lddy, const mtp_bf16* X, int64_t ldx, float* dW,
-                            int64_t lddw, int accumulate, int64_t M, int64_t N, int64_t K, void* stream);
+                            int64_t lddw, int accumulate, int64_t M, int64_t N, int64_t K, void* workspace,
+                            size_t workspace_bytes, void* stream);
 /* The launch plan of a backward product with output [M x N] and contraction K (dgrad: M, K_out, N; wgrad:
- * N, K, M in the names above; wgrad != 0 selects mtp_linear_wgrad's plan), as mtp_gemm_plan; launches
- * nothing. */
+ * N, K, M in the names above; wgrad != 0 selects mtp_linear_wgrad's plan) and the workspace it needs, as
+ * mtp_gemm_plan; launches nothing. */
 mtp_status mtp_gemm_plan_backward(int64_t M, int64_t N, int64_t K, int wgrad, int* tile_m, int* tile_n,
-                                  int* split_k);
+                                  int* split_k, size_t* workspace_bytes);
 
 /*
  * Rotary position embedding of the query and key heads of one rank's QKV
@@ -295,28 +313,32 @@ mtp_status mtp_rope_qk(mtp_bf16* QKV, int64_t ldo, int64_t M, const int32_t* pos
  * ascending expert order and ascending token order within an expert:
  *   expert_offsets [E+1] (int32, offsets[0] = 0, offsets[E] = T*k),
  *   token_idx [T*k] (int32 token of each dispatched row),
- *   token_w  [T*k] (fp32 softmax probability, not renormalised).
+ *   token_w  [T*k] (fp32 softmax probability of each dispatched row, not
+ *            renormalised),
+ * and the inverse map token_rows [T*k] (int32): token_rows[t*k + s] is the
+ * dispatched row of token t's s-th choice, most probable first.
  * logits is [T x E] fp32 (pitch E).  Requires 1 <= k <= min(E, 8), E <= 64.
  */
 mtp_status mtp_moe_route(const float* logits, int64_t T, int E, int k, int32_t* expert_offsets,
-                         int32_t* token_idx, float* token_w, void* stream);
+                         int32_t* token_idx, float* token_w, int32_t* token_rows, void* stream);
 
 /*
  * Expert MLPs of an MoE layer as grouped GEMMs over the routed rows, and the
  * weighted combine:
  *   for each dispatched row j of expert e (token t = token_idx[j]):
- *     z_j = SwiGLU(X[t] . W1t_e^T)                 -> Z_ws[j] (bf16, [T*k x F])
- *     Yacc[t] += token_w[j] * (z_j . W2t_e^T)      (fp32; Yacc is zeroed first)
- *   Y = bf16(Yacc)  ([T x H]).
+ *     z_j = SwiGLU(X[t] . W1t_e^T)            -> Z_ws[j]   (bf16, [T*k x F])
+ *     y_j = z_j . W2t_e^T                     -> Y_rows[j] (fp32, [T*k x H])
+ *   Y[t] = bf16(sum over s = 0..k-1 of token_w[r_s] * y_{r_s}),
+ *          r_s = token_rows[t*k + s], added in that order in fp32
+ *          ([T x H]; deterministic for every k).
  * W1t is [E][2F x H] ([gate; up] per expert), W2t is [E][H x F].  The routing
  * tables are device arrays as written by mtp_moe_route (no host copy is
- * made).  With k = 2 every output element is the sum of two products added
- * to zero, so the fp32 result does not depend on their order.
+ * made).  Z_ws and Y_rows are caller-owned scratch; nothing needs zeroing.
  */
 mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, int64_t F, int k,
                                const int32_t* expert_offsets, const int32_t* token_idx,
-                               const float* token_w, const mtp_bf16* W1t, const mtp_bf16* W2t,
-                               mtp_bf16* Z_ws, float* Yacc, mtp_bf16* Y, void* stream);
+                               const float* token_w, const int32_t* token_rows, const mtp_bf16* W1t,
+                               const mtp_bf16* W2t, mtp_bf16* Z_ws, float* Y_rows, mtp_bf16* Y, void* stream);
 
 /*
  * The launch plan the GEMM calls would use for an [M x K] . [N x K]^T
@@ -331,16 +353,14 @@ mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, i
  * is long enough to pay for the partial sums' traffic; when whole waves fill
  * the CUs and a ragged last wave does not, the whole waves may run one tile
  * per workgroup and only the remaining tiles split (*split_k is then their
- * chunk count).  The same size rules as mtp_column_linear apply; nothing is
- * launched.
- * mtp_row_linear_partial plans as act = NONE.
+ * chunk count).  *workspace_bytes (may be NULL) receives the workspace that
+ * plan needs (0 for one workgroup per tile): a GEMM call given at least that
+ * much takes this plan.  The same size rules as mtp_column_linear apply;
+ * nothing is launched.  mtp_row_linear_partial plans as act = NONE; an MLP
+ * (mtp_mlp_forward) needs the larger of its fc1 and fc2 plans' workspaces.
  */
 mtp_status mtp_gemm_plan(int64_t M, int64_t N, int64_t K, mtp_act act, int* tile_m, int* tile_n,
-                         int* split_k);
-
-/* Frees the split-K workspaces of the current device after waiting for the
- * device to finish its work.  Later calls allocate again as needed. */
-mtp_status mtp_release_workspaces(void);
+                         int* split_k, size_t* workspace_bytes);
 
 /* Static text for a status code. */
 const char* mtp_status_string(mtp_status s);

@@ -9,7 +9,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmtp.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["gemm.hip", "gemm_f8.hip", "fp8.hip", "moe.hip", "rope.hip", "norm.hip", "api.hip"]
+SOURCES = ["gemm.hip", "gemm_fwd_col.hip", "gemm_fwd_swiglu.hip", "gemm_fwd_row.hip", "gemm_bwd_dgrad.hip",
+           "gemm_bwd_wgrad.hip", "gemm_grouped.hip", "gemm_f8.hip", "fp8.hip", "moe.hip", "rope.hip", "norm.hip", "api.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++20", "-munsafe-fp-atomics",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
 
@@ -28,7 +29,7 @@ def build(verbose: bool = False, extra=()) -> str:
             raise RuntimeError(f"hipcc failed on {src}")
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
     if verbose:

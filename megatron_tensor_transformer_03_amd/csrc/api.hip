@@ -2,7 +2,8 @@
 //
 // Every check runs before the first launch, so a rejected call enqueues
 // nothing and touches no output.  The only state is a per-device cache of
-// "is this a gfx950" filled on first use.
+// "is this a gfx950" and of the CU count, filled on first use; the library
+// allocates, frees and synchronises nothing.
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdint.h>
@@ -82,6 +83,13 @@ mtp_status check_dims(int64_t M, int64_t N, int64_t K) {
 // 32-bit byte offsets: a tile's rows (up to 256, plus the up-projection offset for SwiGLU) must span
 // less than 2 GiB.
 constexpr int64_t kWindow = (int64_t)1 << 31;
+
+// The caller's split-schedule workspace: NULL (then its size counts as 0) or 16-byte aligned.
+mtp_status check_ws(const void* ws, size_t bytes, size_t* avail) {
+  if (ws && misaligned(ws)) return fail(MTP_ERR_ALIGN, "workspace is not 16-byte aligned");
+  *avail = ws ? bytes : 0;
+  return MTP_OK;
+}
 mtp_status check_window(const char* name, int64_t rows, int64_t ld) {
   if (2 * rows * ld >= kWindow - 64)
     return fail(MTP_ERR_SHAPE, "%s: %lld rows of pitch %lld exceed the 2 GiB addressing window", name,
@@ -115,7 +123,8 @@ const char* mtp_status_string(mtp_status s) {
   return "unknown status";
 }
 
-mtp_status mtp_gemm_plan(int64_t M, int64_t N, int64_t K, mtp_act act, int* tile_m, int* tile_n, int* split_k) {
+mtp_status mtp_gemm_plan(int64_t M, int64_t N, int64_t K, mtp_act act, int* tile_m, int* tile_n, int* split_k,
+                         size_t* workspace_bytes) {
   TRY(check_dims(M, N, K));
   if (act != MTP_ACT_NONE && act != MTP_ACT_GELU && act != MTP_ACT_SWIGLU)
     return fail(MTP_ERR_SHAPE, "unknown activation %d", (int)act);
@@ -127,12 +136,33 @@ mtp_status mtp_gemm_plan(int64_t M, int64_t N, int64_t K, mtp_act act, int* tile
   *tile_m = pl.bm;
   *tile_n = pl.bn;
   *split_k = pl.split_groups > 0 ? pl.split_chunks : 0;
+  if (workspace_bytes) *workspace_bytes = pl.ws_bytes;
+  g_err[0] = 0;
+  return MTP_OK;
+}
+
+mtp_status mtp_fp8_gemm_plan(int64_t M, int64_t N, int64_t K, mtp_act act, int* tile_m, int* tile_n, int* split_k,
+                             size_t* workspace_bytes) {
+  TRY(check_dims(M, N, K));
+  if (K % 16 != 0) return fail(MTP_ERR_SHAPE, "the inner dimension %lld is not a multiple of 16", (long long)K);
+  if (act != MTP_ACT_NONE && act != MTP_ACT_GELU && act != MTP_ACT_SWIGLU)
+    return fail(MTP_ERR_SHAPE, "unknown activation %d", (int)act);
+  if (act == MTP_ACT_SWIGLU && N % 2 != 0) return fail(MTP_ERR_SHAPE, "SwiGLU needs an even N (got %lld)", (long long)N);
+  if (!tile_m || !tile_n || !split_k) return fail(MTP_ERR_NULL, "an output pointer is NULL");
+  TRY(check_device());
+  // (the E4M3 kernels count K in pairs of codes and have no 128 x 128 tile with a 64-deep step)
+  const mtp::GemmPlan pl = mtp::gemm_plan(act == MTP_ACT_SWIGLU ? mtp::MODE_SWIGLU : mtp::MODE_COL, M,
+                                          act == MTP_ACT_SWIGLU ? N / 2 : N, K / 2, 0, false);
+  *tile_m = pl.bm;
+  *tile_n = pl.bn;
+  *split_k = pl.split_groups > 0 ? pl.split_chunks : 0;
+  if (workspace_bytes) *workspace_bytes = pl.ws_bytes;
   g_err[0] = 0;
   return MTP_OK;
 }
 
 mtp_status mtp_gemm_plan_backward(int64_t M, int64_t N, int64_t K, int wgrad, int* tile_m, int* tile_n,
-                                  int* split_k) {
+                                  int* split_k, size_t* workspace_bytes) {
   if (M < 1 || N < 1 || K < 1 || M > kIntMax || N > kIntMax || K > kIntMax)
     return fail(MTP_ERR_SHAPE, "sizes must be in [1, 2^31-1] (M=%lld N=%lld K=%lld)", (long long)M, (long long)N,
                 (long long)K);
@@ -142,17 +172,14 @@ mtp_status mtp_gemm_plan_backward(int64_t M, int64_t N, int64_t K, int wgrad, in
   *tile_m = pl.bm;
   *tile_n = pl.bn;
   *split_k = pl.split_groups > 0 ? pl.split_chunks : 0;
+  if (workspace_bytes) *workspace_bytes = pl.ws_bytes;
   g_err[0] = 0;
   return MTP_OK;
 }
 
-mtp_status mtp_release_workspaces(void) {
-  TRY(check_device());
-  return launched(mtp::release_split_workspaces(), "release workspaces");
-}
-
 mtp_status mtp_column_linear(const mtp_bf16* X, int64_t ldx, const mtp_bf16* Wt, int64_t ldw, const mtp_bf16* bias,
-                             mtp_bf16* Y, int64_t ldy, int64_t M, int64_t N, int64_t K, mtp_act act, void* stream) {
+                             mtp_bf16* Y, int64_t ldy, int64_t M, int64_t N, int64_t K, mtp_act act,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   TRY(check_dims(M, N, K));
   if (act != MTP_ACT_NONE && act != MTP_ACT_GELU && act != MTP_ACT_SWIGLU)
     return fail(MTP_ERR_SHAPE, "unknown activation %d", (int)act);
@@ -164,8 +191,11 @@ mtp_status mtp_column_linear(const mtp_bf16* X, int64_t ldx, const mtp_bf16* Wt,
   TRY(check_vec(bias, "bias"));
   TRY(check_window("X", 256, ldx));
   TRY(check_window("Wt", (act == MTP_ACT_SWIGLU ? nout : 0) + 256, ldw));
+  size_t ws_avail = 0;
+  TRY(check_ws(workspace, workspace_bytes, &ws_avail));
   TRY(check_device());
   mtp::GemmParams p;
+  p.ws = workspace; p.ws_bytes = ws_avail;
   p.A = X; p.lda = ldx; p.B = Wt; p.ldb = ldw; p.bias = bias; p.Y = Y; p.ldy = ldy;
   p.M = (int)M; p.Nout = (int)nout; p.K = (int)K; p.up_offset = nout; p.a_src_rows = M;
   p.act = act == MTP_ACT_GELU ? 1 : 0;
@@ -175,7 +205,8 @@ mtp_status mtp_column_linear(const mtp_bf16* X, int64_t ldx, const mtp_bf16* Wt,
 
 mtp_status mtp_row_linear_partial(const mtp_bf16* Z, int64_t ldz, const mtp_bf16* Wt, int64_t ldw, float* Yacc,
                                   int64_t ldacc, int accumulate, const mtp_bf16* bias, mtp_bf16* Y, int64_t ldy,
-                                  int64_t M, int64_t N, int64_t Kp, void* stream) {
+                                  int64_t M, int64_t N, int64_t Kp,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   TRY(check_dims(M, N, Kp));
   TRY(check_mat(Z, "Z", Kp, ldz));
   TRY(check_mat(Wt, "Wt", Kp, ldw));
@@ -186,8 +217,11 @@ mtp_status mtp_row_linear_partial(const mtp_bf16* Z, int64_t ldz, const mtp_bf16
   TRY(check_vec(bias, "bias"));
   TRY(check_window("Z", 256, ldz));
   TRY(check_window("Wt", 256, ldw));
+  size_t ws_avail = 0;
+  TRY(check_ws(workspace, workspace_bytes, &ws_avail));
   TRY(check_device());
   mtp::GemmParams p;
+  p.ws = workspace; p.ws_bytes = ws_avail;
   p.A = Z; p.lda = ldz; p.B = Wt; p.ldb = ldw; p.Yacc = Yacc; p.ldacc = ldacc; p.accumulate = accumulate ? 1 : 0;
   p.bias = bias; p.Y = Y; p.ldy = ldy; p.M = (int)M; p.Nout = (int)N; p.K = (int)Kp; p.a_src_rows = M;
   return launched(mtp::gemm(p, mtp::MODE_ROW, (hipStream_t)stream), "row-parallel partial");
@@ -196,7 +230,8 @@ mtp_status mtp_row_linear_partial(const mtp_bf16* Z, int64_t ldz, const mtp_bf16
 mtp_status mtp_row_linear_bda(const mtp_bf16* Z, int64_t ldz, const mtp_bf16* Wt, int64_t ldw, float* Yacc,
                               int64_t ldacc, int accumulate, const mtp_bf16* bias, const mtp_bf16* residual,
                               int64_t ldr, const uint8_t* keep, int64_t ldk, float p_drop, mtp_bf16* Y, int64_t ldy,
-                              int64_t M, int64_t N, int64_t Kp, void* stream) {
+                              int64_t M, int64_t N, int64_t Kp,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   TRY(check_dims(M, N, Kp));
   TRY(check_mat(Z, "Z", Kp, ldz));
   TRY(check_mat(Wt, "Wt", Kp, ldw));
@@ -215,8 +250,11 @@ mtp_status mtp_row_linear_bda(const mtp_bf16* Z, int64_t ldz, const mtp_bf16* Wt
   TRY(check_window("residual", M, ldr));
   TRY(check_window("Z", 256, ldz));
   TRY(check_window("Wt", 256, ldw));
+  size_t ws_avail = 0;
+  TRY(check_ws(workspace, workspace_bytes, &ws_avail));
   TRY(check_device());
   mtp::GemmParams p;
+  p.ws = workspace; p.ws_bytes = ws_avail;
   p.A = Z; p.lda = ldz; p.B = Wt; p.ldb = ldw; p.Yacc = Yacc; p.ldacc = Yacc ? ldacc : 0;
   p.accumulate = accumulate ? 1 : 0; p.bias = bias; p.Y = Y; p.ldy = ldy;
   p.M = (int)M; p.Nout = (int)N; p.K = (int)Kp; p.a_src_rows = M;
@@ -258,7 +296,8 @@ mtp_status mtp_norm_fold_weights(const mtp_bf16* Wt, int64_t ldw, int64_t N, int
 
 mtp_status mtp_norm_column_linear(const mtp_bf16* X, int64_t ldx, const float* stats, const mtp_bf16* Wf,
                                   int64_t ldw, const float* colsum, const float* bias_f, mtp_bf16* Y, int64_t ldy,
-                                  int64_t M, int64_t N, int64_t K, mtp_act act, void* stream) {
+                                  int64_t M, int64_t N, int64_t K, mtp_act act,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   TRY(check_dims(M, N, K));
   if (act != MTP_ACT_NONE && act != MTP_ACT_GELU && act != MTP_ACT_SWIGLU)
     return fail(MTP_ERR_SHAPE, "unknown activation %d", (int)act);
@@ -273,8 +312,11 @@ mtp_status mtp_norm_column_linear(const mtp_bf16* X, int64_t ldx, const float* s
   TRY(check_vec(bias_f, "bias_f"));
   TRY(check_window("X", 256, ldx));
   TRY(check_window("Wf", (act == MTP_ACT_SWIGLU ? nout : 0) + 256, ldw));
+  size_t ws_avail = 0;
+  TRY(check_ws(workspace, workspace_bytes, &ws_avail));
   TRY(check_device());
   mtp::GemmParams p;
+  p.ws = workspace; p.ws_bytes = ws_avail;
   p.A = X; p.lda = ldx; p.B = Wf; p.ldb = ldw; p.Y = Y; p.ldy = ldy;
   p.M = (int)M; p.Nout = (int)nout; p.K = (int)K; p.up_offset = nout; p.a_src_rows = M;
   p.act = act == MTP_ACT_GELU ? 1 : 0;
@@ -331,7 +373,8 @@ static mtp_status check_f8(const void* p, const char* name, int64_t K, int64_t l
 
 mtp_status mtp_fp8_column_linear(const uint8_t* Xq, int64_t ldx, const float* x_scale_inv, const uint8_t* Wq,
                                  int64_t ldw, const float* w_scale_inv, const mtp_bf16* bias, mtp_bf16* Y,
-                                 int64_t ldy, int64_t M, int64_t N, int64_t K, mtp_act act, void* stream) {
+                                 int64_t ldy, int64_t M, int64_t N, int64_t K, mtp_act act,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   TRY(check_dims(M, N, K));
   if (K % 16 != 0) return fail(MTP_ERR_SHAPE, "the inner dimension %lld is not a multiple of 16", (long long)K);
   if (act != MTP_ACT_NONE && act != MTP_ACT_GELU && act != MTP_ACT_SWIGLU)
@@ -344,8 +387,11 @@ mtp_status mtp_fp8_column_linear(const uint8_t* Xq, int64_t ldx, const float* x_
   TRY(check_vec(bias, "bias"));
   TRY(check_window("Xq", 128, ldx));
   TRY(check_window("Wq", ((act == MTP_ACT_SWIGLU ? nout : 0) + 256) / 2 + 1, ldw));
+  size_t ws_avail = 0;
+  TRY(check_ws(workspace, workspace_bytes, &ws_avail));
   TRY(check_device());
   mtp::GemmParams p;
+  p.ws = workspace; p.ws_bytes = ws_avail;
   p.A = reinterpret_cast<const uint16_t*>(Xq); p.lda = ldx / 2;
   p.B = reinterpret_cast<const uint16_t*>(Wq); p.ldb = ldw / 2;
   p.bias = bias; p.Y = Y; p.ldy = ldy;
@@ -359,7 +405,7 @@ mtp_status mtp_fp8_column_linear(const uint8_t* Xq, int64_t ldx, const float* x_
 mtp_status mtp_fp8_row_linear_partial(const uint8_t* Zq, int64_t ldz, const float* z_scale_inv, const uint8_t* Wq,
                                       int64_t ldw, const float* w_scale_inv, float* Yacc, int64_t ldacc,
                                       int accumulate, const mtp_bf16* bias, mtp_bf16* Y, int64_t ldy, int64_t M,
-                                      int64_t N, int64_t Kp, void* stream) {
+                                      int64_t N, int64_t Kp, void* workspace, size_t workspace_bytes, void* stream) {
   TRY(check_dims(M, N, Kp));
   if (Kp % 16 != 0) return fail(MTP_ERR_SHAPE, "the inner dimension %lld is not a multiple of 16", (long long)Kp);
   TRY(check_f8(Zq, "Zq", Kp, ldz, z_scale_inv, "z_scale_inv"));
@@ -371,8 +417,11 @@ mtp_status mtp_fp8_row_linear_partial(const uint8_t* Zq, int64_t ldz, const floa
   TRY(check_vec(bias, "bias"));
   TRY(check_window("Zq", 128, ldz));
   TRY(check_window("Wq", 128, ldw));
+  size_t ws_avail = 0;
+  TRY(check_ws(workspace, workspace_bytes, &ws_avail));
   TRY(check_device());
   mtp::GemmParams p;
+  p.ws = workspace; p.ws_bytes = ws_avail;
   p.A = reinterpret_cast<const uint16_t*>(Zq); p.lda = ldz / 2;
   p.B = reinterpret_cast<const uint16_t*>(Wq); p.ldb = ldw / 2;
   p.Yacc = Yacc; p.ldacc = Yacc ? ldacc : 0; p.accumulate = accumulate ? 1 : 0;
@@ -383,7 +432,8 @@ mtp_status mtp_fp8_row_linear_partial(const uint8_t* Zq, int64_t ldz, const floa
 
 mtp_status mtp_mlp_forward(const mtp_bf16* X, int64_t M, int64_t H, int64_t F, int p, int r0, int r1,
                            const mtp_bf16* W1t, const mtp_bf16* b1, const mtp_bf16* W2t, const mtp_bf16* b2,
-                           mtp_act act, mtp_bf16* Z_ws, float* Yacc, mtp_bf16* Y, void* stream) {
+                           mtp_act act, mtp_bf16* Z_ws, float* Yacc, mtp_bf16* Y,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   if (p < 1 || F < 1 || F % p != 0) return fail(MTP_ERR_SHAPE, "F=%lld must be a positive multiple of p=%d", (long long)F, p);
   if (r0 < 0 || r1 > p || r0 >= r1) return fail(MTP_ERR_SHAPE, "rank range [%d, %d) is not inside [0, %d)", r0, r1, p);
   if (act != MTP_ACT_NONE && act != MTP_ACT_GELU && act != MTP_ACT_SWIGLU)
@@ -407,10 +457,13 @@ mtp_status mtp_mlp_forward(const mtp_bf16* X, int64_t M, int64_t H, int64_t F, i
   TRY(check_window("X", 256, H));
   TRY(check_window("W1t", (act == MTP_ACT_SWIGLU ? Fl : 0) + 256, H));
   TRY(check_window("W2t", 256, F));
+  size_t ws_avail = 0;
+  TRY(check_ws(workspace, workspace_bytes, &ws_avail));
   TRY(check_device());
   hipStream_t st = (hipStream_t)stream;
   for (int r = r0; r < r1; ++r) {
     mtp::GemmParams f1;
+    f1.ws = workspace; f1.ws_bytes = ws_avail;
     f1.A = X; f1.lda = H; f1.B = W1t + (int64_t)r * N1 * H; f1.ldb = H;
     f1.bias = b1 ? b1 + (int64_t)r * N1 : nullptr;
     f1.Y = Z_ws; f1.ldy = Fl; f1.M = (int)M; f1.Nout = (int)Fl; f1.K = (int)H; f1.up_offset = Fl; f1.a_src_rows = M;
@@ -418,6 +471,7 @@ mtp_status mtp_mlp_forward(const mtp_bf16* X, int64_t M, int64_t H, int64_t F, i
     mtp_status s = launched(mtp::gemm(f1, act == MTP_ACT_SWIGLU ? mtp::MODE_SWIGLU : mtp::MODE_COL, st), "fc1");
     if (s != MTP_OK) return s;
     mtp::GemmParams f2;
+    f2.ws = workspace; f2.ws_bytes = ws_avail;
     f2.A = Z_ws; f2.lda = Fl; f2.B = W2t + (int64_t)r * Fl; f2.ldb = F;
     f2.Yacc = Yacc; f2.ldacc = H; f2.accumulate = r > r0 ? 1 : 0;
     const bool last = full && r == p - 1;
@@ -431,19 +485,20 @@ mtp_status mtp_mlp_forward(const mtp_bf16* X, int64_t M, int64_t H, int64_t F, i
 
 mtp_status mtp_qkv_forward(const mtp_bf16* X, int64_t ldx, int64_t M, int64_t H, const mtp_bf16* Wqkv_t, int64_t ldw,
                            const mtp_bf16* bias, int nq_local, int ng_local, int head_dim, mtp_bf16* QKV, int64_t ldo,
-                           void* stream) {
+                           void* workspace, size_t workspace_bytes, void* stream) {
   if (nq_local < 1 || ng_local < 1 || head_dim < 1)
     return fail(MTP_ERR_SHAPE, "heads, groups and head_dim must be >= 1");
   if (nq_local % ng_local != 0)
     return fail(MTP_ERR_SHAPE, "query heads per rank (%d) must be a multiple of key/value groups per rank (%d)",
                 nq_local, ng_local);
   const int64_t N = ((int64_t)nq_local + 2 * (int64_t)ng_local) * head_dim;
-  return mtp_column_linear(X, ldx, Wqkv_t, ldw, bias, QKV, ldo, M, N, H, MTP_ACT_NONE, stream);
+  return mtp_column_linear(X, ldx, Wqkv_t, ldw, bias, QKV, ldo, M, N, H, MTP_ACT_NONE, workspace, workspace_bytes,
+                           stream);
 }
 
 mtp_status mtp_linear_dgrad(const mtp_bf16* dY, int64_t lddy, const mtp_bf16* Wt, int64_t ldw, float* dXacc,
                             int64_t ldacc, int accumulate, mtp_bf16* dX, int64_t lddx, int64_t M, int64_t N, int64_t K,
-                            void* stream) {
+                            void* workspace, size_t workspace_bytes, void* stream) {
   // dX [M x K] = dY [M x N] . Wt [N x K]: the product C = A B^T with A = dY (contraction N along its rows'
   // columns) and B = Wt read row-major-K (its rows are the contraction index)
   TRY(check_dims(M, K, N));
@@ -459,8 +514,11 @@ mtp_status mtp_linear_dgrad(const mtp_bf16* dY, int64_t lddy, const mtp_bf16* Wt
   if (dX) TRY(check_mat(dX, "dX", K, lddx));
   TRY(check_window("dY", 256, lddy));
   TRY(check_window("Wt", N, ldw));
+  size_t ws_avail = 0;
+  TRY(check_ws(workspace, workspace_bytes, &ws_avail));
   TRY(check_device());
   mtp::GemmParams p;
+  p.ws = workspace; p.ws_bytes = ws_avail;
   p.A = dY; p.lda = lddy; p.B = Wt; p.ldb = ldw; p.Y = dX; p.ldy = dX ? lddx : 0; p.Yacc = dXacc;
   p.ldacc = dXacc ? ldacc : 0; p.accumulate = accumulate ? 1 : 0;
   p.M = (int)M; p.Nout = (int)K; p.K = (int)N; p.a_src_rows = M;
@@ -468,7 +526,8 @@ mtp_status mtp_linear_dgrad(const mtp_bf16* dY, int64_t lddy, const mtp_bf16* Wt
 }
 
 mtp_status mtp_linear_wgrad(const mtp_bf16* dY, int64_t lddy, const mtp_bf16* X, int64_t ldx, float* dW, int64_t lddw,
-                            int accumulate, int64_t M, int64_t N, int64_t K, void* stream) {
+                            int accumulate, int64_t M, int64_t N, int64_t K,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   // dWt [N x K] (+)= dY^T [N x M] . X [M x K]: C = A B^T with A = dY and B = X both read row-major-K (their
   // rows are the contraction index M)
   if (M < 1 || N < 1 || K < 1) return fail(MTP_ERR_SHAPE, "sizes must be >= 1 (M=%lld N=%lld K=%lld)", (long long)M,
@@ -482,8 +541,11 @@ mtp_status mtp_linear_wgrad(const mtp_bf16* dY, int64_t lddy, const mtp_bf16* X,
                                              (long long)lddw, (long long)K);
   TRY(check_window("dY", M, lddy));
   TRY(check_window("X", M, ldx));
+  size_t ws_avail = 0;
+  TRY(check_ws(workspace, workspace_bytes, &ws_avail));
   TRY(check_device());
   mtp::GemmParams p;
+  p.ws = workspace; p.ws_bytes = ws_avail;
   p.A = dY; p.lda = lddy; p.B = X; p.ldb = ldx; p.Yacc = dW; p.ldacc = lddw; p.accumulate = accumulate ? 1 : 0;
   p.M = (int)N; p.Nout = (int)K; p.K = (int)M; p.a_src_rows = N;
   return launched(mtp::gemm_backward(p, true, true, (hipStream_t)stream), "linear wgrad");
@@ -512,24 +574,27 @@ mtp_status mtp_rope_qk(mtp_bf16* QKV, int64_t ldo, int64_t M, const int32_t* pos
 }
 
 mtp_status mtp_moe_route(const float* logits, int64_t T, int E, int k, int32_t* expert_offsets, int32_t* token_idx,
-                         float* token_w, void* stream) {
-  if (!logits || !expert_offsets || !token_idx || !token_w) return fail(MTP_ERR_NULL, "a routing pointer is NULL");
-  if (misaligned(logits) || misaligned(expert_offsets) || misaligned(token_idx) || misaligned(token_w))
+                         float* token_w, int32_t* token_rows, void* stream) {
+  if (!logits || !expert_offsets || !token_idx || !token_w || !token_rows)
+    return fail(MTP_ERR_NULL, "a routing pointer is NULL");
+  if (misaligned(logits) || misaligned(expert_offsets) || misaligned(token_idx) || misaligned(token_w) ||
+      misaligned(token_rows))
     return fail(MTP_ERR_ALIGN, "routing arrays must be 16-byte aligned");
   if (E < 1 || E > mtp::kMaxExperts) return fail(MTP_ERR_SHAPE, "E=%d must be in [1, %d]", E, mtp::kMaxExperts);
   if (k < 1 || k > E || k > 8) return fail(MTP_ERR_SHAPE, "k=%d must be in [1, min(E, 8)]", k);
   if (T < 1 || T * k > kIntMax) return fail(MTP_ERR_SHAPE, "T=%lld out of range", (long long)T);
   TRY(check_device());
-  return launched(mtp::moe_route(logits, (int)T, E, k, expert_offsets, token_idx, token_w, (hipStream_t)stream),
+  return launched(mtp::moe_route(logits, (int)T, E, k, expert_offsets, token_idx, token_w, token_rows,
+                                 (hipStream_t)stream),
                   "router");
 }
 
 mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, int64_t F, int k,
                                const int32_t* expert_offsets, const int32_t* token_idx, const float* token_w,
-                               const mtp_bf16* W1t, const mtp_bf16* W2t, mtp_bf16* Z_ws, float* Yacc, mtp_bf16* Y,
-                               void* stream) {
-  if (!expert_offsets || !token_idx || !token_w) return fail(MTP_ERR_NULL, "a routing table is NULL");
-  if (misaligned(expert_offsets) || misaligned(token_idx) || misaligned(token_w))
+                               const int32_t* token_rows, const mtp_bf16* W1t, const mtp_bf16* W2t, mtp_bf16* Z_ws,
+                               float* Y_rows, mtp_bf16* Y, void* stream) {
+  if (!expert_offsets || !token_idx || !token_w || !token_rows) return fail(MTP_ERR_NULL, "a routing table is NULL");
+  if (misaligned(expert_offsets) || misaligned(token_idx) || misaligned(token_w) || misaligned(token_rows))
     return fail(MTP_ERR_ALIGN, "routing tables must be 16-byte aligned");
   if (E < 1 || E > mtp::kMaxExperts) return fail(MTP_ERR_SHAPE, "E=%d must be in [1, %d]", E, mtp::kMaxExperts);
   if (k < 1 || k > E || k > 8) return fail(MTP_ERR_SHAPE, "k=%d must be in [1, min(E, 8)]", k);
@@ -540,7 +605,7 @@ mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, i
   TRY(check_mat(W1t, "W1t", H, H));
   TRY(check_mat(W2t, "W2t", F, F));
   TRY(check_mat(Z_ws, "Z_ws", F, F));
-  TRY(check_mat(Yacc, "Yacc", H, H));
+  TRY(check_mat(Y_rows, "Y_rows", H, H));
   TRY(check_mat(Y, "Y", H, H));
   TRY(check_window("X", T, H));
   TRY(check_window("W1t", F + 256, H));
@@ -548,21 +613,22 @@ mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, i
   TRY(check_window("Z_ws", 256, F));
   TRY(check_device());
   hipStream_t st = (hipStream_t)stream;
-  mtp_status s = launched(mtp::fill_zero_f32(Yacc, T, H, H, st), "zero Yacc");
-  if (s != MTP_OK) return s;
+  // grouped fc1: gather each dispatched row's token, SwiGLU epilogue -> Z_ws (dispatched order)
   mtp::GemmParams f1;
   f1.A = X; f1.lda = H; f1.a_rows = token_idx; f1.B = W1t; f1.ldb = H; f1.up_offset = F;
   f1.Y = Z_ws; f1.ldy = F; f1.Nout = (int)F; f1.K = (int)H; f1.a_src_rows = T;
   f1.group_offsets = expert_offsets; f1.groups = E; f1.group_stride_B = 2 * F * H;
-  s = launched(mtp::gemm_grouped(f1, mtp::MODE_SWIGLU, (int)(T * k), st), "grouped fc1");
+  mtp_status s = launched(mtp::gemm_grouped(f1, mtp::MODE_SWIGLU, (int)(T * k), st), "grouped fc1");
   if (s != MTP_OK) return s;
+  // grouped fc2: each dispatched row's fp32 output -> Y_rows
   mtp::GemmParams f2;
-  f2.A = Z_ws; f2.lda = F; f2.B = W2t; f2.ldb = F; f2.Yacc = Yacc; f2.ldacc = H;
-  f2.row_w = token_w; f2.out_rows = token_idx; f2.Nout = (int)H; f2.K = (int)F; f2.a_src_rows = T * k;
+  f2.A = Z_ws; f2.lda = F; f2.B = W2t; f2.ldb = F; f2.Yacc = Y_rows; f2.ldacc = H;
+  f2.Nout = (int)H; f2.K = (int)F; f2.a_src_rows = T * k;
   f2.group_offsets = expert_offsets; f2.groups = E; f2.group_stride_B = H * F;
-  s = launched(mtp::gemm_grouped(f2, mtp::MODE_COMBINE, (int)(T * k), st), "grouped fc2");
+  s = launched(mtp::gemm_grouped(f2, mtp::MODE_ROW, (int)(T * k), st), "grouped fc2");
   if (s != MTP_OK) return s;
-  return launched(mtp::f32_to_bf16_rows(Yacc, H, Y, H, T, H, st), "combine to bf16");
+  // weighted combine in each token's slot order, one bf16 rounding
+  return launched(mtp::moe_combine(Y_rows, H, token_rows, token_w, (int)T, k, (int)H, Y, H, st), "combine");
 }
 
 }  // extern "C"

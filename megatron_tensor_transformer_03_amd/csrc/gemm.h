@@ -7,7 +7,7 @@ namespace mtp {
 
 constexpr int kMaxExperts = 64;
 
-enum GemmMode { MODE_COL = 0, MODE_SWIGLU = 1, MODE_ROW = 2, MODE_COMBINE = 3 };
+enum GemmMode { MODE_COL = 0, MODE_SWIGLU = 1, MODE_ROW = 2 };
 
 // C = A . B^T over K, A [rows x K] (pitch lda, optional row gather), B [N x K] (pitch ldb).
 struct GemmParams {
@@ -21,10 +21,8 @@ struct GemmParams {
   const uint16_t* bias = nullptr;   // [N] (COL/ROW) or [2 * Nout] (SWIGLU)
   uint16_t* Y = nullptr;            // bf16 output
   int64_t ldy = 0;
-  float* Yacc = nullptr;            // fp32 partial / combine target
+  float* Yacc = nullptr;            // fp32 partial (grouped: the rows' fp32 outputs)
   int64_t ldacc = 0;
-  const float* row_w = nullptr;     // COMBINE: weight of each row
-  const int32_t* out_rows = nullptr;// COMBINE: output row of each row
   int M = 0;                        // rows (ungrouped)
   int Nout = 0;                     // output columns (SWIGLU: half the B rows used)
   int K = 0;
@@ -48,22 +46,42 @@ struct GemmParams {
   // both before the epilogue); K, lda and ldb then count pairs of one-byte codes
   const float* f8_scale_a = nullptr;
   const float* f8_scale_b = nullptr;
+  // Caller-owned workspace of the split schedule (NULL / 0: plans that need none): per-tile arrival counters
+  // (int32, zero between launches) in the first kSplitCounterBytes bytes, then the partial-tile slots.
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
   float* sk_ws = nullptr;           // split schedule: partial-tile slots (set at launch)
   int sk_chunks = 0;                // split schedule: K chunks per tile
   int sk_dp_tiles = 0;              // split schedule: leading tiles run whole (a multiple of the grid)
-  int* sk_cnt = nullptr;            // split schedule: per-tile arrival counters, zero between launches
+  int* sk_cnt = nullptr;            // split schedule: per-tile arrival counters (set at launch)
 };
 
-// Tile and schedule of a launch (split_groups 0: one workgroup per tile).
+// The split schedule's workspace starts with a counter block of fixed size (one int32 per output tile, for up
+// to kSplitMaxTiles tiles; split plans are only made for launches with at most that many), then the slots.  The
+// block's size does not depend on the launch, so a launch's slots never overlap the counters of another launch
+// that shares the workspace.
+constexpr int64_t kSplitMaxTiles = 4096;
+constexpr size_t kSplitCounterBytes = 4 * kSplitMaxTiles;
+
+// Tile and schedule of a launch (split_groups 0: one workgroup per tile) and the workspace it needs.
 struct GemmPlan {
   int bm = 0, bn = 0, split_groups = 0, id = 0, split_chunks = 0, dp_tiles = 0;
+  size_t ws_bytes = 0;
 };
-// row_major_k: 0 both operands K-contiguous; 1 B row-major-K (dgrad); 2 both row-major-K (wgrad)
-GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k = 0, bool allow_small = true);
-hipError_t release_split_workspaces();
+// row_major_k: 0 both operands K-contiguous; 1 B row-major-K (dgrad); 2 both row-major-K (wgrad).  Only
+// schedules whose workspace fits in ws_avail bytes are considered (one tile per workgroup needs none).
+GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k = 0, bool allow_small = true,
+                   size_t ws_avail = SIZE_MAX);
 
 enum GemmEpilogue { EPI_PLAIN = 0, EPI_NORM = 1, EPI_BDA = 2 };
 hipError_t gemm(const GemmParams& p, int mode, hipStream_t st, int epi = EPI_PLAIN);
+// per-mode forward dispatch (gemm_fwd_col.hip, gemm_fwd_swiglu.hip, gemm_fwd_row.hip) and the backward products
+// (gemm_bwd_dgrad.hip, gemm_bwd_wgrad.hip)
+hipError_t gemm_fwd_col(const GemmParams& p, hipStream_t st, int epi);
+hipError_t gemm_fwd_swiglu(const GemmParams& p, hipStream_t st, int epi);
+hipError_t gemm_fwd_row(const GemmParams& p, hipStream_t st, int epi);
+hipError_t gemm_dgrad(const GemmParams& p, hipStream_t st);
+hipError_t gemm_wgrad(const GemmParams& p, hipStream_t st);
 // MODE_ROW products whose A (and/or B) operand is stored [K x M] ([K x N]): lda / ldb are those pitches.
 hipError_t gemm_backward(const GemmParams& p, bool a_row_major_k, bool b_row_major_k, hipStream_t st);
 // E4M3 x E4M3 products (gemm_f8.hip): COL (none / GeLU), SWIGLU and ROW epilogues.
@@ -92,9 +110,9 @@ hipError_t norm_fold(const uint16_t* Wt, int64_t ldw, int N, int K, const uint16
 
 // MoE helpers (moe.hip).
 hipError_t moe_route(const float* logits, int T, int E, int k, int32_t* offsets, int32_t* token_idx,
-                     float* token_w, hipStream_t st);
-hipError_t fill_zero_f32(float* dst, int64_t rows, int64_t cols, int64_t ld, hipStream_t st);
-hipError_t f32_to_bf16_rows(const float* src, int64_t lds, uint16_t* dst, int64_t ldd, int64_t rows,
-                            int64_t cols, hipStream_t st);
+                     float* token_w, int32_t* token_rows, hipStream_t st);
+// out[t] = bf16(sum over s < k, in slot order, of token_w[r] * rows[r]), r = token_rows[t * k + s]; H % 4 == 0.
+hipError_t moe_combine(const float* rows, int64_t ldr, const int32_t* token_rows, const float* token_w, int T, int k,
+                       int H, uint16_t* out, int64_t ldo, hipStream_t st);
 
 }  // namespace mtp

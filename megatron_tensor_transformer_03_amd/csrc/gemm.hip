@@ -1,10 +1,9 @@
-// Launch planning and dispatch of the bf16 GEMM kernels (the kernel template is in gemm_kernel.h), the
-// split-K workspace, and the backward products.
+// Launch planning of the GEMM kernels and the top-level dispatch by mode (the kernel template is in
+// gemm_kernel.h; its instantiations are spread over gemm_fwd_*.hip, gemm_bwd_*.hip and gemm_grouped.hip so that
+// they compile in parallel).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <map>
-#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -13,22 +12,12 @@
 namespace mtp {
 
 // ------------------------------------------------------------------------------------------ launch
-// Workspace of the split schedule, per (device, stream): two partial-tile slots per workgroup and one
-// arrival counter per tile.  Counters are zero between launches (the last arrival on a tile resets its
-// counter), so they are cleared only when allocated.  Launches on one stream are ordered, so they can
-// share the stream's workspace.
 namespace {
-struct SplitWs {
-  float* ws = nullptr;
-  int* cnt = nullptr;
-  size_t ws_bytes = 0;
-  int64_t cnt_n = 0;
-};
-std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, SplitWs> g_ws;
 int g_cus[64] = {0};
 }  // namespace
 
+// CU count of the current device, read once per device (a plain attribute query: no allocation, no
+// synchronisation).
 int cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -38,30 +27,6 @@ int cu_count() {
     g_cus[dev] = n;
   }
   return g_cus[dev];
-}
-
-hipError_t split_workspace(hipStream_t st, size_t ws_bytes, int64_t cnt_n, float** ws, int** cnt) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  SplitWs& w = g_ws[{dev, st}];
-  if (w.ws_bytes < ws_bytes || w.cnt_n < cnt_n) {
-    if (w.ws || w.cnt) {
-      if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;  // earlier launches may still use them
-      if (w.ws) (void)hipFree(w.ws);
-      if (w.cnt) (void)hipFree(w.cnt);
-      w = SplitWs{};
-    }
-    if ((e = hipMalloc(&w.ws, ws_bytes)) != hipSuccess) return e;
-    if ((e = hipMalloc(&w.cnt, cnt_n * sizeof(int))) != hipSuccess) return e;
-    if ((e = fill_zero_f32(reinterpret_cast<float*>(w.cnt), 1, cnt_n, cnt_n, st)) != hipSuccess) return e;
-    w.ws_bytes = ws_bytes;
-    w.cnt_n = cnt_n;
-  }
-  *ws = w.ws;
-  *cnt = w.cnt;
-  return hipSuccess;
 }
 
 // Schedule choice, by a cost model in microseconds.  One workgroup per tile: (waves of tiles over the CUs) x
@@ -74,8 +39,9 @@ hipError_t split_workspace(hipStream_t st, size_t ws_bytes, int64_t cnt_n, float
 // output) and win on long K with few tiles (4096 x 1280 x 8192: 80 tiles of 256 x 256, 31% of the CUs
 // busy, 240 units in 3 chunks).  Hybrid: whole waves of tiles one per workgroup, then only the remaining
 // tiles split.  R and BW were fitted to the measured times of these schedules at the workloads' shapes
-// (within ~10%).
-GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k, bool allow_small) {
+// (within ~10%).  A split schedule needs a workspace (the tiles' arrival counters, then the split tiles'
+// partial slots); only schedules whose workspace fits in ws_avail are considered.
+GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k, bool allow_small, size_t ws_avail) {
   struct Opt { int bm, bn; double eff; int id; int ns_bk; int64_t slot_bytes; };
   // Relative efficiencies per output, against the 256 x 256 tile.  The forward products run both large
   // tiles with a 64-deep K step in two stages, where the 256 x 192 tile measured 0.80-0.86 at the workload
@@ -110,11 +76,11 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k
     const double tile_t = fwd ? 2.0 * o.bm * o.bn * (double)K / (o.eff * kR) : o.bm * o.bn / o.eff;
     const int64_t full_waves = tiles / (cus > 0 ? cus : 1);
     const double t_dp = (double)((tiles + cus - 1) / (cus > 0 ? cus : 1)) * tile_t;
-    if (t_dp < best_t * 0.999) { best_t = t_dp; best = GemmPlan{o.bm, (int)nbo, 0, o.id, 0, 0}; }
+    if (t_dp < best_t * 0.999) { best_t = t_dp; best = GemmPlan{o.bm, (int)nbo, 0, o.id, 0, 0, 0}; }
     // split-K (all tiles, or the tiles past the whole waves): S chunks of at least 4 ring passes; per unit
     // a pipeline fill of about 1.5 passes; chosen only when clearly faster
     const int64_t passes = (K + o.ns_bk - 1) / o.ns_bk;
-    if (o.slot_bytes == 0 || cus < 8 || cus % 8 != 0) continue;
+    if (o.slot_bytes == 0 || cus < 8 || cus % 8 != 0 || tiles > kSplitMaxTiles) continue;
     for (int hybrid = 0; hybrid < 2; ++hybrid) {
       const int64_t dp_tiles = hybrid ? full_waves * cus : 0;
       const int64_t split_tiles = tiles - dp_tiles;
@@ -122,12 +88,14 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k
       if (hybrid && (!fwd || o.id != 0 || dp_tiles == 0 || split_tiles == 0)) continue;
       for (int S : {2, 3, 4, 5, 6, 8}) {
         if (passes < 4 * S || split_tiles * S * o.slot_bytes > ((int64_t)512 << 20)) continue;
+        const size_t ws = kSplitCounterBytes + (size_t)(split_tiles * S * o.slot_bytes);
+        if (ws > ws_avail) continue;
         const int64_t waves = (split_tiles * S + cus - 1) / cus;
         const double t_sk = full_waves * hybrid * tile_t + waves * tile_t * (1.0 / S + 1.5 / passes) +
                             (fwd ? 2.0 * split_tiles * S * o.slot_bytes / kBW : tile_t * 0.03 * S);
         if (t_sk < best_t * 0.95) {
           best_t = t_sk;
-          best = GemmPlan{o.bm, (int)nbo, cus, o.id, S, (int)dp_tiles};
+          best = GemmPlan{o.bm, (int)nbo, cus, o.id, S, (int)dp_tiles, ws};
         }
       }
     }
@@ -135,73 +103,17 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k
   return best;
 }
 
-template <int MODE, int EPI = EPI_PLAIN>
-static hipError_t dispatch(const GemmParams& p, hipStream_t st) {
-  const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K, 0);
-  switch (pl.id) {
-    case 0: return launch_cfg<BigFwdTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
-    case 1:
-      if constexpr (MODE != MODE_SWIGLU)
-        return launch_cfg<WideFwdTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
-      return hipErrorInvalidValue;
-    case 2: return launch_cfg<HalfTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
-    default: return launch_cfg<SmallTile, MODE, false, false, false, EPI>(p, 0, st);  // (never split)
-  }
-}
-
-// Backward products: dgrad reads B row-major-K (AT = false, BT = true), wgrad both operands.
-template <bool AT, bool BT>
-static hipError_t dispatch_t(const GemmParams& p, hipStream_t st) {
-  const GemmPlan pl = gemm_plan(MODE_ROW, p.M, p.Nout, p.K, AT ? 2 : 1);
-  if (pl.id == 0) return launch_cfg<BigTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
-  if (pl.id == 4) return launch_cfg<SmallTTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
-  if (pl.id == 1) return launch_cfg<WideTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
-  return launch_cfg<HalfTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
-}
-
 hipError_t gemm_backward(const GemmParams& p, bool a_row_major_k, bool b_row_major_k, hipStream_t st) {
-  if (!a_row_major_k && b_row_major_k) return dispatch_t<false, true>(p, st);
-  if (a_row_major_k && b_row_major_k) return dispatch_t<true, true>(p, st);
+  if (!a_row_major_k && b_row_major_k) return gemm_dgrad(p, st);
+  if (a_row_major_k && b_row_major_k) return gemm_wgrad(p, st);
   return hipErrorInvalidValue;
 }
 
-hipError_t release_split_workspaces() {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if ((e = hipDeviceSynchronize()) != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  for (auto it = g_ws.begin(); it != g_ws.end();) {
-    if (it->first.first == dev) {
-      if (it->second.ws) (void)hipFree(it->second.ws);
-      if (it->second.cnt) (void)hipFree(it->second.cnt);
-      it = g_ws.erase(it);
-    } else {
-      ++it;
-    }
-  }
-  return hipSuccess;
-}
-
 hipError_t gemm(const GemmParams& p, int mode, hipStream_t st, int epi) {
-  if (epi == EPI_NORM) {
-    if (mode == MODE_COL) return dispatch<MODE_COL, EPI_NORM>(p, st);
-    if (mode == MODE_SWIGLU) return dispatch<MODE_SWIGLU, EPI_NORM>(p, st);
-    return hipErrorInvalidValue;
-  }
-  if (epi == EPI_BDA) return mode == MODE_ROW ? dispatch<MODE_ROW, EPI_BDA>(p, st) : hipErrorInvalidValue;
   switch (mode) {
-    case MODE_COL: return dispatch<MODE_COL>(p, st);
-    case MODE_SWIGLU: return dispatch<MODE_SWIGLU>(p, st);
-    case MODE_ROW: return dispatch<MODE_ROW>(p, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t gemm_grouped(const GemmParams& p, int mode, int rows_upper, hipStream_t st) {
-  switch (mode) {
-    case MODE_SWIGLU: return launch_cfg<BigFwdTile, MODE_SWIGLU, true>(p, rows_upper, st);
-    case MODE_COMBINE: return launch_cfg<BigFwdTile, MODE_COMBINE, true>(p, rows_upper, st);
+    case MODE_COL: return gemm_fwd_col(p, st, epi);
+    case MODE_SWIGLU: return gemm_fwd_swiglu(p, st, epi);
+    case MODE_ROW: return gemm_fwd_row(p, st, epi);
     default: return hipErrorInvalidValue;
   }
 }

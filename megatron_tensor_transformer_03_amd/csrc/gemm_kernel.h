@@ -9,9 +9,9 @@
 //   MODE_SWIGLU : column-parallel gate+up, bf16(silu(gate + bg) * (up + bu))
 //   MODE_ROW    : row-parallel partial in fp32 (Yacc = P or Yacc += P), and on the
 //                 last shard bf16(Yacc + bias): the local form of Y = sum_i Y_i
-//   MODE_COMBINE: MoE expert output, Yacc[token] += w * acc (fp32 atomics)
-// and a grouped variant (MoE experts) whose row tiles are laid over the
-// ragged per-expert row ranges read from device memory.
+// and a grouped variant (MoE experts, SWIGLU fc1 and ROW fc2 with fp32 row
+// outputs) whose row tiles are laid over the ragged per-expert row ranges read
+// from device memory.
 //
 // Design (gfx950, CDNA4):
 //  * A tile configuration (Cfg) fixes the block tile BM x BN, the wave grid, the
@@ -40,8 +40,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <map>
-#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -49,9 +47,8 @@
 
 namespace mtp {
 
-// split-K workspace and CU count (gemm.hip)
+// CU count of the current device (gemm.hip)
 int cu_count();
-hipError_t split_workspace(hipStream_t st, size_t ws_bytes, int64_t cnt_n, float** ws, int** cnt);
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -578,7 +575,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   const int ncol0 = tn * NB_OUT + (wave % WAVES_N) * TNO;        // first output column of the wave tile
   // Bias of this lane's output columns, read once with clamped indices (columns past Nout are computed but
   // never stored): per-element loads under branches would each wait a full memory latency.
-  constexpr bool kBias = MODE != MODE_COMBINE;
+  constexpr bool kBias = true;
   constexpr bool kNorm = EPI == EPI_NORM;
   float bias_g[kBias ? FNO : 1][4][4], bias_u[MODE == MODE_SWIGLU ? FNO : 1][4][4];
   // norm epilogue: column sums of the folded weight (gate and up parts) and each fragment row's statistics
@@ -730,8 +727,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     }
     return;
   }
-  // Direct stores: ROW with an fp32 target (the uniform choices are made once, outside the element loops)
-  // and COMBINE.
+  // Direct stores: ROW with an fp32 target (the uniform choices are made once, outside the element loops).
   auto direct = [&](auto ACCUM, auto WITH_Y) {
     constexpr bool accum = decltype(ACCUM)::value, with_y = decltype(WITH_Y)::value;
     float* const yacc = p.Yacc;
@@ -774,12 +770,6 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
               bda4(orow, n, v);
               store4_bf16(y + orow * ldy + n, v, valid);
             }
-          } else if constexpr (MODE == MODE_COMBINE) {
-            const float w = p.row_w[orow];
-            float* dst = yacc + (int64_t)p.out_rows[orow] * ldacc + n;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (r < valid) atomicAdd(dst + r, w * v[r]);
           }
         }
       }
@@ -795,8 +785,6 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
       if (p.Y) direct(F_{}, T_{});
       else direct(F_{}, F_{});
     }
-  } else {
-    direct(F_{}, F_{});
   }
   };
 
@@ -873,10 +861,14 @@ static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStrea
       const size_t slot = (size_t)C::FM * C::FN * 16 * sizeof(float) * C::NT;
       // whole tiles first: whole waves of the grid, leaving at least one tile to split
       if (dp_tiles < 0 || dp_tiles % split_groups != 0 || dp_tiles >= tiles) return hipErrorInvalidValue;
+      // the caller's workspace: the counter block, then the slots of the split tiles (the plan was chosen to fit)
+      if (tiles > kSplitMaxTiles || !p.ws ||
+          p.ws_bytes < kSplitCounterBytes + (size_t)(tiles - dp_tiles) * split_chunks * slot)
+        return hipErrorInvalidValue;
       p.sk_chunks = split_chunks;
       p.sk_dp_tiles = dp_tiles;
-      hipError_t e = split_workspace(st, (size_t)(tiles - dp_tiles) * split_chunks * slot, tiles, &p.sk_ws, &p.sk_cnt);
-      if (e != hipSuccess) return e;
+      p.sk_cnt = static_cast<int*>(p.ws);
+      p.sk_ws = reinterpret_cast<float*>(static_cast<char*>(p.ws) + kSplitCounterBytes);
       if (kfull)
         hipLaunchKernelGGL((gemm_kernel<C, MODE, false, true, true, AT, BT, EPI, F8>), dim3(split_groups), dim3(C::NT), 0, st, p);
       else
@@ -921,5 +913,31 @@ using WideTile = Cfg<MTP_WIDE_CFG>;            // 8 waves (64 x 96), 112 KB
 using HalfTile = Cfg<MTP_HALF_CFG>;            // 8 waves (64 x 64), 96 KB
 using SmallTile = Cfg<MTP_SMALL_CFG>;          // 8 waves (32 x 64), 128 KB
 using SmallTTile = Cfg<128, 128, 4, 2, 32, 4, true>;  // row-major-K operands: 8 waves (32 x 64), 64 KB
+
+
+// Forward dispatch of one mode and epilogue: the planner's tile and schedule (within the caller's workspace).
+template <int MODE, int EPI = EPI_PLAIN>
+static hipError_t dispatch_fwd(const GemmParams& p, hipStream_t st) {
+  const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K, 0, true, p.ws ? p.ws_bytes : 0);
+  switch (pl.id) {
+    case 0: return launch_cfg<BigFwdTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+    case 1:
+      if constexpr (MODE != MODE_SWIGLU)
+        return launch_cfg<WideFwdTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+      return hipErrorInvalidValue;
+    case 2: return launch_cfg<HalfTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+    default: return launch_cfg<SmallTile, MODE, false, false, false, EPI>(p, 0, st);  // (never split)
+  }
+}
+
+// Backward products: dgrad reads B row-major-K (AT = false, BT = true), wgrad both operands.
+template <bool AT, bool BT>
+static hipError_t dispatch_bwd(const GemmParams& p, hipStream_t st) {
+  const GemmPlan pl = gemm_plan(MODE_ROW, p.M, p.Nout, p.K, AT ? 2 : 1, true, p.ws ? p.ws_bytes : 0);
+  if (pl.id == 0) return launch_cfg<BigTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+  if (pl.id == 4) return launch_cfg<SmallTTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+  if (pl.id == 1) return launch_cfg<WideTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+  return launch_cfg<HalfTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+}
 
 }  // namespace mtp

@@ -1,14 +1,16 @@
 // MoE routing and small elementwise kernels.
 //
 // Router ("ai阅读megatron", MoELayer forward: router logits -> top-k ->
-// dispatch): per token, softmax over the E experts in fp32 and the k largest
+// dispatch -> weighted combine): per token, softmax over the E experts in fp32 and the k largest
 // logits (softmax is monotone, so this is the k most probable experts; ties go
 // to the lower expert index).  The dispatch tables group rows by expert in
 // ascending expert order and keep tokens ascending within an expert, which
 // needs a stable scatter: one workgroup walks the tokens in 1024-token
 // chunks, ranks each token within its expert by wave ballots plus an
 // across-wave prefix, and carries the running per-expert base between chunks.
-// Each token's logits are read once into registers.  The work is O(T * E); it is not a GEMM.
+// Each token's logits are read once into registers.  The work is O(T * E); it is not a GEMM.  The router
+// also records, for each token, the dispatched row of each of its k choices (most probable first): the
+// combine reads a token's k expert outputs through it in that fixed order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -79,7 +81,8 @@ template <int EMAX>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ token_idx,
-                                                              float* __restrict__ token_w) {
+                                                              float* __restrict__ token_w,
+                                                              int32_t* __restrict__ token_rows) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int base[kMaxExperts];
   __shared__ int wcnt[kMaxExperts][kRouteWaves];
@@ -141,6 +144,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __res
         for (int w = 0; w < wave; ++w) pos += wcnt[e][w];
         token_idx[pos] = t;
         token_w[pos] = c.w[s];
+        token_rows[(int64_t)t * k + s] = pos;
       }
     }
     __syncthreads();
@@ -153,23 +157,26 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __res
   }
 }
 
-__global__ void fill_zero_kernel(float* __restrict__ dst, int64_t rows, int64_t cols, int64_t ld) {
-  const int64_t total = rows * cols;
+// The weighted combine, token-major: thread i owns 4 consecutive columns of one token and adds the token's k
+// expert outputs in slot order (fp32 fused multiply-adds in a fixed order, so the result does not depend on
+// scheduling), then rounds once to bf16.  HBM-bound: T k H fp32 read, T H bf16 written.
+__global__ void combine_kernel(const float* __restrict__ rows, int64_t ldr, const int32_t* __restrict__ token_rows,
+                               const float* __restrict__ token_w, int T, int k, int H4,
+                               uint16_t* __restrict__ out, int64_t ldo) {
+  const int64_t total = (int64_t)T * H4;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = i / cols;
-    dst[r * ld + (i - r * cols)] = 0.f;
-  }
-}
-
-__global__ void f32_to_bf16_kernel(const float* __restrict__ src, int64_t lds, uint16_t* __restrict__ dst, int64_t ldd,
-                                   int64_t rows, int64_t cols4) {
-  const int64_t total = rows * cols4;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = i / cols4, c = (i - r * cols4) * 4;
-    const float4 v = *reinterpret_cast<const float4*>(src + r * lds + c);
+    const int64_t t = i / H4;
+    const int c = 4 * (int)(i - t * H4);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < k; ++s) {
+      const int r = token_rows[t * k + s];
+      const float w = token_w[r];
+      const float4 y = *reinterpret_cast<const float4*>(rows + (int64_t)r * ldr + c);
+      v.x = fmaf(w, y.x, v.x); v.y = fmaf(w, y.y, v.y); v.z = fmaf(w, y.z, v.z); v.w = fmaf(w, y.w, v.w);
+    }
     const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)v.x) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.y) << 16);
     const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)v.z) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.w) << 16);
-    *reinterpret_cast<uint2*>(dst + r * ldd + c) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(out + t * ldo + c) = make_uint2(lo, hi);
   }
 }
 
@@ -179,28 +186,27 @@ static unsigned grid_for(int64_t n) {
 }
 
 hipError_t moe_route(const float* logits, int T, int E, int k, int32_t* offsets, int32_t* token_idx, float* token_w,
-                     hipStream_t st) {
+                     int32_t* token_rows, hipStream_t st) {
   if (E <= 8)
-    hipLaunchKernelGGL(route_kernel<8>, dim3(1), dim3(kRouteThreads), 0, st, logits, T, E, k, offsets, token_idx, token_w);
+    hipLaunchKernelGGL(route_kernel<8>, dim3(1), dim3(kRouteThreads), 0, st, logits, T, E, k, offsets, token_idx, token_w,
+                       token_rows);
   else if (E <= 16)
-    hipLaunchKernelGGL(route_kernel<16>, dim3(1), dim3(kRouteThreads), 0, st, logits, T, E, k, offsets, token_idx, token_w);
+    hipLaunchKernelGGL(route_kernel<16>, dim3(1), dim3(kRouteThreads), 0, st, logits, T, E, k, offsets, token_idx, token_w,
+                       token_rows);
   else if (E <= 32)
-    hipLaunchKernelGGL(route_kernel<32>, dim3(1), dim3(kRouteThreads), 0, st, logits, T, E, k, offsets, token_idx, token_w);
+    hipLaunchKernelGGL(route_kernel<32>, dim3(1), dim3(kRouteThreads), 0, st, logits, T, E, k, offsets, token_idx, token_w,
+                       token_rows);
   else
-    hipLaunchKernelGGL(route_kernel<64>, dim3(1), dim3(kRouteThreads), 0, st, logits, T, E, k, offsets, token_idx, token_w);
+    hipLaunchKernelGGL(route_kernel<64>, dim3(1), dim3(kRouteThreads), 0, st, logits, T, E, k, offsets, token_idx, token_w,
+                       token_rows);
   return hipGetLastError();
 }
 
-hipError_t fill_zero_f32(float* dst, int64_t rows, int64_t cols, int64_t ld, hipStream_t st) {
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(rows * cols)), dim3(256), 0, st, dst, rows, cols, ld);
-  return hipGetLastError();
-}
-
-// cols must be a multiple of 4 and both pitches multiples of 4 (callers validate pitches as multiples of 8).
-hipError_t f32_to_bf16_rows(const float* src, int64_t lds, uint16_t* dst, int64_t ldd, int64_t rows, int64_t cols,
-                            hipStream_t st) {
-  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(grid_for(rows * cols / 4)), dim3(256), 0, st, src, lds, dst, ldd, rows,
-                     cols / 4);
+// H must be a multiple of 4, and both pitches (callers validate them as multiples of 8).
+hipError_t moe_combine(const float* rows, int64_t ldr, const int32_t* token_rows, const float* token_w, int T, int k,
+                       int H, uint16_t* out, int64_t ldo, hipStream_t st) {
+  hipLaunchKernelGGL(combine_kernel, dim3(grid_for((int64_t)T * (H / 4))), dim3(256), 0, st, rows, ldr, token_rows,
+                     token_w, T, k, H / 4, out, ldo);
   return hipGetLastError();
 }
 

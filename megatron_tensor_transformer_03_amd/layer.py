@@ -9,8 +9,9 @@ attention is not part of this path), and the MLP with fc1 column-parallel
 router and the expert MLPs ("ai阅读megatron", MoELayer forward).
 
 ``dims`` uses the keys of ``synth.configs``; ``inputs`` holds device tensors
-named as there.  Outputs are allocated once by ``RankForward`` and reused by
-every ``step()``.
+named as there.  Outputs, and one zero-filled split-K workspace shared by the
+step's GEMMs (they run in order on one stream), are allocated once by
+``RankForward`` and reused by every ``step()``.
 """
 from __future__ import annotations
 
@@ -26,13 +27,15 @@ class RankForward:
         dev = next(iter(inputs.values())).device
         bf, f32 = torch.bfloat16, torch.float32
         self.out = {}
-        if "E" in dims:  # MoE expert MLP
+        self.ws = None
+        if "E" in dims:  # MoE expert MLP (grouped GEMMs: no split-K workspace)
             T, H, E, F, k = dims["T"], dims["H"], dims["E"], dims["F"], dims["k"]
             self.out.update(offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
                             token_idx=torch.empty(T * k, dtype=torch.int32, device=dev),
                             token_w=torch.empty(T * k, dtype=f32, device=dev),
+                            token_rows=torch.empty(T * k, dtype=torch.int32, device=dev),
                             Z=torch.empty(T * k, F, dtype=bf, device=dev),
-                            Yacc=torch.empty(T, H, dtype=f32, device=dev),
+                            Y_rows=torch.empty(T * k, H, dtype=f32, device=dev),
                             Y=torch.empty(T, H, dtype=bf, device=dev))
             return
         M, H, p = dims["M"], dims["H"], dims["p"]
@@ -48,6 +51,14 @@ class RankForward:
                 self.out["attn_partial"] = torch.empty(M, H, dtype=f32, device=dev)
         F_l = dims["F"] // p
         self.out["Z"] = torch.empty(M, F_l, dtype=bf, device=dev)
+        # the step's GEMMs as (M, N, K, act) in mtp_gemm_plan's terms: one workspace fits them all
+        shapes = [(M, H, F_l, mtp.ACT_NONE), (M, inputs["W1t"].shape[0] // (p if dims["ranks"] == "all" else 1), H,
+                                              dims["act"])]
+        if "nq" in dims:
+            shapes.append((M, self.out["qkv"].shape[1], H, mtp.ACT_NONE))
+        if "ctx" in inputs:
+            shapes.append((M, H, inputs["ctx"].shape[1], mtp.ACT_NONE))
+        self.ws = mtp.workspace_for(shapes, dev)
         if dims["ranks"] == "all":
             self.out["Y"] = torch.empty(M, H, dtype=bf, device=dev)
             if p > 1:  # fp32 sum over the shards
@@ -61,15 +72,15 @@ class RankForward:
         d, t, o = self.d, self.t, self.out
         if "E" in d:
             return [("route", lambda: mtp.mtp_moe_route(t["logits"], d["k"], o["offsets"], o["token_idx"],
-                                                          o["token_w"])),
+                                                          o["token_w"], o["token_rows"])),
                     ("moe_mlp", lambda: mtp.mtp_moe_mlp_forward(t["X"], d["E"], d["F"], d["k"], o["offsets"],
-                                                                o["token_idx"], o["token_w"], t["W1t"], t["W2t"],
-                                                                o["Z"], o["Yacc"], o["Y"]))]
+                                                                o["token_idx"], o["token_w"], o["token_rows"],
+                                                                t["W1t"], t["W2t"], o["Z"], o["Y_rows"], o["Y"]))]
         p = d["p"]
         out = []
         if "nq" in d:
             out.append(("qkv", lambda: mtp.mtp_qkv_forward(t["X"], t["Wqkv_t"], t.get("bqkv"), d["nq"] // p,
-                                                           d["ng"] // p, d["d"], o["qkv"])))
+                                                           d["ng"] // p, d["d"], o["qkv"], workspace=self.ws)))
         if "rope" in d:
             r = d["rope"]
             out.append(("rope", lambda: mtp.mtp_rope_qk(o["qkv"], self.positions, d["nq"] // p, d["ng"] // p, d["d"],
@@ -77,22 +88,27 @@ class RankForward:
         if "ctx" in t:
             if p == 1:  # the whole layer: the all-reduce is the identity, bias added here
                 out.append(("out_proj", lambda: mtp.mtp_row_linear_partial(t["ctx"], t["Wo_t"], None, False,
-                                                                           t.get("bo"), o["attn_out"])))
+                                                                           t.get("bo"), o["attn_out"],
+                                                                           workspace=self.ws)))
             else:       # this rank's fp32 partial of the all-reduce
-                out.append(("out_proj", lambda: mtp.mtp_row_linear_partial(t["ctx"], t["Wo_t"], o["attn_partial"])))
+                out.append(("out_proj", lambda: mtp.mtp_row_linear_partial(t["ctx"], t["Wo_t"], o["attn_partial"],
+                                                                           workspace=self.ws)))
         if d["ranks"] == "all" and p > 1:
             # every shard in turn; the all-reduce is the fp32 sum in rank order
             out.append(("mlp", lambda: mtp.mtp_mlp_forward(t["X"], t["W1t"], t.get("b1"), t["W2t"], t.get("b2"),
-                                                           d["act"], p, 0, p, o["Z"], o["Yacc"], o["Y"])))
+                                                           d["act"], p, 0, p, o["Z"], o["Yacc"], o["Y"],
+                                                           workspace=self.ws)))
         else:
             # one shard (p = 1: the whole MLP): fc1 column linear with bias + activation fused, then fc2 as a
             # row-parallel partial; with p = 1 the sum over shards is the identity and b2 is added in its epilogue
-            out.append(("fc1", lambda: mtp.mtp_column_linear(t["X"], t["W1t"], t.get("b1"), o["Z"], d["act"])))
+            out.append(("fc1", lambda: mtp.mtp_column_linear(t["X"], t["W1t"], t.get("b1"), o["Z"], d["act"],
+                                                             workspace=self.ws)))
             if p == 1:
                 out.append(("fc2", lambda: mtp.mtp_row_linear_partial(o["Z"], t["W2t"], None, False, t.get("b2"),
-                                                                      o["Y"])))
+                                                                      o["Y"], workspace=self.ws)))
             else:
-                out.append(("fc2", lambda: mtp.mtp_row_linear_partial(o["Z"], t["W2t"], o["mlp_partial"])))
+                out.append(("fc2", lambda: mtp.mtp_row_linear_partial(o["Z"], t["W2t"], o["mlp_partial"],
+                                                                      workspace=self.ws)))
         return out
 
     def step(self, mark=None):
@@ -147,21 +163,26 @@ class PreNormLayer:
         if "rope" in dims:
             self.positions = torch.arange(M, dtype=torch.int32, device=dev)
         self.act = act
+        self.ws = mtp.workspace_for([(M, self.out["qkv"].shape[1], H, mtp.ACT_NONE), (M, H, inputs["ctx"].shape[1],
+                                     mtp.ACT_NONE), (M, inputs["W1t"].shape[0], H, act), (M, H, F, mtp.ACT_NONE)],
+                                    dev)
 
     def calls(self):
         d, t, x, o = self.d, self.t, self.x, self.out
         out = [("norm1", lambda: mtp.mtp_norm_stats(t["X"], o["stats1"], self.kind, self.eps)),
-               ("qkv", lambda: mtp.mtp_norm_column_linear(t["X"], o["stats1"], *self.qkv_w, o["qkv"]))]
+               ("qkv", lambda: mtp.mtp_norm_column_linear(t["X"], o["stats1"], *self.qkv_w, o["qkv"],
+                                                          workspace=self.ws))]
         if "rope" in d:
             r = d["rope"]
             out.append(("rope", lambda: mtp.mtp_rope_qk(o["qkv"], self.positions, d["nq"], d["ng"], d["d"],
                                                         r["rotary_dim"], r["base"], r["interleaved"])))
         out += [("attn_bda", lambda: mtp.mtp_row_linear_bda(t["ctx"], t["Wo_t"], t["X"], o["h1"], bias=t.get("bo"),
-                                                             keep=x["keep1"], p_drop=x["p_drop"])),
+                                                             keep=x["keep1"], p_drop=x["p_drop"], workspace=self.ws)),
                 ("norm2", lambda: mtp.mtp_norm_stats(o["h1"], o["stats2"], self.kind, self.eps)),
-                ("fc1", lambda: mtp.mtp_norm_column_linear(o["h1"], o["stats2"], *self.fc1_w, o["Z"], self.act)),
+                ("fc1", lambda: mtp.mtp_norm_column_linear(o["h1"], o["stats2"], *self.fc1_w, o["Z"], self.act,
+                                                           workspace=self.ws)),
                 ("mlp_bda", lambda: mtp.mtp_row_linear_bda(o["Z"], t["W2t"], o["h1"], o["out"], bias=t.get("b2"),
-                                                           keep=x["keep2"], p_drop=x["p_drop"]))]
+                                                           keep=x["keep2"], p_drop=x["p_drop"], workspace=self.ws))]
         return out
 
     def step(self, mark=None):

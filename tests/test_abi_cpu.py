@@ -37,17 +37,17 @@ def test_library_exports_every_header_symbol():
 
 def test_abi_version_and_strings():
     L = mtp.lib()
-    assert L.mtp_abi_version() == 1
+    assert L.mtp_abi_version() == 2
     for s in range(6):
         assert L.mtp_status_string(s)
     assert L.mtp_status_string(99) == b"unknown status"
 
 
 def col(**kw):
-    a = dict(X=P, ldx=64, Wt=P2, ldw=64, bias=None, Y=P3, ldy=32, M=16, N=32, K=64, act=0)
+    a = dict(X=P, ldx=64, Wt=P2, ldw=64, bias=None, Y=P3, ldy=32, M=16, N=32, K=64, act=0, ws=None, wsb=0)
     a.update(kw)
     return mtp.lib().mtp_column_linear(a["X"], a["ldx"], a["Wt"], a["ldw"], a["bias"], a["Y"], a["ldy"], a["M"],
-                                       a["N"], a["K"], a["act"], None)
+                                       a["N"], a["K"], a["act"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -60,6 +60,7 @@ def col(**kw):
     (dict(M=1 << 31), SHAPE),
     (dict(act=2, N=31), SHAPE),                    # SwiGLU needs even N
     (dict(act=7), SHAPE),
+    (dict(ws=BAD, wsb=1 << 20), ALIGN),            # a workspace must be 16-byte aligned
 ])
 def test_column_linear_rejects(kw, status):
     assert col(**kw) == status
@@ -70,13 +71,15 @@ def test_column_linear_rejects(kw, status):
 def test_valid_call_without_gpu_is_unsupported_not_launched():
     assert col() == UNSUPPORTED
     assert col(act=2, N=32, ldy=16) == UNSUPPORTED
+    assert col(ws=P4, wsb=1 << 20) == UNSUPPORTED        # with a workspace
+    assert col(ws=None, wsb=1 << 20) == UNSUPPORTED      # a size without a workspace counts as none
 
 
 def row(**kw):
     a = dict(Z=P, ldz=64, Wt=P2, ldw=128, Yacc=P3, ldacc=32, acc=0, bias=None, Y=None, ldy=0, M=8, N=32, Kp=64)
     a.update(kw)
     return mtp.lib().mtp_row_linear_partial(a["Z"], a["ldz"], a["Wt"], a["ldw"], a["Yacc"], a["ldacc"], a["acc"],
-                                            a["bias"], a["Y"], a["ldy"], a["M"], a["N"], a["Kp"], None)
+                                            a["bias"], a["Y"], a["ldy"], a["M"], a["N"], a["Kp"], None, 0, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -96,7 +99,7 @@ def mlp(**kw):
              Y=P2)
     a.update(kw)
     return mtp.lib().mtp_mlp_forward(a["X"], a["M"], a["H"], a["F"], a["p"], a["r0"], a["r1"], a["W1t"], a["b1"],
-                                     a["W2t"], a["b2"], a["act"], a["Z"], a["Yacc"], a["Y"], None)
+                                     a["W2t"], a["b2"], a["act"], a["Z"], a["Yacc"], a["Y"], None, 0, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -123,52 +126,62 @@ def test_mlp_valid_forms_reach_the_device_check():
 def test_qkv_gqa_rule():
     L = mtp.lib()
     # 3 query heads over 2 key/value groups violates the grouping rule
-    assert L.mtp_qkv_forward(P, 64, 16, 64, P2, 64, None, 3, 2, 8, P3, 64, None) == SHAPE
-    assert L.mtp_qkv_forward(P, 64, 16, 64, P2, 64, None, 4, 0, 8, P3, 64, None) == SHAPE
-    assert L.mtp_qkv_forward(P, 64, 16, 64, P2, 64, None, 4, 2, 8, P3, 56, None) == SHAPE  # ldo < (4+4)*8
+    assert L.mtp_qkv_forward(P, 64, 16, 64, P2, 64, None, 3, 2, 8, P3, 64, None, 0, None) == SHAPE
+    assert L.mtp_qkv_forward(P, 64, 16, 64, P2, 64, None, 4, 0, 8, P3, 64, None, 0, None) == SHAPE
+    assert L.mtp_qkv_forward(P, 64, 16, 64, P2, 64, None, 4, 2, 8, P3, 56, None, 0, None) == SHAPE  # ldo < (4+4)*8
 
 
 def test_moe_rejects():
     L = mtp.lib()
-    assert L.mtp_moe_route(None, 16, 8, 2, P, P2, P3, None) == NULL
-    assert L.mtp_moe_route(P, 16, 8, 9, P, P2, P3, None) == SHAPE
-    assert L.mtp_moe_route(P, 16, 65, 2, P, P2, P3, None) == SHAPE
-    assert L.mtp_moe_route(P, 16, 2, 3, P, P2, P3, None) == SHAPE
-    assert L.mtp_moe_route(P, 0, 8, 2, P, P2, P3, None) == SHAPE
-    assert L.mtp_moe_route(BAD, 16, 8, 2, P, P2, P3, None) == ALIGN
-    args = [P, 64, 64, 8, 128, 2, P2, P3, P4, P, P2, P3, P4, P]
+    assert L.mtp_moe_route(None, 16, 8, 2, P, P2, P3, P4, None) == NULL
+    assert L.mtp_moe_route(P, 16, 8, 2, P, P2, P3, None, None) == NULL     # token_rows is required
+    assert L.mtp_moe_route(P, 16, 8, 9, P, P2, P3, P4, None) == SHAPE
+    assert L.mtp_moe_route(P, 16, 65, 2, P, P2, P3, P4, None) == SHAPE
+    assert L.mtp_moe_route(P, 16, 2, 3, P, P2, P3, P4, None) == SHAPE
+    assert L.mtp_moe_route(P, 0, 8, 2, P, P2, P3, P4, None) == SHAPE
+    assert L.mtp_moe_route(BAD, 16, 8, 2, P, P2, P3, P4, None) == ALIGN
+    assert L.mtp_moe_route(P, 16, 8, 2, P, P2, P3, BAD, None) == ALIGN
+    # X, T, H, E, F, k, offsets, token_idx, token_w, token_rows, W1t, W2t, Z_ws, Y_rows, Y
+    args = [P, 64, 64, 8, 128, 2, P2, P3, P4, P, P2, P3, P4, P, P2]
     bad = list(args)
     bad[4] = 100  # F % 8
     assert L.mtp_moe_mlp_forward(*bad, None) == SHAPE
     bad = list(args)
     bad[6] = None
     assert L.mtp_moe_mlp_forward(*bad, None) == NULL
+    bad = list(args)
+    bad[9] = None  # token_rows
+    assert L.mtp_moe_mlp_forward(*bad, None) == NULL
+    bad = list(args)
+    bad[13] = None  # Y_rows
+    assert L.mtp_moe_mlp_forward(*bad, None) == NULL
 
 
 @pytest.mark.skipif(_gpu_present(), reason="on a GPU box a valid call would launch")
 def test_moe_valid_call_reaches_the_device_check():
     L = mtp.lib()
-    assert L.mtp_moe_route(P, 16, 8, 2, P, P2, P3, None) == UNSUPPORTED
-    assert L.mtp_moe_mlp_forward(P, 64, 64, 8, 128, 2, P2, P3, P4, P, P2, P3, P4, P, None) == UNSUPPORTED
+    assert L.mtp_moe_route(P, 16, 8, 2, P, P2, P3, P4, None) == UNSUPPORTED
+    assert L.mtp_moe_mlp_forward(P, 64, 64, 8, 128, 2, P2, P3, P4, P, P2, P3, P4, P, P2, None) == UNSUPPORTED
 
 
 def test_gemm_plan_rejects():
     L = mtp.lib()
     o = [ctypes.c_int(0) for _ in range(3)]
-    a = [ctypes.addressof(x) for x in o]
+    ws = ctypes.c_size_t(0)
+    a = [ctypes.addressof(x) for x in o] + [ctypes.addressof(ws)]
     assert L.mtp_gemm_plan(0, 8, 8, 0, *a) == SHAPE
     assert L.mtp_gemm_plan(8, 8, 12, 0, *a) == SHAPE      # K not a multiple of 8
     assert L.mtp_gemm_plan(8, 7, 8, 2, *a) == SHAPE       # SwiGLU with odd N
     assert L.mtp_gemm_plan(8, 8, 8, 5, *a) == SHAPE       # unknown activation
-    assert L.mtp_gemm_plan(8, 8, 8, 0, a[0], None, a[2]) == NULL
+    assert L.mtp_gemm_plan(8, 8, 8, 0, a[0], None, a[2], a[3]) == NULL
 
 
 @pytest.mark.skipif(_gpu_present(), reason="on a GPU box the plan is computed")
-def test_gemm_plan_and_release_need_a_device():
+def test_gemm_plan_needs_a_device():
     L = mtp.lib()
     o = [ctypes.c_int(0) for _ in range(3)]
-    assert L.mtp_gemm_plan(4096, 4096, 4096, 0, *[ctypes.addressof(x) for x in o]) == UNSUPPORTED
-    assert L.mtp_release_workspaces() == UNSUPPORTED
+    ptrs = [ctypes.addressof(x) for x in o]
+    assert L.mtp_gemm_plan(4096, 4096, 4096, 0, *ptrs, None) == UNSUPPORTED   # the workspace size is optional
 
 
 def test_rope_rejects():
@@ -225,7 +238,7 @@ def dgrad(**kw):
     a = dict(dY=P, lddy=64, Wt=P2, ldw=40, dXacc=P3, ldacc=40, acc=0, dX=None, lddx=0, M=8, N=64, K=40)
     a.update(kw)
     return mtp.lib().mtp_linear_dgrad(a["dY"], a["lddy"], a["Wt"], a["ldw"], a["dXacc"], a["ldacc"], a["acc"],
-                                      a["dX"], a["lddx"], a["M"], a["N"], a["K"], None)
+                                      a["dX"], a["lddx"], a["M"], a["N"], a["K"], None, 0, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -247,7 +260,7 @@ def wgrad(**kw):
     a = dict(dY=P, lddy=40, X=P2, ldx=24, dW=P3, lddw=24, acc=0, M=13, N=33, K=17)
     a.update(kw)
     return mtp.lib().mtp_linear_wgrad(a["dY"], a["lddy"], a["X"], a["ldx"], a["dW"], a["lddw"], a["acc"], a["M"],
-                                      a["N"], a["K"], None)
+                                      a["N"], a["K"], None, 0, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -290,7 +303,7 @@ def test_norm_entry_points_reject():
     ncl = lambda **kw: L.mtp_norm_column_linear(
         kw.get("X", P), kw.get("ldx", 64), kw.get("stats", P2), kw.get("Wf", P3), kw.get("ldw", 64),
         kw.get("colsum", None), kw.get("bias_f", None), kw.get("Y", P4), kw.get("ldy", 32), kw.get("M", 8),
-        kw.get("N", 32), kw.get("K", 64), kw.get("act", 0), None)
+        kw.get("N", 32), kw.get("K", 64), kw.get("act", 0), None, 0, None)
     assert ncl(stats=None) == NULL and ncl(X=None) == NULL and ncl(Y=None) == NULL
     assert ncl(stats=P2 + 4) == ALIGN and ncl(colsum=BAD) == ALIGN
     assert ncl(act=2, N=31) == SHAPE and ncl(act=7) == SHAPE and ncl(ldy=16) == SHAPE
@@ -302,7 +315,7 @@ def bda(**kw):
     a.update(kw)
     return mtp.lib().mtp_row_linear_bda(a["Z"], a["ldz"], a["Wt"], a["ldw"], a["Yacc"], a["ldacc"], a["acc"],
                                         a["bias"], a["res"], a["ldr"], a["keep"], a["ldk"], a["p"], a["Y"], a["ldy"],
-                                        a["M"], a["N"], a["Kp"], None)
+                                        a["M"], a["N"], a["Kp"], None, 0, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -320,7 +333,7 @@ def test_norm_and_bda_valid_calls_reach_the_device_check():
     L = mtp.lib()
     assert L.mtp_norm_stats(P, 64, 4, 64, 1, 1e-6, P2, None) == UNSUPPORTED
     assert L.mtp_norm_fold_weights(P, 64, 16, 64, P2, None, None, 1, P3, 64, None, P4, None) == UNSUPPORTED
-    assert L.mtp_norm_column_linear(P, 64, P2, P3, 64, None, None, P4, 32, 8, 64, 64, 2, None) == UNSUPPORTED
+    assert L.mtp_norm_column_linear(P, 64, P2, P3, 64, None, None, P4, 32, 8, 64, 64, 2, None, 0, None) == UNSUPPORTED
     assert bda() == UNSUPPORTED
     assert bda(keep=None, p=0.0, Yacc=P2, ldacc=40, acc=1) == UNSUPPORTED
 
@@ -335,7 +348,7 @@ def test_fp8_entry_points_reject():
     col = lambda **kw: L.mtp_fp8_column_linear(
         kw.get("Xq", P), kw.get("ldx", 64), kw.get("xs", P2), kw.get("Wq", P3), kw.get("ldw", 64), kw.get("ws", P4),
         kw.get("bias", None), kw.get("Y", P), kw.get("ldy", 32), kw.get("M", 8), kw.get("N", 32), kw.get("K", 64),
-        kw.get("act", 0), None)
+        kw.get("act", 0), None, 0, None)
     assert col(xs=None) == NULL and col(ws=None) == NULL and col(Wq=None) == NULL
     assert col(K=56, ldx=64, ldw=64) == SHAPE          # K % 16
     assert col(ldx=72) == SHAPE and col(ldw=48) == SHAPE  # code pitches: multiples of 16, >= K
@@ -343,7 +356,7 @@ def test_fp8_entry_points_reject():
     row = lambda **kw: L.mtp_fp8_row_linear_partial(
         kw.get("Zq", P), kw.get("ldz", 64), kw.get("zs", P2), kw.get("Wq", P3), kw.get("ldw", 64), kw.get("ws", P4),
         kw.get("Yacc", P), kw.get("ldacc", 32), kw.get("acc", 0), None, kw.get("Y", None), kw.get("ldy", 0),
-        kw.get("M", 8), kw.get("N", 32), kw.get("Kp", 64), None)
+        kw.get("M", 8), kw.get("N", 32), kw.get("Kp", 64), None, 0, None)
     assert row(Yacc=None) == NULL and row(Yacc=None, Y=P2, ldy=32, acc=1) == NULL and row(zs=None) == NULL
     assert row(Kp=40, ldz=48, ldw=48) == SHAPE and row(ldacc=30) == SHAPE
 
@@ -352,8 +365,8 @@ def test_fp8_entry_points_reject():
 def test_fp8_valid_calls_reach_the_device_check():
     L = mtp.lib()
     assert L.mtp_fp8_quantize(P, 64, 4, 64, P2, 64, P3, P4, None) == UNSUPPORTED
-    assert L.mtp_fp8_column_linear(P, 64, P2, P3, 64, P4, None, P, 32, 8, 32, 64, 1, None) == UNSUPPORTED
-    assert L.mtp_fp8_row_linear_partial(P, 64, P2, P3, 64, P4, P, 32, 1, None, None, 0, 8, 32, 64, None) == UNSUPPORTED
+    assert L.mtp_fp8_column_linear(P, 64, P2, P3, 64, P4, None, P, 32, 8, 32, 64, 1, None, 0, None) == UNSUPPORTED
+    assert L.mtp_fp8_row_linear_partial(P, 64, P2, P3, 64, P4, P, 32, 1, None, None, 0, 8, 32, 64, None, 0, None) == UNSUPPORTED
 
 
 def test_fp8_scratch_size_matches_header():
@@ -366,11 +379,24 @@ def test_fp8_scratch_size_matches_header():
 def test_gemm_plan_backward_rejects_and_needs_a_device():
     L = mtp.lib()
     o = [ctypes.c_int(0) for _ in range(3)]
-    ptrs = [ctypes.addressof(x) for x in o]
+    ws = ctypes.c_size_t(0)
+    ptrs = [ctypes.addressof(x) for x in o] + [ctypes.addressof(ws)]
     assert L.mtp_gemm_plan_backward(0, 8, 8, 0, *ptrs) == SHAPE
-    assert L.mtp_gemm_plan_backward(8, 8, 8, 1, None, ptrs[1], ptrs[2]) == NULL
+    assert L.mtp_gemm_plan_backward(8, 8, 8, 1, None, ptrs[1], ptrs[2], ptrs[3]) == NULL
     if not _gpu_present():
         assert L.mtp_gemm_plan_backward(8, 8, 8, 0, *ptrs) == UNSUPPORTED
+
+
+def test_fp8_gemm_plan_rejects_and_needs_a_device():
+    L = mtp.lib()
+    o = [ctypes.c_int(0) for _ in range(3)]
+    ws = ctypes.c_size_t(0)
+    ptrs = [ctypes.addressof(x) for x in o] + [ctypes.addressof(ws)]
+    assert L.mtp_fp8_gemm_plan(8, 8, 24, 0, *ptrs) == SHAPE     # K % 16
+    assert L.mtp_fp8_gemm_plan(8, 7, 32, 2, *ptrs) == SHAPE     # SwiGLU with odd N
+    assert L.mtp_fp8_gemm_plan(8, 8, 32, 0, ptrs[0], ptrs[1], None, ptrs[3]) == NULL
+    if not _gpu_present():
+        assert L.mtp_fp8_gemm_plan(8, 8, 32, 0, *ptrs) == UNSUPPORTED
 
 
 def test_fp8_delayed_rejects():
