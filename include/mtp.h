@@ -96,6 +96,24 @@ mtp_status mtp_column_linear(const mtp_bf16* X, int64_t ldx, const mtp_bf16* Wt,
                              int64_t K, mtp_act act, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation): mtp_column_linear with the split-K
+ * workspace taken from a static device array of the library,
+ * MTP_STATIC_SCRATCH_BYTES per GPU (held until the process ends), instead of a
+ * caller argument.  The call allocates nothing.  scratch_bytes (at most
+ * MTP_STATIC_SCRATCH_BYTES, else MTP_ERR_SHAPE) is how much of it the plan may
+ * use, as workspace_bytes for mtp_column_linear: the same value gives the
+ * same plan and bitwise the same output (0: one workgroup per tile).  Every
+ * call on a GPU shares that GPU's array and each call that splits first
+ * clears its counter block, so calls that overlap on one GPU (different
+ * streams, concurrent graphs) race; calls ordered on one stream do not.
+ */
+#define MTP_STATIC_SCRATCH_BYTES (32u << 20)
+mtp_status mtp_column_linear_static(const mtp_bf16* X, int64_t ldx, const mtp_bf16* Wt, int64_t ldw,
+                                    const mtp_bf16* bias, mtp_bf16* Y, int64_t ldy, int64_t M, int64_t N,
+                                    int64_t K, mtp_act act, size_t scratch_bytes, void* stream);
+
+/*
  * RowParallelLinear partial product of one shard (Y_i = X_i W_i) and the
  * local form of the all-reduce Y = sum_i Y_i:
  *   P = Z[M x Kp] . Wt[N x Kp]^T in fp32, no bias.  Wt is this rank's input

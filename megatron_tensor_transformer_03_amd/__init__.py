@@ -16,6 +16,7 @@ import re
 ACT_NONE, ACT_GELU, ACT_SWIGLU = 0, 1, 2
 NORM_LAYER, NORM_RMS = 0, 1
 FP8_WS_FLOATS = 1024  # scratch of mtp_fp8_quantize (fp32 elements)
+STATIC_SCRATCH_BYTES = 32 << 20  # the static scratch of mtp_column_linear_static
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmtp.so")
@@ -42,6 +43,7 @@ def lib():
         sz = ctypes.c_size_t
         sig = {
             "mtp_column_linear": [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, ci, vp, sz, vp],
+            "mtp_column_linear_static": [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, ci, sz, vp],
             "mtp_row_linear_partial": [vp, i64, vp, i64, vp, i64, ci, vp, vp, i64, i64, i64, i64, vp, sz, vp],
             "mtp_mlp_forward": [vp, i64, i64, i64, ci, ci, ci, vp, vp, vp, vp, ci, vp, vp, vp, vp, sz, vp],
             "mtp_qkv_forward": [vp, i64, i64, i64, vp, i64, vp, ci, ci, ci, vp, i64, vp, sz, vp],
@@ -253,6 +255,17 @@ def mtp_column_linear(X, Wt, bias, Y, act=ACT_NONE, workspace=None):
     N = Wt.shape[0]
     _check("mtp_column_linear", lib().mtp_column_linear(
         _ptr(X), _ld(X), _ptr(Wt), _ld(Wt), _ptr(bias), _ptr(Y), _ld(Y), M, N, K, act, *_ws(workspace),
+        _stream(X)))
+    return Y
+
+
+def mtp_column_linear_static(X, Wt, bias, Y, act=ACT_NONE, scratch_bytes=0):
+    """mtp_column_linear on the library's static scratch (allocates nothing): ``scratch_bytes`` of it, at most
+    STATIC_SCRATCH_BYTES, may be used by the split-K schedule."""
+    M, K = X.shape
+    N = Wt.shape[0]
+    _check("mtp_column_linear_static", lib().mtp_column_linear_static(
+        _ptr(X), _ld(X), _ptr(Wt), _ld(Wt), _ptr(bias), _ptr(Y), _ld(Y), M, N, K, act, int(scratch_bytes),
         _stream(X)))
     return Y
 

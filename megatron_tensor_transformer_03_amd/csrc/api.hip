@@ -203,6 +203,33 @@ mtp_status mtp_column_linear(const mtp_bf16* X, int64_t ldx, const mtp_bf16* Wt,
                   "column linear");
 }
 
+mtp_status mtp_column_linear_static(const mtp_bf16* X, int64_t ldx, const mtp_bf16* Wt, int64_t ldw,
+                                    const mtp_bf16* bias, mtp_bf16* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                    mtp_act act, size_t scratch_bytes, void* stream) {
+  TRY(check_dims(M, N, K));
+  if (act != MTP_ACT_NONE && act != MTP_ACT_GELU && act != MTP_ACT_SWIGLU)
+    return fail(MTP_ERR_SHAPE, "unknown activation %d", (int)act);
+  if (act == MTP_ACT_SWIGLU && N % 2 != 0) return fail(MTP_ERR_SHAPE, "SwiGLU needs an even N (got %lld)", (long long)N);
+  if (scratch_bytes > (size_t)MTP_STATIC_SCRATCH_BYTES)
+    return fail(MTP_ERR_SHAPE, "scratch_bytes %zu exceeds the static scratch of %zu bytes", scratch_bytes,
+                (size_t)MTP_STATIC_SCRATCH_BYTES);
+  const int64_t nout = act == MTP_ACT_SWIGLU ? N / 2 : N;
+  TRY(check_mat(X, "X", K, ldx));
+  TRY(check_mat(Wt, "Wt", K, ldw));
+  TRY(check_mat(Y, "Y", nout, ldy));
+  TRY(check_vec(bias, "bias"));
+  TRY(check_window("X", 256, ldx));
+  TRY(check_window("Wt", (act == MTP_ACT_SWIGLU ? nout : 0) + 256, ldw));
+  TRY(check_device());
+  mtp::GemmParams p;
+  p.A = X; p.lda = ldx; p.B = Wt; p.ldb = ldw; p.bias = bias; p.Y = Y; p.ldy = ldy;
+  p.M = (int)M; p.Nout = (int)nout; p.K = (int)K; p.up_offset = nout; p.a_src_rows = M;
+  p.act = act == MTP_ACT_GELU ? 1 : 0;
+  return launched(mtp::gemm_column_static(p, act == MTP_ACT_SWIGLU ? mtp::MODE_SWIGLU : mtp::MODE_COL, scratch_bytes,
+                                          (hipStream_t)stream),
+                  "column linear (static scratch)");
+}
+
 mtp_status mtp_row_linear_partial(const mtp_bf16* Z, int64_t ldz, const mtp_bf16* Wt, int64_t ldw, float* Yacc,
                                   int64_t ldacc, int accumulate, const mtp_bf16* bias, mtp_bf16* Y, int64_t ldy,
                                   int64_t M, int64_t N, int64_t Kp,

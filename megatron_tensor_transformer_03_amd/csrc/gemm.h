@@ -82,6 +82,9 @@ hipError_t gemm_fwd_swiglu(const GemmParams& p, hipStream_t st, int epi);
 hipError_t gemm_fwd_row(const GemmParams& p, hipStream_t st, int epi);
 hipError_t gemm_dgrad(const GemmParams& p, hipStream_t st);
 hipError_t gemm_wgrad(const GemmParams& p, hipStream_t st);
+// COL / SWIGLU product whose split-K workspace is the library's static scratch (static_scratch.hip), at most
+// scratch_bytes of it (p.ws is ignored).
+hipError_t gemm_column_static(GemmParams p, int mode, size_t scratch_bytes, hipStream_t st);
 // MODE_ROW products whose A (and/or B) operand is stored [K x M] ([K x N]): lda / ldb are those pitches.
 hipError_t gemm_backward(const GemmParams& p, bool a_row_major_k, bool b_row_major_k, hipStream_t st);
 // E4M3 x E4M3 products (gemm_f8.hip): COL (none / GeLU), SWIGLU and ROW epilogues.

@@ -27,7 +27,7 @@ def _gpu_present():
 def test_library_exports_every_header_symbol():
     L = mtp.lib()
     names = mtp.header_symbols()
-    assert len(names) == 23
+    assert len(names) == 24
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", mtp.LIB_PATH], capture_output=True, text=True).stdout
@@ -162,6 +162,24 @@ def test_moe_valid_call_reaches_the_device_check():
     L = mtp.lib()
     assert L.mtp_moe_route(P, 16, 8, 2, P, P2, P3, P4, None) == UNSUPPORTED
     assert L.mtp_moe_mlp_forward(P, 64, 64, 8, 128, 2, P2, P3, P4, P, P2, P3, P4, P, P2, None) == UNSUPPORTED
+
+
+def test_column_linear_static_rejects_oversize_scratch_and_bad_args():
+    L = mtp.lib()
+    lim = mtp.STATIC_SCRATCH_BYTES
+    call = lambda **kw: L.mtp_column_linear_static(
+        kw.get("X", P), 64, P2, 64, None, kw.get("Y", P3), 32, 16, 32, 64, kw.get("act", 0), kw.get("sb", 0), None)
+    assert call(sb=lim + 1) == SHAPE and b"static scratch" in L.mtp_last_error()
+    assert call(X=None) == NULL and call(Y=BAD) == ALIGN and call(act=9) == SHAPE
+    if not _gpu_present():
+        assert call(sb=lim) == UNSUPPORTED and call() == UNSUPPORTED
+
+
+def test_static_scratch_size_matches_header():
+    import re
+    with open(mtp.HEADER) as f:
+        m = re.search(r"#define MTP_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == mtp.STATIC_SCRATCH_BYTES
 
 
 def test_gemm_plan_rejects():
