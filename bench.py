@@ -5,14 +5,20 @@ A step is one pass of the per-rank hot path over one batch of synthetic input
 already resident in HBM: QKV column-parallel GEMM + bias, attention
 out-projection row-parallel GEMM, fc1 column-parallel GEMM with fused bias +
 GeLU (or SwiGLU), fc2 row-parallel GEMM (and for the MoE workload the router
-and the grouped expert GEMMs).  The default workload is the GPT-345M-shaped
-layer at TP=1 with 4096 tokens; --workload picks another.
+and the grouped expert GEMMs).  The default workload is one rank's share of a
+GPT-3 175B-shaped layer at TP=8 (2048 tokens); --workload picks another.
 
-Prints one JSON line: TFLOP/s (algorithmic 2*M*N*K over the step's GEMMs,
-whole steps timed), the dominant kernel's roofline position (HIP events
-around that kernel in every timed step, on the stream the kernels are
-launched on; events without the system-scope cache fence, so timing does not
-flush the caches), and the CPU oracle timed on a bounded sample of the same
+Timing is cold by default: before every timed step an untimed 1 GiB write
+evicts the 256 MB memory-side cache (the rank's weights would otherwise stay
+resident across steps), and each step is bracketed by HIP events.  The same
+steps back to back (warm) are timed as well and reported beside it.
+
+Prints one JSON line: TFLOP/s (algorithmic 2*M*N*K over the step's GEMMs),
+the dominant kernel's roofline position (HIP events around that kernel in
+every timed step, on the stream the kernels are launched on; events without
+the system-scope cache fence, so timing does not flush the caches) against
+the nominal dense bf16 peak and against a peak calibrated on this GPU with an
+MFMA-only loop, and the CPU oracle timed on a bounded sample of the same
 workload on this host's cores.
 """
 import argparse
@@ -340,7 +346,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gpt345m", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="gpt3_175b_rank0", choices=sorted(WORKLOADS))
+    ap.add_argument("--warm", action="store_true",
+                    help="time back-to-back steps as the headline (default: a 1 GiB cache-evicting write before each "
+                         "timed step; warm figures are reported in either case)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
@@ -468,24 +477,67 @@ def main():
                 launch()
         torch.cuda.synchronize()
     pre, dom_launch, post = launchers
-    dom_events = []
-    torch.cuda.synchronize()
-    start = timer.record()
-    for _ in range(args.steps):
-        pre()
-        e0 = timer.record()
-        dom_launch()
-        dom_events.append((e0, timer.record()))
-        post()
-    stop = timer.record()
-    torch.cuda.synchronize()
-    ms = timer.elapsed_ms(start, stop) / args.steps
-    dom_ms = [timer.elapsed_ms(e0, e1) for e0, e1 in dom_events]
-    timer.release([start, stop] + [e for pair in dom_events for e in pair])
-    dom_avg = sum(dom_ms) / len(dom_ms)
+
+    # Cold: an untimed write of 1 GiB before every timed step evicts the 256 MB memory-side cache; each step is
+    # bracketed by events (the flush lies outside every bracket).  Warm: the same steps back to back.
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+
+    def timed(cold):
+        step_ms, dom_ms = [], []
+        torch.cuda.synchronize()
+        ev_all = []
+        if not cold:
+            start = timer.record()
+        for _ in range(args.steps):
+            if cold:
+                flush_buf.fill_(1.0)
+                s0 = timer.record()
+            pre()
+            e0 = timer.record()
+            dom_launch()
+            e1 = timer.record()
+            post()
+            if cold:
+                s1 = timer.record()
+                ev_all.append((s0, e0, e1, s1))
+            else:
+                ev_all.append((None, e0, e1, None))
+        if not cold:
+            stop = timer.record()
+        torch.cuda.synchronize()
+        for s0, e0, e1, s1 in ev_all:
+            dom_ms.append(timer.elapsed_ms(e0, e1))
+            if cold:
+                step_ms.append(timer.elapsed_ms(s0, s1))
+        events = [e for quad in ev_all for e in quad if e is not None]
+        if cold:
+            ms = sum(step_ms) / len(step_ms)
+        else:
+            ms = timer.elapsed_ms(start, stop) / args.steps
+            events += [start, stop]
+        timer.release(events)
+        return ms, sum(dom_ms) / len(dom_ms)
+
+    ms_warm, dom_warm = timed(False)
+    ms_cold, dom_cold = timed(True)
+    del flush_buf
+    ms, dom_avg = (ms_warm, dom_warm) if args.warm else (ms_cold, dom_cold)
     achieved = flop_by_label[dom] / (dom_avg * 1e-3) / 1e12
     flop = w.flop
     value = flop / (ms * 1e-3) / 1e12
+
+    # calibrated peak: an MFMA-only loop over every CU (8 waves each), about 20 ms
+    cal_out = torch.empty(4096, dtype=torch.float32, device="cuda")
+    cal_blocks, cal_iters = 4 * torch.cuda.get_device_properties(0).multi_processor_count, 20000
+    mtp.mtp_mfma_calibrate(cal_out, cal_blocks, 200)
+    torch.cuda.synchronize()
+    c0 = timer.record()
+    mtp.mtp_mfma_calibrate(cal_out, cal_blocks, cal_iters)
+    c1 = timer.record()
+    torch.cuda.synchronize()
+    cal_ms = timer.elapsed_ms(c0, c1)
+    timer.release([c0, c1])
+    cal_peak = cal_blocks * 8 * cal_iters * 8 * 32768 / (cal_ms * 1e-3) / 1e12
     traffic = measured_traffic(w.name, dom)
 
     # non-GEMM kernels of the step, against the HBM roofline: algorithmic bytes per launch / event time
@@ -520,7 +572,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "desc": w.desc, "flop_per_step": flop,
                    "launch": "hip_graph" if args.graphs else "eager",
+                   "timing": "warm (steps back to back)" if args.warm else
+                             "cold (1 GiB write before each timed step evicts the 256 MB memory-side cache)",
                    "pct_of_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+                   "calibrated_mfma_peak_tflops": round(cal_peak, 1),
+                   "pct_of_calibrated_peak": round(100 * value / cal_peak, 2),
+                   "cold": {"ms_per_step": round(ms_cold, 5), "value": round(flop / (ms_cold * 1e-3) / 1e12, 2),
+                            "dominant_kernel_us": round(1000 * dom_cold, 2)},
+                   "warm": {"ms_per_step": round(ms_warm, 5), "value": round(flop / (ms_warm * 1e-3) / 1e12, 2),
+                            "dominant_kernel_us": round(1000 * dom_warm, 2)},
                    "gemms": [[lb, m, n, k] for lb, m, n, k in w.gemms],
                    "per_gemm_us": {lb: round(1000 * v, 2) for lb, v in avg.items()},
                    "per_gemm_tflops": {lb: round(flop_by_label[lb] / (avg[lb] * 1e-3) / 1e12, 1)
@@ -530,7 +590,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": dom, "kernel_us": round(1000 * dom_avg, 2),
                      "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "calibrated_peak": round(cal_peak, 1), "frac_of_calibrated": round(achieved / cal_peak, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

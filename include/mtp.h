@@ -380,6 +380,16 @@ mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, i
 mtp_status mtp_gemm_plan(int64_t M, int64_t N, int64_t K, mtp_act act, int* tile_m, int* tile_n,
                          int* split_k, size_t* workspace_bytes);
 
+/*
+ * Measurement helper (not part of the layer): an MFMA-only loop of `blocks`
+ * workgroups of 8 waves, each wave issuing iters x 8 independent
+ * v_mfma_f32_32x32x16_bf16 (32768 FLOP each) with no memory traffic, to
+ * calibrate the bf16 rate the chip sustains at the clock it runs under such
+ * a load.  FLOP = blocks * 8 * iters * 8 * 32768.  out: blocks fp32 (device,
+ * written only in a case that does not occur; it keeps the work live).
+ */
+mtp_status mtp_mfma_calibrate(float* out, int blocks, int iters, void* stream);
+
 /* Static text for a status code. */
 const char* mtp_status_string(mtp_status s);
 /* Detail of the last failing call on this thread ("" if none). */

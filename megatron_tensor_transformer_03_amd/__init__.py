@@ -44,6 +44,7 @@ def lib():
         sig = {
             "mtp_column_linear": [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, ci, vp, sz, vp],
             "mtp_column_linear_static": [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, ci, sz, vp],
+            "mtp_mfma_calibrate": [vp, ci, ci, vp],
             "mtp_row_linear_partial": [vp, i64, vp, i64, vp, i64, ci, vp, vp, i64, i64, i64, i64, vp, sz, vp],
             "mtp_mlp_forward": [vp, i64, i64, i64, ci, ci, ci, vp, vp, vp, vp, ci, vp, vp, vp, vp, sz, vp],
             "mtp_qkv_forward": [vp, i64, i64, i64, vp, i64, vp, ci, ci, ci, vp, i64, vp, sz, vp],
@@ -268,6 +269,11 @@ def mtp_column_linear_static(X, Wt, bias, Y, act=ACT_NONE, scratch_bytes=0):
         _ptr(X), _ld(X), _ptr(Wt), _ld(Wt), _ptr(bias), _ptr(Y), _ld(Y), M, N, K, act, int(scratch_bytes),
         _stream(X)))
     return Y
+
+
+def mtp_mfma_calibrate(out, blocks, iters):
+    """Enqueue the MFMA-only calibration loop (measurement helper); FLOP = blocks * 8 * iters * 8 * 32768."""
+    _check("mtp_mfma_calibrate", lib().mtp_mfma_calibrate(_ptr(out), blocks, iters, _stream(out)))
 
 
 def mtp_row_linear_partial(Z, Wt, Yacc=None, accumulate=False, bias=None, Y=None, workspace=None):

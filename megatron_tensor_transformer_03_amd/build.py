@@ -11,7 +11,7 @@ LIB = os.path.join(HERE, "libmtp.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["gemm.hip", "gemm_fwd_col.hip", "gemm_fwd_swiglu.hip", "gemm_fwd_row.hip", "gemm_bwd_dgrad.hip",
            "gemm_bwd_wgrad.hip", "gemm_grouped.hip", "gemm_f8.hip", "fp8.hip", "moe.hip", "rope.hip", "norm.hip", "api.hip",
-           "static_scratch.hip"]
+           "static_scratch.hip", "calibrate.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++20", "-munsafe-fp-atomics",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
 

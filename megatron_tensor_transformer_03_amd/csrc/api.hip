@@ -658,4 +658,12 @@ mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, i
   return launched(mtp::moe_combine(Y_rows, H, token_rows, token_w, (int)T, k, (int)H, Y, H, st), "combine");
 }
 
+mtp_status mtp_mfma_calibrate(float* out, int blocks, int iters, void* stream) {
+  if (!out) return fail(MTP_ERR_NULL, "out is NULL");
+  if (reinterpret_cast<uintptr_t>(out) & 3u) return fail(MTP_ERR_ALIGN, "out is not 4-byte aligned");
+  if (blocks < 1 || iters < 1) return fail(MTP_ERR_SHAPE, "blocks and iters must be >= 1");
+  TRY(check_device());
+  return launched(mtp::mfma_calibrate(out, blocks, iters, (hipStream_t)stream), "mfma calibration");
+}
+
 }  // extern "C"

@@ -100,6 +100,9 @@ hipError_t fp8_quantize_delayed(const uint16_t* X, int64_t ldx, int M, int K, ui
 // rows_upper: total rows over all groups (an upper bound is enough; spare tiles exit).
 hipError_t gemm_grouped(const GemmParams& p, int mode, int rows_upper, hipStream_t st);
 
+// MFMA-only loop over `blocks` workgroups of 8 waves, `iters` x 8 products of 32 x 32 x 16 per wave (calibrate.hip).
+hipError_t mfma_calibrate(float* out, int blocks, int iters, hipStream_t st);
+
 // Rotary position embedding of the first `heads` heads of each row, in place (rope.hip).
 hipError_t rope_qk(uint16_t* qkv, int64_t ldo, int M, const int32_t* positions, int heads, int head_dim,
                    int rotary_dim, double base, bool interleaved, hipStream_t st);

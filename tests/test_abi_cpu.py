@@ -27,7 +27,7 @@ def _gpu_present():
 def test_library_exports_every_header_symbol():
     L = mtp.lib()
     names = mtp.header_symbols()
-    assert len(names) == 24
+    assert len(names) == 25
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", mtp.LIB_PATH], capture_output=True, text=True).stdout
@@ -173,6 +173,15 @@ def test_column_linear_static_rejects_oversize_scratch_and_bad_args():
     assert call(X=None) == NULL and call(Y=BAD) == ALIGN and call(act=9) == SHAPE
     if not _gpu_present():
         assert call(sb=lim) == UNSUPPORTED and call() == UNSUPPORTED
+
+
+def test_mfma_calibrate_rejects():
+    L = mtp.lib()
+    assert L.mtp_mfma_calibrate(None, 256, 10, None) == NULL
+    assert L.mtp_mfma_calibrate(P + 2, 256, 10, None) == ALIGN
+    assert L.mtp_mfma_calibrate(P, 0, 10, None) == SHAPE and L.mtp_mfma_calibrate(P, 256, 0, None) == SHAPE
+    if not _gpu_present():
+        assert L.mtp_mfma_calibrate(P, 256, 10, None) == UNSUPPORTED
 
 
 def test_static_scratch_size_matches_header():
