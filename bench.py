@@ -38,17 +38,23 @@ METRIC = "TFLOP/s per TP-rank QKV+MLP forward (bf16) and % of MI355X MFMA peak"
 WORKLOADS = {"gpt345m": 1, "gpt3_175b_rank0": 2, "llama70b_rank0": 3, "moe": 4, "tiny": 0}
 
 
+KERNEL_SOURCES = ("gemm_kernel.h", "gemm.h", "gemm.hip", "gemm_fwd_col.hip", "gemm_fwd_swiglu.hip", "gemm_fwd_row.hip",
+                  "gemm_grouped.hip", "moe.hip", "rope.hip")
+
+
 def kernel_source_hash():
+    """Hash of the sources of the forward GEMM, grouped-GEMM, MoE and RoPE kernels: a counter record taken on
+    other sources is not used."""
     h = hashlib.sha256()
-    for f in ("gemm_kernel.h", "gemm.hip", "gemm.h"):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "megatron_tensor_transformer_03_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, kernel_label):
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+def measured_traffic(workload, kernel_label, cold=True):
+    """HBM bytes per launch of the dominant kernel (in cold or warm steps) from the committed rocprofv3 counter
+    runs, if they were taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -57,7 +63,7 @@ def measured_traffic(workload, kernel_label):
     e = rec.get(workload, {}).get(kernel_label)
     if not e or e.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return e["hbm_bytes_per_launch"]
+    return e["hbm_bytes_per_launch" if cold else "hbm_bytes_per_launch_warm"]
 
 
 class _FenceFreeEvents:
@@ -538,7 +544,7 @@ def main():
     cal_ms = timer.elapsed_ms(c0, c1)
     timer.release([c0, c1])
     cal_peak = cal_blocks * 8 * cal_iters * 8 * 32768 / (cal_ms * 1e-3) / 1e12
-    traffic = measured_traffic(w.name, dom)
+    traffic = measured_traffic(w.name, dom, cold=not args.warm)
 
     # non-GEMM kernels of the step, against the HBM roofline: algorithmic bytes per launch / event time
     aux = {}
