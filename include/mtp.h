@@ -352,11 +352,27 @@ mtp_status mtp_moe_route(const float* logits, int64_t T, int E, int k, int32_t* 
  * W1t is [E][2F x H] ([gate; up] per expert), W2t is [E][H x F].  The routing
  * tables are device arrays as written by mtp_moe_route (no host copy is
  * made).  Z_ws and Y_rows are caller-owned scratch; nothing needs zeroing.
+ * workspace: as for the GEMM calls (16-byte aligned or NULL, first 16 KiB
+ * zero before first use and left zero).  When it holds the bytes that
+ * mtp_moe_plan reports, the fc2 product runs each expert's last, partial
+ * row tile in K chunks on otherwise idle CUs, the chunks added in a fixed
+ * order (deterministic; the sum order of those rows differs from the
+ * unsplit one by fp32 rounding only); with less, or NULL, it runs unsplit.
  */
 mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, int64_t F, int k,
                                const int32_t* expert_offsets, const int32_t* token_idx,
                                const float* token_w, const int32_t* token_rows, const mtp_bf16* W1t,
-                               const mtp_bf16* W2t, mtp_bf16* Z_ws, float* Y_rows, mtp_bf16* Y, void* stream);
+                               const mtp_bf16* W2t, mtp_bf16* Z_ws, float* Y_rows, mtp_bf16* Y,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The split of mtp_moe_mlp_forward's fc2 product for these sizes on the
+ * current device: K chunks per expert tail tile (0: none) and the workspace
+ * bytes that split needs (0 when none).  Rejects what mtp_moe_mlp_forward
+ * rejects for the same sizes.
+ */
+mtp_status mtp_moe_plan(int64_t T, int64_t H, int E, int64_t F, int k, int* split_chunks,
+                        size_t* workspace_bytes);
 
 /*
  * The launch plan the GEMM calls would use for an [M x K] . [N x K]^T

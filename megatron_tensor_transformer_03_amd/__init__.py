@@ -49,7 +49,8 @@ def lib():
             "mtp_mlp_forward": [vp, i64, i64, i64, ci, ci, ci, vp, vp, vp, vp, ci, vp, vp, vp, vp, sz, vp],
             "mtp_qkv_forward": [vp, i64, i64, i64, vp, i64, vp, ci, ci, ci, vp, i64, vp, sz, vp],
             "mtp_moe_route": [vp, i64, ci, ci, vp, vp, vp, vp, vp],
-            "mtp_moe_mlp_forward": [vp, i64, i64, ci, i64, ci, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+            "mtp_moe_mlp_forward": [vp, i64, i64, ci, i64, ci, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "mtp_moe_plan": [i64, i64, ci, i64, ci, vp, vp],
             "mtp_gemm_plan": [i64, i64, i64, ci, vp, vp, vp, vp],
             "mtp_gemm_plan_backward": [i64, i64, i64, ci, vp, vp, vp, vp],
             "mtp_fp8_gemm_plan": [i64, i64, i64, ci, vp, vp, vp, vp],
@@ -344,11 +345,21 @@ def mtp_moe_route(logits, k, expert_offsets, token_idx, token_w, token_rows):
         _stream(logits)))
 
 
-def mtp_moe_mlp_forward(X, E, F, k, expert_offsets, token_idx, token_w, token_rows, W1t, W2t, Z_ws, Y_rows, Y):
+def mtp_moe_mlp_forward(X, E, F, k, expert_offsets, token_idx, token_w, token_rows, W1t, W2t, Z_ws, Y_rows, Y,
+                        workspace=None):
     """Expert SwiGLU MLPs over the routed rows (fp32 row outputs into Y_rows [T*k x H]) and the weighted combine
-    in each token's slot order into Y [T x H]."""
+    in each token's slot order into Y [T x H].  ``workspace`` (mtp_moe_plan's bytes) lets fc2 split the experts'
+    tail tiles."""
     T, H = X.shape
     _check("mtp_moe_mlp_forward", lib().mtp_moe_mlp_forward(
         _ptr(X), T, H, E, F, k, _ptr(expert_offsets), _ptr(token_idx), _ptr(token_w), _ptr(token_rows), _ptr(W1t),
-        _ptr(W2t), _ptr(Z_ws), _ptr(Y_rows), _ptr(Y), _stream(X)))
+        _ptr(W2t), _ptr(Z_ws), _ptr(Y_rows), _ptr(Y), *_ws(workspace), _stream(X)))
     return Y
+
+
+def mtp_moe_plan(T, H, E, F, k):
+    """(split_chunks, workspace_bytes) of mtp_moe_mlp_forward's fc2 for these sizes (0, 0: unsplit)."""
+    sc = ctypes.c_int(0)
+    ws = ctypes.c_size_t(0)
+    _check("mtp_moe_plan", lib().mtp_moe_plan(T, H, E, F, k, ctypes.addressof(sc), ctypes.addressof(ws)))
+    return sc.value, ws.value

@@ -619,7 +619,7 @@ mtp_status mtp_moe_route(const float* logits, int64_t T, int E, int k, int32_t* 
 mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, int64_t F, int k,
                                const int32_t* expert_offsets, const int32_t* token_idx, const float* token_w,
                                const int32_t* token_rows, const mtp_bf16* W1t, const mtp_bf16* W2t, mtp_bf16* Z_ws,
-                               float* Y_rows, mtp_bf16* Y, void* stream) {
+                               float* Y_rows, mtp_bf16* Y, void* workspace, size_t workspace_bytes, void* stream) {
   if (!expert_offsets || !token_idx || !token_w || !token_rows) return fail(MTP_ERR_NULL, "a routing table is NULL");
   if (misaligned(expert_offsets) || misaligned(token_idx) || misaligned(token_w) || misaligned(token_rows))
     return fail(MTP_ERR_ALIGN, "routing tables must be 16-byte aligned");
@@ -638,6 +638,8 @@ mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, i
   TRY(check_window("W1t", F + 256, H));
   TRY(check_window("W2t", 256, F));
   TRY(check_window("Z_ws", 256, F));
+  size_t ws_avail = 0;
+  TRY(check_ws(workspace, workspace_bytes, &ws_avail));
   TRY(check_device());
   hipStream_t st = (hipStream_t)stream;
   // grouped fc1: gather each dispatched row's token, SwiGLU epilogue -> Z_ws (dispatched order)
@@ -652,10 +654,29 @@ mtp_status mtp_moe_mlp_forward(const mtp_bf16* X, int64_t T, int64_t H, int E, i
   f2.A = Z_ws; f2.lda = F; f2.B = W2t; f2.ldb = F; f2.Yacc = Y_rows; f2.ldacc = H;
   f2.Nout = (int)H; f2.K = (int)F; f2.a_src_rows = T * k;
   f2.group_offsets = expert_offsets; f2.groups = E; f2.group_stride_B = H * F;
-  s = launched(mtp::gemm_grouped(f2, mtp::MODE_ROW, (int)(T * k), st), "grouped fc2");
+  // split tails when the plan asks for them and the caller's workspace holds them
+  const mtp::GroupedPlan pl = mtp::grouped_plan(mtp::MODE_ROW, T * k, E, H, F);
+  const int chunks = pl.split_chunks > 1 && pl.ws_bytes <= ws_avail ? pl.split_chunks : 0;
+  f2.ws = workspace; f2.ws_bytes = ws_avail;
+  s = launched(mtp::gemm_grouped(f2, mtp::MODE_ROW, (int)(T * k), st, chunks), "grouped fc2");
   if (s != MTP_OK) return s;
   // weighted combine in each token's slot order, one bf16 rounding
   return launched(mtp::moe_combine(Y_rows, H, token_rows, token_w, (int)T, k, (int)H, Y, H, st), "combine");
+}
+
+mtp_status mtp_moe_plan(int64_t T, int64_t H, int E, int64_t F, int k, int* split_chunks, size_t* workspace_bytes) {
+  if (!split_chunks || !workspace_bytes) return fail(MTP_ERR_NULL, "an output pointer is NULL");
+  if (E < 1 || E > mtp::kMaxExperts) return fail(MTP_ERR_SHAPE, "E=%d must be in [1, %d]", E, mtp::kMaxExperts);
+  if (k < 1 || k > E || k > 8) return fail(MTP_ERR_SHAPE, "k=%d must be in [1, min(E, 8)]", k);
+  TRY(check_dims(T, 2 * F, H));
+  TRY(check_dims(T, H, F));
+  if (T * k > kIntMax) return fail(MTP_ERR_SHAPE, "T*k exceeds 2^31-1");
+  TRY(check_device());
+  const mtp::GroupedPlan pl = mtp::grouped_plan(mtp::MODE_ROW, T * k, E, H, F);
+  *split_chunks = pl.split_chunks;
+  *workspace_bytes = pl.ws_bytes;
+  g_err[0] = 0;
+  return MTP_OK;
 }
 
 mtp_status mtp_mfma_calibrate(float* out, int blocks, int iters, void* stream) {

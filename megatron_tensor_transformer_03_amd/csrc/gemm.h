@@ -53,6 +53,8 @@ struct GemmParams {
   float* sk_ws = nullptr;           // split schedule: partial-tile slots (set at launch)
   int sk_chunks = 0;                // split schedule: K chunks per tile
   int sk_dp_tiles = 0;              // split schedule: leading tiles run whole (a multiple of the grid)
+  int sk_slot_tiles = 0;            // split schedule: tiles with partial slots in the workspace (set at launch)
+  int sk_full_slots = 0;            // grouped split-tail schedule: workgroups of whole tiles before the tail units
   int* sk_cnt = nullptr;            // split schedule: per-tile arrival counters (set at launch)
 };
 
@@ -97,8 +99,16 @@ hipError_t fp8_quantize(const uint16_t* X, int64_t ldx, int M, int K, uint8_t* X
 // Delayed scaling: s from the max of hist[0 .. hlen-1]; this tensor's amax then goes to hist[step % hlen].
 hipError_t fp8_quantize_delayed(const uint16_t* X, int64_t ldx, int M, int K, uint8_t* Xq, int64_t ldq, float* hist,
                                 int hlen, int64_t step, float* ws, float* scale_inv, hipStream_t st);
-// rows_upper: total rows over all groups (an upper bound is enough; spare tiles exit).
-hipError_t gemm_grouped(const GemmParams& p, int mode, int rows_upper, hipStream_t st);
+// rows_upper: total rows over all groups (an upper bound is enough; spare tiles exit).  split_chunks > 1: the
+// split-tail schedule (each group's last, partial row tile in split_chunks K chunks, in p.ws).
+hipError_t gemm_grouped(const GemmParams& p, int mode, int rows_upper, hipStream_t st, int split_chunks = 0);
+// Split-tail plan of a grouped product (SWIGLU or ROW, 256 x 256 tiles): K chunks per tail tile (0: none) and
+// the workspace it needs.
+struct GroupedPlan {
+  int split_chunks = 0;
+  size_t ws_bytes = 0;
+};
+GroupedPlan grouped_plan(int mode, int64_t rows_upper, int groups, int64_t Nout, int64_t K);
 
 // MFMA-only loop over `blocks` workgroups of 8 waves, `iters` x 8 products of 32 x 32 x 16 per wave (calibrate.hip).
 hipError_t mfma_calibrate(float* out, int blocks, int iters, hipStream_t st);

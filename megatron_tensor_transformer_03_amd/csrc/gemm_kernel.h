@@ -545,9 +545,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
       constexpr int Q = FM * FN * 4;   // float4 per thread
       constexpr int kSc1 = 16;         // cache policy: device scope
       const int64_t slot_bytes = (int64_t)Q * C::NT * 16;
-      // (the workspace holds the slots of the split tiles only: tiles_m * tiles_n - sk_dp_tiles of them)
-      const __amdgpu_buffer_rsrc_t ws =
-          make_rsrc(p.sk_ws, (int64_t)(tiles_m * tiles_n - p.sk_dp_tiles) * S * slot_bytes);
+      // (the workspace holds the slots of the split tiles only: sk_slot_tiles of them)
+      const __amdgpu_buffer_rsrc_t ws = make_rsrc(p.sk_ws, (int64_t)p.sk_slot_tiles * S * slot_bytes);
       typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
       const int mine = (int)(slot_of(sk_which_chunk, sk_wtile) * slot_bytes) + 16 * tid;
 #pragma unroll
@@ -843,7 +842,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   }
   };
 
-  if constexpr (SPLIT) {
+  if constexpr (SPLIT && !GROUPED) {
     // Split schedule: every tile's K range is cut into S chunks of whole ring passes, and the units
     // (tile, chunk) are dealt out chunk-major, unit u to logical workgroup u mod G, so the units that run at
     // the same time are the same K chunk of neighbouring tiles: they stream the same K slices of the shared
@@ -875,14 +874,31 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     int row_base = 0, rows = p.M;  // rows of this tile's group (all rows when ungrouped)
     const uint16_t* __restrict__ B = p.B;
     if constexpr (GROUPED) {
-      // blockIdx.x = row-tile slot * tiles_n + tn; slots are laid over the groups in order.
+      // blockIdx.x = row-tile slot * tiles_n + tn; slots are laid over the groups in order.  Split-tail form
+      // (SPLIT): the first sk_full_slots workgroups run each group's whole BM-row tiles only; after them come
+      // the tail units, (chunk c, group g, column tile tn) chunk-major: K chunk c of the group's last, partial
+      // row tile, whose S chunks are added by the last to finish (as in the split schedule above).  The tail
+      // tiles are the ones that make a last, mostly idle wave; cut in S, they fill the CUs the whole tiles
+      // leave free.
       const int tiles_n = (p.Nout + NB_OUT - 1) / NB_OUT;
+      if (SPLIT && (int)blockIdx.x >= p.sk_full_slots) {
+        const int u = (int)blockIdx.x - p.sk_full_slots;
+        const int per_c = p.groups * tiles_n;
+        const int c = u / per_c, r = u - c * per_c, g = r / tiles_n;
+        tn = r - g * tiles_n;
+        const int lo = p.group_offsets[g], hi = p.group_offsets[g + 1];
+        if ((hi - lo) % BM == 0) return;  // no partial tile in this group
+        const int r0 = (int)((int64_t)c * RI / S), r1 = (int)((int64_t)(c + 1) * RI / S);
+        run_tile((hi - lo) / BM, tn, lo, hi - lo, B + (int64_t)g * p.group_stride_B, r0 * NS, r1 * NS, r, r, c, 0,
+                 S - 1, true);
+        return;
+      }
       int slot = blockIdx.x / tiles_n;
       tn = blockIdx.x - slot * tiles_n;
       int g = 0;
       for (; g < p.groups; ++g) {
         const int lo = p.group_offsets[g], hi = p.group_offsets[g + 1];
-        const int nt = (hi - lo + BM - 1) / BM;
+        const int nt = SPLIT ? (hi - lo) / BM : (hi - lo + BM - 1) / BM;
         if (slot < nt) { row_base = lo; rows = hi - lo; break; }
         slot -= nt;
       }
@@ -922,12 +938,37 @@ static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStrea
         return hipErrorInvalidValue;
       p.sk_chunks = split_chunks;
       p.sk_dp_tiles = dp_tiles;
+      p.sk_slot_tiles = (int)(tiles - dp_tiles);
       p.sk_cnt = static_cast<int*>(p.ws);
       p.sk_ws = reinterpret_cast<float*>(static_cast<char*>(p.ws) + kSplitCounterBytes);
       if (kfull)
         hipLaunchKernelGGL((gemm_kernel<C, MODE, false, true, true, AT, BT, EPI, F8>), dim3(split_groups), dim3(C::NT), 0, st, p);
       else
         hipLaunchKernelGGL((gemm_kernel<C, MODE, false, false, true, AT, BT, EPI, F8>), dim3(split_groups), dim3(C::NT), 0, st,
+                           p);
+      return hipGetLastError();
+    }
+  } else {
+    if (split_chunks > 1) {
+      // split tails: whole tiles of every group (at most grid_rows_upper / BM row tiles in all), then
+      // split_chunks tail units per (group, column tile); the workspace holds a counter and split_chunks slots
+      // per (group, column tile)
+      const size_t slot = (size_t)C::FM * C::FN * 16 * sizeof(float) * C::NT;
+      const int64_t tail_tiles = (int64_t)p.groups * tiles_n;
+      const int64_t full_slots = (int64_t)(grid_rows_upper / C::BM) * tiles_n;
+      const int64_t units = full_slots + tail_tiles * split_chunks;
+      if (tail_tiles > kSplitMaxTiles || units > 0x7FFFFFFF || !p.ws ||
+          p.ws_bytes < kSplitCounterBytes + (size_t)tail_tiles * split_chunks * slot)
+        return hipErrorInvalidValue;
+      p.sk_chunks = split_chunks;
+      p.sk_slot_tiles = (int)tail_tiles;
+      p.sk_full_slots = (int)full_slots;
+      p.sk_cnt = static_cast<int*>(p.ws);
+      p.sk_ws = reinterpret_cast<float*>(static_cast<char*>(p.ws) + kSplitCounterBytes);
+      if (kfull)
+        hipLaunchKernelGGL((gemm_kernel<C, MODE, true, true, true, AT, BT, EPI, F8>), dim3((unsigned)units), dim3(C::NT), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm_kernel<C, MODE, true, false, true, AT, BT, EPI, F8>), dim3((unsigned)units), dim3(C::NT), 0, st,
                            p);
       return hipGetLastError();
     }

@@ -28,7 +28,7 @@ class RankForward:
         bf, f32 = torch.bfloat16, torch.float32
         self.out = {}
         self.ws = None
-        if "E" in dims:  # MoE expert MLP (grouped GEMMs: no split-K workspace)
+        if "E" in dims:  # MoE expert MLP (grouped GEMMs; the workspace lets fc2 split the experts' tail tiles)
             T, H, E, F, k = dims["T"], dims["H"], dims["E"], dims["F"], dims["k"]
             self.out.update(offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
                             token_idx=torch.empty(T * k, dtype=torch.int32, device=dev),
@@ -37,6 +37,7 @@ class RankForward:
                             Z=torch.empty(T * k, F, dtype=bf, device=dev),
                             Y_rows=torch.empty(T * k, H, dtype=f32, device=dev),
                             Y=torch.empty(T, H, dtype=bf, device=dev))
+            self.ws = mtp.gemm_workspace(mtp.mtp_moe_plan(T, H, E, F, k)[1], dev)
             return
         M, H, p = dims["M"], dims["H"], dims["p"]
         if "nq" in dims:
@@ -75,7 +76,8 @@ class RankForward:
                                                           o["token_w"], o["token_rows"])),
                     ("moe_mlp", lambda: mtp.mtp_moe_mlp_forward(t["X"], d["E"], d["F"], d["k"], o["offsets"],
                                                                 o["token_idx"], o["token_w"], o["token_rows"],
-                                                                t["W1t"], t["W2t"], o["Z"], o["Y_rows"], o["Y"]))]
+                                                                t["W1t"], t["W2t"], o["Z"], o["Y_rows"], o["Y"],
+                                                                workspace=self.ws))]
         p = d["p"]
         out = []
         if "nq" in d:

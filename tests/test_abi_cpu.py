@@ -27,7 +27,7 @@ def _gpu_present():
 def test_library_exports_every_header_symbol():
     L = mtp.lib()
     names = mtp.header_symbols()
-    assert len(names) == 25
+    assert len(names) == 26
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", mtp.LIB_PATH], capture_output=True, text=True).stdout
@@ -141,8 +141,8 @@ def test_moe_rejects():
     assert L.mtp_moe_route(P, 0, 8, 2, P, P2, P3, P4, None) == SHAPE
     assert L.mtp_moe_route(BAD, 16, 8, 2, P, P2, P3, P4, None) == ALIGN
     assert L.mtp_moe_route(P, 16, 8, 2, P, P2, P3, BAD, None) == ALIGN
-    # X, T, H, E, F, k, offsets, token_idx, token_w, token_rows, W1t, W2t, Z_ws, Y_rows, Y
-    args = [P, 64, 64, 8, 128, 2, P2, P3, P4, P, P2, P3, P4, P, P2]
+    # X, T, H, E, F, k, offsets, token_idx, token_w, token_rows, W1t, W2t, Z_ws, Y_rows, Y, workspace, bytes
+    args = [P, 64, 64, 8, 128, 2, P2, P3, P4, P, P2, P3, P4, P, P2, None, 0]
     bad = list(args)
     bad[4] = 100  # F % 8
     assert L.mtp_moe_mlp_forward(*bad, None) == SHAPE
@@ -155,13 +155,24 @@ def test_moe_rejects():
     bad = list(args)
     bad[13] = None  # Y_rows
     assert L.mtp_moe_mlp_forward(*bad, None) == NULL
+    bad = list(args)
+    bad[15], bad[16] = BAD, 1 << 20  # misaligned workspace
+    assert L.mtp_moe_mlp_forward(*bad, None) == ALIGN
+    sc, ws = ctypes.c_int(-1), ctypes.c_size_t(7)
+    assert L.mtp_moe_plan(64, 64, 8, 128, 2, None, ctypes.addressof(ws)) == NULL
+    assert L.mtp_moe_plan(64, 64, 8, 128, 2, ctypes.addressof(sc), None) == NULL
+    assert L.mtp_moe_plan(64, 64, 65, 128, 2, ctypes.addressof(sc), ctypes.addressof(ws)) == SHAPE
+    assert L.mtp_moe_plan(64, 64, 8, 128, 9, ctypes.addressof(sc), ctypes.addressof(ws)) == SHAPE
+    assert L.mtp_moe_plan(64, 64, 8, 100, 2, ctypes.addressof(sc), ctypes.addressof(ws)) == SHAPE
 
 
 @pytest.mark.skipif(_gpu_present(), reason="on a GPU box a valid call would launch")
 def test_moe_valid_call_reaches_the_device_check():
     L = mtp.lib()
     assert L.mtp_moe_route(P, 16, 8, 2, P, P2, P3, P4, None) == UNSUPPORTED
-    assert L.mtp_moe_mlp_forward(P, 64, 64, 8, 128, 2, P2, P3, P4, P, P2, P3, P4, P, P2, None) == UNSUPPORTED
+    assert L.mtp_moe_mlp_forward(P, 64, 64, 8, 128, 2, P2, P3, P4, P, P2, P3, P4, P, P2, None, 0, None) == UNSUPPORTED
+    sc, ws = ctypes.c_int(-1), ctypes.c_size_t(7)
+    assert L.mtp_moe_plan(64, 64, 8, 128, 2, ctypes.addressof(sc), ctypes.addressof(ws)) == UNSUPPORTED
 
 
 def test_column_linear_static_rejects_oversize_scratch_and_bad_args():

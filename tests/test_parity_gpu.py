@@ -1099,6 +1099,63 @@ def test_router_tables(T, E, k):
     assert np.array_equal(rows.cpu().numpy(), _expected_token_rows(logits, k, r_offs, r_idx))
 
 
+def _crafted_logits(pairs, E, seed):
+    """Router logits that send token t to the experts pairs[t] (most probable first): those get 3 + u and
+    2 + u, the others -1 - u (u in [0, 0.5), distinct per entry)."""
+    rng = np.random.default_rng(seed)
+    T = len(pairs)
+    L = (-1.0 - 0.5 * rng.random((T, E))).astype(np.float32)
+    for t, ex in enumerate(pairs):
+        for s, e in enumerate(ex):
+            L[t, e] = np.float32(3.0 - s + 0.5 * rng.random())
+    return L
+
+
+@pytest.mark.parametrize("case", ["k1", "k2"])
+def test_moe_split_tails_match_oracle(case):
+    # The fc2 product's split-tail schedule: each expert's whole 256-row tiles run whole, its last, partial row
+    # tile in K chunks whose sums the last finisher adds.  Routing crafted so that the experts cover the tail
+    # cases: a whole multiple of 256 rows (no tail unit), fewer than 256 rows (only a tail), none at all, and
+    # whole tiles plus a ragged tail.  With the plan's workspace (split) and with none (unsplit), Y equals
+    # the oracle for every token.
+    if case == "k1":
+        E, k, counts = 5, 1, [256, 300, 0, 100, 549]
+        pairs = [(e,) for e, c in enumerate(counts) for _ in range(c)]
+    else:
+        E, k = 4, 2
+        pairs = [(0, 2)] * 256 + [(1, 2)] * 144  # rows per expert: 256, 144, 400, 0
+    T, H, F = len(pairs), 256, 2048
+    perm = np.random.default_rng(7).permutation(T)  # experts' tokens interleaved
+    pairs = [pairs[i] for i in perm]
+    sc, need = mtp.mtp_moe_plan(T, H, E, F, k)
+    say("moe split tails", case, "T", T, "chunks", sc, "workspace", need)
+    assert sc > 1 and need > 0
+    Xb = synth.normal_bf16(611, T, H, 1.0)
+    W1b = synth.normal_bf16(612, E * 2 * F, H, 0.05)
+    W2b = synth.normal_bf16(613, E * H, F, 0.05)
+    logits = _crafted_logits(pairs, E, 614)
+    X, W1t, W2t = to_dev(Xb), to_dev(W1b), to_dev(W2b)
+    lg = torch.from_numpy(logits).cuda()
+    i32 = dict(dtype=torch.int32, device="cuda")
+    offs, idx, rows = torch.empty(E + 1, **i32), torch.empty(T * k, **i32), torch.empty(T * k, **i32)
+    w = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    mtp.mtp_moe_route(lg, k, offs, idx, w, rows)
+    r_offs, _, _ = oracle.moe_route(logits, k)
+    assert np.array_equal(offs.cpu().numpy(), r_offs)
+    R, _ = oracle.moe_mlp(Xb, logits, [W1b[e * 2 * F:(e + 1) * 2 * F] for e in range(E)],
+                          [W2b[e * H:(e + 1) * H] for e in range(E)], k)
+    for ws in (mtp.gemm_workspace(need), None):
+        Z = torch.empty(T * k, F, dtype=torch.bfloat16, device="cuda")
+        Y_rows = torch.full((T * k, H), float("nan"), dtype=torch.float32, device="cuda")
+        Y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+        mtp.mtp_moe_mlp_forward(X, E, F, k, offs, idx, w, rows, W1t, W2t, Z, Y_rows, Y, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.isfinite(Y_rows).all()  # every routed row written
+        _close(widen_bits(bits(Y)), R, f"moe split tails {case} {'split' if ws is not None else 'unsplit'}")
+        if ws is not None:
+            assert int(ws[:16384].count_nonzero()) == 0  # the tail counters are left zero
+
+
 # ----------------------------------------------------------------------------- HIP graph replay
 @pytest.mark.parametrize("index", [1, 3, 4])
 def test_graph_replays_match_eager(index):
