@@ -363,6 +363,33 @@ def test_moe_distinct_experts_bind_each_row_to_its_own_expert(E, k):
     assert not np.allclose(rev, ref, rtol=1e-3)
 
 
+@pytest.mark.parametrize("mutant", ["reversed_experts", "shifted_offsets"])
+def test_moe_binding_pin_catches_planted_mutants(mutant, monkeypatch):
+    # Plant a binding mistake in the oracle and check that the distinct-expert pin above would fail: the
+    # oracle's rows bound to the experts in reverse order, or each expert's row range shifted by one row (its
+    # first row handed to the previous expert).
+    E, k, T, H, F = 4, 2, 23, 16, 8
+    X = synth.normal_bf16(171, T, H, 1.0)
+    logits = synth.normal_f32(172, T, E)
+    W1 = [synth.normal_bf16(180 + e, 2 * F, H, 0.3) for e in range(E)]
+    W2 = [synth.normal_bf16(190 + e, H, F, 0.3 * 4.0 ** e) for e in range(E)]
+    ref = _moe_by_dense_mlps(X, logits, W1, W2, k)
+    if mutant == "reversed_experts":
+        out, _ = oracle.moe_mlp(X, logits, W1[::-1], W2[::-1], k)
+    else:
+        route = oracle.moe_route
+
+        def shifted(lg, kk):
+            offsets, idx, w = route(lg, kk)
+            offsets = offsets.copy()
+            offsets[1:-1] += 1
+            return offsets, idx, w
+
+        monkeypatch.setattr(oracle, "moe_route", shifted)
+        out, _ = oracle.moe_mlp(X, logits, W1, W2, k)
+    assert not np.allclose(out, ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
+
+
 def test_moe_token_subset_matches_full():
     T, H, F, E = 12, 8, 4, 3
     X = synth.normal_bf16(141, T, H, 1.0)
