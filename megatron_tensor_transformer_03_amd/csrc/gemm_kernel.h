@@ -831,7 +831,66 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
+  // fp32 partial alone (no bf16 output): staged through LDS like the bf16 outputs, one 32-row fragment row of
+  // the wave tile at a time (32 x TN fp32, the size of a bf16 wave region), so that each store instruction
+  // writes whole 16-byte units of 2-3 consecutive rows instead of 32 bytes of each of 32 rows (the
+  // accumulator layout).  16-byte units are permuted per row (XOR with row mod 8), so the 8 lanes an LDS
+  // access serves together hit distinct banks on the write (8 rows, one unit) and on the read (one row, 8
+  // consecutive units).  Each wave's region is its own: no cross-wave synchronisation.
+  auto staged_f32 = [&](auto ACCUM) {
+    constexpr bool accum = decltype(ACCUM)::value;
+    constexpr int UPR = TN / 4;        // 16-byte units per row
+    constexpr int REG = 32 * TN * 2;   // region per wave, in uint16
+    constexpr int WPS = C::STAGE / REG;
+    static_assert(UPR % 8 == 0 && (32 * UPR) % 64 == 0, "unit layout");
+    static_assert(WPS >= 1 && (NWAVES + WPS - 1) / WPS <= NS, "staging fits");
+    const int si = wave / WPS;
+    float* const reg = reinterpret_cast<float*>(
+        (si == 0 ? lds0 : si == 1 ? lds1 : si == 2 ? lds2 : si == 3 ? lds3 : lds4) + (wave % WPS) * REG);
+    auto unit_at = [&](int row, int u) { return row * TN + 4 * (u ^ (row & 7)); };
+    float* const yacc = p.Yacc;
+    const int64_t ldacc = p.ldacc;
+    const int n0 = tn * BN + wn0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<float4*>(reg + unit_at(fr, 8 * j + 2 * jj + (lane >> 5))) =
+              make_float4(acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]);
+#pragma unroll 4
+      for (int q = 0; q < 32 * UPR / 64; ++q) {
+        const int id = 64 * q + lane;
+        const int row = id / UPR, u = id % UPR;
+        float4 v = *reinterpret_cast<const float4*>(reg + unit_at(row, u));
+        const int m = m0 + wm0 + 32 * i + row;
+        const int n = n0 + 4 * u;
+        const int valid = p.Nout - n;
+        if (m < rows && valid > 0) {
+          float* dst = yacc + ((int64_t)row_base + m) * ldacc + n;
+          if (valid >= 4) {
+            if constexpr (accum) {
+              const float4 o = *reinterpret_cast<const float4*>(dst);
+              v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+            }
+            *reinterpret_cast<float4*>(dst) = v;
+          } else {
+            const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int r = 0; r < 3; ++r)
+              if (r < valid) dst[r] = accum ? dst[r] + e[r] : e[r];
+          }
+        }
+      }
+    }
+  };
   if constexpr (MODE == MODE_ROW) {
+    if (!p.Y) {
+      if (p.accumulate) staged_f32(T_{});
+      else staged_f32(F_{});
+      return;
+    }
     if (p.accumulate) {
       if (p.Y) direct(T_{}, T_{});
       else direct(T_{}, F_{});
