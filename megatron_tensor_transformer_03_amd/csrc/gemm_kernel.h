@@ -519,13 +519,37 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   }(std::make_integer_sequence<int, NS - 1>{});
   ring_barrier();
   if constexpr (C::EARLY) read_frags(lds0, 0, std::integral_constant<int, 0>{});
-  for (int kt = kt0; kt < kt1; kt += NS) {
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      if constexpr (kSpread)
-        (step_spread(std::integral_constant<int, I>{}, kt + I), ...);
-      else
-        (step(std::integral_constant<int, I>{}, kt + I), ...);
-    }(std::make_integer_sequence<int, NS>{});
+  // Grouped products: a group's last row tile often holds few rows.  When it holds at most BM / 2, the waves
+  // of the lower half of the tile (wave rows WAVES_M / 2 ..) have no row to compute: they still issue their
+  // share of the DMA and meet every barrier, but read no fragments and issue no MFMAs.  Waves w and w + 4 share
+  // a SIMD and lie in different halves, so every SIMD keeps one computing wave and the tile takes about half
+  // the MFMA time.  (The choice is uniform per wave and made once, around two straight-line loops.)
+  bool idle_half = false;
+  if constexpr (GROUPED && kSpread && C::WAVES_M == 4 && NWAVES == 8)
+    idle_half = rows - m0 <= BM / 2 && wm0 >= BM / 2;
+  auto step_idle = [&](auto I, int kt) {
+    constexpr int i = decltype(I)::value;
+    uint16_t* nxt = stage_buf(std::integral_constant<int, (i + NS - 1) % NS>{});
+    const int k0n = (kt + NS - 1) * BK;
+#pragma unroll
+    for (int j = 0; j < D; ++j) dma_slot(k0n, nxt, j);
+    ring_barrier();
+  };
+  if (idle_half) {
+    for (int kt = kt0; kt < kt1; kt += NS) {
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        (step_idle(std::integral_constant<int, I>{}, kt + I), ...);
+      }(std::make_integer_sequence<int, NS>{});
+    }
+  } else {
+    for (int kt = kt0; kt < kt1; kt += NS) {
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        if constexpr (kSpread)
+          (step_spread(std::integral_constant<int, I>{}, kt + I), ...);
+        else
+          (step(std::integral_constant<int, I>{}, kt + I), ...);
+      }(std::make_integer_sequence<int, NS>{});
+    }
   }
   // The last steps prefetched stages past K (never consumed); drain them before the epilogue reuses LDS.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
