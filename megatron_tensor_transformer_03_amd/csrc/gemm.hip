@@ -41,7 +41,8 @@ int cu_count() {
 // tiles split.  R and BW were fitted to the measured times of these schedules at the workloads' shapes
 // (within ~10%).  A split schedule needs a workspace (the tiles' arrival counters, then the split tiles'
 // partial slots); only schedules whose workspace fits in ws_avail are considered.
-GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k, bool allow_small, size_t ws_avail) {
+GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k, bool allow_small, size_t ws_avail,
+                   bool f8) {
   struct Opt { int bm, bn; double eff; int id; int ns_bk; int64_t slot_bytes; };
   // Relative efficiencies per output, against the 256 x 256 tile.  The forward products run both large
   // tiles with a 64-deep K step in two stages, where the 256 x 192 tile measured 0.80-0.86 at the workload
@@ -50,7 +51,9 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k
   // forms.)
   const double wide_eff = row_major_k ? 0.95 : 0.85;
   const double half_eff = row_major_k ? 0.85 : 0.75;
-  const Opt opts[] = {{256, 256, 1.00, 0, 128, 256 << 10}, {256, 192, wide_eff, 1, 128, 192 << 10},
+  // (ns_bk: K per ring pass, the split schedule's unit; the forward 256 x 192 tile's split ring passes 6 K
+  // steps, so its step count is padded to a multiple of 6 with zero steps, charged below)
+  const Opt opts[] = {{256, 256, 1.00, 0, 128, 256 << 10}, {256, 192, wide_eff, 1, row_major_k || f8 ? 128 : 384, 192 << 10},
                       {256, 128, half_eff, 2, 128, 128 << 10}, {128, 128, 0.72, 3, 256, 0},
                       {128, 128, 0.72, 4, 128, 64 << 10}};
   constexpr double kR = 5.5e12 * 1e-6;   // FLOP per microsecond of one CU
@@ -73,7 +76,8 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k
     // (the backward products keep the relative model they were tuned with: tile time o.bm o.bn / eff, a
     // per-tile cost of 0.03 tile per chunk for the partial sums, no hybrid)
     const bool fwd = row_major_k == 0;
-    const double tile_t = fwd ? 2.0 * o.bm * o.bn * (double)K / (o.eff * kR) : o.bm * o.bn / o.eff;
+    const double kpad = (double)((K + o.ns_bk - 1) / o.ns_bk * o.ns_bk) / (double)((K + 63) / 64 * 64);
+    const double tile_t = fwd ? 2.0 * o.bm * o.bn * (double)K * kpad / (o.eff * kR) : o.bm * o.bn / o.eff;
     const int64_t full_waves = tiles / (cus > 0 ? cus : 1);
     const double t_dp = (double)((tiles + cus - 1) / (cus > 0 ? cus : 1)) * tile_t;
     if (t_dp < best_t * 0.999) { best_t = t_dp; best = GemmPlan{o.bm, (int)nbo, 0, o.id, 0, 0, 0}; }

@@ -10,7 +10,7 @@ namespace mtp {
 
 template <int MODE>
 static hipError_t dispatch_f8(const GemmParams& p, hipStream_t st) {
-  const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K, 0, false, p.ws ? p.ws_bytes : 0);
+  const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K, 0, false, p.ws ? p.ws_bytes : 0, true);
   switch (pl.id) {
     case 0:
       return launch_cfg<BigTile, MODE, false, false, false, EPI_PLAIN, true>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);

@@ -54,9 +54,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int NS_, bool EARLY_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int NS_, bool EARLY_, int NSB_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BK = BK_, NS = NS_;
+  // Split ring (NSB = NS + 1, two-stage forms without EARLY): the B operand's tiles get a ring of NSB stages of
+  // their own, the A operand's keep NS, where the LDS cannot hold NS + 1 stages of both (256 x 192: 3 x 56 KB
+  // does not fit, 2 x 32 + 3 x 24 KB does).  Each B tile is then loaded two steps ahead of its use.
+  static constexpr int NSB = NSB_ ? NSB_ : NS;
+  static constexpr bool AB = NSB != NS;
+  static constexpr int RING = AB ? NS * NSB : NS;  // K steps per loop iteration (each stage a compile-time choice)
   // EARLY: the first fragments of step k + 1 are read during the last MFMAs of step k (the barrier ending a
   // step then makes the stage two steps ahead visible, so the ring needs one more stage for the same lead)
   static constexpr bool EARLY = EARLY_;
@@ -79,7 +85,10 @@ struct Cfg {
   static_assert(NWAVES % 4 == 0, "whole waves per SIMD");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "32 x 32 fragments");
   static_assert(BM % ROWS_PER_DMA == 0 && BN % ROWS_PER_DMA == 0, "DMA groups");
-  static_assert(NS * STAGE * 2 + (SPARE ? 1024 : 0) <= 160 * 1024, "LDS capacity");
+  static_assert((AB ? (NS * BM + NSB * BN) * BK * 2 : NS * STAGE * 2) + (SPARE ? 1024 : 0) <= 160 * 1024,
+                "LDS capacity");
+  static_assert(!AB || (!EARLY && NS == 2 && NSB == 3 && GA % NWAVES == 0 && GB % NWAVES == 0),
+                "split ring: two A stages, three B stages, whole A and B slots per wave");
 };
 
 // Element offset of (row, 16-byte chunk) in an LDS stage: rows of BK elements, chunks permuted by XOR with
@@ -199,12 +208,18 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   static_assert(!F8 || (BK == 32 && !AT && !BT && !GROUPED && EPI == EPI_PLAIN), "E4M3: plain K-major tiles");
   constexpr int NB_OUT = MODE == MODE_SWIGLU ? BN / 2 : BN;  // output columns per tile
 
-  // one LDS variable per stage (see the design notes); unused ones are a token 16 bytes
-  __shared__ __attribute__((aligned(16))) uint16_t lds0[C::STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t lds1[C::STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t lds2[NS > 2 ? C::STAGE : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t lds3[NS > 3 ? C::STAGE : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t lds4[NS > 4 ? C::STAGE : 8];
+  // one LDS variable per stage (see the design notes); unused ones are a token 16 bytes.  In the split ring
+  // lds0 / lds1 hold the A tiles and ldsb0 .. ldsb2 the B tiles.
+  constexpr int SA = C::AB ? BM * BK : C::STAGE;
+  constexpr int SB = C::AB ? BN * BK : 8;
+  __shared__ __attribute__((aligned(16))) uint16_t lds0[SA];
+  __shared__ __attribute__((aligned(16))) uint16_t lds1[SA];
+  __shared__ __attribute__((aligned(16))) uint16_t lds2[NS > 2 ? SA : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t lds3[NS > 3 ? SA : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t lds4[NS > 4 ? SA : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t ldsb0[SB];
+  __shared__ __attribute__((aligned(16))) uint16_t ldsb1[SB];
+  __shared__ __attribute__((aligned(16))) uint16_t ldsb2[C::NSB > 2 ? SB : 8];
   __shared__ __attribute__((aligned(16))) uint16_t lds_spare[C::SPARE ? 512 : 8];  // dropped unless used
   auto stage_buf = [&](auto I) -> uint16_t* {
     constexpr int i = decltype(I)::value;
@@ -214,6 +229,30 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     else if constexpr (i == 3) return lds3;
     else return lds4;
   };
+  auto bstage_buf = [&](auto I) -> uint16_t* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return ldsb0;
+    else if constexpr (i == 1) return ldsb1;
+    else return ldsb2;
+  };
+  // Wave w's private epilogue staging region of R elements, carved from the stage buffers in order (the
+  // main loop has drained by then).
+  auto stage_region = [&](auto RC) -> uint16_t* {
+    constexpr int R = decltype(RC)::value;
+    const int w = threadIdx.x >> 6;
+    if constexpr (!C::AB) {
+      constexpr int WPS = C::STAGE / R;
+      static_assert(WPS >= 1 && (NWAVES + WPS - 1) / WPS <= NS, "staging fits");
+      const int si = w / WPS;
+      return (si == 0 ? lds0 : si == 1 ? lds1 : si == 2 ? lds2 : si == 3 ? lds3 : lds4) + (w % WPS) * R;
+    } else {
+      constexpr int PA = SA / R, PB = SB / R;  // regions per A / B buffer
+      static_assert(PA >= 1 && PB >= 1 && NS * PA + C::NSB * PB >= NWAVES, "staging fits");
+      if (w < NS * PA) return (w / PA == 0 ? lds0 : lds1) + (w % PA) * R;
+      const int w2 = w - NS * PA, si = w2 / PB;
+      return (si == 0 ? ldsb0 : si == 1 ? ldsb1 : ldsb2) + (w2 % PB) * R;
+    }
+  };
 
   __shared__ int sk_flag;
   // K steps, rounded up to a multiple of NS: the loop body covers NS steps (one per LDS stage, each stage a
@@ -221,11 +260,12 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   // step count is a multiple of NS and every chunk is in range; otherwise chunks at or past K read as zero,
   // so padding steps multiply zeros.
   const int KT = (p.K + BK - 1) / BK;
-  const int KTS = (KT + NS - 1) / NS * NS;
+  constexpr int RING = C::RING;
+  const int KTS = (KT + RING - 1) / RING * RING;
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.Nout + NB_OUT - 1) / NB_OUT;
   // split schedule (SPLIT only): each tile's RI ring passes in S chunks, partial sums of tile t in slots
   // t * S .. t * S + S - 1
-  const int RI = KTS / NS;
+  const int RI = KTS / RING;
   const int G = gridDim.x;
   const int S = p.sk_chunks;
   auto slot_of = [&](int c, int t) { return t * S + c; };
@@ -376,10 +416,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13,
                                                              14, 15));
   };
-  auto read_frags = [&](const uint16_t* sbuf, int ks, auto SET) {
+  auto read_frags2 = [&](const uint16_t* sA, const uint16_t* sB, int ks, auto SET) {
     constexpr int q = decltype(SET)::value;
-    const uint16_t* sA = sbuf;
-    const uint16_t* sB = sbuf + BM * BK;
     if constexpr (F8) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) fa[q][i] = read_f8(sA, wm0 + 32 * i + fr);
@@ -398,6 +436,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
       }
     }
   };
+  auto read_frags = [&](const uint16_t* sbuf, int ks, auto SET) { read_frags2(sbuf, sbuf + BM * BK, ks, SET); };
   auto mma = [&](auto SET) {
     constexpr int q = decltype(SET)::value;
 #pragma unroll
@@ -513,7 +552,87 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     }(std::make_integer_sequence<int, KS>{});
     ring_barrier();
   };
+  // ---- split ring (C::AB): A tiles in NS = 2 stages, B tiles in NSB = 3.  Each wave's first JA DMA slots are A
+  // rows and the rest B rows; step kt loads the A tile of step kt + 1 and the B tile of step kt + 2, A slots
+  // first, so at the end of a step the newest JB loads (the B tile two steps ahead) may stay in flight.
+  constexpr int JA = C::AB ? GA / NWAVES : D, JB = D - JA;
+  constexpr int kNewerAB = C::AB ? (C::NSB - 2) * JB : 0;
+  constexpr int kWaitAB = 0x0F70 | (kNewerAB & 15) | ((kNewerAB >> 4) << 14);
+  auto ring_barrier_ab = [&]() {
+    __builtin_amdgcn_s_waitcnt(kWaitAB);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto dma_slot_ab = [&](auto J, int k0a, int k0b, uint16_t* sA, uint16_t* sB) {
+    constexpr int j = decltype(J)::value;
+    constexpr bool is_a = j < JA;
+    const int k0 = is_a ? k0a : k0b;
+    const int soff = k0 < p.K ? 2 * k0 : 0;
+    const int g = j * NWAVES + wave_u;  // uniform
+    uint32_t vo = d_off[j];
+    if constexpr (!KFULL) vo = k0 + d_kc[j] < p.K ? vo : kOOB;
+    uint16_t* dst = is_a ? sA + g * ROWS_PER_DMA * BK : sB + (g - GA) * ROWS_PER_DMA * BK;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_rsrc : b_rsrc, (lds_ptr)dst, 16, vo, soff, 0, 0);
+  };
+  // One K step of the split ring on A stage IA and B stage IB, scheduled as step_spread.
+  auto step_spread_ab = [&](auto IA, auto IB, int kt) {
+    constexpr int ia = decltype(IA)::value, ib = decltype(IB)::value;
+    const uint16_t* curA = stage_buf(std::integral_constant<int, ia>{});
+    const uint16_t* curB = bstage_buf(std::integral_constant<int, ib>{});
+    uint16_t* nxtA = stage_buf(std::integral_constant<int, (ia + 1) % NS>{});
+    uint16_t* nxtB = bstage_buf(std::integral_constant<int, (ib + C::NSB - 1) % C::NSB>{});
+    const int k0a = (kt + 1) * BK, k0b = (kt + C::NSB - 1) * BK;
+    constexpr int NM = FM * FN;
+    static_assert(2 * D <= KS * NM, "every DMA slot finds an MFMA");
+    read_frags2(curA, curB, 0, std::integral_constant<int, 0>{});
+    [&]<int... S>(std::integer_sequence<int, S...>) {
+      ([&] {
+        constexpr int ks = S;
+        if constexpr (ks + 1 < KS) read_frags2(curA, curB, ks + 1, std::integral_constant<int, (ks + 1) & 1>{});
+        [&]<int... MI>(std::integer_sequence<int, MI...>) {
+          ([&] {
+            constexpr int mi = MI, gm = ks * NM + mi, a = mi / FN, b = mi % FN;
+            if constexpr (!F8)
+              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][b], fa[ks & 1][a], acc[a][b], 0, 0, 0);
+            if constexpr (gm % 2 == 1 && gm / 2 < D)
+              dma_slot_ab(std::integral_constant<int, gm / 2>{}, k0a, k0b, nxtA, nxtB);
+          }(), ...);
+        }(std::make_integer_sequence<int, NM>{});
+        constexpr int NR = ks + 1 < KS ? FM + FN : 0;
+        [&]<int... MI>(std::integer_sequence<int, MI...>) {
+          ([&] {
+            constexpr int mi = MI, gm = ks * NM + mi;
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if constexpr (mi < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if constexpr (gm % 2 == 1 && gm / 2 < D) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+          }(), ...);
+        }(std::make_integer_sequence<int, NM>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }(), ...);
+    }(std::make_integer_sequence<int, KS>{});
+    ring_barrier_ab();
+  };
+
   if constexpr (SPLIT) __syncthreads();  // the previous tile's epilogue may still read the LDS stages
+  if constexpr (C::AB) {
+    // prologue: A of step kt0, B of steps kt0 and kt0 + 1
+    const int k0 = kt0 * BK;
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+      (dma_slot_ab(std::integral_constant<int, J>{}, k0, k0, stage_buf(std::integral_constant<int, 0>{}),
+                   bstage_buf(std::integral_constant<int, 0>{})), ...);
+    }(std::make_integer_sequence<int, D>{});
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+      (dma_slot_ab(std::integral_constant<int, JA + J>{}, k0, k0 + BK, stage_buf(std::integral_constant<int, 0>{}),
+                   bstage_buf(std::integral_constant<int, 1>{})), ...);
+    }(std::make_integer_sequence<int, JB>{});
+    ring_barrier_ab();
+    for (int kt = kt0; kt < kt1; kt += RING) {
+      [&]<int... U>(std::integer_sequence<int, U...>) {
+        (step_spread_ab(std::integral_constant<int, U % NS>{}, std::integral_constant<int, U % C::NSB>{}, kt + U), ...);
+      }(std::make_integer_sequence<int, RING>{});
+    }
+  } else {
   [&]<int... I>(std::integer_sequence<int, I...>) {
     (dma_stage((kt0 + I) * BK, stage_buf(std::integral_constant<int, I>{})), ...);
   }(std::make_integer_sequence<int, NS - 1>{});
@@ -550,6 +669,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
           (step(std::integral_constant<int, I>{}, kt + I), ...);
       }(std::make_integer_sequence<int, NS>{});
     }
+  }
   }
   // The last steps prefetched stages past K (never consumed); drain them before the epilogue reuses LDS.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -760,10 +880,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     constexpr int W = (UPR & -UPR) < 32 ? (UPR & -UPR) : 32;
     constexpr int RP = 32 / W;
     static_assert(UPR % 8 == 0 && (TM * UPR) % 64 == 0, "unit layout");
-    constexpr int WPS = C::STAGE / (TM * TNO);  // wave regions per LDS stage
-    static_assert(WPS >= 1 && (NWAVES + WPS - 1) / WPS <= NS, "staging fits");
-    const int si = wave / WPS;
-    uint16_t* reg = (si == 0 ? lds0 : si == 1 ? lds1 : si == 2 ? lds2 : si == 3 ? lds3 : lds4) + (wave % WPS) * TM * TNO;
+    uint16_t* reg = stage_region(std::integral_constant<int, TM * TNO>{});
     auto unit_at = [&](int row, int u) { return row * TNO + 4 * (u ^ ((row / RP) & (W - 1))); };
     auto stage_tile = [&](auto gelu) {
 #pragma unroll
@@ -865,12 +982,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     constexpr bool accum = decltype(ACCUM)::value;
     constexpr int UPR = TN / 4;        // 16-byte units per row
     constexpr int REG = 32 * TN * 2;   // region per wave, in uint16
-    constexpr int WPS = C::STAGE / REG;
     static_assert(UPR % 8 == 0 && (32 * UPR) % 64 == 0, "unit layout");
-    static_assert(WPS >= 1 && (NWAVES + WPS - 1) / WPS <= NS, "staging fits");
-    const int si = wave / WPS;
-    float* const reg = reinterpret_cast<float*>(
-        (si == 0 ? lds0 : si == 1 ? lds1 : si == 2 ? lds2 : si == 3 ? lds3 : lds4) + (wave % WPS) * REG);
+    float* const reg = reinterpret_cast<float*>(stage_region(std::integral_constant<int, REG>{}));
     auto unit_at = [&](int row, int u) { return row * TN + 4 * (u ^ (row & 7)); };
     float* const yacc = p.Yacc;
     const int64_t ldacc = p.ldacc;
@@ -949,7 +1062,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
       const int c = v / TR, tr = v - c * TR;
       const int r0 = (int)((int64_t)c * RI / S), r1 = (int)((int64_t)(c + 1) * RI / S);
       tile_coords(TD + tr, tiles_m, tiles_n, tm, tn);
-      run_tile(tm, tn, 0, p.M, p.B, r0 * NS, r1 * NS, TD + tr, tr, c, 0, S - 1, true);
+      run_tile(tm, tn, 0, p.M, p.B, r0 * RING, r1 * RING, TD + tr, tr, c, 0, S - 1, true);
     }
   } else {
     // ---- tile placement
@@ -972,7 +1085,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
         const int lo = p.group_offsets[g], hi = p.group_offsets[g + 1];
         if ((hi - lo) % BM == 0) return;  // no partial tile in this group
         const int r0 = (int)((int64_t)c * RI / S), r1 = (int)((int64_t)(c + 1) * RI / S);
-        run_tile((hi - lo) / BM, tn, lo, hi - lo, B + (int64_t)g * p.group_stride_B, r0 * NS, r1 * NS, r, r, c, 0,
+        run_tile((hi - lo) / BM, tn, lo, hi - lo, B + (int64_t)g * p.group_stride_B, r0 * RING, r1 * RING, r, r, c, 0,
                  S - 1, true);
         return;
       }
@@ -1009,7 +1122,7 @@ static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStrea
     tiles = (int64_t)((p.M + C::BM - 1) / C::BM) * tiles_n;
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const bool kfull = p.K % (C::BK * C::NS) == 0;  // whole chunks and a step count that fills the ring
+  const bool kfull = p.K % (C::BK * C::RING) == 0;  // whole chunks and a step count that fills the ring
   if constexpr (!GROUPED) {
     if (split_groups > 0 && split_chunks > 1) {
       const size_t slot = (size_t)C::FM * C::FN * 16 * sizeof(float) * C::NT;
@@ -1084,10 +1197,12 @@ using BigTile = Cfg<MTP_BIG_CFG>;              // 8 waves (wave tile 64 x 128), 
 // in two stages: 128-byte rows per DMA instead of 64, 2-4% faster at the workload shapes.  The row-major-K
 // (backward) and E4M3 forms keep the 32-deep ring their layouts are built on.
 using BigFwdTile = Cfg<256, 256, 4, 2, 64, 2, false>;  // 8 waves (64 x 128), 2 x 64 KB LDS stages
-// Likewise the 256 x 192 tile: in this form it runs at 0.80-0.86 of the 256 x 256 tile's rate per output and
-// beats it where its tile count fills whole waves (175B-shard out-projection 98.5 against 113 us, fc2 295
-// against 326, QKV 211 against 237; 345M QKV 30.9 against 33.0).
-using WideFwdTile = Cfg<256, 192, 4, 2, 64, 2, false>;  // 8 waves (64 x 96), 2 x 56 KB LDS stages
+// Likewise the 256 x 192 tile, in the split ring (A tiles in two stages, B tiles in three: 2 x 32 + 3 x 24 KB),
+// which loads each B tile two steps ahead: against the plain two-stage ring at the 175B-shard shapes, 3-6%
+// faster with the weight cached and 8-14% with it streaming from HBM (QKV 236.7 -> 204.4 us, fc1 267.0 ->
+// 234.5, fc2 270.5 -> 244.8), bitwise the same sums.  It beats the 256 x 256 tile where its tile count fills
+// whole waves.
+using WideFwdTile = Cfg<256, 192, 4, 2, 64, 2, false, 3>;  // 8 waves (64 x 96), split ring, 136 KB
 using WideTile = Cfg<MTP_WIDE_CFG>;            // 8 waves (64 x 96), 112 KB
 using HalfTile = Cfg<MTP_HALF_CFG>;            // 8 waves (64 x 64), 96 KB
 using SmallTile = Cfg<MTP_SMALL_CFG>;          // 8 waves (32 x 64), 128 KB

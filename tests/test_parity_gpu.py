@@ -133,7 +133,9 @@ def test_integer_exact_row_partials_and_sum(M, N, Kp, p):
     (300, 190, 2048, (256, 128, 4), False),
     (900, 4100, 5120, (256, 256, 3), True),    # 40 passes in 3 chunks
     (4100, 4100, 4096, (256, 256, 3), True),   # hybrid: 256 of the 289 tiles whole, the other 33 in 3 chunks
-    (640, 3000, 12288, (256, 192, 5), True),   # 96 passes in 5 chunks (19 or 20 each)
+    (544, 7488, 10752, (256, 192, 2), True),   # the split-ring 256 x 192 tile: 28 passes of 6 K steps in 2 chunks
+    # (not split: the split ring with K = 1040, 17 K steps (the last ragged) padded to 18 with a zero step)
+    (1408, 5952, 1040, (256, 192, 0), True),
 ])
 def test_split_schedule_integer_exact(M, N, K, plan, sampled):
     say("split int column", M, N, K)
