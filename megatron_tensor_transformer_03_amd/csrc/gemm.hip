@@ -43,7 +43,7 @@ int cu_count() {
 // partial slots); only schedules whose workspace fits in ws_avail are considered.
 GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k, bool allow_small, size_t ws_avail,
                    bool f8) {
-  struct Opt { int bm, bn; double eff; int id; int ns_bk; int64_t slot_bytes; };
+  struct Opt { int bm, bn; double eff; int id; int ns_bk; int64_t slot_bytes; int pad_k; };
   // Relative efficiencies per output, against the 256 x 256 tile.  The forward products run both large
   // tiles with a 64-deep K step in two stages, where the 256 x 192 tile measured 0.80-0.86 at the workload
   // shapes.  (Its 32-deep four-stage form, used by the backward products, ranged from 0.6 to 1.1 of the
@@ -51,11 +51,12 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k
   // forms.)
   const double wide_eff = row_major_k ? 0.95 : 0.85;
   const double half_eff = row_major_k ? 0.85 : 0.75;
-  // (ns_bk: K per ring pass, the split schedule's unit; the forward 256 x 192 tile's split ring passes 6 K
-  // steps, so its step count is padded to a multiple of 6 with zero steps, charged below)
-  const Opt opts[] = {{256, 256, 1.00, 0, 128, 256 << 10}, {256, 192, wide_eff, 1, row_major_k || f8 ? 128 : 384, 192 << 10},
-                      {256, 128, half_eff, 2, 128, 128 << 10}, {128, 128, 0.72, 3, 256, 0},
-                      {128, 128, 0.72, 4, 128, 64 << 10}};
+  // ns_bk: K per ring pass (the split schedule's unit, and the granularity the step count is padded to with
+  // zero steps, charged to the tile's time below); the forward 256 x 192 tile's split ring passes 6 K steps
+  const bool sr = !row_major_k && !f8;  // the forward 256 x 192 tile runs the split ring
+  const Opt opts[] = {{256, 256, 1.00, 0, 128, 256 << 10, 128}, {256, 192, wide_eff, 1, sr ? 384 : 128, 192 << 10, sr ? 384 : 128},
+                      {256, 128, half_eff, 2, 128, 128 << 10, 128}, {128, 128, 0.72, 3, 256, 0, 256},
+                      {128, 128, 0.72, 4, 128, 64 << 10, 128}};
   constexpr double kR = 5.5e12 * 1e-6;   // FLOP per microsecond of one CU
   constexpr double kBW = 3.0e12 * 1e-6;  // bytes per microsecond of the partial-tile traffic
   const int cus = cu_count();
@@ -76,14 +77,16 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k
     // (the backward products keep the relative model they were tuned with: tile time o.bm o.bn / eff, a
     // per-tile cost of 0.03 tile per chunk for the partial sums, no hybrid)
     const bool fwd = row_major_k == 0;
-    const double kpad = (double)((K + o.ns_bk - 1) / o.ns_bk * o.ns_bk) / (double)((K + 63) / 64 * 64);
+    const double kpad = (double)((K + o.pad_k - 1) / o.pad_k * o.pad_k) / (double)((K + 63) / 64 * 64);
     const double tile_t = fwd ? 2.0 * o.bm * o.bn * (double)K * kpad / (o.eff * kR) : o.bm * o.bn / o.eff;
     const int64_t full_waves = tiles / (cus > 0 ? cus : 1);
     const double t_dp = (double)((tiles + cus - 1) / (cus > 0 ? cus : 1)) * tile_t;
     if (t_dp < best_t * 0.999) { best_t = t_dp; best = GemmPlan{o.bm, (int)nbo, 0, o.id, 0, 0, 0}; }
-    // split-K (all tiles, or the tiles past the whole waves): S chunks of at least 4 ring passes; per unit
-    // a pipeline fill of about 1.5 passes; chosen only when clearly faster
+    // split-K (all tiles, or the tiles past the whole waves): S chunks of whole ring passes and at least 8 K
+    // steps of 64 (32-deep rings: 8 steps of 32 per chunk, K counted the same); per unit a pipeline fill of
+    // about 192 K (3 steps of 64); chosen only when clearly faster
     const int64_t passes = (K + o.ns_bk - 1) / o.ns_bk;
+    const int64_t pass_steps = o.ns_bk / 64;
     if (o.slot_bytes == 0 || cus < 8 || cus % 8 != 0 || tiles > kSplitMaxTiles) continue;
     for (int hybrid = 0; hybrid < 2; ++hybrid) {
       const int64_t dp_tiles = hybrid ? full_waves * cus : 0;
@@ -91,11 +94,12 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k
       // (the hybrid form was measured on the 256 x 256 tile only)
       if (hybrid && (!fwd || o.id != 0 || dp_tiles == 0 || split_tiles == 0)) continue;
       for (int S : {2, 3, 4, 5, 6, 8}) {
-        if (passes < 4 * S || split_tiles * S * o.slot_bytes > ((int64_t)512 << 20)) continue;
+        if (passes * pass_steps < 8 * S || passes < S || split_tiles * S * o.slot_bytes > ((int64_t)512 << 20))
+          continue;
         const size_t ws = kSplitCounterBytes + (size_t)(split_tiles * S * o.slot_bytes);
         if (ws > ws_avail) continue;
         const int64_t waves = (split_tiles * S + cus - 1) / cus;
-        const double t_sk = full_waves * hybrid * tile_t + waves * tile_t * (1.0 / S + 1.5 / passes) +
+        const double t_sk = full_waves * hybrid * tile_t + waves * tile_t * (1.0 / S + 192.0 / (double)K) +
                             (fwd ? 2.0 * split_tiles * S * o.slot_bytes / kBW : tile_t * 0.03 * S);
         if (t_sk < best_t * 0.95) {
           best_t = t_sk;

@@ -31,9 +31,10 @@ GroupedPlan grouped_plan(int mode, int64_t rows_upper, int groups, int64_t Nout,
   const int64_t tiles_n = (Nout + nb - 1) / nb;
   const int64_t tail = (int64_t)groups * tiles_n, full = rows_upper / C::BM * tiles_n;
   if (tail > kSplitMaxTiles || full + tail > 4 * (int64_t)cus) return pl;
-  const int64_t passes = (K + C::BK * C::NS - 1) / (C::BK * C::NS);
+  // (as the dense split: chunks of whole ring passes and at least 8 K steps)
+  const int64_t passes = (K + C::BK * C::RING - 1) / (C::BK * C::RING);
   const int S = 3 * tail <= 2 * (int64_t)cus ? 3 : 2;
-  if (passes < 4 * S) return pl;
+  if (passes * C::RING < 8 * S || passes < S) return pl;
   const size_t slot = (size_t)C::FM * C::FN * 16 * sizeof(float) * C::NT;
   pl.split_chunks = S;
   pl.ws_bytes = kSplitCounterBytes + (size_t)tail * S * slot;

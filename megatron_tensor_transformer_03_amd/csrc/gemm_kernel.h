@@ -258,7 +258,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   // K steps, rounded up to a multiple of NS: the loop body covers NS steps (one per LDS stage, each stage a
   // compile-time choice) and has no branches, so the compiler's wait counts stay exact.  With KFULL the
   // step count is a multiple of NS and every chunk is in range; otherwise chunks at or past K read as zero,
-  // so padding steps multiply zeros.
+  // so padding steps multiply zeros.  (The split ring's loop covers RING = 6 steps; its step count is padded
+  // the same way.)
   const int KT = (p.K + BK - 1) / BK;
   constexpr int RING = C::RING;
   const int KTS = (KT + RING - 1) / RING * RING;
@@ -627,11 +628,27 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
                    bstage_buf(std::integral_constant<int, 1>{})), ...);
     }(std::make_integer_sequence<int, JB>{});
     ring_barrier_ab();
-    for (int kt = kt0; kt < kt1; kt += RING) {
-      [&]<int... U>(std::integer_sequence<int, U...>) {
-        (step_spread_ab(std::integral_constant<int, U % NS>{}, std::integral_constant<int, U % C::NSB>{}, kt + U), ...);
-      }(std::make_integer_sequence<int, RING>{});
-    }
+    // (grouped products: the idle lower half of a short last row tile, as in the two-stage ring below)
+    bool idle_half = false;
+    if constexpr (GROUPED && C::WAVES_M == 4 && NWAVES == 8) idle_half = rows - m0 <= BM / 2 && wm0 >= BM / 2;
+    auto step_idle_ab = [&](auto IA, auto IB, int kt) {
+      constexpr int ia = decltype(IA)::value, ib = decltype(IB)::value;
+      uint16_t* nxtA = stage_buf(std::integral_constant<int, (ia + 1) % NS>{});
+      uint16_t* nxtB = bstage_buf(std::integral_constant<int, (ib + C::NSB - 1) % C::NSB>{});
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        (dma_slot_ab(std::integral_constant<int, J>{}, (kt + 1) * BK, (kt + C::NSB - 1) * BK, nxtA, nxtB), ...);
+      }(std::make_integer_sequence<int, D>{});
+      ring_barrier_ab();
+    };
+    auto run_ab = [&](auto STEP) {
+      for (int kt = kt0; kt < kt1; kt += RING) {
+        [&]<int... U>(std::integer_sequence<int, U...>) {
+          (STEP(std::integral_constant<int, U % NS>{}, std::integral_constant<int, U % C::NSB>{}, kt + U), ...);
+        }(std::make_integer_sequence<int, RING>{});
+      }
+    };
+    if (idle_half) run_ab(step_idle_ab);
+    else run_ab(step_spread_ab);
   } else {
   [&]<int... I>(std::integer_sequence<int, I...>) {
     (dma_stage((kt0 + I) * BK, stage_buf(std::integral_constant<int, I>{})), ...);
@@ -705,11 +722,17 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
           }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's slot stores have completed
       __syncthreads();
+      // (the split ring of the 256 x 256 tile fills the LDS exactly: its flag is the first word of the last
+      // B stage, free once the main loop has drained; every wave reads it before any can go on to overwrite
+      // it with epilogue staging)
+      int* const flag = C::AB ? reinterpret_cast<int*>(ldsb2) : &sk_flag;
       if (tid == 0)
-        sk_flag = __hip_atomic_fetch_add(p.sk_cnt + sk_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                  sk_last - sk_first;
+        *flag = __hip_atomic_fetch_add(p.sk_cnt + sk_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                sk_last - sk_first;
       __syncthreads();
-      if (!sk_flag) return;
+      const bool last = *flag != 0;
+      __syncthreads();
+      if (!last) return;
       if (tid == 0) __hip_atomic_store(p.sk_cnt + sk_tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       // The S slots are added in chunk order, in batches of up to 16 float4 per thread (half the partial tile
       // at most, so the batch's registers fit beside the accumulators): all loads of one slot's batch are
@@ -1195,7 +1218,8 @@ static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStrea
 using BigTile = Cfg<MTP_BIG_CFG>;              // 8 waves (wave tile 64 x 128), 128 KB LDS ring
 // The bf16 forward products (plain and grouped, K-major operands) take the same tile with a 64-deep K step
 // in two stages: 128-byte rows per DMA instead of 64, 2-4% faster at the workload shapes.  The row-major-K
-// (backward) and E4M3 forms keep the 32-deep ring their layouts are built on.
+// (backward) and E4M3 forms keep the 32-deep ring their layouts are built on.  (Its split ring, 2 x 32 +
+// 3 x 32 KB, fills the LDS and the registers: with two waves per SIMD it spills.)
 using BigFwdTile = Cfg<256, 256, 4, 2, 64, 2, false>;  // 8 waves (64 x 128), 2 x 64 KB LDS stages
 // Likewise the 256 x 192 tile, in the split ring (A tiles in two stages, B tiles in three: 2 x 32 + 3 x 24 KB),
 // which loads each B tile two steps ahead: against the plain two-stage ring at the 175B-shard shapes, 3-6%
