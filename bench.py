@@ -399,7 +399,7 @@ def main():
 
     if args.vs_hipblaslt:
         res = {}
-        for (M, N, K) in [(8192, 8192, 8192), (4096, 7168, 8192)]:
+        for (M, N, K) in [(8192, 8192, 8192), (4096, 7168, 8192), (2048, 12288, 6144)]:
             X = torch.randn(M, K, device="cuda").to(torch.bfloat16)
             W = (torch.randn(N, K, device="cuda") * 0.02).to(torch.bfloat16)
             Y = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
