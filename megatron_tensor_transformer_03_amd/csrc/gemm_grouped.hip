@@ -9,8 +9,8 @@ namespace mtp {
 
 hipError_t gemm_grouped(const GemmParams& p, int mode, int rows_upper, hipStream_t st, int split_chunks) {
   switch (mode) {
-    case MODE_SWIGLU: return launch_cfg<BigFwdTile, MODE_SWIGLU, true>(p, rows_upper, st, 0, split_chunks);
-    case MODE_ROW: return launch_cfg<BigFwdTile, MODE_ROW, true>(p, rows_upper, st, 0, split_chunks);
+    case MODE_SWIGLU: return launch_cfg<GroupedTile, MODE_SWIGLU, true>(p, rows_upper, st, 0, split_chunks);
+    case MODE_ROW: return launch_cfg<GroupedTile, MODE_ROW, true>(p, rows_upper, st, 0, split_chunks);
     default: return hipErrorInvalidValue;
   }
 }
@@ -26,7 +26,7 @@ GroupedPlan grouped_plan(int mode, int64_t rows_upper, int groups, int64_t Nout,
   GroupedPlan pl;
   const int cus = cu_count();
   if (cus <= 0 || groups <= 0 || rows_upper <= 0 || (mode != MODE_SWIGLU && mode != MODE_ROW)) return pl;
-  using C = BigFwdTile;
+  using C = GroupedTile;
   const int64_t nb = mode == MODE_SWIGLU ? C::BN / 2 : C::BN;
   const int64_t tiles_n = (Nout + nb - 1) / nb;
   const int64_t tail = (int64_t)groups * tiles_n, full = rows_upper / C::BM * tiles_n;
