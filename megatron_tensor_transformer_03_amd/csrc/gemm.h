@@ -55,6 +55,8 @@ struct GemmParams {
   int sk_dp_tiles = 0;              // split schedule: leading tiles run whole (a multiple of the grid)
   int sk_slot_tiles = 0;            // split schedule: tiles with partial slots in the workspace (set at launch)
   int sk_full_slots = 0;            // grouped split-tail schedule: workgroups of whole tiles before the tail units
+  int sk_share = 0;                 // shared-tail split: tiles whose K tails one workgroup runs (0: other forms)
+  int sk_cut = 0;                   // shared-tail split: ring passes of each tile's first piece
   int* sk_cnt = nullptr;            // split schedule: per-tile arrival counters (set at launch)
 };
 
@@ -66,9 +68,13 @@ constexpr int64_t kSplitMaxTiles = 4096;
 constexpr size_t kSplitCounterBytes = 4 * kSplitMaxTiles;
 
 // Tile and schedule of a launch (split_groups 0: one workgroup per tile) and the workspace it needs.
+// share > 0: the shared-tail split (fewer tiles than CUs): each tile's first K passes in a workgroup of its own,
+// the remaining passes of `share` tiles in one further workgroup (split_chunks = 2, split_groups = tiles +
+// tiles / share).
 struct GemmPlan {
   int bm = 0, bn = 0, split_groups = 0, id = 0, split_chunks = 0, dp_tiles = 0;
   size_t ws_bytes = 0;
+  int share = 0;
 };
 // row_major_k: 0 both operands K-contiguous; 1 B row-major-K (dgrad); 2 both row-major-K (wgrad).  Only
 // schedules whose workspace fits in ws_avail bytes are considered (one tile per workgroup needs none).

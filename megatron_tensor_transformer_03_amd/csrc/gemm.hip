@@ -107,6 +107,20 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k
         }
       }
     }
+    // shared tails (the forward split-ring tiles, fewer tiles than CUs, both spread evenly over the 8 XCDs):
+    // tiles / cus of each tile's K in a workgroup of its own, the rest of `share` tiles in one more; the time is
+    // that share of a tile plus a fill, plus one partial tile per tile written and read back
+    const int64_t extra = cus - tiles;
+    if (fwd && sr && o.id == 1 && extra > 0 && tiles % 8 == 0 && extra % 8 == 0 &&
+        (tiles / 8) % (extra / 8) == 0 && passes >= 2) {
+      const int share = (int)(tiles / extra);
+      const size_t ws = kSplitCounterBytes + (size_t)(tiles * 2 * o.slot_bytes);
+      const double t_sh = tile_t * ((double)tiles / cus + 192.0 / (double)K) + 2.0 * tiles * o.slot_bytes / kBW;
+      if (ws <= ws_avail && t_sh < best_t * 0.95) {
+        best_t = t_sh;
+        best = GemmPlan{o.bm, (int)nbo, (int)(tiles + tiles / share), o.id, 2, 0, ws, share};
+      }
+    }
   }
   return best;
 }

@@ -1072,6 +1072,27 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     // one workgroup each, G at a time; only the remaining tiles are cut into chunks, so a ragged last wave
     // of tiles is spread over every CU while the full waves pay no partial-sum traffic.
     const int T = tiles_m * tiles_n;
+    if (p.sk_share > 0) {
+      // Shared tails (fewer tiles than CUs: the 175B-shard QKV has 192 tiles of 256 x 192 on 256 CUs): every
+      // workgroup runs about the same K work.  Block b lands on XCD b mod 8; per XCD the first T / 8 blocks run
+      // the first sk_cut ring passes of the XCD's T / 8 tiles (in the usual XCD-contiguous tile order), the
+      // others the remaining passes of sk_share tiles each, one after another.  Each tile has two partial
+      // sums, added by the later finisher in piece order (the split protocol below).
+      const int per = T / 8, xcd = (int)blockIdx.x & 7, r = (int)blockIdx.x >> 3;
+      int tm, tn;
+      if (r < per) {
+        const int t = xcd * per + r;
+        tile_coords(t, tiles_m, tiles_n, tm, tn);
+        run_tile(tm, tn, 0, p.M, p.B, 0, p.sk_cut * RING, t, t, 0, 0, 1, true);
+      } else {
+        for (int q = 0; q < p.sk_share; ++q) {
+          const int t = xcd * per + (r - per) * p.sk_share + q;
+          tile_coords(t, tiles_m, tiles_n, tm, tn);
+          run_tile(tm, tn, 0, p.M, p.B, p.sk_cut * RING, KTS, t, t, 1, 0, 1, true);
+        }
+      }
+      return;
+    }
     const int TD = p.sk_dp_tiles, TR = T - TD;
     const int U = TD + TR * S;
     for (int u = xcd_remap(blockIdx.x, G); u < U; u += G) {
@@ -1134,7 +1155,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
 
 template <class C, int MODE, bool GROUPED, bool AT = false, bool BT = false, int EPI = EPI_PLAIN, bool F8 = false>
 static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStream_t st, int split_groups = 0,
-                             int split_chunks = 0, int dp_tiles = 0) {
+                             int split_chunks = 0, int dp_tiles = 0, int share = 0) {
   GemmParams p = p0;
   const int nb = MODE == MODE_SWIGLU ? C::BN / 2 : C::BN;
   const int tiles_n = (p.Nout + nb - 1) / nb;
@@ -1151,6 +1172,19 @@ static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStrea
       const size_t slot = (size_t)C::FM * C::FN * 16 * sizeof(float) * C::NT;
       // whole tiles first: whole waves of the grid, leaving at least one tile to split
       if (dp_tiles < 0 || dp_tiles % split_groups != 0 || dp_tiles >= tiles) return hipErrorInvalidValue;
+      if (share > 0) {
+        // shared tails: per XCD, tiles / 8 first pieces and tiles / 8 / share tail workgroups; the first piece
+        // of each tile gets the share of the K passes that balances the two kinds of workgroup
+        if (split_chunks != 2 || dp_tiles != 0 || tiles % 8 != 0 || (tiles / 8) % share != 0 ||
+            split_groups != tiles + tiles / share)
+          return hipErrorInvalidValue;
+        const int64_t ri = (((int64_t)p.K + C::BK - 1) / C::BK + C::RING - 1) / C::RING;
+        int64_t cut = (ri * share + (share + 1) / 2) / (share + 1);
+        cut = cut < 1 ? 1 : (cut > ri - 1 ? ri - 1 : cut);
+        if (ri < 2) return hipErrorInvalidValue;
+        p.sk_share = share;
+        p.sk_cut = (int)cut;
+      }
       // the caller's workspace: the counter block, then the slots of the split tiles (the plan was chosen to fit)
       if (tiles > kSplitMaxTiles || !p.ws ||
           p.ws_bytes < kSplitCounterBytes + (size_t)(tiles - dp_tiles) * split_chunks * slot)
@@ -1242,10 +1276,13 @@ template <int MODE, int EPI = EPI_PLAIN>
 static hipError_t dispatch_fwd(const GemmParams& p, hipStream_t st) {
   const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K, 0, true, p.ws ? p.ws_bytes : 0);
   switch (pl.id) {
-    case 0: return launch_cfg<BigFwdTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+    case 0:
+      return launch_cfg<BigFwdTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles,
+                                                                    pl.share);
     case 1:
       if constexpr (MODE != MODE_SWIGLU)
-        return launch_cfg<WideFwdTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+        return launch_cfg<WideFwdTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks,
+                                                                       pl.dp_tiles, pl.share);
       return hipErrorInvalidValue;
     case 2: return launch_cfg<HalfTile, MODE, false, false, false, EPI>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
     default: return launch_cfg<SmallTile, MODE, false, false, false, EPI>(p, 0, st);  // (never split)

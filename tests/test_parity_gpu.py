@@ -134,6 +134,9 @@ def test_integer_exact_row_partials_and_sum(M, N, Kp, p):
     (900, 4100, 5120, (256, 256, 3), True),    # 40 passes in 3 chunks
     (4100, 4100, 4096, (256, 256, 3), True),   # hybrid: 256 of the 289 tiles whole, the other 33 in 3 chunks
     (544, 7488, 10752, (256, 192, 2), True),   # the split-ring 256 x 192 tile: 28 passes of 6 K steps in 2 chunks
+    # (shared tails: 192 tiles on 256 CUs, each tile's first 24 of 32 passes in its own workgroup, the last 8 of
+    # three tiles in one more; the 175B-shard QKV shape)
+    (2048, 4608, 12288, (256, 192, 2), True),
     # (not split: the split ring with K = 1040, 17 K steps (the last ragged) padded to 18 with a zero step)
     (1408, 5952, 1040, (256, 192, 0), True),
 ])
