@@ -59,7 +59,9 @@ struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BK = BK_, NS = NS_;
   // Split ring (NSB = NS + 1, two-stage forms without EARLY): the B operand's tiles get a ring of NSB stages of
   // their own, the A operand's keep NS, where the LDS cannot hold NS + 1 stages of both (256 x 192: 3 x 56 KB
-  // does not fit, 2 x 32 + 3 x 24 KB does).  Each B tile is then loaded two steps ahead of its use.
+  // does not fit, 2 x 32 + 3 x 24 KB does).  Each B tile is then loaded two steps ahead of its use.  (A fourth
+  // B stage would add no lead: loads retire in issue order, so waiting at the end of step kt for the A tile of
+  // step kt + 1, issued during step kt, also waits for the B tile of step kt + 2, issued during step kt - 1.)
   static constexpr int NSB = NSB_ ? NSB_ : NS;
   static constexpr bool AB = NSB != NS;
   static constexpr int RING = AB ? NS * NSB : NS;  // K steps per loop iteration (each stage a compile-time choice)
