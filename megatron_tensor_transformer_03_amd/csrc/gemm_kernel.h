@@ -59,9 +59,10 @@ struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BK = BK_, NS = NS_;
   // Split ring (NSB = NS + 1, two-stage forms without EARLY): the B operand's tiles get a ring of NSB stages of
   // their own, the A operand's keep NS, where the LDS cannot hold NS + 1 stages of both (256 x 192: 3 x 56 KB
-  // does not fit, 2 x 32 + 3 x 24 KB does).  Each B tile is then loaded two steps ahead of its use.  (A fourth
-  // B stage would add no lead: loads retire in issue order, so waiting at the end of step kt for the A tile of
-  // step kt + 1, issued during step kt, also waits for the B tile of step kt + 2, issued during step kt - 1.)
+  // does not fit, 2 x 32 + 3 x 24 KB does).  Each B tile is loaded two steps ahead of its use, and so is each
+  // A tile, into its own stage right after a barrier inside the step that reads it (see step_spread_ab).
+  // (A fourth B stage would add no lead: loads retire in issue order, so the wait for the A tile of step
+  // kt + 1 also waits for every B tile issued before it.)
   static constexpr int NSB = NSB_ ? NSB_ : NS;
   static constexpr bool AB = NSB != NS;
   static constexpr int RING = AB ? NS * NSB : NS;  // K steps per loop iteration (each stage a compile-time choice)
@@ -555,22 +556,35 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     }(std::make_integer_sequence<int, KS>{});
     ring_barrier();
   };
-  // ---- split ring (C::AB): A tiles in NS = 2 stages, B tiles in NSB = 3.  Each wave's first JA DMA slots are A
-  // rows and the rest B rows; step kt loads the A tile of step kt + 1 and the B tile of step kt + 2, A slots
-  // first, so at the end of a step the newest JB loads (the B tile two steps ahead) may stay in flight.
+  // ---- split ring (C::AB): A tiles in NS = 2 stages, B tiles in NSB = 3, with a barrier inside each step.
+  // Step kt reads A stage kt % 2 and B stage kt % 3.  Its B slots (the B tile of step kt + 2, into the B stage
+  // consumed in step kt - 1) are spread over the first half of its MFMAs.  Its fragment reads of the last k
+  // step are issued during the MFMAs of the one before; once every wave's reads have returned (lgkmcnt(0)) and
+  // the waves meet at the mid-step barrier, no wave reads A stage kt % 2 again, and the A slots reload it with
+  // the A tile of step kt + 2 during the MFMAs of the last k step.  Both operands thus load two steps ahead:
+  // the A tile lands within ~1.25 steps (instead of within the rest of a step, had it waited for the stage
+  // consumed in step kt - 1), enough for an activation read from HBM rather than from cache.  At the end of
+  // step kt everything issued in step kt - 1 (the tiles of step kt + 1) has landed, while the D loads of step
+  // kt may stay in flight (loads complete in issue order).  The MFMA order per accumulator is unchanged.
   constexpr int JA = C::AB ? GA / NWAVES : D, JB = D - JA;
-  constexpr int kNewerAB = C::AB ? (C::NSB - 2) * JB : 0;
-  constexpr int kWaitAB = 0x0F70 | (kNewerAB & 15) | ((kNewerAB >> 4) << 14);
+  constexpr int kWaitAB = 0x0F70 | (D & 15) | ((D >> 4) << 14);  // vmcnt(D)
   auto ring_barrier_ab = [&]() {
     __builtin_amdgcn_s_waitcnt(kWaitAB);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  auto dma_slot_ab = [&](auto J, int k0a, int k0b, uint16_t* sA, uint16_t* sB) {
+  auto mid_barrier_ab = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's fragment reads have returned
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto dma_slot_ab = [&](auto J, int k0, uint16_t* sA, uint16_t* sB) {
     constexpr int j = decltype(J)::value;
     constexpr bool is_a = j < JA;
-    const int k0 = is_a ? k0a : k0b;
     const int soff = k0 < p.K ? 2 * k0 : 0;
     const int g = j * NWAVES + wave_u;  // uniform
     uint32_t vo = d_off[j];
@@ -578,37 +592,43 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     uint16_t* dst = is_a ? sA + g * ROWS_PER_DMA * BK : sB + (g - GA) * ROWS_PER_DMA * BK;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a_rsrc : b_rsrc, (lds_ptr)dst, 16, vo, soff, 0, 0);
   };
-  // One K step of the split ring on A stage IA and B stage IB, scheduled as step_spread.
+  // One K step of the split ring on A stage IA and B stage IB.  Issue order: an MFMA, then (while this k
+  // step's reads remain) one fragment read, then (after odd MFMAs of the first k steps) one B slot; in the last
+  // k step, after the mid-step barrier, one A slot after each of its first MFMAs.
   auto step_spread_ab = [&](auto IA, auto IB, int kt) {
     constexpr int ia = decltype(IA)::value, ib = decltype(IB)::value;
-    const uint16_t* curA = stage_buf(std::integral_constant<int, ia>{});
+    uint16_t* curA = stage_buf(std::integral_constant<int, ia>{});
     const uint16_t* curB = bstage_buf(std::integral_constant<int, ib>{});
-    uint16_t* nxtA = stage_buf(std::integral_constant<int, (ia + 1) % NS>{});
     uint16_t* nxtB = bstage_buf(std::integral_constant<int, (ib + C::NSB - 1) % C::NSB>{});
-    const int k0a = (kt + 1) * BK, k0b = (kt + C::NSB - 1) * BK;
+    const int k2 = (kt + 2) * BK;
     constexpr int NM = FM * FN;
-    static_assert(2 * D <= KS * NM, "every DMA slot finds an MFMA");
+    static_assert(C::NSB == 3, "the B tile of step kt + 2 goes to the stage consumed in step kt - 1");
+    static_assert(2 * JB <= (KS - 1) * NM && JA <= NM, "every DMA slot finds an MFMA");
     read_frags2(curA, curB, 0, std::integral_constant<int, 0>{});
     [&]<int... S>(std::integer_sequence<int, S...>) {
       ([&] {
         constexpr int ks = S;
-        if constexpr (ks + 1 < KS) read_frags2(curA, curB, ks + 1, std::integral_constant<int, (ks + 1) & 1>{});
+        constexpr bool last = ks + 1 == KS;
+        if constexpr (!last) read_frags2(curA, curB, ks + 1, std::integral_constant<int, (ks + 1) & 1>{});
+        if constexpr (last) mid_barrier_ab();
         [&]<int... MI>(std::integer_sequence<int, MI...>) {
           ([&] {
             constexpr int mi = MI, gm = ks * NM + mi, a = mi / FN, b = mi % FN;
             if constexpr (!F8)
               acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][b], fa[ks & 1][a], acc[a][b], 0, 0, 0);
-            if constexpr (gm % 2 == 1 && gm / 2 < D)
-              dma_slot_ab(std::integral_constant<int, gm / 2>{}, k0a, k0b, nxtA, nxtB);
+            if constexpr (!last && gm % 2 == 1 && gm / 2 < JB)
+              dma_slot_ab(std::integral_constant<int, JA + gm / 2>{}, k2, curA, nxtB);
+            if constexpr (last && mi < JA) dma_slot_ab(std::integral_constant<int, mi>{}, k2, curA, nxtB);
           }(), ...);
         }(std::make_integer_sequence<int, NM>{});
-        constexpr int NR = ks + 1 < KS ? FM + FN : 0;
+        constexpr int NR = last ? 0 : FM + FN;
         [&]<int... MI>(std::integer_sequence<int, MI...>) {
           ([&] {
             constexpr int mi = MI, gm = ks * NM + mi;
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if constexpr (mi < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if constexpr (gm % 2 == 1 && gm / 2 < D) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+            if constexpr ((!last && gm % 2 == 1 && gm / 2 < JB) || (last && mi < JA))
+              __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
           }(), ...);
         }(std::make_integer_sequence<int, NM>{});
         __builtin_amdgcn_sched_barrier(0);
@@ -619,27 +639,30 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
 
   if constexpr (SPLIT) __syncthreads();  // the previous tile's epilogue may still read the LDS stages
   if constexpr (C::AB) {
-    // prologue: A of step kt0, B of steps kt0 and kt0 + 1
-    const int k0 = kt0 * BK;
+    // prologue: the A and B tiles of steps kt0 and kt0 + 1
     [&]<int... J>(std::integer_sequence<int, J...>) {
-      (dma_slot_ab(std::integral_constant<int, J>{}, k0, k0, stage_buf(std::integral_constant<int, 0>{}),
+      (dma_slot_ab(std::integral_constant<int, J>{}, kt0 * BK, stage_buf(std::integral_constant<int, 0>{}),
                    bstage_buf(std::integral_constant<int, 0>{})), ...);
-    }(std::make_integer_sequence<int, D>{});
-    [&]<int... J>(std::integer_sequence<int, J...>) {
-      (dma_slot_ab(std::integral_constant<int, JA + J>{}, k0, k0 + BK, stage_buf(std::integral_constant<int, 0>{}),
+      (dma_slot_ab(std::integral_constant<int, J>{}, (kt0 + 1) * BK, stage_buf(std::integral_constant<int, 1>{}),
                    bstage_buf(std::integral_constant<int, 1>{})), ...);
-    }(std::make_integer_sequence<int, JB>{});
-    ring_barrier_ab();
-    // (grouped products: the idle lower half of a short last row tile, as in the two-stage ring below)
+    }(std::make_integer_sequence<int, D>{});
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    // (grouped products: the idle lower half of a short last row tile, as in the two-stage ring below; the
+    // idle waves issue the same loads and meet the same barriers)
     bool idle_half = false;
     if constexpr (GROUPED && C::WAVES_M == 4 && NWAVES == 8) idle_half = rows - m0 <= BM / 2 && wm0 >= BM / 2;
     auto step_idle_ab = [&](auto IA, auto IB, int kt) {
       constexpr int ia = decltype(IA)::value, ib = decltype(IB)::value;
-      uint16_t* nxtA = stage_buf(std::integral_constant<int, (ia + 1) % NS>{});
+      uint16_t* curA = stage_buf(std::integral_constant<int, ia>{});
       uint16_t* nxtB = bstage_buf(std::integral_constant<int, (ib + C::NSB - 1) % C::NSB>{});
       [&]<int... J>(std::integer_sequence<int, J...>) {
-        (dma_slot_ab(std::integral_constant<int, J>{}, (kt + 1) * BK, (kt + C::NSB - 1) * BK, nxtA, nxtB), ...);
-      }(std::make_integer_sequence<int, D>{});
+        (dma_slot_ab(std::integral_constant<int, JA + J>{}, (kt + 2) * BK, curA, nxtB), ...);
+      }(std::make_integer_sequence<int, JB>{});
+      mid_barrier_ab();
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        (dma_slot_ab(std::integral_constant<int, J>{}, (kt + 2) * BK, curA, nxtB), ...);
+      }(std::make_integer_sequence<int, JA>{});
       ring_barrier_ab();
     };
     auto run_ab = [&](auto STEP) {
