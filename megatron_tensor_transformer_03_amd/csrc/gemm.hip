@@ -51,10 +51,12 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k
   // forms.)
   const double wide_eff = row_major_k ? 0.95 : 0.85;
   const double half_eff = row_major_k ? 0.85 : 0.75;
-  // ns_bk: K per ring pass (the split schedule's unit, and the granularity the step count is padded to with
-  // zero steps, charged to the tile's time below); the forward 256 x 192 tile's split ring passes 6 K steps
-  const bool sr = !row_major_k && !f8;  // the forward 256 x 192 tile runs the split ring
-  const Opt opts[] = {{256, 256, 1.00, 0, 128, 256 << 10, 128}, {256, 192, wide_eff, 1, sr ? 384 : 128, 192 << 10, sr ? 384 : 128},
+  // ns_bk: K per ring pass (the split schedule's unit); pad_k: the granularity the step count is padded to
+  // with zero steps, charged to the tile's time below.  The forward bf16 256 x 256 and 256 x 192 tiles run the
+  // split ring: passes of 6 K steps, and no step past K.
+  const bool sr = !row_major_k && !f8;
+  const int sr_k = sr ? 384 : 128, sr_pad = sr ? 64 : 128;
+  const Opt opts[] = {{256, 256, 1.00, 0, sr_k, 256 << 10, sr_pad}, {256, 192, wide_eff, 1, sr_k, 192 << 10, sr_pad},
                       {256, 128, half_eff, 2, 128, 128 << 10, 128}, {128, 128, 0.72, 3, 256, 0, 256},
                       {128, 128, 0.72, 4, 128, 64 << 10, 128}};
   constexpr double kR = 5.5e12 * 1e-6;   // FLOP per microsecond of one CU

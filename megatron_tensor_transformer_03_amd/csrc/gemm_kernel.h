@@ -261,8 +261,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   // K steps, rounded up to a multiple of NS: the loop body covers NS steps (one per LDS stage, each stage a
   // compile-time choice) and has no branches, so the compiler's wait counts stay exact.  With KFULL the
   // step count is a multiple of NS and every chunk is in range; otherwise chunks at or past K read as zero,
-  // so padding steps multiply zeros.  (The split ring's loop covers RING = 6 steps; its step count is padded
-  // the same way.)
+  // so padding steps multiply zeros.  (The split ring's loop covers RING = 6 steps; the split schedule counts
+  // in such passes, KTS rounds up to one, and the loop stops after step KT - 1.)
   const int KT = (p.K + BK - 1) / BK;
   constexpr int RING = C::RING;
   const int KTS = (KT + RING - 1) / RING * RING;
@@ -665,11 +665,23 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
       }(std::make_integer_sequence<int, JA>{});
       ring_barrier_ab();
     };
+    // Whole ring passes in the loop, then the K steps left of a last partial pass one by one (the same
+    // stages); steps past the last K step are not run.
     auto run_ab = [&](auto STEP) {
-      for (int kt = kt0; kt < kt1; kt += RING) {
+      const int kend = kt1 < KT ? kt1 : KT;
+      const int kpass_end = kt0 + (kend - kt0) / RING * RING;
+      int kt = kt0;
+      for (; kt < kpass_end; kt += RING) {
         [&]<int... U>(std::integer_sequence<int, U...>) {
           (STEP(std::integral_constant<int, U % NS>{}, std::integral_constant<int, U % C::NSB>{}, kt + U), ...);
         }(std::make_integer_sequence<int, RING>{});
+      }
+      if (kt < kend) {
+        [&]<int... U>(std::integer_sequence<int, U...>) {
+          (void)((kt + U < kend ? (STEP(std::integral_constant<int, U % NS>{},
+                                       std::integral_constant<int, U % C::NSB>{}, kt + U), true)
+                                : false) && ...);
+        }(std::make_integer_sequence<int, RING - 1>{});
       }
     };
     if (idle_half) run_ab(step_idle_ab);
@@ -1191,7 +1203,9 @@ static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStrea
     tiles = (int64_t)((p.M + C::BM - 1) / C::BM) * tiles_n;
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const bool kfull = p.K % (C::BK * C::RING) == 0;  // whole chunks and a step count that fills the ring
+  // KFULL: no chunk of a K step lies past K.  The two-stage and EARLY rings also pad the step count to a
+  // multiple of their ring with zero steps, which must read as zero; the split ring runs no step past K.
+  const bool kfull = C::AB ? p.K % C::BK == 0 : p.K % (C::BK * C::RING) == 0;
   if constexpr (!GROUPED) {
     if (split_groups > 0 && split_chunks > 1) {
       const size_t slot = (size_t)C::FM * C::FN * 16 * sizeof(float) * C::NT;
@@ -1275,20 +1289,23 @@ static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStrea
 // (8 waves of 64 x 128: against 128 x 64 wave tiles, 1.25-1.45x faster on some MI355X boards and even on
 // the others, in every mode, at every workload shape; outputs bitwise equal)
 using BigTile = Cfg<MTP_BIG_CFG>;              // 8 waves (wave tile 64 x 128), 128 KB LDS ring
-// The bf16 forward products (plain and grouped, K-major operands) take the same tile with a 64-deep K step
-// in two stages: 128-byte rows per DMA instead of 64, 2-4% faster at the workload shapes.  The row-major-K
-// (backward) and E4M3 forms keep the 32-deep ring their layouts are built on.  (Its split ring, 2 x 32 +
-// 3 x 32 KB, fills the LDS and the registers: with two waves per SIMD it spills.)
-using BigFwdTile = Cfg<256, 256, 4, 2, 64, 2, false>;  // 8 waves (64 x 128), 2 x 64 KB LDS stages
-// The grouped (MoE) products have the register room the dense ones lack (no bias or norm epilogue state), so
-// they take the 256 x 256 tile in the split ring: at the MoE workload's shapes, where every expert's weights
-// stream from HBM, the expert MLP ran 2781 against 2944 us (5.5%).
-using GroupedTile = Cfg<256, 256, 4, 2, 64, 2, false, 3>;  // 8 waves (64 x 128), split ring, 160 KB
-// Likewise the 256 x 192 tile, in the split ring (A tiles in two stages, B tiles in three: 2 x 32 + 3 x 24 KB),
-// which loads each B tile two steps ahead: against the plain two-stage ring at the 175B-shard shapes, 3-6%
-// faster with the weight cached and 8-14% with it streaming from HBM (QKV 236.7 -> 204.4 us, fc1 267.0 ->
-// 234.5, fc2 270.5 -> 244.8), bitwise the same sums.  It beats the 256 x 256 tile where its tile count fills
-// whole waves.
+// The bf16 forward products (plain and grouped, K-major operands) take the same tile with a 64-deep K step in
+// the split ring (A tiles in two stages, B tiles in three: 2 x 32 + 3 x 32 KB, the whole LDS), each stage
+// reloaded two steps ahead (step_spread_ab): 128-byte rows per DMA instead of 64.  The row-major-K (backward)
+// and E4M3 forms keep the 32-deep ring their layouts are built on.  Against the plain two-stage 64-deep ring
+// (both operands reloaded one step ahead) at the 70B-shard shapes: the layer step 828 -> 785 us cold (fc1
+// 457 -> 427, QKV 142 -> 127), 8192^3 852 -> 830 us; with both operands cached 0-8% slower (70B fc2 shape
+// 193 -> 208 us), and at K = 1024 (345M fc1) 1-7% slower.  The split-K forms spill some registers outside
+// the main loop (bias, norm and split epilogue state).
+using BigFwdTile = Cfg<256, 256, 4, 2, 64, 2, false, 3>;  // 8 waves (64 x 128), split ring, 160 KB
+// The grouped (MoE) products take it too: at the MoE workload's shapes, where every expert's weights stream
+// from HBM, the expert MLP ran 2781 against 2944 us (5.5%) on it, before the A stages were reloaded early.
+using GroupedTile = BigFwdTile;
+// Likewise the 256 x 192 tile, in the split ring (2 x 32 + 3 x 24 KB): against the plain two-stage ring at
+// the 175B-shard shapes, 3-6% faster with the weight cached and 8-14% with it streaming from HBM (QKV
+// 236.7 -> 204.4 us, fc1 267.0 -> 234.5, fc2 270.5 -> 244.8); reloading the A stages early then took the cold
+// shapes a further 9-16% (QKV 258 -> 221 us, fc1 299 -> 252, fc2 290 -> 264).  It beats the 256 x 256 tile
+// where its tile count fills whole waves.
 using WideFwdTile = Cfg<256, 192, 4, 2, 64, 2, false, 3>;  // 8 waves (64 x 96), split ring, 136 KB
 using WideTile = Cfg<MTP_WIDE_CFG>;            // 8 waves (64 x 96), 112 KB
 using HalfTile = Cfg<MTP_HALF_CFG>;            // 8 waves (64 x 64), 96 KB

@@ -131,13 +131,13 @@ def test_integer_exact_row_partials_and_sum(M, N, Kp, p):
 @pytest.mark.parametrize("M,N,K,plan,sampled", [
     (300, 1280, 7168, (256, 128, 6), False),   # 56 ring passes in 6 chunks (9 or 10 each)
     (300, 190, 2048, (256, 128, 4), False),
-    (900, 4100, 5120, (256, 256, 3), True),    # 40 passes in 3 chunks
+    (900, 4100, 7008, (256, 256, 3), True),    # 110 K steps (the last ragged) in 19 ring passes, 3 chunks
     (4100, 4100, 4096, (256, 256, 3), True),   # hybrid: 256 of the 289 tiles whole, the other 33 in 3 chunks
     (544, 7488, 10752, (256, 192, 2), True),   # the split-ring 256 x 192 tile: 28 passes of 6 K steps in 2 chunks
     # (shared tails: 192 tiles on 256 CUs, each tile's first 24 of 32 passes in its own workgroup, the last 8 of
     # three tiles in one more; the 175B-shard QKV shape)
     (2048, 4608, 12288, (256, 192, 2), True),
-    # (not split: the split ring with K = 1040, 17 K steps (the last ragged) padded to 18 with a zero step)
+    # (not split: the split ring with K = 1040, 17 K steps, the last ragged: two whole passes and five steps)
     (1408, 5952, 1040, (256, 192, 0), True),
 ])
 def test_split_schedule_integer_exact(M, N, K, plan, sampled):
@@ -171,7 +171,7 @@ def test_split_schedule_integer_exact(M, N, K, plan, sampled):
     assert np.array_equal(bits(Yb)[rows], oracle.round_bf16(S + widen_bits(bb)[None, :]))
 
 
-@pytest.mark.parametrize("M,F,K,plan", [(300, 200, 2048, (256, 64, 4)), (400, 4100, 5120, (256, 128, 3)),
+@pytest.mark.parametrize("M,F,K,plan", [(300, 200, 2048, (256, 64, 4)), (400, 4100, 7000, (256, 128, 3)),
                                          (900, 8200, 2048, (256, 128, 3))])  # (the last one hybrid)
 def test_split_schedule_swiglu(M, F, K, plan):
     say("split swiglu", M, F, K)
