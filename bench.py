@@ -366,8 +366,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     ap.add_argument("--vs-hipblaslt", action="store_true",
-                    help="only time two plain column GEMMs (8192^3 and 4096x7168x8192, no bias or activation) "
-                         "through this library and through torch's linear (hipBLASLt), 5 launches each, for a "
+                    help="only time three plain column GEMMs (8192^3, 4096x7168x8192 and 2048x12288x6144, no "
+                         "bias or activation) through this library and through torch's linear (hipBLASLt): 3 "
+                         "warm-up launches each, then 5 alternating batches of 4, the median batch; also the "
                          "side-by-side counter run")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -404,17 +405,24 @@ def main():
             W = (torch.randn(N, K, device="cuda") * 0.02).to(torch.bfloat16)
             Y = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
             ws = mtp.workspace_for([(M, N, K, mtp.ACT_NONE)])
-            for name, fn in [("mtp", lambda: mtp.mtp_column_linear(X, W, None, Y, workspace=ws)),
-                             ("hipblaslt", lambda: torch.nn.functional.linear(X, W))]:
-                torch.cuda.synchronize()
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                fn()
-                a.record()
-                for _ in range(4):
+            fns = [("mtp", lambda: mtp.mtp_column_linear(X, W, None, Y, workspace=ws)),
+                   ("hipblaslt", lambda: torch.nn.functional.linear(X, W))]
+            for _, fn in fns:  # warm-up (code loading, clocks)
+                for _ in range(3):
                     fn()
-                b.record()
-                b.synchronize()
-                res[f"{name} {M}x{N}x{K}"] = round(a.elapsed_time(b) / 4 * 1000, 1)
+            times = {name: [] for name, _ in fns}
+            for _ in range(5):  # the two libraries alternate; the median of 5 batches of 4 launches
+                for name, fn in fns:
+                    torch.cuda.synchronize()
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    for _ in range(4):
+                        fn()
+                    b.record()
+                    b.synchronize()
+                    times[name].append(a.elapsed_time(b) / 4 * 1000)
+            for name, t in times.items():
+                res[f"{name} {M}x{N}x{K}"] = round(sorted(t)[2], 1)
         print(json.dumps({"us_per_launch": res}), flush=True)
         return
 
