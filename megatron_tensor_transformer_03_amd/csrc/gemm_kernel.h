@@ -453,7 +453,6 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[q][j], fa[q][i], acc[i][j], 0, 0, 0);
   };
   constexpr int KS = F8 ? 1 : BK / 16;  // MFMA k steps per K step
-  constexpr bool kSpread = !C::EARLY && !F8 && !AT && !BT;  // main loop of step_spread
   static_assert(!C::EARLY || (NS * KS) % 2 == 0, "fragment sets alternate consistently across the ring");
   // vmcnt(n): wait until at most n of this wave's DMA instructions are outstanding (expcnt, lgkmcnt free).
   // The barrier ending step kt makes stage kt + LEAD visible: the DMAs newer than that stage may stay out.
@@ -501,57 +500,6 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
           read_frags(cur, ks, std::integral_constant<int, 0>{});
           mma(std::integral_constant<int, 0>{});
         }
-      }(), ...);
-    }(std::make_integer_sequence<int, KS>{});
-    ring_barrier();
-  };
-  // The two-stage 64-deep forms (EARLY = false, bf16, K-major operands).  Each wave's DMA slots of the next
-  // step are spread over the first half of this step's MFMAs (one slot after every second MFMA) instead of
-  // being issued together at its start: a burst of DMAs from all waves fills the load queue, and a wave stalled
-  // on a DMA issue cannot issue MFMAs, while slots issued in the second half would land too late for the
-  // barrier.  The fragments of k step ks + 1 are read into the other fragment set during the MFMAs of ks (one
-  // read after each of the first MFMAs).  The MFMA order per accumulator is unchanged (bitwise the same sums).
-  auto dma_slot = [&](int k0, uint16_t* sbuf, int j) {
-    const int soff = k0 < p.K ? 2 * k0 : 0;
-    const int g = j * NWAVES + wave_u;  // uniform
-    uint32_t vo = d_off[j];
-    if constexpr (!KFULL) vo = k0 + d_kc[j] < p.K ? vo : kOOB;
-    uint16_t* dst = sbuf + g * ROWS_PER_DMA * BK;
-    if constexpr (C::SPARE) dst = g < GA + C::GB ? dst : lds_spare;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(g < GA ? a_rsrc : b_rsrc, (lds_ptr)dst, 16, vo, soff, 0, 0);
-  };
-  auto step_spread = [&](auto I, int kt) {
-    constexpr int i = decltype(I)::value;
-    const uint16_t* cur = stage_buf(std::integral_constant<int, i>{});
-    uint16_t* nxt = stage_buf(std::integral_constant<int, (i + NS - 1) % NS>{});
-    const int k0n = (kt + NS - 1) * BK;
-    constexpr int NM = FM * FN;
-    static_assert(2 * D <= KS * NM, "every DMA slot finds an MFMA");
-    read_frags(cur, 0, std::integral_constant<int, 0>{});
-    [&]<int... S>(std::integer_sequence<int, S...>) {
-      ([&] {
-        constexpr int ks = S;
-        if constexpr (ks + 1 < KS) read_frags(cur, ks + 1, std::integral_constant<int, (ks + 1) & 1>{});
-        [&]<int... MI>(std::integer_sequence<int, MI...>) {
-          ([&] {
-            constexpr int mi = MI, gm = ks * NM + mi, a = mi / FN, b = mi % FN;
-            if constexpr (!F8)
-              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][b], fa[ks & 1][a], acc[a][b], 0, 0, 0);
-            if constexpr (gm % 2 == 1 && gm / 2 < D) dma_slot(k0n, nxt, gm / 2);
-          }(), ...);
-        }(std::make_integer_sequence<int, NM>{});
-        // issue order: an MFMA, then (while this k step's reads remain) one fragment read, then (after odd MFMAs
-        // of the first half) one DMA slot
-        constexpr int NR = ks + 1 < KS ? FM + FN : 0;
-        [&]<int... MI>(std::integer_sequence<int, MI...>) {
-          ([&] {
-            constexpr int mi = MI, gm = ks * NM + mi;
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if constexpr (mi < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if constexpr (gm % 2 == 1 && gm / 2 < D) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-          }(), ...);
-        }(std::make_integer_sequence<int, NM>{});
-        __builtin_amdgcn_sched_barrier(0);
       }(), ...);
     }(std::make_integer_sequence<int, KS>{});
     ring_barrier();
@@ -648,8 +596,11 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     }(std::make_integer_sequence<int, D>{});
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    // (grouped products: the idle lower half of a short last row tile, as in the two-stage ring below; the
-    // idle waves issue the same loads and meet the same barriers)
+    // Grouped products: a group's last row tile often holds few rows.  When it holds at most BM / 2, the waves
+    // of the lower half of the tile (wave rows WAVES_M / 2 ..) have no row to compute: they issue their share
+    // of the loads and meet every barrier, but read no fragments and issue no MFMAs.  Waves w and w + 4 share
+    // a SIMD and lie in different halves, so every SIMD keeps one computing wave and the tile takes about half
+    // the MFMA time.  (The choice is uniform per wave and made once, around two straight-line loops.)
     bool idle_half = false;
     if constexpr (GROUPED && C::WAVES_M == 4 && NWAVES == 8) idle_half = rows - m0 <= BM / 2 && wm0 >= BM / 2;
     auto step_idle_ab = [&](auto IA, auto IB, int kt) {
@@ -692,37 +643,10 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   }(std::make_integer_sequence<int, NS - 1>{});
   ring_barrier();
   if constexpr (C::EARLY) read_frags(lds0, 0, std::integral_constant<int, 0>{});
-  // Grouped products: a group's last row tile often holds few rows.  When it holds at most BM / 2, the waves
-  // of the lower half of the tile (wave rows WAVES_M / 2 ..) have no row to compute: they still issue their
-  // share of the DMA and meet every barrier, but read no fragments and issue no MFMAs.  Waves w and w + 4 share
-  // a SIMD and lie in different halves, so every SIMD keeps one computing wave and the tile takes about half
-  // the MFMA time.  (The choice is uniform per wave and made once, around two straight-line loops.)
-  bool idle_half = false;
-  if constexpr (GROUPED && kSpread && C::WAVES_M == 4 && NWAVES == 8)
-    idle_half = rows - m0 <= BM / 2 && wm0 >= BM / 2;
-  auto step_idle = [&](auto I, int kt) {
-    constexpr int i = decltype(I)::value;
-    uint16_t* nxt = stage_buf(std::integral_constant<int, (i + NS - 1) % NS>{});
-    const int k0n = (kt + NS - 1) * BK;
-#pragma unroll
-    for (int j = 0; j < D; ++j) dma_slot(k0n, nxt, j);
-    ring_barrier();
-  };
-  if (idle_half) {
-    for (int kt = kt0; kt < kt1; kt += NS) {
-      [&]<int... I>(std::integer_sequence<int, I...>) {
-        (step_idle(std::integral_constant<int, I>{}, kt + I), ...);
-      }(std::make_integer_sequence<int, NS>{});
-    }
-  } else {
-    for (int kt = kt0; kt < kt1; kt += NS) {
-      [&]<int... I>(std::integer_sequence<int, I...>) {
-        if constexpr (kSpread)
-          (step_spread(std::integral_constant<int, I>{}, kt + I), ...);
-        else
-          (step(std::integral_constant<int, I>{}, kt + I), ...);
-      }(std::make_integer_sequence<int, NS>{});
-    }
+  for (int kt = kt0; kt < kt1; kt += NS) {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (step(std::integral_constant<int, I>{}, kt + I), ...);
+    }(std::make_integer_sequence<int, NS>{});
   }
   }
   // The last steps prefetched stages past K (never consumed); drain them before the epilogue reuses LDS.
