@@ -594,8 +594,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
       (dma_slot_ab(std::integral_constant<int, J>{}, (kt0 + 1) * BK, stage_buf(std::integral_constant<int, 1>{}),
                    bstage_buf(std::integral_constant<int, 1>{})), ...);
     }(std::make_integer_sequence<int, D>{});
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
+    ring_barrier_ab();  // the tiles of step kt0 have landed; those of step kt0 + 1 land by the end of step kt0
     // Grouped products: a group's last row tile often holds few rows.  When it holds at most BM / 2, the waves
     // of the lower half of the tile (wave rows WAVES_M / 2 ..) have no row to compute: they issue their share
     // of the loads and meet every barrier, but read no fragments and issue no MFMAs.  Waves w and w + 4 share
