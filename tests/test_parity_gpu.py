@@ -171,6 +171,32 @@ def test_split_schedule_integer_exact(M, N, K, plan, sampled):
     assert np.array_equal(bits(Yb)[rows], oracle.round_bf16(S + widen_bits(bb)[None, :]))
 
 
+# The split ring (both large forward tiles) with short K: a step count below one ring pass of 6, or one pass
+# and a step, and ragged last steps; the loads of steps past K in the prologue and the first steps must not
+# reach the sums.  Integer-valued inputs: bit-exact.
+@pytest.mark.parametrize("M,N,K,plan", [
+    (2048, 6144, 64, (256, 192, 0)),    # one step
+    (2048, 6144, 136, (256, 192, 0)),   # three steps, the last ragged
+    (4096, 4096, 192, (256, 256, 0)),   # three steps
+    (4096, 4096, 456, (256, 256, 0)),   # a whole pass and two steps, the last ragged
+])
+def test_split_ring_short_k_integer_exact(M, N, K, plan):
+    say("split ring short K", M, N, K)
+    assert mtp.mtp_gemm_plan(M, N, K) == plan
+    Xb, Wb = synth.ternary_bf16(281, M, K), synth.ternary_bf16(282, N, K)
+    bb = synth.ternary_bf16(283, 1, N)[0]
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    mtp.mtp_column_linear(to_dev(Xb), to_dev(Wb), to_dev(bb), Y, workspace=WS)
+    Yacc = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    mtp.mtp_row_linear_partial(to_dev(Xb), to_dev(Wb), Yacc, workspace=WS)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 64, 284)
+    P = oracle.row_parallel_partials([np.ascontiguousarray(Xb[rows])], Wb, 1)
+    S = oracle.row_parallel_sum(P)
+    assert np.array_equal(Yacc.cpu().numpy()[rows].astype(np.float64), S)
+    assert np.array_equal(bits(Y)[rows], oracle.round_bf16(S + widen_bits(bb)[None, :]))
+
+
 @pytest.mark.parametrize("M,F,K,plan", [(300, 200, 2048, (256, 64, 4)), (400, 4100, 7000, (256, 128, 3)),
                                          (900, 8200, 2048, (256, 128, 3))])  # (the last one hybrid)
 def test_split_schedule_swiglu(M, F, K, plan):
