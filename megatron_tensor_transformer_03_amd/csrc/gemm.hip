@@ -45,8 +45,8 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k
                    bool f8) {
   struct Opt { int bm, bn; double eff; int id; int ns_bk; int64_t slot_bytes; int pad_k; };
   // Relative efficiencies per output, against the 256 x 256 tile.  The forward products run both large
-  // tiles with a 64-deep K step in two stages, where the 256 x 192 tile measured 0.80-0.86 at the workload
-  // shapes.  (Its 32-deep four-stage form, used by the backward products, ranged from 0.6 to 1.1 of the
+  // tiles with a 64-deep K step (two stages then, where the 256 x 192 tile measured 0.80-0.86 at the
+  // workload shapes; both run the split ring now).  (Its 32-deep four-stage form, used by the backward products, ranged from 0.6 to 1.1 of the
   // 256 x 256 tile's rate depending on the board; the backward figures were measured on the transposed
   // forms.)
   const double wide_eff = row_major_k ? 0.95 : 0.85;

@@ -57,7 +57,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int NS_, bool EARLY_, int NSB_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BK = BK_, NS = NS_;
-  // Split ring (NSB = NS + 1, two-stage forms without EARLY): the B operand's tiles get a ring of NSB stages of
+  // Split ring (NSB = NS + 1 with NS = 2, without EARLY): the B operand's tiles get a ring of NSB stages of
   // their own, the A operand's keep NS, where the LDS cannot hold NS + 1 stages of both (256 x 192: 3 x 56 KB
   // does not fit, 2 x 32 + 3 x 24 KB does).  Each B tile is loaded two steps ahead of its use, and so is each
   // A tile, into its own stage right after a barrier inside the step that reads it (see step_spread_ab).
@@ -1126,8 +1126,8 @@ static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStrea
     tiles = (int64_t)((p.M + C::BM - 1) / C::BM) * tiles_n;
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  // KFULL: no chunk of a K step lies past K.  The two-stage and EARLY rings also pad the step count to a
-  // multiple of their ring with zero steps, which must read as zero; the split ring runs no step past K.
+  // KFULL: no chunk of a K step lies past K.  The 32-deep rings also pad the step count to a multiple of
+  // their ring with zero steps, which must read as zero; the split ring runs no step past K.
   const bool kfull = C::AB ? p.K % C::BK == 0 : p.K % (C::BK * C::RING) == 0;
   if constexpr (!GROUPED) {
     if (split_groups > 0 && split_chunks > 1) {
