@@ -266,7 +266,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   // compile-time choice) and has no branches, so the compiler's wait counts stay exact.  With KFULL the
   // step count is a multiple of NS and every chunk is in range; otherwise chunks at or past K read as zero,
   // so padding steps multiply zeros.  (The split ring's loop covers RING = 6 steps; the split schedule counts
-  // in such passes, KTS rounds up to one, and the loop stops after step KT - 1.)
+  // in such passes and KTS rounds up to one; the steps of a last partial pass run after the loop, each behind
+  // a uniform branch, and none past step KT - 1.)
   const int KT = (p.K + BK - 1) / BK;
   constexpr int RING = C::RING;
   const int KTS = (KT + RING - 1) / RING * RING;
