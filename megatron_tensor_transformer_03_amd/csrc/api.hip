@@ -152,7 +152,7 @@ mtp_status mtp_fp8_gemm_plan(int64_t M, int64_t N, int64_t K, mtp_act act, int* 
   TRY(check_device());
   // (the E4M3 kernels count K in pairs of codes and have no 128 x 128 tile with a 64-deep step)
   const mtp::GemmPlan pl = mtp::gemm_plan(act == MTP_ACT_SWIGLU ? mtp::MODE_SWIGLU : mtp::MODE_COL, M,
-                                          act == MTP_ACT_SWIGLU ? N / 2 : N, K / 2, 0, false, SIZE_MAX, true);
+                                          act == MTP_ACT_SWIGLU ? N / 2 : N, K / 2, 0, false, SIZE_MAX);
   *tile_m = pl.bm;
   *tile_n = pl.bn;
   *split_k = pl.split_groups > 0 ? pl.split_chunks : 0;

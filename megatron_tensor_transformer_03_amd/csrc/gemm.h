@@ -78,9 +78,9 @@ struct GemmPlan {
 };
 // row_major_k: 0 both operands K-contiguous; 1 B row-major-K (dgrad); 2 both row-major-K (wgrad).  Only
 // schedules whose workspace fits in ws_avail bytes are considered (one tile per workgroup needs none).
-// f8: the E4M3 products (32-deep tiles throughout; K counts pairs of codes).
+// The E4M3 products plan with K counted in pairs of codes and allow_small = false.
 GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k = 0, bool allow_small = true,
-                   size_t ws_avail = SIZE_MAX, bool f8 = false);
+                   size_t ws_avail = SIZE_MAX);
 
 enum GemmEpilogue { EPI_PLAIN = 0, EPI_NORM = 1, EPI_BDA = 2 };
 hipError_t gemm(const GemmParams& p, int mode, hipStream_t st, int epi = EPI_PLAIN);

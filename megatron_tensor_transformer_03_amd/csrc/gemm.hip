@@ -41,8 +41,7 @@ int cu_count() {
 // tiles split.  R and BW were fitted to the measured times of these schedules at the workloads' shapes
 // (within ~10%).  A split schedule needs a workspace (the tiles' arrival counters, then the split tiles'
 // partial slots); only schedules whose workspace fits in ws_avail are considered.
-GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k, bool allow_small, size_t ws_avail,
-                   bool f8) {
+GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k, bool allow_small, size_t ws_avail) {
   struct Opt { int bm, bn; double eff; int id; int ns_bk; int64_t slot_bytes; int pad_k; };
   // Relative efficiencies per output, against the 256 x 256 tile.  The forward products run both large
   // tiles with a 64-deep K step (two stages then, where the 256 x 192 tile measured 0.80-0.86 at the
@@ -54,7 +53,7 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k
   // ns_bk: K per ring pass (the split schedule's unit); pad_k: the granularity the step count is padded to
   // with zero steps, charged to the tile's time below.  The forward bf16 256 x 256 and 256 x 192 tiles run the
   // split ring: passes of 6 K steps, and no step past K.
-  const bool sr = !row_major_k && !f8;
+  const bool sr = !row_major_k;
   const int sr_k = sr ? 384 : 128, sr_pad = sr ? 64 : 128;
   const Opt opts[] = {{256, 256, 1.00, 0, sr_k, 256 << 10, sr_pad}, {256, 192, wide_eff, 1, sr_k, 192 << 10, sr_pad},
                       {256, 128, half_eff, 2, 128, 128 << 10, 128}, {128, 128, 0.72, 3, 256, 0, 256},

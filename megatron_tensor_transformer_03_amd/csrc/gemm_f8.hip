@@ -10,14 +10,15 @@ namespace mtp {
 
 template <int MODE>
 static hipError_t dispatch_f8(const GemmParams& p, hipStream_t st) {
-  const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K, 0, false, p.ws ? p.ws_bytes : 0, true);
+  const GemmPlan pl = gemm_plan(MODE, p.M, p.Nout, p.K, 0, false, p.ws ? p.ws_bytes : 0);
   switch (pl.id) {
     case 0:
-      return launch_cfg<BigTile, MODE, false, false, false, EPI_PLAIN, true>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+      return launch_cfg<BigFwdTile, MODE, false, false, false, EPI_PLAIN, true>(p, 0, st, pl.split_groups, pl.split_chunks,
+                                                                                pl.dp_tiles, pl.share);
     case 1:
       if constexpr (MODE != MODE_SWIGLU)
-        return launch_cfg<WideTile, MODE, false, false, false, EPI_PLAIN, true>(p, 0, st, pl.split_groups,
-                                                                                pl.split_chunks, pl.dp_tiles);
+        return launch_cfg<WideFwdTile, MODE, false, false, false, EPI_PLAIN, true>(p, 0, st, pl.split_groups,
+                                                                                   pl.split_chunks, pl.dp_tiles, pl.share);
       return hipErrorInvalidValue;
     default:
       return launch_cfg<HalfTile, MODE, false, false, false, EPI_PLAIN, true>(p, 0, st, pl.split_groups,

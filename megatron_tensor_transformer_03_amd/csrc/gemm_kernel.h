@@ -212,7 +212,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
                 "norm epilogue on column products, bias-dropout-add on row products");
   // E4M3 operands: the same bytes per LDS row (BK = 32 two-byte units = 64 one-byte codes), one
   // 32 x 32 x 64 MFMA per K step instead of two 32 x 32 x 16 ones
-  static_assert(!F8 || (BK == 32 && !AT && !BT && !GROUPED && EPI == EPI_PLAIN), "E4M3: plain K-major tiles");
+  static_assert(!F8 || ((BK == 32 || C::AB) && !AT && !BT && !GROUPED && EPI == EPI_PLAIN), "E4M3: plain K-major tiles");
   constexpr int NB_OUT = MODE == MODE_SWIGLU ? BN / 2 : BN;  // output columns per tile
 
   // one LDS variable per stage (see the design notes); unused ones are a token 16 bytes.  In the split ring
@@ -416,12 +416,13 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     }
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // E4M3 fragment: lane holds row (lane & 31) and the 32 codes of 16-byte chunks 2 (lane / 32) and
-  // 2 (lane / 32) + 1 of the 64-code K step.  Both operands use the same k assignment, so the MFMA's sum
-  // over k is the product's whatever order the hardware pairs the codes in.
-  auto read_f8 = [&](const uint16_t* s, int row) -> i32x8 {
-    const bf16x8 lo = *reinterpret_cast<const bf16x8*>(s + swz<C>(row, 2 * fk));
-    const bf16x8 hi = *reinterpret_cast<const bf16x8*>(s + swz<C>(row, 2 * fk + 1));
+  // E4M3 fragment of MFMA k step ks: lane holds row (lane & 31) and the 32 codes of 16-byte chunks
+  // 4 ks + 2 (lane / 32) and 4 ks + 2 (lane / 32) + 1 (a 64-code MFMA step per 4 chunks of the LDS row).  Both
+  // operands use the same k assignment, so the MFMA's sum over k is the product's whatever order the hardware
+  // pairs the codes in.
+  auto read_f8 = [&](const uint16_t* s, int row, int ks) -> i32x8 {
+    const bf16x8 lo = *reinterpret_cast<const bf16x8*>(s + swz<C>(row, 4 * ks + 2 * fk));
+    const bf16x8 hi = *reinterpret_cast<const bf16x8*>(s + swz<C>(row, 4 * ks + 2 * fk + 1));
     return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13,
                                                              14, 15));
   };
@@ -429,9 +430,9 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     constexpr int q = decltype(SET)::value;
     if constexpr (F8) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa[q][i] = read_f8(sA, wm0 + 32 * i + fr);
+      for (int i = 0; i < FM; ++i) fa[q][i] = read_f8(sA, wm0 + 32 * i + fr, ks);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[q][j] = read_f8(sB, wn0 + 32 * j + fr);
+      for (int j = 0; j < FN; ++j) fb[q][j] = read_f8(sB, wn0 + 32 * j + fr, ks);
     } else {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -457,7 +458,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
         else
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[q][j], fa[q][i], acc[i][j], 0, 0, 0);
   };
-  constexpr int KS = F8 ? 1 : BK / 16;  // MFMA k steps per K step
+  constexpr int KS = F8 ? BK / 32 : BK / 16;  // MFMA k steps per K step (32 x 32 x 64 codes, 32 x 32 x 16 bf16)
   static_assert(!C::EARLY || (NS * KS) % 2 == 0, "fragment sets alternate consistently across the ring");
   // vmcnt(n): wait until at most n of this wave's DMA instructions are outstanding (expcnt, lgkmcnt free).
   // The barrier ending step kt makes stage kt + LEAD visible: the DMAs newer than that stage may stay out.
@@ -567,7 +568,10 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
         [&]<int... MI>(std::integer_sequence<int, MI...>) {
           ([&] {
             constexpr int mi = MI, gm = ks * NM + mi, a = mi / FN, b = mi % FN;
-            if constexpr (!F8)
+            if constexpr (F8)
+              acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[ks & 1][b], fa[ks & 1][a], acc[a][b], 0, 0, 0,
+                                                                         0, 0, 0);
+            else
               acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][b], fa[ks & 1][a], acc[a][b], 0, 0, 0);
             if constexpr (!last && gm % 2 == 1 && gm / 2 < JB)
               dma_slot_ab(std::integral_constant<int, JA + gm / 2>{}, k2, curA, nxtB);
@@ -579,7 +583,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
           ([&] {
             constexpr int mi = MI, gm = ks * NM + mi;
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if constexpr (mi < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if constexpr (mi < NR) __builtin_amdgcn_sched_group_barrier(0x100, F8 ? 2 : 1, 0);  // one fragment's reads
             if constexpr ((!last && gm % 2 == 1 && gm / 2 < JB) || (last && mi < JA))
               __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
           }(), ...);
