@@ -43,19 +43,15 @@ int cu_count() {
 // partial slots); only schedules whose workspace fits in ws_avail are considered.
 GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k, bool allow_small, size_t ws_avail) {
   struct Opt { int bm, bn; double eff; int id; int ns_bk; int64_t slot_bytes; int pad_k; };
-  // Relative efficiencies per output, against the 256 x 256 tile.  The forward products run both large
-  // tiles with a 64-deep K step (two stages then, where the 256 x 192 tile measured 0.80-0.86 at the
-  // workload shapes; both run the split ring now).  (Its 32-deep four-stage form, used by the backward products, ranged from 0.6 to 1.1 of the
-  // 256 x 256 tile's rate depending on the board; the backward figures were measured on the transposed
-  // forms.)
+  // Relative efficiencies per output, against the 256 x 256 tile: the 256 x 192 tile measured 0.80-0.86 at
+  // the forward workload shapes (both in two 64-deep stages then; both run the split ring now), and its
+  // 32-deep four-stage form 0.6-1.1 on the transposed (backward) forms depending on the board.
   const double wide_eff = row_major_k ? 0.95 : 0.85;
   const double half_eff = row_major_k ? 0.85 : 0.75;
   // ns_bk: K per ring pass (the split schedule's unit); pad_k: the granularity the step count is padded to
-  // with zero steps, charged to the tile's time below.  The forward bf16 256 x 256 and 256 x 192 tiles run the
-  // split ring: passes of 6 K steps, and no step past K.
-  const bool sr = !row_major_k;
-  const int sr_k = sr ? 384 : 128, sr_pad = sr ? 64 : 128;
-  const Opt opts[] = {{256, 256, 1.00, 0, sr_k, 256 << 10, sr_pad}, {256, 192, wide_eff, 1, sr_k, 192 << 10, sr_pad},
+  // with zero steps, charged to the tile's time below.  The 256 x 256 and 256 x 192 tiles run the split ring
+  // (passes of 6 K steps, no step past K) in every form.
+  const Opt opts[] = {{256, 256, 1.00, 0, 384, 256 << 10, 64}, {256, 192, wide_eff, 1, 384, 192 << 10, 64},
                       {256, 128, half_eff, 2, 128, 128 << 10, 128}, {128, 128, 0.72, 3, 256, 0, 256},
                       {128, 128, 0.72, 4, 128, 64 << 10, 128}};
   constexpr double kR = 5.5e12 * 1e-6;   // FLOP per microsecond of one CU
@@ -108,11 +104,11 @@ GemmPlan gemm_plan(int mode, int64_t M, int64_t Nout, int64_t K, int row_major_k
         }
       }
     }
-    // shared tails (the forward split-ring tiles, fewer tiles than CUs, both spread evenly over the 8 XCDs):
+    // shared tails (the forward 256 x 192 tile, fewer tiles than CUs, both spread evenly over the 8 XCDs):
     // tiles / cus of each tile's K in a workgroup of its own, the rest of `share` tiles in one more; the time is
     // that share of a tile plus a fill, plus one partial tile per tile written and read back
     const int64_t extra = cus - tiles;
-    if (fwd && sr && o.id == 1 && extra > 0 && tiles % 8 == 0 && extra % 8 == 0 &&
+    if (fwd && o.id == 1 && extra > 0 && tiles % 8 == 0 && extra % 8 == 0 &&
         (tiles / 8) % (extra / 8) == 0 && passes >= 2) {
       const int share = (int)(tiles / extra);
       const size_t ws = kSplitCounterBytes + (size_t)(tiles * 2 * o.slot_bytes);

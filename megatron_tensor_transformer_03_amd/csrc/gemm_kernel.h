@@ -203,8 +203,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, CPR = C::CPR, RPL = C::RPL;
   constexpr int D = C::D, GA = C::GA, ROWS_PER_DMA = C::ROWS_PER_DMA;
   static_assert(MODE != MODE_SWIGLU || TN % 64 == 0, "gate/up fragment pairs");
-  static_assert(!(AT || BT) || (BK == 32 && !GROUPED && (MODE == MODE_COL || MODE == MODE_ROW)),
-                "row-major-K operands: K step 32, plain column/row epilogues");
+  static_assert(!(AT || BT) || ((BK == 32 || C::AB) && !GROUPED && (MODE == MODE_COL || MODE == MODE_ROW)),
+                "row-major-K operands: K step 32 or the split ring, plain column/row epilogues");
   static_assert(!AT || BM == 128 || BM == 256, "A rows of 256 or 512 bytes");
   static_assert(!BT || BN == 128 || BN == 192 || BN == 256, "B rows of 256, 384 or 512 bytes");
   static_assert(EPI == EPI_PLAIN || (!GROUPED && (EPI == EPI_NORM ? (MODE == MODE_COL || MODE == MODE_SWIGLU)
@@ -539,7 +539,9 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   auto dma_slot_ab = [&](auto J, int k0, uint16_t* sA, uint16_t* sB) {
     constexpr int j = decltype(J)::value;
     constexpr bool is_a = j < JA;
-    const int soff = k0 < p.K ? 2 * k0 : 0;
+    // the K position: a column offset for K-major operands, a row offset for row-major-K ones
+    constexpr bool tr = is_a ? AT : BT;
+    const int soff = k0 < p.K ? (tr ? 2 * k0 * (int)(is_a ? p.lda : p.ldb) : 2 * k0) : 0;
     const int g = j * NWAVES + wave_u;  // uniform
     uint32_t vo = d_off[j];
     if constexpr (!KFULL) vo = k0 + d_kc[j] < p.K ? vo : kOOB;
@@ -1206,41 +1208,32 @@ static hipError_t launch_cfg(const GemmParams& p0, int grid_rows_upper, hipStrea
   return hipGetLastError();
 }
 
-#ifndef MTP_BIG_CFG
-#define MTP_BIG_CFG 256, 256, 4, 2, 32, 4, true
-#endif
-#ifndef MTP_WIDE_CFG
-#define MTP_WIDE_CFG 256, 192, 4, 2, 32, 4, true
-#endif
 #ifndef MTP_HALF_CFG
 #define MTP_HALF_CFG 256, 128, 4, 2, 32, 4, true
 #endif
 #ifndef MTP_SMALL_CFG
 #define MTP_SMALL_CFG 128, 128, 4, 2, 64, 4, true
 #endif
-// (8 waves of 64 x 128: against 128 x 64 wave tiles, 1.25-1.45x faster on some MI355X boards and even on
-// the others, in every mode, at every workload shape; outputs bitwise equal)
-using BigTile = Cfg<MTP_BIG_CFG>;              // 8 waves (wave tile 64 x 128), 128 KB LDS ring
-// The bf16 forward products (plain and grouped, K-major operands) take the same tile with a 64-deep K step in
-// the split ring (A tiles in two stages, B tiles in three: 2 x 32 + 3 x 32 KB, the whole LDS), each stage
-// reloaded two steps ahead (step_spread_ab): 128-byte rows per DMA instead of 64.  The row-major-K (backward)
-// and E4M3 forms keep the 32-deep ring their layouts are built on.  Against the plain two-stage 64-deep ring
-// (both operands reloaded one step ahead) at the 70B-shard shapes: the layer step 828 -> 785 us cold (fc1
-// 457 -> 427, QKV 142 -> 127), 8192^3 852 -> 830 us; with both operands cached 0-8% slower (70B fc2 shape
-// 193 -> 208 us), and at K = 1024 (345M fc1) 1-7% slower.  The split-K forms spill some registers outside
-// the main loop (bias, norm and split epilogue state).
+// The large tiles run the split ring with a 64-deep K step (A tiles in two stages, B tiles in three), each
+// stage reloaded two steps ahead (step_spread_ab), in every form: bf16 forward (plain and grouped), E4M3
+// (K counted in pairs of codes) and backward (row-major-K operands).  256 x 256: 8 waves of 64 x 128 (against
+// 128 x 64 wave tiles 1.25-1.45x faster on some MI355X boards and even on the others, outputs bitwise equal),
+// 2 x 32 + 3 x 32 KB, the whole LDS.  Against the plain two-stage 64-deep ring (both operands reloaded one step
+// ahead) at the 70B-shard shapes: the layer step 828 -> 785 us cold (fc1 457 -> 427, QKV 142 -> 127), 8192^3
+// 852 -> 830 us; with both operands cached 0-8% slower, at K = 1024 (345M fc1) 1-7%.  Against the 32-deep
+// four-stage ring (128-byte rows per DMA instead of 64): the E4M3 175B-shard linears 11-12% faster, the
+// backward dgrad 9-21% and wgrad 2-5%.  The split-K forms spill some registers outside the main loop (bias,
+// norm and split epilogue state).  The grouped (MoE) products run 2781 against 2944 us on it (before the A
+// stages were reloaded early) where every expert's weights stream from HBM.
 using BigFwdTile = Cfg<256, 256, 4, 2, 64, 2, false, 3>;  // 8 waves (64 x 128), split ring, 160 KB
-// The grouped (MoE) products take it too: at the MoE workload's shapes, where every expert's weights stream
-// from HBM, the expert MLP ran 2781 against 2944 us (5.5%) on it, before the A stages were reloaded early.
 using GroupedTile = BigFwdTile;
-// Likewise the 256 x 192 tile, in the split ring (2 x 32 + 3 x 24 KB): against the plain two-stage ring at
-// the 175B-shard shapes, 3-6% faster with the weight cached and 8-14% with it streaming from HBM (QKV
-// 236.7 -> 204.4 us, fc1 267.0 -> 234.5, fc2 270.5 -> 244.8); reloading the A stages early then took the cold
-// shapes a further 9-16% (QKV 258 -> 221 us, fc1 299 -> 252, fc2 290 -> 264).  It beats the 256 x 256 tile
-// where its tile count fills whole waves.
+// Likewise the 256 x 192 tile (2 x 32 + 3 x 24 KB): against the plain two-stage ring at the 175B-shard shapes,
+// 3-6% faster with the weight cached and 8-14% with it streaming from HBM (QKV 236.7 -> 204.4 us, fc1 267.0 ->
+// 234.5, fc2 270.5 -> 244.8); reloading the A stages early then took the cold shapes a further 9-16% (QKV
+// 258 -> 221 us, fc1 299 -> 252, fc2 290 -> 264).  It beats the 256 x 256 tile where its tile count fills
+// whole waves.
 using WideFwdTile = Cfg<256, 192, 4, 2, 64, 2, false, 3>;  // 8 waves (64 x 96), split ring, 136 KB
-using WideTile = Cfg<MTP_WIDE_CFG>;            // 8 waves (64 x 96), 112 KB
-using HalfTile = Cfg<MTP_HALF_CFG>;            // 8 waves (64 x 64), 96 KB
+using HalfTile = Cfg<MTP_HALF_CFG>;            // 8 waves (64 x 64), 32-deep four-stage ring, 96 KB
 using SmallTile = Cfg<MTP_SMALL_CFG>;          // 8 waves (32 x 64), 128 KB
 using SmallTTile = Cfg<128, 128, 4, 2, 32, 4, true>;  // row-major-K operands: 8 waves (32 x 64), 64 KB
 
@@ -1267,9 +1260,9 @@ static hipError_t dispatch_fwd(const GemmParams& p, hipStream_t st) {
 template <bool AT, bool BT>
 static hipError_t dispatch_bwd(const GemmParams& p, hipStream_t st) {
   const GemmPlan pl = gemm_plan(MODE_ROW, p.M, p.Nout, p.K, AT ? 2 : 1, true, p.ws ? p.ws_bytes : 0);
-  if (pl.id == 0) return launch_cfg<BigTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+  if (pl.id == 0) return launch_cfg<BigFwdTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
   if (pl.id == 4) return launch_cfg<SmallTTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
-  if (pl.id == 1) return launch_cfg<WideTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
+  if (pl.id == 1) return launch_cfg<WideFwdTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
   return launch_cfg<HalfTile, MODE_ROW, false, AT, BT>(p, 0, st, pl.split_groups, pl.split_chunks, pl.dp_tiles);
 }
 
