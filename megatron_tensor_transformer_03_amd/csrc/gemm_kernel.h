@@ -681,35 +681,53 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
       const __amdgpu_buffer_rsrc_t ws = make_rsrc(p.sk_ws, (int64_t)p.sk_slot_tiles * S * slot_bytes);
       typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
       const int mine = (int)(slot_of(sk_which_chunk, sk_wtile) * slot_bytes) + 16 * tid;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ws,
-                                                   mine + ((i * FN + j) * 4 + q) * C::NT * 16, 0, kSc1);
-          }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's slot stores have completed
-      __syncthreads();
       // (the split ring of the 256 x 256 tile fills the LDS exactly: its flag is the first word of the last
       // B stage, free once the main loop has drained; every wave reads it before any can go on to overwrite
       // it with epilogue staging)
       int* const flag = C::AB ? reinterpret_cast<int*>(ldsb2) : &sk_flag;
-      if (tid == 0)
-        *flag = __hip_atomic_fetch_add(p.sk_cnt + sk_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                sk_last - sk_first;
-      __syncthreads();
-      const bool last = *flag != 0;
-      __syncthreads();
-      if (!last) return;
+      // A tile of two pieces whose other piece has already counted in: this one is last, and its partial
+      // stays in registers (no store, no count, no reload).  The other piece counted in only once its slot
+      // stores had completed, as below.
+      bool early = false;
+      if (sk_last - sk_first == 1) {
+        if (tid == 0)
+          *flag = __hip_atomic_load(p.sk_cnt + sk_tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1;
+        __syncthreads();
+        early = *flag != 0;
+        __syncthreads();
+      }
+      if (!early) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                           acc[i][j][4 * q + 3]);
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ws,
+                                                     mine + ((i * FN + j) * 4 + q) * C::NT * 16, 0, kSc1);
+            }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's slot stores have completed
+        __syncthreads();
+        if (tid == 0)
+          *flag = __hip_atomic_fetch_add(p.sk_cnt + sk_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  sk_last - sk_first;
+        __syncthreads();
+        const bool last = *flag != 0;
+        __syncthreads();
+        if (!last) return;
+      }
       if (tid == 0) __hip_atomic_store(p.sk_cnt + sk_tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       // The S slots are added in chunk order, in batches of up to 16 float4 per thread (half the partial tile
       // at most, so the batch's registers fit beside the accumulators): all loads of one slot's batch are
-      // issued together and then added, so the reduction waits for 2 S memory round trips, not one per
-      // fragment and slot.  Element e of a thread's slot is fragment e / 4 (i * FN + j), quarter e % 4.
+      // issued together and then added, so the reduction waits for 2 memory round trips per slot read, not
+      // one per fragment and slot.  This piece's own partial is still in the accumulators: when it is the
+      // first or second chunk of the tile it is used from there (a + b = b + a exactly, so the sums are those
+      // of the plain chunk-order reduction); otherwise the first chunk's slot replaces it and its own slot is
+      // read back in turn.  Element e of a thread's slot is fragment e / 4 (i * FN + j), quarter e % 4.
       constexpr int NE = FM * FN * 4, NB = 16, NBATCH = (NE + NB - 1) / NB;
+      const int me = sk_which_chunk;
       auto load_batch = [&](int c, int bb, float4* v) {
         const int sc = (int)(slot_of(c, sk_wtile) * slot_bytes) + 16 * tid;
 #pragma unroll
@@ -718,30 +736,35 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
             v[e] = __builtin_bit_cast(
                 float4, __builtin_amdgcn_raw_buffer_load_b128(ws, sc + (NB * bb + e) * C::NT * 16, 0, kSc1));
       };
-#pragma unroll
-      for (int bb = 0; bb < NBATCH; ++bb) {
-        float4 v[NB];
-        load_batch(sk_first, bb, v);
+      auto add_batch = [&](int bb, const float4* v, bool assign) {
 #pragma unroll
         for (int e = 0; e < NB; ++e) {
           const int ee = NB * bb + e;
           if (ee < NE) {
             const int i = ee / (FN * 4), j = (ee / 4) % FN, q = ee % 4;
-            acc[i][j][4 * q] = v[e].x; acc[i][j][4 * q + 1] = v[e].y;
-            acc[i][j][4 * q + 2] = v[e].z; acc[i][j][4 * q + 3] = v[e].w;
-          }
-        }
-        for (int c = sk_first + 1; c <= sk_last; ++c) {
-          load_batch(c, bb, v);
-#pragma unroll
-          for (int e = 0; e < NB; ++e) {
-            const int ee = NB * bb + e;
-            if (ee < NE) {
-              const int i = ee / (FN * 4), j = (ee / 4) % FN, q = ee % 4;
-              acc[i][j][4 * q] += v[e].x; acc[i][j][4 * q + 1] += v[e].y;
-              acc[i][j][4 * q + 2] += v[e].z; acc[i][j][4 * q + 3] += v[e].w;
+            if (assign) {
+              acc[i][j][4 * q] = v[e].x; acc[i][j][4 * q + 1] = v[e].y;
+              acc[i][j][4 * q + 2] = v[e].z; acc[i][j][4 * q + 3] = v[e].w;
+            } else {
+              acc[i][j][4 * q] = v[e].x + acc[i][j][4 * q]; acc[i][j][4 * q + 1] = v[e].y + acc[i][j][4 * q + 1];
+              acc[i][j][4 * q + 2] = v[e].z + acc[i][j][4 * q + 2];
+              acc[i][j][4 * q + 3] = v[e].w + acc[i][j][4 * q + 3];
             }
           }
+        }
+      };
+      const bool own_in_acc = me <= sk_first + 1;
+#pragma unroll
+      for (int bb = 0; bb < NBATCH; ++bb) {
+        float4 v[NB];
+        if (me != sk_first) {  // the first chunk's slot: added to this piece's (second) partial, or in its place
+          load_batch(sk_first, bb, v);
+          add_batch(bb, v, !own_in_acc);
+        }
+        for (int c = sk_first + 1; c <= sk_last; ++c) {
+          if (own_in_acc && c == me) continue;
+          load_batch(c, bb, v);
+          add_batch(bb, v, false);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
