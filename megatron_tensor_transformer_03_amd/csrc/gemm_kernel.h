@@ -520,8 +520,18 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   // consumed in step kt - 1), enough for an activation read from HBM rather than from cache.  At the end of
   // step kt everything issued in step kt - 1 (the tiles of step kt + 1) has landed, while the D loads of step
   // kt may stay in flight (loads complete in issue order).  The MFMA order per accumulator is unchanged.
+  // One barrier per step (ONEBAR): the mid-step barrier also waits for the tiles of step kt + 1 (everything
+  // older than this step's B slots, vmcnt(JB)); no wave then reads A stage kt % 2 or B stage kt % 3 again, and
+  // step kt + 1's stages are visible, so the end-of-step barrier has nothing left to order: it goes, and the
+  // fragments of step kt + 1's first k step are read during the MFMAs of step kt's last one.  The A tile then
+  // has about one step to land instead of ~1.25, which the 256 x 256 tile's longer step covers; with the
+  // 256 x 192 tile (three quarters of the MFMA time per step) and with split-K pieces the loads arriving later
+  // cost more than the barrier, cold.
+  constexpr bool ONEBAR = C::AB && C::BM == 256 && C::BN == 256 && !SPLIT;
   constexpr int JA = C::AB ? GA / NWAVES : D, JB = D - JA;
   constexpr int kWaitAB = 0x0F70 | (D & 15) | ((D >> 4) << 14);  // vmcnt(D)
+  // lgkmcnt(0), and with ONEBAR vmcnt(JB)
+  constexpr int kWaitMid = ONEBAR ? 0x0070 | (JB & 15) | ((JB >> 4) << 14) : 0xC07F;
   auto ring_barrier_ab = [&]() {
     __builtin_amdgcn_s_waitcnt(kWaitAB);
     asm volatile("" ::: "memory");
@@ -530,7 +540,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   };
   auto mid_barrier_ab = [&]() {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's fragment reads have returned
+    __builtin_amdgcn_s_waitcnt(kWaitMid);  // lgkmcnt(0): this wave's fragment reads have returned
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -550,7 +560,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
   };
   // One K step of the split ring on A stage IA and B stage IB.  Issue order: an MFMA, then (while this k
   // step's reads remain) one fragment read, then (after odd MFMAs of the first k steps) one B slot; in the last
-  // k step, after the mid-step barrier, one A slot after each of its first MFMAs.
+  // k step, after the mid-step barrier, one A slot after each of its first MFMAs (and with ONEBAR one of the
+  // next step's first fragment reads after each of its MFMAs).
   auto step_spread_ab = [&](auto IA, auto IB, int kt) {
     constexpr int ia = decltype(IA)::value, ib = decltype(IB)::value;
     uint16_t* curA = stage_buf(std::integral_constant<int, ia>{});
@@ -560,13 +571,17 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
     constexpr int NM = FM * FN;
     static_assert(C::NSB == 3, "the B tile of step kt + 2 goes to the stage consumed in step kt - 1");
     static_assert(2 * JB <= (KS - 1) * NM && JA <= NM, "every DMA slot finds an MFMA");
-    read_frags2(curA, curB, 0, std::integral_constant<int, 0>{});
+    static_assert(!ONEBAR || KS % 2 == 0, "the last k step uses fragment set 1, the next step's first one set 0");
+    if constexpr (!ONEBAR) read_frags2(curA, curB, 0, std::integral_constant<int, 0>{});
     [&]<int... S>(std::integer_sequence<int, S...>) {
       ([&] {
         constexpr int ks = S;
         constexpr bool last = ks + 1 == KS;
         if constexpr (!last) read_frags2(curA, curB, ks + 1, std::integral_constant<int, (ks + 1) & 1>{});
         if constexpr (last) mid_barrier_ab();
+        if constexpr (last && ONEBAR)
+          read_frags2(stage_buf(std::integral_constant<int, (ia + 1) % NS>{}),
+                      bstage_buf(std::integral_constant<int, (ib + 1) % C::NSB>{}), 0, std::integral_constant<int, 0>{});
         [&]<int... MI>(std::integer_sequence<int, MI...>) {
           ([&] {
             constexpr int mi = MI, gm = ks * NM + mi, a = mi / FN, b = mi % FN;
@@ -580,7 +595,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
             if constexpr (last && mi < JA) dma_slot_ab(std::integral_constant<int, mi>{}, k2, curA, nxtB);
           }(), ...);
         }(std::make_integer_sequence<int, NM>{});
-        constexpr int NR = last ? 0 : FM + FN;
+        constexpr int NR = last && !ONEBAR ? 0 : FM + FN;
         [&]<int... MI>(std::integer_sequence<int, MI...>) {
           ([&] {
             constexpr int mi = MI, gm = ks * NM + mi;
@@ -593,7 +608,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
         __builtin_amdgcn_sched_barrier(0);
       }(), ...);
     }(std::make_integer_sequence<int, KS>{});
-    ring_barrier_ab();
+    if constexpr (!ONEBAR) ring_barrier_ab();
   };
 
   if constexpr (SPLIT) __syncthreads();  // the previous tile's epilogue may still read the LDS stages
@@ -605,7 +620,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
       (dma_slot_ab(std::integral_constant<int, J>{}, (kt0 + 1) * BK, stage_buf(std::integral_constant<int, 1>{}),
                    bstage_buf(std::integral_constant<int, 1>{})), ...);
     }(std::make_integer_sequence<int, D>{});
-    ring_barrier_ab();  // the tiles of step kt0 have landed; those of step kt0 + 1 land by the end of step kt0
+    ring_barrier_ab();  // the tiles of step kt0 have landed; those of step kt0 + 1 land within step kt0
     // Grouped products: a group's last row tile often holds few rows.  When it holds at most BM / 2, the waves
     // of the lower half of the tile (wave rows WAVES_M / 2 ..) have no row to compute: they issue their share
     // of the loads and meet every barrier, but read no fragments and issue no MFMAs.  Waves w and w + 4 share
@@ -624,7 +639,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
       [&]<int... J>(std::integer_sequence<int, J...>) {
         (dma_slot_ab(std::integral_constant<int, J>{}, (kt + 2) * BK, curA, nxtB), ...);
       }(std::make_integer_sequence<int, JA>{});
-      ring_barrier_ab();
+      if constexpr (!ONEBAR) ring_barrier_ab();
     };
     // Whole ring passes in the loop, then the K steps left of a last partial pass one by one (the same
     // stages); steps past the last K step are not run.
@@ -646,7 +661,12 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmParams p_arg) {
       }
     };
     if (idle_half) run_ab(step_idle_ab);
-    else run_ab(step_spread_ab);
+    else {
+      if constexpr (ONEBAR)  // the first k step's fragments of step kt0 (the loop reads the others ahead)
+        read_frags2(stage_buf(std::integral_constant<int, 0>{}), bstage_buf(std::integral_constant<int, 0>{}), 0,
+                    std::integral_constant<int, 0>{});
+      run_ab(step_spread_ab);
+    }
   } else {
   [&]<int... I>(std::integer_sequence<int, I...>) {
     (dma_stage((kt0 + I) * BK, stage_buf(std::integral_constant<int, I>{})), ...);
