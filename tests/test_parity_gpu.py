@@ -173,11 +173,15 @@ def test_split_schedule_integer_exact(M, N, K, plan, sampled):
 
 # The split ring (both large forward tiles) with short K: a step count below one ring pass of 6, or one pass
 # and a step, and ragged last steps; the loads of steps past K in the prologue and the first steps must not
-# reach the sums.  Integer-valued inputs: bit-exact.
+# reach the sums.  The 256 x 256 tile runs one barrier per step (the next step's first fragments read across
+# it, also after the last step).  Integer-valued inputs: bit-exact.
 @pytest.mark.parametrize("M,N,K,plan", [
     (2048, 6144, 64, (256, 192, 0)),    # one step
     (2048, 6144, 136, (256, 192, 0)),   # three steps, the last ragged
+    (4096, 4096, 64, (256, 256, 0)),    # one step
+    (4096, 4096, 136, (256, 256, 0)),   # three steps, the last ragged
     (4096, 4096, 192, (256, 256, 0)),   # three steps
+    (4096, 4096, 392, (256, 256, 0)),   # a whole pass and a ragged step
     (4096, 4096, 456, (256, 256, 0)),   # a whole pass and two steps, the last ragged
 ])
 def test_split_ring_short_k_integer_exact(M, N, K, plan):
